@@ -1,0 +1,190 @@
+"""fp64 CPU oracle for Kimi Delta Attention (KDA).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import this package; the GPU library and its Python
+binding never do, and the two share no code.
+
+The oracle is the plain token-by-token recurrence (Kimi Linear paper notes,
+section 2, "KDA recurrence"), in IEEE double, on the exact input values the GPU
+receives:
+
+    S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+    o_t = S_t^T q_t,          alpha_t = exp(log_alpha_t)  (per key channel)
+
+It is implemented in plain C (``kda_oracle.c``) and called through ctypes.
+Every function here is argument marshalling only.  Pins that tie the oracle to
+the pages and to mathematics it does not itself use live in
+``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain -O2, OpenMP; no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class Oracle:
+    """ctypes handle on one build of the oracle library (the default build, or
+    a deliberately altered copy that a test compiles to check the pins)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        lib.oracle_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
+                                       i32, vp, vp, i32]
+        lib.oracle_prefill.restype = ctypes.c_int
+        lib.oracle_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                           vp, i32]
+        lib.oracle_decode_step.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = [ctypes.c_int]
+        lib.oracle_max_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def prefill(self, *args, **kwargs):
+        return _prefill(self.lib, *args, **kwargs)
+
+    def decode_step(self, *args, **kwargs):
+        return _decode_step(self.lib, *args, **kwargs)
+
+
+_default: Optional[Oracle] = None
+
+
+def _load():
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _default = Oracle(_LIB)
+    return _default.lib
+
+
+def compile_variant(source_text: str, out_path: str) -> Oracle:
+    """Compile a (test-altered) copy of the oracle source and load it."""
+    src = out_path[:-3] + ".c"
+    with open(src, "w") as f:
+        f.write(source_text)
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                           "-o", out_path, src, "-lm"])
+    return Oracle(out_path)
+
+
+def source() -> str:
+    with open(_SRC) as f:
+        return f.read()
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def max_threads(nthreads: Optional[int] = None) -> int:
+    return _load().oracle_max_threads(int(nthreads or default_threads()))
+
+
+def _qkv_dtype(x: np.ndarray) -> int:
+    if x.dtype == np.float32:
+        return F32
+    if x.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"q/k/v must be float32 or uint16 (bf16 bit patterns), got {x.dtype}")
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def prefill(*args, **kwargs) -> Tuple[np.ndarray, np.ndarray]:
+    """Token-by-token fp64 recurrence over a packed batch (see ``_prefill``)."""
+    return _prefill(_load(), *args, **kwargs)
+
+
+def decode_step(*args, **kwargs) -> np.ndarray:
+    """One recurrent token for every (sequence, head) (see ``_decode_step``)."""
+    return _decode_step(_load(), *args, **kwargs)
+
+
+def _prefill(lib, q: np.ndarray, k: np.ndarray, v: np.ndarray, log_alpha: np.ndarray,
+             beta: np.ndarray, initial_state: Optional[np.ndarray] = None,
+             cu_seqlens: Optional[np.ndarray] = None, num_seqs: Optional[int] = None,
+             nthreads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Token-by-token fp64 recurrence over a packed batch.
+
+    q, k: [T, H, dk]; v: [T, H, dv] -- float32, or uint16 holding bf16 bits.
+    log_alpha: [T, H, dk] float32; beta: [T, H] float32.
+    initial_state: [N, H, dk, dv] float32 or None (zeros).
+    cu_seqlens: [N+1] int32 offsets, or None for N equal rows (num_seqs, default 1).
+    Returns (o [T, H, dv] float64, final_state [N, H, dk, dv] float64).
+    """
+    dtype = _qkv_dtype(q)
+    assert k.dtype == q.dtype and v.dtype == q.dtype
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == (T, H, dk) and v.shape == (T, H, dv)
+    assert log_alpha.shape == (T, H, dk) and beta.shape == (T, H)
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        N = cu.shape[0] - 1
+    else:
+        cu = None
+        N = int(num_seqs or 1)
+    q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
+    la = np.ascontiguousarray(log_alpha, dtype=np.float32)
+    be = np.ascontiguousarray(beta, dtype=np.float32)
+    s0 = None
+    if initial_state is not None:
+        s0 = np.ascontiguousarray(initial_state, dtype=np.float32)
+        assert s0.shape == (N, H, dk, dv)
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    fin = np.zeros((N, H, dk, dv), dtype=np.float64)
+    rc = lib.oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(s0),
+                            _ptr(cu), T, N, H, dk, dv, dtype, _ptr(o), _ptr(fin),
+                            int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_prefill rejected its arguments")
+    return o, fin
+
+
+def _decode_step(lib, state: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                 log_alpha: np.ndarray, beta: np.ndarray,
+                 nthreads: Optional[int] = None) -> np.ndarray:
+    """One recurrent token for every (sequence, head); ``state`` (float64
+    [N, H, dk, dv], C-contiguous) is updated in place.  Returns o [N, H, dv]."""
+    assert state.dtype == np.float64 and state.flags.c_contiguous
+    dtype = _qkv_dtype(q)
+    N, H, dk, dv = state.shape
+    assert q.shape == (N, H, dk) and k.shape == (N, H, dk) and v.shape == (N, H, dv)
+    q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
+    la = np.ascontiguousarray(log_alpha, dtype=np.float32)
+    be = np.ascontiguousarray(beta, dtype=np.float32)
+    assert la.shape == (N, H, dk) and be.shape == (N, H)
+    o = np.zeros((N, H, dv), dtype=np.float64)
+    rc = lib.oracle_decode_step(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(la),
+                                _ptr(be), N, H, dk, dv, dtype, _ptr(o),
+                                int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_decode_step rejected its arguments")
+    return o

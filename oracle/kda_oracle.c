@@ -1,0 +1,211 @@
+/*
+ * kda_oracle.c -- fp64 CPU oracle for Kimi Delta Attention (KDA).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The GPU library
+ * never links, includes or calls it, and it shares no source with it.
+ *
+ * What it computes (Kimi Linear paper notes, section 2 "KDA recurrence"):
+ * per head, a fixed dk x dv state S is updated token by token as
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                       (read-out uses the updated state)
+ *
+ * with alpha_t a per-channel decay vector (one forget rate per key channel,
+ * the point of difference from Gated DeltaNet's single scalar per head).
+ * Here alpha_t = exp(log_alpha_t) and beta_t is taken as given (it is already
+ * a sigmoid output in the model).  The state starts at zero or from a supplied
+ * checkpoint (Kimi Linear per-token dataflow notes, "KDA layer inputs, state
+ * update and output"), and the chunk prefill and the fused recurrent decode
+ * compute this same function (paper notes, section 3).
+ *
+ * The product (I - beta k k^T) X is evaluated as X - beta k (k^T X), i.e. the
+ * same matrix product associated right to left; nothing else is reordered.
+ * All arithmetic is IEEE double.  Inputs arrive in the exact dtype the GPU
+ * receives (fp32, or bf16 as raw 16-bit patterns) and are widened exactly.
+ *
+ * Plain C, OpenMP over independent (sequence, head) pairs.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+static double widen(const void *base, int64_t idx, int dtype)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[idx];
+    /* bf16 is the upper half of an IEEE binary32: exact widening */
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/*
+ * One step of the recurrence on one head.
+ *   S  : dk x dv, row c = key channel, column j = value channel (fp64, in/out)
+ *   q,k: dk;  v: dv;  la: dk (log alpha);  o: dv (out);  y: dv scratch
+ */
+static void kda_step(double *S, int dk, int dv,
+                     const double *q, const double *k, const double *v,
+                     const double *la, double beta, double *o, double *y)
+{
+    /* X = Diag(alpha) S : every key channel c forgets at its own rate */
+    for (int c = 0; c < dk; ++c) {
+        double a = exp(la[c]);
+        for (int j = 0; j < dv; ++j)
+            S[(int64_t)c * dv + j] *= a;
+    }
+    /* y = k^T X */
+    for (int j = 0; j < dv; ++j)
+        y[j] = 0.0;
+    for (int c = 0; c < dk; ++c)
+        for (int j = 0; j < dv; ++j)
+            y[j] += k[c] * S[(int64_t)c * dv + j];
+    /* S = X - beta k y^T + beta k v^T */
+    for (int c = 0; c < dk; ++c)
+        for (int j = 0; j < dv; ++j)
+            S[(int64_t)c * dv + j] += beta * k[c] * (v[j] - y[j]);
+    /* o = S^T q with the updated state */
+    for (int j = 0; j < dv; ++j)
+        o[j] = 0.0;
+    for (int c = 0; c < dk; ++c)
+        for (int j = 0; j < dv; ++j)
+            o[j] += q[c] * S[(int64_t)c * dv + j];
+}
+
+static int set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+    return omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/* Number of OpenMP threads a parallel region will use (for reporting). */
+int oracle_max_threads(int nthreads) { return set_threads(nthreads); }
+
+/*
+ * Prefill over a packed batch.
+ *   q,k: [T,H,dk]   v: [T,H,dv]    (dtype: 0 = fp32, 1 = bf16 bit patterns)
+ *   log_alpha: [T,H,dk] fp32       beta: [T,H] fp32
+ *   initial_state: [N,H,dk,dv] fp32, or NULL = zeros
+ *   cu_seqlens: host [N+1] int32 offsets, or NULL = N equal rows of T/N
+ *   o: [T,H,dv] fp64 out            final_state: [N,H,dk,dv] fp64 out or NULL
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_prefill(const void *q, const void *k, const void *v,
+                   const float *log_alpha, const float *beta,
+                   const float *initial_state, const int32_t *cu_seqlens,
+                   int64_t total_tokens, int32_t num_seqs, int32_t H,
+                   int32_t dk, int32_t dv, int32_t dtype,
+                   double *o, double *final_state, int32_t nthreads)
+{
+    if (num_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0 || total_tokens < 0)
+        return -1;
+    if (!cu_seqlens && total_tokens % num_seqs != 0)
+        return -1;
+    set_threads(nthreads);
+    const int64_t units = (int64_t)num_seqs * H;
+    int bad = 0;
+
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t u = 0; u < units; ++u) {
+        const int32_t s = (int32_t)(u / H), h = (int32_t)(u % H);
+        int64_t t0, t1;
+        if (cu_seqlens) {
+            t0 = cu_seqlens[s];
+            t1 = cu_seqlens[s + 1];
+        } else {
+            int64_t len = total_tokens / num_seqs;
+            t0 = (int64_t)s * len;
+            t1 = t0 + len;
+        }
+        if (t0 < 0 || t1 < t0 || t1 > total_tokens) {
+            bad |= 1;
+            continue;
+        }
+        double *S = (double *)calloc((size_t)dk * dv, sizeof(double));
+        double *qv = (double *)malloc(sizeof(double) * (size_t)(3 * dk + 3 * dv));
+        if (!S || !qv) {
+            free(S);
+            free(qv);
+            bad |= 1;
+            continue;
+        }
+        double *kv = qv + dk, *lv = kv + dk, *vv = lv + dk, *ov = vv + dv, *y = ov + dv;
+        if (initial_state) {
+            const float *S0 = initial_state + ((int64_t)s * H + h) * dk * dv;
+            for (int64_t i = 0; i < (int64_t)dk * dv; ++i)
+                S[i] = (double)S0[i];
+        }
+        for (int64_t t = t0; t < t1; ++t) {
+            const int64_t rk = (t * H + h) * dk, rv = (t * H + h) * dv;
+            for (int c = 0; c < dk; ++c) {
+                qv[c] = widen(q, rk + c, dtype);
+                kv[c] = widen(k, rk + c, dtype);
+                lv[c] = (double)log_alpha[rk + c];
+            }
+            for (int j = 0; j < dv; ++j)
+                vv[j] = widen(v, rv + j, dtype);
+            kda_step(S, dk, dv, qv, kv, vv, lv, (double)beta[t * H + h], ov, y);
+            memcpy(o + rv, ov, sizeof(double) * (size_t)dv);
+        }
+        if (final_state)
+            memcpy(final_state + ((int64_t)s * H + h) * dk * dv, S,
+                   sizeof(double) * (size_t)dk * dv);
+        free(S);
+        free(qv);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * One decode token for every (sequence, head): the same step applied once.
+ *   state: [N,H,dk,dv] fp64, read and updated in place
+ *   q,k: [N,H,dk]  v: [N,H,dv] (dtype as above)  log_alpha: [N,H,dk]  beta: [N,H]
+ *   o: [N,H,dv] fp64 out
+ */
+int oracle_decode_step(double *state, const void *q, const void *k, const void *v,
+                       const float *log_alpha, const float *beta,
+                       int32_t num_seqs, int32_t H, int32_t dk, int32_t dv,
+                       int32_t dtype, double *o, int32_t nthreads)
+{
+    if (num_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return -1;
+    set_threads(nthreads);
+    const int64_t units = (int64_t)num_seqs * H;
+    int bad = 0;
+
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+    for (int64_t u = 0; u < units; ++u) {
+        double *qv = (double *)malloc(sizeof(double) * (size_t)(3 * dk + 3 * dv));
+        if (!qv) {
+            bad |= 1;
+            continue;
+        }
+        double *kv = qv + dk, *lv = kv + dk, *vv = lv + dk, *ov = vv + dv, *y = ov + dv;
+        const int64_t rk = u * dk, rv = u * dv;
+        for (int c = 0; c < dk; ++c) {
+            qv[c] = widen(q, rk + c, dtype);
+            kv[c] = widen(k, rk + c, dtype);
+            lv[c] = (double)log_alpha[rk + c];
+        }
+        for (int j = 0; j < dv; ++j)
+            vv[j] = widen(v, rv + j, dtype);
+        kda_step(state + u * dk * dv, dk, dv, qv, kv, vv, lv, (double)beta[u], ov, y);
+        memcpy(o + rv, ov, sizeof(double) * (size_t)dv);
+        free(qv);
+    }
+    return bad ? -1 : 0;
+}

@@ -1,0 +1,87 @@
+"""fp64 NumPy statement of the chunkwise form of KDA (test reference).
+
+The pages describe the prefill as a chunkwise-parallel computation: inside a
+chunk of C tokens the C rank-1 transitions are folded into a dense WY/UT-style
+form (matrices W and U), the output splits into an inter-chunk term (read-out
+of the state entering the chunk) and an intra-chunk term, and only the fixed
+dk x dv state passes from one chunk to the next (Kimi Linear paper notes,
+section 3 "chunkwise parallel"; the listed chunk intermediates are the
+cumulative log-decay g, A_qk, A_kk, w, u, the decayed q and k, the corrected
+values v_new and the chunk states h).
+
+The equations, derived from the recurrence by unrolling it inside a chunk
+(exact algebra, no approximation), for one head and one chunk of rows
+r = 1..C entering with state S0:
+
+    g_r   = sum_{j<=r} log alpha_j               (per channel, restarts per chunk)
+    A_kk[r,i] = beta_r sum_c k_rc k_ic exp(g_rc - g_ic)   for i < r
+    A_qk[r,i] =        sum_c q_rc k_ic exp(g_rc - g_ic)   for i <= r
+    T     = (I + A_kk)^{-1} Diag(beta)
+    W     = T (exp(g) * K),   U = T V
+    N     = U - W S0                               (corrected values)
+    O     = (exp(g) * Q) S0 + A_qk N               (inter + intra)
+    S_C   = Diag(exp(g_C)) S0 + (exp(g_C - g) * K)^T N
+
+This module is test infrastructure: it is not the oracle (the oracle is the
+token-by-token recurrence) and it shares no code with the GPU library.  The
+pins check it against the oracle for several chunk sizes; GPU stage tests
+may compare intermediates with it.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from gated_delta_rule_prefill_amd import inputs as gen
+
+
+def chunk_terms(q, k, v, la, beta):
+    """Intermediates of one chunk (fp64): g, A_kk, A_qk, T, W, U, Khat, Qg."""
+    n = k.shape[0]
+    g = np.cumsum(la, axis=0)
+    gam = np.exp(g)
+    D = g[:, None, :] - g[None, :, :]                     # D[r, i, c] = g_rc - g_ic
+    with np.errstate(over="ignore", invalid="ignore"):
+        E = np.exp(D)
+        L = np.einsum("rc,ic,ric->ri", k, k, E)
+        Aqk = np.einsum("rc,ic,ric->ri", q, k, E)
+    Akk = np.where(np.tri(n, k=-1, dtype=bool), beta[:, None] * L, 0.0)
+    Aqk = np.where(np.tri(n, dtype=bool), Aqk, 0.0)
+    Tm = np.linalg.solve(np.eye(n) + Akk, np.diag(beta))
+    W = Tm @ (gam * k)
+    U = Tm @ v
+    Khat = np.exp(g[-1][None, :] - g) * k
+    Qg = gam * q
+    return dict(g=g, Akk=Akk, Aqk=Aqk, T=Tm, W=W, U=U, Khat=Khat, Qg=Qg, gC=gam[-1])
+
+
+def head_sequence(q, k, v, la, beta, S0, C):
+    """One head of one sequence in chunks of C tokens.  Returns (O, S_final)."""
+    T = q.shape[0]
+    S = S0.copy()
+    O = np.zeros((T, v.shape[1]))
+    for c0 in range(0, T, C):
+        sl = slice(c0, min(c0 + C, T))
+        t = chunk_terms(q[sl], k[sl], v[sl], la[sl], beta[sl])
+        N = t["U"] - t["W"] @ S
+        O[sl] = t["Qg"] @ S + t["Aqk"] @ N
+        S = t["gC"][:, None] * S + t["Khat"].T @ N
+    return O, S
+
+
+def prefill(x: "gen.KDAInputs", C: int):
+    """The whole packed batch in chunks of C tokens (fp64)."""
+    q, k, v = (gen.as_f32(a).astype(np.float64) for a in (x.q, x.k, x.v))
+    la = x.log_alpha.astype(np.float64)
+    be = x.beta.astype(np.float64)
+    lens = x.lengths()
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    O = np.zeros((x.T, x.H, x.dv))
+    F = np.zeros((x.num_seqs, x.H, x.dk, x.dv))
+    for s in range(x.num_seqs):
+        a, b = offs[s], offs[s + 1]
+        for h in range(x.H):
+            S0 = np.zeros((x.dk, x.dv)) if x.initial_state is None else \
+                x.initial_state[s, h].astype(np.float64)
+            O[a:b, h], F[s, h] = head_sequence(q[a:b, h], k[a:b, h], v[a:b, h], la[a:b, h],
+                                               be[a:b, h], S0, C)
+    return O, F

@@ -1,0 +1,42 @@
+"""The pins can fail: each plausible mistake planted in a copy of the oracle
+(on the CPU, in a temporary build) must be caught by at least one pin."""
+import pytest
+
+import oracle
+import pins
+
+# (name, text in kda_oracle.c, replacement)
+MUTANTS = [
+    ("no decay", "S[(int64_t)c * dv + j] *= a;", "S[(int64_t)c * dv + j] *= 1.0;"),
+    ("decay sign", "double a = exp(la[c]);", "double a = exp(-la[c]);"),
+    ("query in correction", "y[j] += k[c] * S[(int64_t)c * dv + j];",
+     "y[j] += q[c] * S[(int64_t)c * dv + j];"),
+    ("correction with undecayed state", "y[j] += k[c] * S[(int64_t)c * dv + j];",
+     "y[j] += k[c] * S[(int64_t)c * dv + j] / exp(la[c]);"),
+    ("correction sign", "(v[j] - y[j]);", "(v[j] + y[j]);"),
+    ("beta dropped on erase", "S[(int64_t)c * dv + j] += beta * k[c] * (v[j] - y[j]);",
+     "S[(int64_t)c * dv + j] += beta * k[c] * v[j] - k[c] * y[j];"),
+    ("read-out with key", "o[j] += q[c] * S[(int64_t)c * dv + j];",
+     "o[j] += k[c] * S[(int64_t)c * dv + j];"),
+    ("read-out before write", "o[j] += q[c] * S[(int64_t)c * dv + j];",
+     "o[j] += q[c] * (S[(int64_t)c * dv + j] - beta * k[c] * (v[j] - y[j]));"),
+    ("bf16 widening", "<< 16;", "<< 15;"),
+    ("initial state ignored", "S[i] = (double)S0[i];", "S[i] = 0.0 * S0[i];"),
+    ("packed offset", "t0 = cu_seqlens[s];", "t0 = cu_seqlens[s] + (s > 0 && cu_seqlens[s] < cu_seqlens[s + 1]);"),
+    ("scalar decay", "lv[c] = (double)log_alpha[rk + c];", "lv[c] = (double)log_alpha[rk];"),
+    ("decode beta", "(double)beta[u]", "(double)beta[0]"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = oracle.source()
+    assert src.count(old) >= 1, f"mutation site for {name!r} not found"
+    mutant = oracle.compile_variant(src.replace(old, new, 1), str(tmp_path / "libmutant.so"))
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except Exception:  # AssertionError, or the mutant rejecting valid input
+            caught.append(pin.__name__)
+    assert caught, f"no pin detects the planted mistake {name!r}"
