@@ -1,0 +1,93 @@
+// kda_common.h -- device-side types and helpers shared by the libkda kernels
+// (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_launch.h"
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// -- element type traits ----------------------------------------------------
+// E is the storage type of q/k/v/o and of the chunk intermediates:
+// __bf16 (bf16 inputs, bf16 MFMA) or float (fp32 inputs, fp32 MFMA).
+template <typename E> struct Vec;
+template <> struct Vec<bf16> {
+    typedef bf16x2 v2;
+    typedef bf16x4 v4;
+    typedef bf16x8 v8;
+};
+template <> struct Vec<float> {
+    typedef f32x2 v2;
+    typedef f32x4 v4;
+    typedef f32x8 v8;
+};
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename E> __device__ __forceinline__ E from_f32(float x);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// -- one 16x16 tile step over 32 contraction slots ----------------------------
+// MFMA operand convention used throughout (16x16 output tiles, wave64):
+//   A operand: lane l supplies row (l & 15) of A, 8 contraction slots
+//              belonging to lane group g = l >> 4;
+//   B operand: lane l supplies column (l & 15) of B, the same 8 slots of g;
+//   D        : lane l holds D[4*g + i][l & 15], i = 0..3.
+// Slot (g, m) of A is multiplied with slot (g, m) of B, so any assignment of
+// the 32 contraction indices to slots works as long as A and B agree.
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma32(f32x8 a, f32x8 b, f32x4 c) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], b[m], c, 0, 0, 0);
+    return c;
+}
+
+// Storage order inside each 32-wide block of a contraction axis for matrices
+// that the state kernel multiplies against register-resident accumulator
+// tiles.  A 16x16 accumulator tile gives lane group g rows 4g..4g+3; two
+// stacked tiles give slots {4g..4g+3, 16+4g..16+4g+3}.  Storing logical index
+// x at perm32(x) puts exactly those 8 indices at 8g..8g+7, so one contiguous
+// load per lane fetches the matching operand slots.
+__device__ __forceinline__ int perm32(int x) {
+    return 8 * ((x & 15) >> 2) + 4 * (x >> 4) + (x & 3);
+}
+__host__ __device__ constexpr int perm_index(int x) {  // any axis length, 32-aligned blocks
+    return (x & ~31) + 8 * ((x & 15) >> 2) + 4 * ((x >> 4) & 1) + (x & 3);
+}
+
+// -- small vector helpers ---------------------------------------------------
+// Vector loads and stores of up to 16 bytes use the vector type directly;
+// 8 x fp32 is split in two 16-byte halves (addresses are 16-byte aligned,
+// not necessarily 32).
+template <typename V, typename E>
+__device__ __forceinline__ V load_vec(const E* p) { return *reinterpret_cast<const V*>(p); }
+template <typename V, typename E>
+__device__ __forceinline__ void store_vec(E* p, V v) { *reinterpret_cast<V*>(p) = v; }
+template <>
+__device__ __forceinline__ f32x8 load_vec<f32x8, float>(const float* p) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+template <>
+__device__ __forceinline__ void store_vec<f32x8, float>(float* p, f32x8 v) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+__device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+
+}  // namespace kda

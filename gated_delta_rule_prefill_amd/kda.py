@@ -1,0 +1,190 @@
+"""Python binding of libkda (ctypes).  Argument marshalling only: every step
+of the computation runs in the HIP kernels behind the C ABI of
+``include/kda.h``.  PyTorch provides device memory and the stream.
+
+There is no fallback: if libkda.so is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
+KDA_DTYPE_F32, KDA_DTYPE_BF16 = 0, 1
+
+# name -> (restype, argtypes) for every entry point of include/kda.h
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "kda_prefill_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, ctypes.c_int]),
+    "kda_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                   _i32, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
+    "kda_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                       ctypes.c_int, _vp, _vp]),
+    "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kda_last_error_message": (ctypes.c_char_p, []),
+    "kda_version": (_i32, []),
+    "kda_set_kernel_timing": (ctypes.c_int, [_i32]),
+    "kda_prefill_kernel_times": (_i32, [ctypes.POINTER(ctypes.c_float),
+                                        ctypes.POINTER(ctypes.c_char_p), _i32]),
+}
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {status_string(status)} ({detail})")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkda.so (built in-tree by ``gated_delta_rule_prefill_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run "
+                              "`python -m gated_delta_rule_prefill_amd.build` (needs hipcc)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().kda_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().kda_last_error_message().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != KDA_OK:
+        raise KDAError(status, where, last_error())
+
+
+def workspace_bytes(total_tokens: int, num_seqs: int, H: int, dk: int, dv: int,
+                    bf16: bool) -> int:
+    return int(lib().kda_prefill_workspace_bytes(int(total_tokens), int(num_seqs), int(H),
+                                                 int(dk), int(dv),
+                                                 KDA_DTYPE_BF16 if bf16 else KDA_DTYPE_F32))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return KDA_DTYPE_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device, stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def prefill(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None,
+            num_seqs: Optional[int] = None, output_final_state: bool = True,
+            final_state=None, out=None, workspace=None, stream=None) -> Tuple[object, object]:
+    """Chunkwise KDA prefill of a packed batch (``kda_prefill``).
+
+    q, k: [T, H, dk]; v: [T, H, dv] (bf16 or fp32, same dtype, CUDA/HIP device);
+    log_alpha: [T, H, dk] fp32; beta: [T, H] fp32;
+    initial_state: [N, H, dk, dv] fp32 or None; cu_seqlens: [N+1] int32 or None
+    (then ``num_seqs`` equal rows, default 1).  ``final_state`` may be the
+    same tensor as ``initial_state``.  Returns (o [T, H, dv], final_state or None).
+    """
+    import torch
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is not None:
+        _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1, "cu_seqlens: int32 [N+1]")
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = int(num_seqs or 1)
+    dev = q.device
+    for name, t, shape, dt in (("k", k, (T, H, dk), q.dtype), ("v", v, (T, H, dv), q.dtype),
+                               ("log_alpha", log_alpha, (T, H, dk), torch.float32),
+                               ("beta", beta, (T, H), torch.float32)):
+        _require(tuple(t.shape) == shape, f"{name}: expected shape {shape}, got {tuple(t.shape)}")
+        _require(t.dtype == dt, f"{name}: expected dtype {dt}, got {t.dtype}")
+    tensors = [q, k, v, log_alpha, beta]
+    if initial_state is not None:
+        _require(tuple(initial_state.shape) == (N, H, dk, dv) and
+                 initial_state.dtype == torch.float32, "initial_state: fp32 [N, H, dk, dv]")
+        tensors.append(initial_state)
+    if cu_seqlens is not None:
+        tensors.append(cu_seqlens)
+    for t in tensors:
+        _require(t.device == dev and t.is_contiguous(), "all inputs: contiguous, on one device")
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    need = workspace_bytes(T, N, H, dk, dv, q.dtype == torch.bfloat16)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _require(workspace.numel() * workspace.element_size() >= need, "workspace too small")
+    st = lib().kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                           _ptr(initial_state), _ptr(cu_seqlens), T, N, H, dk, dv,
+                           _dtype_code(q), _ptr(out), _ptr(final_state), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    _check(st, "kda_prefill")
+    return out, final_state
+
+
+def decode_step(state, q, k, v, log_alpha, beta, out=None, stream=None):
+    """One recurrent KDA token per sequence (``kda_decode_step``); ``state``
+    (fp32 [N, H, dk, dv]) is updated in place.  Returns o [N, H, dv]."""
+    import torch
+    N, H, dk, dv = state.shape
+    _require(state.dtype == torch.float32 and state.is_contiguous(), "state: contiguous fp32")
+    for name, t, shape, dt in (("q", q, (N, H, dk), q.dtype), ("k", k, (N, H, dk), q.dtype),
+                               ("v", v, (N, H, dv), q.dtype),
+                               ("log_alpha", log_alpha, (N, H, dk), torch.float32),
+                               ("beta", beta, (N, H), torch.float32)):
+        _require(tuple(t.shape) == shape, f"{name}: expected shape {shape}, got {tuple(t.shape)}")
+        _require(t.dtype == dt, f"{name}: expected dtype {dt}")
+        _require(t.device == state.device and t.is_contiguous(), f"{name}: contiguous, same device")
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=state.device)
+    st = lib().kda_decode_step(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                               _ptr(beta), N, H, dk, dv, _dtype_code(q), _ptr(out),
+                               _stream(state.device, stream))
+    _check(st, "kda_decode_step")
+    return out
+
+
+def set_kernel_timing(enabled: bool) -> None:
+    _check(lib().kda_set_kernel_timing(1 if enabled else 0), "kda_set_kernel_timing")
+
+
+def prefill_kernel_times():
+    """[(kernel name, ms)] of the last prefill recorded with timing enabled."""
+    ms = (ctypes.c_float * 8)()
+    names = (ctypes.c_char_p * 8)()
+    n = lib().kda_prefill_kernel_times(ms, names, 8)
+    if n < 0:
+        raise RuntimeError("no timed prefill recorded")
+    return [(names[i].decode(), float(ms[i])) for i in range(n)]

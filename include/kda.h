@@ -1,0 +1,141 @@
+/*
+ * kda.h -- C ABI of libkda: Kimi Delta Attention (KDA) prefill and decode on
+ * AMD MI355X (gfx950).
+ *
+ * The operation (Kimi Linear paper notes, section 2 "KDA recurrence"): per
+ * (sequence, head) a fixed dk x dv fp32 state S is updated token by token as
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * where alpha_t = exp(log_alpha_t) is a per-key-channel decay vector and
+ * beta_t the write strength.  kda_prefill evaluates whole sequences with the
+ * chunkwise-parallel form (paper notes, section 3: dense WY/UT form of each
+ * chunk's rank-1 transitions, inter-chunk plus intra-chunk output, only the
+ * fixed-size state passed between chunks); kda_decode_step applies the
+ * recurrence to one token (the fused recurrent decode path).  Both compute
+ * the same function.
+ *
+ * Conventions shared by every call
+ *   Layout     dense row-major.  Tokens of all sequences are packed along the
+ *              first axis; head h of token t of a [T,H,d] tensor is row
+ *              (t*H + h).  The state is [N,H,dk,dv], key channel major (row c
+ *              of a head's state is key channel c).
+ *   Dtypes     q, k, v and o share one dtype (KDA_DTYPE_F32 or KDA_DTYPE_BF16);
+ *              log_alpha, beta and states are always fp32; accumulation is fp32.
+ *   Sizes      dk, dv in {64, 128} (any pairing); H >= 1; num_seqs >= 1.
+ *   Alignment  every pointer 16-byte aligned.
+ *   Ownership  the caller owns every buffer (device memory).  The library
+ *              keeps no pointer after a call returns.
+ *   Streams    work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *              stream).  KDA_OK means "enqueued"; faults during execution
+ *              surface at the caller's next synchronisation.
+ *   Errors     a call returns a status and never aborts, prints or throws.
+ *              Host-checkable argument errors are reported before any HIP
+ *              call is made; kda_last_error_message() gives detail (per
+ *              thread).
+ *   Values     log_alpha must be finite and <= 0 (alpha in (0, 1]).  Within
+ *              every aligned 16-token block of a 64-token chunk the summed
+ *              log_alpha of one channel must stay above -80; inside that range
+ *              results match the recurrence up to rounding, outside it they
+ *              are unspecified.  NaN/Inf inputs propagate.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* NULL/misaligned pointer, bad size or dtype */
+    KDA_ERR_UNSUPPORTED = 2,      /* a head size this build has no kernels for */
+    KDA_ERR_WORKSPACE = 3,        /* caller workspace smaller than required     */
+    KDA_ERR_HIP = 4               /* a HIP runtime call or launch failed        */
+} kda_status;
+
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
+
+/*
+ * Device workspace kda_prefill needs for these sizes (bytes, 256-aligned).
+ * It holds the per-chunk intermediates of the chunkwise form: decayed keys
+ * and queries, the UT-transformed W and U, the intra-chunk A_qk and the
+ * chunk-end decay (paper notes, section 3 and its list of chunk
+ * intermediates).  Returns 0 for invalid sizes.
+ */
+size_t kda_prefill_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                   int32_t dk, int32_t dv, kda_dtype dtype);
+
+/*
+ * Chunkwise prefill of a packed batch (paper notes, sections 2-3).
+ *
+ *   q, k          [T,H,dk] dtype; v [T,H,dv] dtype      (device, read)
+ *   log_alpha     [T,H,dk] fp32, log of the per-channel decay (device, read)
+ *   beta          [T,H] fp32 write strength              (device, read)
+ *   initial_state [N,H,dk,dv] fp32, or NULL = zero state (device, read)
+ *   cu_seqlens    [N+1] int32 offsets 0 = c_0 <= c_1 <= ... <= c_N = T
+ *                 (device; zero-length sequences allowed), or NULL = N equal
+ *                 contiguous sequences of T/N tokens (T % N must be 0).  The
+ *                 offsets are a precondition and are not read on the host.
+ *   total_tokens  T >= 0; num_seqs N >= 1
+ *   o             [T,H,dv] dtype (device, written; must not alias an input)
+ *   final_state   [N,H,dk,dv] fp32 (device, written), or NULL.  May be the
+ *                 same buffer as initial_state (state carried in place).
+ *   workspace     device buffer of at least kda_prefill_workspace_bytes(), or
+ *                 NULL with workspace_bytes 0: the library then allocates and
+ *                 frees one stream-ordered on `stream`.
+ * A sequence of length 0 writes final_state = initial_state (or zeros).
+ */
+kda_status kda_prefill(const void *q, const void *k, const void *v,
+                       const float *log_alpha, const float *beta,
+                       const float *initial_state, const int32_t *cu_seqlens,
+                       int64_t total_tokens, int32_t num_seqs, int32_t H,
+                       int32_t dk, int32_t dv, kda_dtype dtype,
+                       void *o, float *final_state,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent token for each of N sequences (fused recurrent decode,
+ * paper notes, section 3; the state is the only memory a KDA layer keeps per
+ * sequence).  The state is updated in place:
+ *
+ *   state      [N,H,dk,dv] fp32 (device, read and written)
+ *   q, k       [N,H,dk] dtype; v [N,H,dv] dtype (device, read)
+ *   log_alpha  [N,H,dk] fp32; beta [N,H] fp32   (device, read)
+ *   o          [N,H,dv] dtype (device, written; must not alias an input)
+ */
+kda_status kda_decode_step(float *state, const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *beta,
+                           int32_t num_seqs, int32_t H, int32_t dk, int32_t dv,
+                           kda_dtype dtype, void *o, void *stream);
+
+/* Static description of a status code. */
+const char *kda_status_string(kda_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char *kda_last_error_message(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t kda_version(void);
+
+/*
+ * Kernel timing for measurement (not needed for normal use).  While enabled,
+ * kda_prefill records a HIP event before and after each of its kernels on its
+ * stream.  kda_prefill_kernel_times() waits for the last recorded call's
+ * events and writes, for up to max_kernels kernels in launch order, the
+ * elapsed milliseconds (ms) and a static kernel name (names, may be NULL).
+ * It returns the number of kernels of that call, or -1 when nothing was
+ * recorded or a HIP call failed.
+ */
+kda_status kda_set_kernel_timing(int32_t enabled);
+int32_t kda_prefill_kernel_times(float *ms, const char **names, int32_t max_kernels);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,120 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/kda.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_prefill_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+A = 1 << 20  # a 16-byte-aligned fake device address; never dereferenced here
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert "kda_prefill" in names and "kda_decode_step" in names
+    assert set(names) == set(kda.SIGNATURES), (names, sorted(kda.SIGNATURES))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kda.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.kda_version() >= 100
+
+
+def test_status_strings():
+    for s in range(5):
+        assert kda.status_string(s).startswith("KDA_")
+    assert kda.status_string(99) == "unknown kda_status"
+
+
+def test_workspace_bytes():
+    w = kda.workspace_bytes(4096, 1, 32, 128, 128, True)
+    chunks = 4096 // 64 + 1
+    per_chunk_head = 2 * (64 * 128 * 3 + 64 * 64 + 128 * 64) + 128 * 4
+    assert w >= chunks * 32 * per_chunk_head
+    assert w % 256 == 0
+    assert kda.workspace_bytes(0, 1, 1, 64, 64, False) > 0
+    assert kda.workspace_bytes(10, 0, 1, 64, 64, False) == 0
+    assert kda.workspace_bytes(-1, 1, 1, 64, 64, False) == 0
+
+
+def _prefill(**kw):
+    args = dict(q=A, k=A, v=A, la=A, beta=A, s0=None, cu=None, T=128, N=1, H=2, dk=64, dv=64,
+                dtype=kda.KDA_DTYPE_BF16, o=A, fin=None, ws=A, wsb=1 << 40, stream=None)
+    args.update(kw)
+    lib = kda.lib()
+    return lib.kda_prefill(args["q"], args["k"], args["v"], args["la"], args["beta"], args["s0"],
+                           args["cu"], args["T"], args["N"], args["H"], args["dk"], args["dv"],
+                           args["dtype"], args["o"], args["fin"], args["ws"], args["wsb"],
+                           args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(T=-5), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(T=1 << 31), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dv=256), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=7), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(T=129, N=2), kda.KDA_ERR_INVALID_ARGUMENT),    # unequal rows need cu_seqlens
+    (dict(q=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(o=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(k=A + 4), kda.KDA_ERR_INVALID_ARGUMENT),       # misaligned
+    (dict(ws=None, wsb=10), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(wsb=100), kda.KDA_ERR_WORKSPACE),
+])
+def test_prefill_rejects_before_any_hip_call(kw, status):
+    assert _prefill(**kw) == status
+    assert kda.last_error()  # a message explains it
+
+
+def _decode(**kw):
+    args = dict(state=A, q=A, k=A, v=A, la=A, beta=A, N=4, H=2, dk=128, dv=128,
+                dtype=kda.KDA_DTYPE_BF16, o=A, stream=None)
+    args.update(kw)
+    return kda.lib().kda_decode_step(args["state"], args["q"], args["k"], args["v"], args["la"],
+                                     args["beta"], args["N"], args["H"], args["dk"], args["dv"],
+                                     args["dtype"], args["o"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(H=-1), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dk=32), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=2), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(state=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(beta=A + 8), kda.KDA_ERR_INVALID_ARGUMENT),
+])
+def test_decode_rejects_before_any_hip_call(kw, status):
+    assert _decode(**kw) == status
+    assert kda.last_error()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kda, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(kda, "_lib", None)
+    with pytest.raises(ImportError):
+        kda.lib()
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "gated_delta_rule_prefill_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "kda_oracle" not in text and "liboracle" not in text, f
