@@ -12,13 +12,18 @@
 //   g_r       = sum_{j<=r} log alpha_j             per channel (cumulative log-decay)
 //   A_kk[r,i] = beta_r sum_c k_rc k_ic e^{g_rc - g_ic}, i < r
 //   A_qk[r,i] =        sum_c q_rc k_ic e^{g_rc - g_ic}, i <= r
-//   T         = (I + A_kk)^{-1} Diag(beta)         forward substitution in LDS
+//   T         = (I + A_kk)^{-1} Diag(beta)         blocked substitution in LDS
 //   W         = T (e^g * K),   U = T V             MFMA
 //   Khat      = e^{g_C - g} * K,  Qg = e^g * Q,  gamma_C = e^{g_C}
 //
 // and stores W, U, Khat^T, Qg, A_qk and gamma_C for the sequential state
 // kernel.  The state kernel then needs, per chunk, only
 //   N = U - W S,  O = Qg S + A_qk N,  S <- Diag(gamma_C) S + Khat^T N.
+//
+// The inverse of the unit lower-triangular I + A_kk is built blockwise: the
+// four 16x16 diagonal blocks by forward substitution (one lane per column),
+// then the off-diagonal blocks on fp32 MFMA, one block diagonal at a time,
+// stored transposed in the unused upper triangle of A_kk.
 //
 // Decay factors never form 1/gamma over a whole chunk: the chunk is cut into
 // four 16-token blocks with reference log-decays B_R (g just before block R).
@@ -35,8 +40,8 @@ struct IntraLayout {
     static constexpr int PAD = 16 / ES;              // 16-byte row padding (elements)
     static constexpr int LK = DK + PAD;              // row stride of [64][DK] arrays
     static constexpr int LT = CHUNK + PAD;           // row stride of [d][64] / [64][64] arrays
-    static constexpr int LA = CHUNK + 4;             // row stride of the fp32 A_kk array
-    // phase 1 (A tiles): KP|QP and KD;  phase 2+ (W, U): kgT and vT in the same bytes
+    static constexpr int LA = CHUNK + 4;             // row stride of the fp32 A / X array
+    // phase 1 (A tiles): KP|QP and KD;  phase 3+ (W, U): kgT and vT in the same bytes
     static constexpr int P1_BYTES = 2 * CHUNK * LK * ES;
     static constexpr int P2_BYTES = (DK + DV) * LT * ES;
     static constexpr int U1_BYTES = P1_BYTES > P2_BYTES ? P1_BYTES : P2_BYTES;
@@ -47,7 +52,8 @@ struct IntraLayout {
     static constexpr int OFF_AL = (U1_BYTES + 255) & ~255;
     static constexpr int OFF_TL = OFF_AL + CHUNK * LA * 4;
     static constexpr int OFF_TAU = OFF_TL + ((CHUNK * LT * ES + 15) & ~15);
-    static constexpr int OFF_BETA = OFF_TAU + 4 * DK * 4;
+    static constexpr int OFF_ETAB = OFF_TAU + 4 * DK * 4;
+    static constexpr int OFF_BETA = OFF_ETAB + 6 * DK * 4;
     static constexpr int BYTES = OFF_BETA + CHUNK * 4;
 };
 
@@ -68,18 +74,72 @@ __device__ __forceinline__ typename Vec<E>::v8 frag8(const E* p) {
     return load_vec<typename Vec<E>::v8>(p);
 }
 template <typename E>
-__device__ __forceinline__ typename Vec<E>::v8 frag8_scaled(const E* p, const float (&f)[8]) {
+__device__ __forceinline__ typename Vec<E>::v8 frag8_scaled(const E* p, const float* f) {
     typename Vec<E>::v8 v = load_vec<typename Vec<E>::v8>(p);
+    const f32x4 f0 = *reinterpret_cast<const f32x4*>(f);
+    const f32x4 f1 = *reinterpret_cast<const f32x4*>(f + 4);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) v[m] = from_f32<E>(to_f32(v[m]) * f[m]);
+    for (int m = 0; m < 4; ++m) {
+        v[m] = from_f32<E>(to_f32(v[m]) * f0[m]);
+        v[m + 4] = from_f32<E>(to_f32(v[m + 4]) * f1[m]);
+    }
     return v;
 }
 
-// Pairs (R, I) of 16-token blocks with I <= R, spread over the 4 waves.
+// CPT consecutive elements as floats (one vector load)
+template <int CPT, typename E>
+__device__ __forceinline__ void load_row(const E* p, float (&out)[CPT]) {
+    if constexpr (CPT == 2) {
+        const typename Vec<E>::v2 v = *reinterpret_cast<const typename Vec<E>::v2*>(p);
+        out[0] = to_f32(v[0]);
+        out[1] = to_f32(v[1]);
+    } else {
+        out[0] = to_f32(p[0]);
+    }
+}
+
+// Pairs (R, I) of 16-token blocks with I <= R, spread over the 4 waves; the
+// index of an off-diagonal pair in the decay-factor table is R(R-1)/2 + I.
 __device__ __constant__ const int8_t kPairR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 __device__ __constant__ const int8_t kPairI[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 __device__ __constant__ const int8_t kUpperR[6] = {0, 0, 0, 1, 1, 2};
 __device__ __constant__ const int8_t kUpperI[6] = {1, 2, 3, 2, 3, 3};
+__device__ __constant__ const int8_t kOffR[6] = {1, 2, 2, 3, 3, 3};
+__device__ __constant__ const int8_t kOffI[6] = {0, 0, 1, 0, 1, 2};
+
+// Element (r, c) of X = (I + A_kk)^{-1}: unit lower triangular, its strictly
+// lower part stored transposed in the (otherwise zero) upper triangle of sAL.
+template <int LA>
+__device__ __forceinline__ float x_elem(const float* sAL, int r, int c) {
+    return r == c ? 1.f : (r > c ? sAL[c * LA + r] : 0.f);
+}
+
+// X block (R, I), R > I, by one wave on fp32 MFMA:
+//   X_RI = -X_RR * sum_{J=I}^{R-1} A_RJ X_JI
+// The first product's accumulator feeds the second as its B operand:
+// slot (g, m) carries contraction index 4g + m in both.
+template <int LA>
+__device__ __forceinline__ void x_block(float* sAL, int R, int I, int g, int ln) {
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int J = I; J < R; ++J) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int kk = 4 * g + m;
+            const float a = sAL[(16 * R + ln) * LA + 16 * J + kk];
+            const float b = x_elem<LA>(sAL, 16 * J + kk, 16 * I + ln);
+            z = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, z, 0, 0, 0);
+        }
+    }
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int kk = 4 * g + m;
+        const float a = -x_elem<LA>(sAL, 16 * R + ln, 16 * R + kk);
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, z[m], x, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sAL[(16 * I + ln) * LA + 16 * R + 4 * g + i] = x[i];
+}
 
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void prefill_intra_kernel(
@@ -98,11 +158,12 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
     E* sKP = reinterpret_cast<E*>(smem + L::OFF_KP);   // k*e^{g-B}  (phase 1a), then q*e^{g-B} (1b)
     E* sKD = reinterpret_cast<E*>(smem + L::OFF_KD);   // k*e^{B-g}
-    E* sKGT = reinterpret_cast<E*>(smem + L::OFF_KGT); // (e^g * k)^T   (phase 2+)
-    E* sVT = reinterpret_cast<E*>(smem + L::OFF_VT);   // v^T           (phase 2+)
+    E* sKGT = reinterpret_cast<E*>(smem + L::OFF_KGT); // (e^g * k)^T   (phase 3+)
+    E* sVT = reinterpret_cast<E*>(smem + L::OFF_VT);   // v^T           (phase 3+)
     float* sAL = reinterpret_cast<float*>(smem + L::OFF_AL);
     E* sTL = reinterpret_cast<E*>(smem + L::OFF_TL);
     float* sTau = reinterpret_cast<float*>(smem + L::OFF_TAU);
+    float* sEtab = reinterpret_cast<float*>(smem + L::OFF_ETAB);
     float* sBeta = reinterpret_cast<float*>(smem + L::OFF_BETA);
 
     const int cid = blockIdx.x;
@@ -117,8 +178,22 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     const int R = wave;
     const int g = lane >> 4, ln = lane & 15;
     const int c0 = lane * CPT;
+    const int cv0 = lane * CPTV;
 
-    // ---- phase 0: cumulative log-decay inside each 16-token block -------------
+    // ---- phase 0: unconditional loads (rows past the end clamp, then zero) ----
+    float la[16][CPT], kr[16][CPT], qr[16][CPT], vr[16][CPTV];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = 16 * R + r;
+        const size_t tok = (size_t)ci.start + (row < ci.len ? row : ci.len - 1);
+        load_row<CPT>(log_alpha + (tok * H + h) * DK + c0, la[r]);
+        load_row<CPT>(k + (tok * H + h) * DK + c0, kr[r]);
+        load_row<CPT>(q + (tok * H + h) * DK + c0, qr[r]);
+        load_row<CPTV>(v + (tok * H + h) * DV + cv0, vr[r]);
+    }
+    float bt = 0.f;
+    if (wave == 0) bt = beta[((size_t)ci.start + (lane < ci.len ? lane : ci.len - 1)) * H + h];
+    // cumulative log-decay inside each 16-token block (zero past the end)
     float ell[16][CPT];
     {
         float run[CPT];
@@ -126,22 +201,25 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
         for (int e = 0; e < CPT; ++e) run[e] = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = 16 * R + r;
-            if (row < ci.len) {
-                const float* p = log_alpha + ((size_t)(ci.start + row) * H + h) * DK + c0;
+            const bool valid = 16 * R + r < ci.len;
 #pragma unroll
-                for (int e = 0; e < CPT; ++e) run[e] += p[e];
+            for (int e = 0; e < CPT; ++e) {
+                run[e] += valid ? la[r][e] : 0.f;
+                ell[r][e] = run[e];
+                kr[r][e] = valid ? kr[r][e] : 0.f;
+                qr[r][e] = valid ? qr[r][e] : 0.f;
             }
 #pragma unroll
-            for (int e = 0; e < CPT; ++e) ell[r][e] = run[e];
+            for (int e = 0; e < CPTV; ++e) vr[r][e] = valid ? vr[r][e] : 0.f;
         }
 #pragma unroll
         for (int e = 0; e < CPT; ++e) sTau[R * DK + c0 + e] = run[e];
-        if (wave == 0) sBeta[lane] = lane < ci.len ? beta[(size_t)(ci.start + lane) * H + h] : 0.f;
+        if (wave == 0) sBeta[lane] = lane < ci.len ? bt : 0.f;
     }
     __syncthreads();
 
-    float Bref[CPT], toEnd[CPT];   // B_R = g before block R;  g_C - B_R
+    // ---- phase 0b: block references, decay table, decayed keys ---------------
+    float eB[CPT], eTE[CPT];   // e^{B_R} (g before block R);  e^{g_C - B_R}
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
         float a = 0.f, b = 0.f;
@@ -150,28 +228,29 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
             const float tv = sTau[Rp * DK + c0 + e];
             if (Rp < R) a += tv; else b += tv;
         }
-        Bref[e] = a;
-        toEnd[e] = b;
+        eB[e] = fast_exp(a);
+        eTE[e] = fast_exp(b);
     }
-
-    // keys: decayed operands for A_kk / A_qk, Khat^T and gamma_C to the workspace
-    float kreg[16][CPT];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 16 * R + r;
-#pragma unroll
-        for (int e = 0; e < CPT; ++e)
-            kreg[r][e] = row < ci.len ? to_f32(k[((size_t)(ci.start + row) * H + h) * DK + c0 + e]) : 0.f;
+    // e^{B_R - B_I} for the six off-diagonal block pairs (all <= 1)
+    for (int idx = t; idx < 6 * DK; idx += 256) {
+        const int p = idx / DK, c = idx % DK;
+        float d = 0.f;
+        for (int Rp = kOffI[p]; Rp < kOffR[p]; ++Rp) d += sTau[Rp * DK + c];
+        sEtab[idx] = fast_exp(d);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = 16 * R + r;
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
-            const float P = fast_exp(ell[r][e]);
-            const float iP = fast_exp(fminf(-ell[r][e], 80.f));
-            sKP[row * L::LK + c0 + e] = from_f32<E>(kreg[r][e] * P);
-            sKD[row * L::LK + c0 + e] = from_f32<E>(kreg[r][e] * iP);
+            const float P = fast_exp(ell[r][e]);                   // e^{g_r - B_R} <= 1
+            const float iP = fast_exp(fminf(-ell[r][e], 80.f));    // e^{B_R - g_r}
+            sKP[row * L::LK + c0 + e] = from_f32<E>(kr[r][e] * P);
+            sKD[row * L::LK + c0 + e] = from_f32<E>(kr[r][e] * iP);
+            const float kh = kr[r][e] * iP * eTE[e];               // k e^{g_C - g_r}
+            kr[r][e] *= P * eB[e];                                 // now e^{g_r} k  (for W)
+            qr[r][e] *= P;                                         // q e^{g_r - B_R}
+            ell[r][e] = kh;                                        // reuse: Khat value
         }
     }
 #pragma unroll
@@ -181,13 +260,10 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
         for (int r4 = 0; r4 < 4; ++r4) {
             V4 w;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * r4 + i;
-                w[i] = from_f32<E>(kreg[r][e] * fast_exp(toEnd[e] - ell[r][e]));
-            }
+            for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(ell[4 * r4 + i][e]);
             store_vec(dst + perm_index(16 * R + 4 * r4), w);
         }
-        if (R == 0) out.gC[chh * DK + c0 + e] = fast_exp(toEnd[e]);
+        if (R == 0) out.gC[chh * DK + c0 + e] = eTE[e];
     }
     __syncthreads();
 
@@ -195,19 +271,14 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     // A operand k_r e^{g_r - B_R}; B operand k_i e^{B_I - g_i} * e^{B_R - B_I}.
     for (int p = wave; p < 10; p += 4) {
         const int PR = kPairR[p], PI = kPairI[p];
+        const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int cb = 32 * s + 8 * g;
-            float f[8];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                float d = 0.f;
-                for (int Rp = PI; Rp < PR; ++Rp) d += sTau[Rp * DK + cb + m];
-                f[m] = fast_exp(d);   // e^{B_R - B_I} <= 1
-            }
             const V8 a = frag8<E>(sKP + (16 * PR + ln) * L::LK + cb);
-            const V8 b = frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f);
+            const V8 b = PR == PI ? frag8<E>(sKD + (16 * PI + ln) * L::LK + cb)
+                                  : frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f + cb);
             acc = mma32(a, b, acc);
         }
 #pragma unroll
@@ -228,14 +299,10 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     for (int r = 0; r < 16; ++r) {
         const int row = 16 * R + r;
         typename Vec<E>::v2 qg2;
-        float qv[CPT];
-#pragma unroll
-        for (int e = 0; e < CPT; ++e)
-            qv[e] = row < ci.len ? to_f32(q[((size_t)(ci.start + row) * H + h) * DK + c0 + e]) : 0.f;
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
-            sKP[row * L::LK + c0 + e] = from_f32<E>(qv[e] * fast_exp(ell[r][e]));
-            const E val = from_f32<E>(qv[e] * fast_exp(Bref[e] + ell[r][e]));
+            sKP[row * L::LK + c0 + e] = from_f32<E>(qr[r][e]);
+            const E val = from_f32<E>(qr[r][e] * eB[e]);
             if constexpr (CPT == 2) qg2[e] = val;
             else out.Qg[(chh * CHUNK + row) * DK + perm_index(c0 + e)] = val;
         }
@@ -246,18 +313,13 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     // ---- phase 1c: A_qk^T tiles (rows i of block I, columns r of block R) -------
     for (int p = wave; p < 10; p += 4) {
         const int PR = kPairR[p], PI = kPairI[p];
+        const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int cb = 32 * s + 8 * g;
-            float f[8];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                float d = 0.f;
-                for (int Rp = PI; Rp < PR; ++Rp) d += sTau[Rp * DK + cb + m];
-                f[m] = fast_exp(d);   // e^{B_R - B_I} <= 1
-            }
-            const V8 a = frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f);
+            const V8 a = PR == PI ? frag8<E>(sKD + (16 * PI + ln) * L::LK + cb)
+                                  : frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f + cb);
             const V8 b = frag8<E>(sKP + (16 * PR + ln) * L::LK + cb);
             acc = mma32(a, b, acc);
         }
@@ -279,53 +341,66 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     }
     __syncthreads();   // sKP / sKD dead: their bytes become kgT and vT
 
-    // ---- phase 2: (e^g k)^T and v^T in LDS, token-contiguous ------------------
+    // ---- phase 3a: (e^g k)^T and v^T in LDS; diagonal 16x16 inverses ----------
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
         V8 lo, hi;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            lo[r] = from_f32<E>(kreg[r][e] * fast_exp(Bref[e] + ell[r][e]));
-            hi[r] = from_f32<E>(kreg[r + 8][e] * fast_exp(Bref[e] + ell[r + 8][e]));
+            lo[r] = from_f32<E>(kr[r][e]);
+            hi[r] = from_f32<E>(kr[r + 8][e]);
         }
         store_vec(sKGT + (c0 + e) * L::LT + 16 * R, lo);
         store_vec(sKGT + (c0 + e) * L::LT + 16 * R + 8, hi);
     }
-    {
-        const int cv0 = lane * CPTV;
 #pragma unroll
-        for (int e = 0; e < CPTV; ++e) {
-            V8 lo, hi;
+    for (int e = 0; e < CPTV; ++e) {
+        V8 lo, hi;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int row = 16 * R + r;
-                lo[r] = row < ci.len ? v[((size_t)(ci.start + row) * H + h) * DV + cv0 + e] : from_f32<E>(0.f);
-                hi[r] = row + 8 < ci.len ? v[((size_t)(ci.start + row + 8) * H + h) * DV + cv0 + e] : from_f32<E>(0.f);
-            }
-            store_vec(sVT + (cv0 + e) * L::LT + 16 * R, lo);
-            store_vec(sVT + (cv0 + e) * L::LT + 16 * R + 8, hi);
+        for (int r = 0; r < 8; ++r) {
+            lo[r] = from_f32<E>(vr[r][e]);
+            hi[r] = from_f32<E>(vr[r + 8][e]);
         }
+        store_vec(sVT + (cv0 + e) * L::LT + 16 * R, lo);
+        store_vec(sVT + (cv0 + e) * L::LT + 16 * R + 8, hi);
     }
-
-    // ---- phase 3: T = (I + A_kk)^{-1} Diag(beta) by forward substitution -------
-    // Lane j of wave 0 solves (I + A) x = e_j for column j of the inverse.
     if (wave == 0) {
-        float x[CHUNK];
+        // lane (blk, j) solves (I + A_blk) x = e_j on diagonal block blk
+        const int blk = lane >> 4, j = lane & 15;
+        const float* Ab = sAL + 16 * blk * L::LA + 16 * blk;
+        float x[16];
 #pragma unroll
-        for (int i = 0; i < CHUNK; ++i) x[i] = 0.f;
+        for (int i = 0; i < 16; ++i) x[i] = 0.f;
 #pragma unroll
-        for (int r = 0; r < CHUNK; ++r) {
-            float acc = (r == lane) ? 1.f : 0.f;
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == j) ? 1.f : 0.f;
 #pragma unroll
             for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(sAL + r * L::LA + 4 * i4);
-                acc -= a[0] * x[4 * i4] + a[1] * x[4 * i4 + 1] + a[2] * x[4 * i4 + 2] + a[3] * x[4 * i4 + 3];
+                const f32x4 a = *reinterpret_cast<const f32x4*>(Ab + r * L::LA + 4 * i4);
+                acc -= a[0] * x[4 * i4] + a[1] * x[4 * i4 + 1] + a[2] * x[4 * i4 + 2] +
+                       a[3] * x[4 * i4 + 3];
             }
             x[r] = acc;
         }
-        const float bj = sBeta[lane];
+        float* Xt = sAL + (16 * blk + j) * L::LA + 16 * blk;   // row j of the block, transposed store
 #pragma unroll
-        for (int r = 0; r < CHUNK; ++r) sTL[r * L::LT + lane] = from_f32<E>(x[r] * bj);
+        for (int r = 0; r < 16; ++r)
+            if (r > j) Xt[r] = x[r];
+    }
+    __syncthreads();
+
+    // ---- phase 3b-d: off-diagonal blocks of X, one block-diagonal at a time ----
+    if (wave < 3) x_block<L::LA>(sAL, wave + 1, wave, g, ln);          // (1,0) (2,1) (3,2)
+    __syncthreads();
+    if (wave < 2) x_block<L::LA>(sAL, wave + 2, wave, g, ln);          // (2,0) (3,1)
+    __syncthreads();
+    if (wave == 0) x_block<L::LA>(sAL, 3, 0, g, ln);                   // (3,0)
+    __syncthreads();
+
+    // ---- phase 3e: T = X Diag(beta) in the operand dtype ----------------------
+    for (int idx = t; idx < CHUNK * CHUNK; idx += 256) {
+        const int r = idx >> 6, c = idx & 63;
+        sTL[r * L::LT + c] = from_f32<E>(x_elem<L::LA>(sAL, r, c) * sBeta[c]);
     }
     __syncthreads();
 

@@ -8,14 +8,16 @@
 //   O = Qg S + A_qk N              (inter-chunk read-out + intra-chunk causal part)
 //   S = Diag(gamma_C) S + Khat^T N
 //
-// One wave per (sequence, head, 16 value columns): the columns of S evolve
-// independently, so a head's state is split over DV/16 waves that never
-// communicate.  The fp32 state tile (DK x 16) lives in MFMA accumulator
-// registers for the whole sequence and is read from / written to HBM once.
-// Every product takes its register-resident operand (S or N) directly from
-// accumulator tiles: a tile's lane group g holds rows 4g..4g+3, which is the
-// operand slot set that the perm32 storage order of W, Qg, Khat^T and A_qk
-// matches, so no LDS round trip is needed inside the serial loop.
+// One workgroup per (sequence, head, 16 value columns): the columns of S evolve
+// independently, so a head's state is split over DV/16 workgroups that never
+// communicate.  Wave 0 computes; it keeps the fp32 state tile (DK x 16) in MFMA
+// accumulator registers for the whole sequence.  Waves 1-3 stage the next
+// chunk's operands into an LDS double buffer while wave 0 works on the current
+// one, so the serial loop never waits on HBM/L2 latency.
+//
+// Every product takes its register-resident operand (S or N) straight from
+// accumulator tiles: a 16x16 tile gives lane group g rows 4g..4g+3, the slot
+// set that the perm32 storage order of W, Qg, Khat^T and A_qk matches.
 #include "kda_common.h"
 
 namespace kda {
@@ -30,20 +32,120 @@ struct ChunkBufsC {
     const float* gC;
 };
 
-// Workgroups are grouped so that the DV/16 waves of one (sequence, head)
-// have block indices congruent mod 8: blocks are dispatched round-robin over
-// the 8 XCDs, so the waves that share a chunk's W/Qg/Khat/A_qk share one L2.
+// LDS image of one chunk's operands.  Rows are XOR-swizzled in 16-byte units
+// so that the 16 rows a ds_read_b128 touches fall in distinct banks.
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(64) void prefill_state_kernel(
+struct StateLayout {
+    static constexpr int ES = sizeof(E);
+    static constexpr int W_RB = DK * ES;                    // row bytes of W / Qg
+    static constexpr int K_RB = CHUNK * ES;                 // row bytes of Khat^T / A_qk / U^T
+    static constexpr int OFF_W = 0;
+    static constexpr int OFF_Q = OFF_W + CHUNK * W_RB;
+    static constexpr int OFF_K = OFF_Q + CHUNK * W_RB;
+    static constexpr int OFF_A = OFF_K + DK * K_RB;
+    static constexpr int OFF_U = OFF_A + CHUNK * K_RB;      // this slice's 16 rows of U^T
+    static constexpr int OFF_G = OFF_U + 16 * K_RB;
+    static constexpr int BYTES = OFF_G + DK * 4;
+    static constexpr int NBUF = 2 * BYTES <= 150 * 1024 ? 2 : 1;
+    static constexpr int UNITS = BYTES / 16;
+    static constexpr int LOADERS = 3;                       // waves 1..3
+    static constexpr int PER_LANE = (UNITS + 64 * LOADERS - 1) / (64 * LOADERS);
+};
+
+__device__ __forceinline__ int swz(int row, int unit, int row_bytes) {
+    const int units = row_bytes / 16;
+    const int rows_per_256 = row_bytes >= 256 ? 1 : 256 / row_bytes;
+    return row * row_bytes + 16 * (unit ^ ((row / rows_per_256) % units));
+}
+
+// 16-byte units of one chunk's operands, in LDS-image order:
+// unit x -> (global source, LDS byte offset).
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void unit_map(int x, const ChunkBufsC<E>& cb, size_t chh, int j0,
+                                         const unsigned char*& src, int& dst)
+{
+    using L = StateLayout<E, DK, DV>;
+    constexpr int UW = CHUNK * L::W_RB / 16, UK = DK * L::K_RB / 16, UA = CHUNK * L::K_RB / 16;
+    constexpr int UU = 16 * L::K_RB / 16;
+    if (x < UW) {
+        src = (const unsigned char*)(cb.W + chh * CHUNK * DK) + 16 * x;
+        dst = L::OFF_W + swz(x / (L::W_RB / 16), x % (L::W_RB / 16), L::W_RB);
+    } else if ((x -= UW) < UW) {
+        src = (const unsigned char*)(cb.Qg + chh * CHUNK * DK) + 16 * x;
+        dst = L::OFF_Q + swz(x / (L::W_RB / 16), x % (L::W_RB / 16), L::W_RB);
+    } else if ((x -= UW) < UK) {
+        src = (const unsigned char*)(cb.Kh + chh * DK * CHUNK) + 16 * x;
+        dst = L::OFF_K + swz(x / (L::K_RB / 16), x % (L::K_RB / 16), L::K_RB);
+    } else if ((x -= UK) < UA) {
+        src = (const unsigned char*)(cb.Aqk + chh * CHUNK * CHUNK) + 16 * x;
+        dst = L::OFF_A + swz(x / (L::K_RB / 16), x % (L::K_RB / 16), L::K_RB);
+    } else if ((x -= UA) < UU) {
+        src = (const unsigned char*)(cb.Ut + (chh * DV + j0) * CHUNK) + 16 * x;
+        dst = L::OFF_U + 16 * x;
+    } else {
+        x -= UU;
+        src = (const unsigned char*)(cb.gC + chh * DK) + 16 * x;
+        dst = L::OFF_G + 16 * x;
+    }
+}
+
+template <typename E, int DK, int DV>
+struct Stager {
+    using L = StateLayout<E, DK, DV>;
+    f32x4 reg[L::PER_LANE];
+    int dst[L::PER_LANE];
+
+    __device__ __forceinline__ void issue(const ChunkBufsC<E>& cb, size_t chh, int j0, int lt) {
+#pragma unroll
+        for (int i = 0; i < L::PER_LANE; ++i) {
+            const int x = lt + 64 * L::LOADERS * i;
+            dst[i] = -1;
+            if (x < L::UNITS) {
+                const unsigned char* src;
+                unit_map<E, DK, DV>(x, cb, chh, j0, src, dst[i]);
+                reg[i] = *reinterpret_cast<const f32x4*>(src);
+            }
+        }
+    }
+    __device__ __forceinline__ void commit(unsigned char* buf) {
+#pragma unroll
+        for (int i = 0; i < L::PER_LANE; ++i)
+            if (dst[i] >= 0) *reinterpret_cast<f32x4*>(buf + dst[i]) = reg[i];
+    }
+};
+
+// 8 operand elements at (row, element offset) of a swizzled LDS matrix
+template <typename E>
+__device__ __forceinline__ typename Vec<E>::v8 lds_frag(const unsigned char* base, int row,
+                                                        int elem, int row_bytes)
+{
+    using V8 = typename Vec<E>::v8;
+    if constexpr (sizeof(E) == 2) {
+        return *reinterpret_cast<const V8*>(base + swz(row, elem * 2 / 16, row_bytes));
+    } else {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(base + swz(row, elem * 4 / 16, row_bytes));
+        const f32x4 b = *reinterpret_cast<const f32x4*>(base + swz(row, elem * 4 / 16 + 1, row_bytes));
+        return V8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+}
+
+// Workgroups are grouped so that the DV/16 slices of one (sequence, head)
+// have block indices congruent mod 8: blocks are dispatched round-robin over
+// the 8 XCDs, so the slices that read the same chunk operands share one L2.
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void prefill_state_kernel(
     ChunkBufsC<E> cb, const int32_t* __restrict__ seq_chunk_start,
     const ChunkInfo* __restrict__ chunks, const float* __restrict__ S0,
     float* __restrict__ S_final, E* __restrict__ o, int H, int n_pairs)
 {
+    using L = StateLayout<E, DK, DV>;
     using V4 = typename Vec<E>::v4;
     using V8 = typename Vec<E>::v8;
     constexpr int NSL = DV / 16;  // value slices per head
     constexpr int KT = DK / 16;   // accumulator tiles of S
     constexpr int KS = DK / 32;   // contraction steps over key channels
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::NBUF * L::BYTES];
 
     const int b = blockIdx.x;
     const int xcd = b & 7, q8 = b >> 3;
@@ -51,85 +153,121 @@ __global__ __launch_bounds__(64) void prefill_state_kernel(
     const int pair = grp * 8 + xcd;
     if (pair >= n_pairs) return;
     const int s = pair / H, h = pair % H;
-    const int l = threadIdx.x, g = l >> 4, ln = l & 15;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int l = tid & 63, g = l >> 4, ln = l & 15;
     const int j0 = slice * 16;
-
-    // S tile t: lane holds S[16t + 4g + i][j0 + ln], i = 0..3
-    f32x4 S[KT];
-    const size_t sbase = (size_t)pair * DK * DV;
-#pragma unroll
-    for (int t = 0; t < KT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[t][i] = S0 ? S0[sbase + (size_t)(16 * t + 4 * g + i) * DV + j0 + ln] : 0.f;
-
     const int c_begin = seq_chunk_start[s], c_end = seq_chunk_start[s + 1];
+    const size_t sbase = (size_t)pair * DK * DV;
+
+    Stager<E, DK, DV> stage;
+    const int lt = tid - 64;  // loader lane index 0..191
+    if (wave > 0 && c_begin < c_end) {
+        stage.issue(cb, (size_t)c_begin * H + h, j0, lt);
+        stage.commit(smem);
+    }
+
+    // S tile t: lane holds S[16t + 4g + i][j0 + ln], i = 0..3 (wave 0 only)
+    f32x4 S[KT];
+    if (wave == 0) {
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[t][i] = 0.f;
+        if (S0) {
+#pragma unroll
+            for (int t = 0; t < KT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[t][i] = S0[sbase + (size_t)(16 * t + 4 * g + i) * DV + j0 + ln];
+        }
+    }
+    __syncthreads();
+
     for (int cid = c_begin; cid < c_end; ++cid) {
-        const ChunkInfo ci = chunks[cid];
-        const size_t chh = (size_t)cid * H + h;
+        const int it = cid - c_begin;
+        const unsigned char* buf = smem + (it % L::NBUF) * L::BYTES;
+        if (wave == 0) {
+            const ChunkInfo ci = chunks[cid];
+            // S as an MFMA operand: slots of step ks = rows {32ks+4g..+3, 32ks+16+4g..+3}
+            V8 Sf[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    Sf[ks][i] = from_f32<E>(S[2 * ks][i]);
+                    Sf[ks][4 + i] = from_f32<E>(S[2 * ks + 1][i]);
+                }
 
-        // S as an MFMA operand: slots of step ks = rows {32ks+4g..+3, 32ks+16+4g..+3}
-        V8 Sf[KS];
+            // N = U - W S   (N tile R: lane holds N[16R + 4g + i][j0 + ln])
+            f32x4 N[4];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+            for (int R = 0; R < 4; ++R) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                Sf[ks][i] = from_f32<E>(S[2 * ks][i]);
-                Sf[ks][4 + i] = from_f32<E>(S[2 * ks + 1][i]);
+                for (int ks = 0; ks < KS; ++ks)
+                    acc = mma32(lds_frag<E>(buf + L::OFF_W, 16 * R + ln, 32 * ks + 8 * g, L::W_RB),
+                                Sf[ks], acc);
+                const V4 u = *reinterpret_cast<const V4*>(buf + L::OFF_U + ln * L::K_RB +
+                                                         (16 * R + 4 * g) * L::ES);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) N[R][i] = to_f32(u[i]) - acc[i];
+            }
+            V8 Nf[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    Nf[ks][i] = from_f32<E>(N[2 * ks][i]);
+                    Nf[ks][4 + i] = from_f32<E>(N[2 * ks + 1][i]);
+                }
+
+            // S = Diag(gamma_C) S + Khat^T N   (the serial dependency: issue first)
+#pragma unroll
+            for (int t = 0; t < KT; ++t) {
+                const f32x4 gc = *reinterpret_cast<const f32x4*>(buf + L::OFF_G + (16 * t + 4 * g) * 4);
+                f32x4 acc = S[t] * gc;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    acc = mma32(lds_frag<E>(buf + L::OFF_K, 16 * t + ln, 32 * ks + 8 * g, L::K_RB),
+                                Nf[ks], acc);
+                S[t] = acc;
             }
 
-        // N = U - W S   (N tile R: lane holds N[16R + 4g + i][j0 + ln])
-        f32x4 N[4];
+            // O^T = S0^T Qg^T + N^T A_qk^T with S0 the chunk-start state (held in Sf)
 #pragma unroll
-        for (int R = 0; R < 4; ++R) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const E* wrow = cb.W + (chh * CHUNK + 16 * R + ln) * DK + 8 * g;
+            for (int R = 0; R < 4; ++R) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc = mma32(load_vec<V8>(wrow + 32 * ks), Sf[ks], acc);
-            const V4 u = load_vec<V4>(cb.Ut + (chh * DV + j0 + ln) * CHUNK + 16 * R + 4 * g);
+                for (int ks = 0; ks < KS; ++ks)
+                    acc = mma32(Sf[ks], lds_frag<E>(buf + L::OFF_Q, 16 * R + ln, 32 * ks + 8 * g, L::W_RB),
+                                acc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) N[R][i] = to_f32(u[i]) - acc[i];
+                for (int ks = 0; ks <= R / 2; ++ks)
+                    acc = mma32(Nf[ks], lds_frag<E>(buf + L::OFF_A, 16 * R + ln, 32 * ks + 8 * g, L::K_RB),
+                                acc);
+                const int r = 16 * R + ln;
+                if (r < ci.len) {
+                    V4 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[i]);
+                    store_vec(o + ((size_t)(ci.start + r) * H + h) * DV + j0 + 4 * g, w);
+                }
+            }
+        } else if (L::NBUF == 2 && cid + 1 < c_end) {
+            stage.issue(cb, (size_t)(cid + 1) * H + h, j0, lt);
+            stage.commit(smem + ((it + 1) % 2) * L::BYTES);
         }
-        V8 Nf[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                Nf[ks][i] = from_f32<E>(N[2 * ks][i]);
-                Nf[ks][4 + i] = from_f32<E>(N[2 * ks + 1][i]);
+        __syncthreads();
+        if (L::NBUF == 1 && cid + 1 < c_end) {
+            if (wave > 0) {
+                stage.issue(cb, (size_t)(cid + 1) * H + h, j0, lt);
+                stage.commit(smem);
             }
-
-        // O^T = S^T Qg^T + N^T A_qk^T   (tile R: lane holds O[16R + ln][j0 + 4g + i])
-#pragma unroll
-        for (int R = 0; R < 4; ++R) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const E* qrow = cb.Qg + (chh * CHUNK + 16 * R + ln) * DK + 8 * g;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc = mma32(Sf[ks], load_vec<V8>(qrow + 32 * ks), acc);
-            const E* arow = cb.Aqk + (chh * CHUNK + 16 * R + ln) * CHUNK + 8 * g;
-#pragma unroll
-            for (int ks = 0; ks <= R / 2; ++ks) acc = mma32(Nf[ks], load_vec<V8>(arow + 32 * ks), acc);
-            const int r = 16 * R + ln;
-            if (r < ci.len) {
-                V4 w;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[i]);
-                store_vec(o + ((size_t)(ci.start + r) * H + h) * DV + j0 + 4 * g, w);
-            }
-        }
-
-        // S = Diag(gamma_C) S + Khat^T N
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            const f32x4 gc = load_vec<f32x4>(cb.gC + chh * DK + 16 * t + 4 * g);
-            S[t] *= gc;
-            const E* krow = cb.Kh + (chh * DK + 16 * t + ln) * CHUNK + 8 * g;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) S[t] = mma32(load_vec<V8>(krow + 32 * ks), Nf[ks], S[t]);
+            __syncthreads();
         }
     }
 
-    if (S_final) {
+    if (wave == 0 && S_final) {
 #pragma unroll
         for (int t = 0; t < KT; ++t)
 #pragma unroll
@@ -148,7 +286,7 @@ static hipError_t launch_state_t(void* const* bufs, const int32_t* seq_chunk_sta
     const long long blocks = (long long)groups * 8 * (DV / 16);
     ChunkBufsC<E> cb{(const E*)bufs[0], (const E*)bufs[1], (const E*)bufs[2],
                      (const E*)bufs[3], (const E*)bufs[4], (const float*)bufs[5]};
-    hipLaunchKernelGGL((prefill_state_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(64), 0,
+    hipLaunchKernelGGL((prefill_state_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, cb, seq_chunk_start, chunks, S0, S_final, (E*)o, H, n_pairs);
     return hipGetLastError();
 }
