@@ -25,10 +25,11 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Workspace layout of one prefill call.
+// Workspace layout of one prefill call: one record per (chunk, head) slot,
+// then the chunk table.
 struct Plan {
     int64_t max_chunks = 0;
-    size_t off[6] = {};     // W, Qg, Kh, Aqk, Ut, gC
+    size_t rec_bytes = 0;   // bytes of one (chunk, head) record
     size_t off_seq = 0;     // seq_chunk_start [N+1]
     size_t off_chunks = 0;  // ChunkInfo [max_chunks]
     size_t total = 0;
@@ -37,22 +38,10 @@ struct Plan {
 bool make_plan(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype,
                Plan& p) {
     if (T < 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return false;
-    const size_t es = dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    const int es = dtype == KDA_DTYPE_BF16 ? 2 : 4;
     p.max_chunks = (T + kda::CHUNK - 1) / kda::CHUNK + N;
-    const size_t units = (size_t)p.max_chunks * (size_t)H;
-    const size_t per[6] = {
-        (size_t)kda::CHUNK * dk * es,        // W
-        (size_t)kda::CHUNK * dk * es,        // Qg
-        (size_t)dk * kda::CHUNK * es,        // Kh
-        (size_t)kda::CHUNK * kda::CHUNK * es,  // Aqk
-        (size_t)dv * kda::CHUNK * es,        // Ut
-        (size_t)dk * 4,                      // gC
-    };
-    size_t at = 0;
-    for (int i = 0; i < 6; ++i) {
-        p.off[i] = at;
-        at += align256(units * per[i]);
-    }
+    p.rec_bytes = kda::rec_layout(es, dk, dv).bytes;
+    size_t at = align256((size_t)p.max_chunks * (size_t)H * p.rec_bytes);
     p.off_seq = at;
     at += align256(((size_t)N + 1) * 4);
     p.off_chunks = at;
@@ -174,8 +163,6 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
                 return fail(KDA_ERR_HIP, std::string("hipMallocAsync: ") + hipGetErrorString(e));
             owned = true;
         }
-        void* bufs[6];
-        for (int i = 0; i < 6; ++i) bufs[i] = ws + plan.off[i];
         int32_t* seq_start = reinterpret_cast<int32_t*>(ws + plan.off_seq);
         kda::ChunkInfo* chunks = reinterpret_cast<kda::ChunkInfo*>(ws + plan.off_chunks);
 
@@ -190,12 +177,12 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
                 st = check_launch(kda::launch_prefill_intra(q, k, v, log_alpha, beta, chunks,
                                                             seq_start + num_seqs,
                                                             (int)plan.max_chunks, H, dk, dv, bf16,
-                                                            bufs, stream),
+                                                            ws, stream),
                                   "intra-chunk kernel", stream);
                 timer.mark("prefill_intra");
             }
             if (st == KDA_OK) {
-                st = check_launch(kda::launch_prefill_state(bufs, seq_start, chunks, initial_state,
+                st = check_launch(kda::launch_prefill_state(ws, seq_start, chunks, initial_state,
                                                             final_state, o, num_seqs, H, dk, dv,
                                                             bf16, stream),
                                   "state kernel", stream);

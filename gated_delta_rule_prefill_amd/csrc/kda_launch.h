@@ -17,16 +17,39 @@ struct ChunkInfo {
     int32_t pad;
 };
 
+// Per-(chunk, head) record of the chunk intermediates in the workspace
+// (byte offsets; es = element size of q/k/v, 2 or 4).  One contiguous
+// record lets the state kernel stage a chunk with loop-invariant offsets.
+//   W    [64][dk]   e^g-decayed keys through the UT transform, channels perm32
+//   Qg   [64][dk]   e^g-decayed queries, channels perm32
+//   Kh   [dk][64]   (e^{g_C - g} k)^T, tokens perm32
+//   Aqk  [64][64]   intra-chunk query-key weights, key tokens perm32
+//   gC   [dk] fp32  e^{g_C}
+//   Ut   [dv][64]   U^T, natural token order
+struct RecLayout {
+    size_t w, q, k, a, g, u, bytes;
+};
+constexpr RecLayout rec_layout(int es, int dk, int dv) {
+    return RecLayout{0,
+                     (size_t)CHUNK * dk * es,
+                     (size_t)2 * CHUNK * dk * es,
+                     (size_t)3 * CHUNK * dk * es,
+                     (size_t)3 * CHUNK * dk * es + (size_t)CHUNK * CHUNK * es,
+                     (size_t)3 * CHUNK * dk * es + (size_t)CHUNK * CHUNK * es + (size_t)dk * 4,
+                     ((size_t)3 * CHUNK * dk * es + (size_t)CHUNK * CHUNK * es + (size_t)dk * 4 +
+                      (size_t)dv * CHUNK * es + 255) & ~(size_t)255};
+}
+
 hipError_t launch_chunk_table(const int32_t* cu, int64_t T, int N, int32_t* seq_chunk_start,
                               ChunkInfo* chunks, int max_chunks, hipStream_t stream);
 
-// bufs: W, Qg, Kh, Aqk, Ut, gC (per-chunk intermediates in the workspace)
+// rec: [max_chunks * H] records of rec_layout() bytes
 hipError_t launch_prefill_intra(const void* q, const void* k, const void* v, const float* la,
                                 const float* beta, const ChunkInfo* chunks,
                                 const int32_t* n_chunks, int max_chunks, int H, int dk, int dv,
-                                bool bf16_io, void* const* bufs, hipStream_t stream);
+                                bool bf16_io, void* rec, hipStream_t stream);
 
-hipError_t launch_prefill_state(void* const* bufs, const int32_t* seq_chunk_start,
+hipError_t launch_prefill_state(const void* rec, const int32_t* seq_chunk_start,
                                 const ChunkInfo* chunks, const float* S0, float* S_final,
                                 void* o, int N, int H, int dk, int dv, bool bf16_io,
                                 hipStream_t stream);

@@ -16,8 +16,8 @@
 //   W         = T (e^g * K),   U = T V             MFMA
 //   Khat      = e^{g_C - g} * K,  Qg = e^g * Q,  gamma_C = e^{g_C}
 //
-// and stores W, U, Khat^T, Qg, A_qk and gamma_C for the sequential state
-// kernel.  The state kernel then needs, per chunk, only
+// and stores W, U, Khat^T, Qg, A_qk and gamma_C (one record per chunk and
+// head) for the sequential state kernel.  The state kernel then needs, per chunk, only
 //   N = U - W S,  O = Qg S + A_qk N,  S <- Diag(gamma_C) S + Khat^T N.
 //
 // The inverse of the unit lower-triangular I + A_kk is built blockwise: the
@@ -57,15 +57,25 @@ struct IntraLayout {
     static constexpr int BYTES = OFF_BETA + CHUNK * 4;
 };
 
-// Pointers to the per-(chunk, head) intermediates in the workspace.
-template <typename E>
-struct ChunkBufs {
-    E* W;        // [NC*H][64][DK]   channels in perm32 order
-    E* Qg;       // [NC*H][64][DK]   channels in perm32 order
-    E* Kh;       // [NC*H][DK][64]   Khat^T, tokens in perm32 order
-    E* Aqk;      // [NC*H][64][64]   key tokens in perm32 order
-    E* Ut;       // [NC*H][DV][64]   U^T, natural token order
-    float* gC;   // [NC*H][DK]       gamma_C = exp(g_C)
+// Pointers into one (chunk, head) record of the workspace (see rec_layout).
+template <typename E, int DK, int DV>
+struct ChunkOut {
+    E* W;
+    E* Qg;
+    E* Kh;
+    E* Aqk;
+    float* gC;
+    E* Ut;
+    __device__ ChunkOut(unsigned char* rec, size_t chh) {
+        constexpr RecLayout RL = rec_layout(sizeof(E), DK, DV);
+        unsigned char* base = rec + chh * RL.bytes;
+        W = reinterpret_cast<E*>(base + RL.w);
+        Qg = reinterpret_cast<E*>(base + RL.q);
+        Kh = reinterpret_cast<E*>(base + RL.k);
+        Aqk = reinterpret_cast<E*>(base + RL.a);
+        gC = reinterpret_cast<float*>(base + RL.g);
+        Ut = reinterpret_cast<E*>(base + RL.u);
+    }
 };
 
 // 8 consecutive operand elements from LDS, optionally scaled per channel.
@@ -114,29 +124,33 @@ __device__ __forceinline__ float x_elem(const float* sAL, int r, int c) {
     return r == c ? 1.f : (r > c ? sAL[c * LA + r] : 0.f);
 }
 
-// X block (R, I), R > I, by one wave on fp32 MFMA:
+// X block (R, I), R > I (NJ = R - I), by one wave on fp32 MFMA:
 //   X_RI = -X_RR * sum_{J=I}^{R-1} A_RJ X_JI
 // The first product's accumulator feeds the second as its B operand:
 // slot (g, m) carries contraction index 4g + m in both.
-template <int LA>
+template <int LA, int NJ>
 __device__ __forceinline__ void x_block(float* sAL, int R, int I, int g, int ln) {
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    for (int J = I; J < R; ++J) {
+    float a[NJ][4], b[NJ][4], xr[4];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+        const int J = I + jj;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int kk = 4 * g + m;
-            const float a = sAL[(16 * R + ln) * LA + 16 * J + kk];
-            const float b = x_elem<LA>(sAL, 16 * J + kk, 16 * I + ln);
-            z = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, z, 0, 0, 0);
+            a[jj][m] = sAL[(16 * R + ln) * LA + 16 * J + kk];
+            b[jj][m] = x_elem<LA>(sAL, 16 * J + kk, 16 * I + ln);
         }
     }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xr[m] = -x_elem<LA>(sAL, 16 * R + ln, 16 * R + 4 * g + m);
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) z = __builtin_amdgcn_mfma_f32_16x16x4f32(a[jj][m], b[jj][m], z, 0, 0, 0);
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int kk = 4 * g + m;
-        const float a = -x_elem<LA>(sAL, 16 * R + ln, 16 * R + kk);
-        x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, z[m], x, 0, 0, 0);
-    }
+    for (int m = 0; m < 4; ++m) x = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[m], z[m], x, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sAL[(16 * I + ln) * LA + 16 * R + 4 * g + i] = x[i];
 }
@@ -146,7 +160,7 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const ChunkInfo* __restrict__ chunks, const int32_t* __restrict__ n_chunks_ptr, int H,
-    ChunkBufs<E> out)
+    unsigned char* __restrict__ rec)
 {
     using L = IntraLayout<E, DK, DV>;
     using V4 = typename Vec<E>::v4;
@@ -171,6 +185,7 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     const int h = blockIdx.y;
     const ChunkInfo ci = chunks[cid];
     const size_t chh = (size_t)cid * H + h;
+    const ChunkOut<E, DK, DV> out(rec, chh);
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -255,7 +270,7 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     }
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
-        E* dst = out.Kh + (chh * DK + c0 + e) * CHUNK;
+        E* dst = out.Kh + (c0 + e) * CHUNK;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             V4 w;
@@ -263,7 +278,7 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
             for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(ell[4 * r4 + i][e]);
             store_vec(dst + perm_index(16 * R + 4 * r4), w);
         }
-        if (R == 0) out.gC[chh * DK + c0 + e] = eTE[e];
+        if (R == 0) out.gC[c0 + e] = eTE[e];
     }
     __syncthreads();
 
@@ -272,15 +287,17 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     for (int p = wave; p < 10; p += 4) {
         const int PR = kPairR[p], PI = kPairI[p];
         const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        V8 a[KS], b[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int cb = 32 * s + 8 * g;
-            const V8 a = frag8<E>(sKP + (16 * PR + ln) * L::LK + cb);
-            const V8 b = PR == PI ? frag8<E>(sKD + (16 * PI + ln) * L::LK + cb)
-                                  : frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f + cb);
-            acc = mma32(a, b, acc);
+            a[s] = frag8<E>(sKP + (16 * PR + ln) * L::LK + cb);
+            b[s] = PR == PI ? frag8<E>(sKD + (16 * PI + ln) * L::LK + cb)
+                            : frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f + cb);
         }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mma32(a[s], b[s], acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * PR + 4 * g + i, col = 16 * PI + ln;
@@ -304,9 +321,9 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
             sKP[row * L::LK + c0 + e] = from_f32<E>(qr[r][e]);
             const E val = from_f32<E>(qr[r][e] * eB[e]);
             if constexpr (CPT == 2) qg2[e] = val;
-            else out.Qg[(chh * CHUNK + row) * DK + perm_index(c0 + e)] = val;
+            else out.Qg[row * DK + perm_index(c0 + e)] = val;
         }
-        if constexpr (CPT == 2) store_vec(out.Qg + (chh * CHUNK + row) * DK + perm_index(c0), qg2);
+        if constexpr (CPT == 2) store_vec(out.Qg + row * DK + perm_index(c0), qg2);
     }
     __syncthreads();
 
@@ -314,15 +331,17 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     for (int p = wave; p < 10; p += 4) {
         const int PR = kPairR[p], PI = kPairI[p];
         const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        V8 a[KS], b[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int cb = 32 * s + 8 * g;
-            const V8 a = PR == PI ? frag8<E>(sKD + (16 * PI + ln) * L::LK + cb)
-                                  : frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f + cb);
-            const V8 b = frag8<E>(sKP + (16 * PR + ln) * L::LK + cb);
-            acc = mma32(a, b, acc);
+            a[s] = PR == PI ? frag8<E>(sKD + (16 * PI + ln) * L::LK + cb)
+                            : frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f + cb);
+            b[s] = frag8<E>(sKP + (16 * PR + ln) * L::LK + cb);
         }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mma32(a[s], b[s], acc);
         const int r = 16 * PR + ln;
         V4 w;
 #pragma unroll
@@ -330,14 +349,14 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
             const int col = 16 * PI + 4 * g + i;
             w[i] = from_f32<E>(r >= col ? acc[i] : 0.f);
         }
-        store_vec(out.Aqk + (chh * CHUNK + r) * CHUNK + perm_index(16 * PI + 4 * g), w);
+        store_vec(out.Aqk + r * CHUNK + perm_index(16 * PI + 4 * g), w);
     }
     for (int u = wave - 2; u >= 0 && u < 6; u += 2) {
         const int UR = kUpperR[u], UI = kUpperI[u];
         V4 z;
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = from_f32<E>(0.f);
-        store_vec(out.Aqk + (chh * CHUNK + 16 * UR + ln) * CHUNK + perm_index(16 * UI + 4 * g), z);
+        store_vec(out.Aqk + (16 * UR + ln) * CHUNK + perm_index(16 * UI + 4 * g), z);
     }
     __syncthreads();   // sKP / sKD dead: their bytes become kgT and vT
 
@@ -390,11 +409,11 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     __syncthreads();
 
     // ---- phase 3b-d: off-diagonal blocks of X, one block-diagonal at a time ----
-    if (wave < 3) x_block<L::LA>(sAL, wave + 1, wave, g, ln);          // (1,0) (2,1) (3,2)
+    if (wave < 3) x_block<L::LA, 1>(sAL, wave + 1, wave, g, ln);          // (1,0) (2,1) (3,2)
     __syncthreads();
-    if (wave < 2) x_block<L::LA>(sAL, wave + 2, wave, g, ln);          // (2,0) (3,1)
+    if (wave < 2) x_block<L::LA, 2>(sAL, wave + 2, wave, g, ln);          // (2,0) (3,1)
     __syncthreads();
-    if (wave == 0) x_block<L::LA>(sAL, 3, 0, g, ln);                   // (3,0)
+    if (wave == 0) x_block<L::LA, 3>(sAL, 3, 0, g, ln);                   // (3,0)
     __syncthreads();
 
     // ---- phase 3e: T = X Diag(beta) in the operand dtype ----------------------
@@ -407,36 +426,50 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     // ---- phase 4: W^T = (e^g K)^T T^T and U = T V on MFMA ---------------------
     // T is lower triangular, so output block R' only needs key tokens < 16R'+16.
     for (int ct = wave; ct < DK / 16; ct += 4) {
+        V8 a[2], b[4][2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) a[s] = frag8<E>(sKGT + (16 * ct + ln) * L::LT + 32 * s + 8 * g);
+#pragma unroll
+        for (int Rq = 0; Rq < 4; ++Rq)
+#pragma unroll
+            for (int s = 0; s <= Rq / 2; ++s) b[Rq][s] = frag8<E>(sTL + (16 * Rq + ln) * L::LT + 32 * s + 8 * g);
+        f32x4 acc[4];
+#pragma unroll
+        for (int Rq = 0; Rq < 4; ++Rq) acc[Rq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int Rq = 2 * s; Rq < 4; ++Rq) acc[Rq] = mma32(a[s], b[Rq][s], acc[Rq]);
 #pragma unroll
         for (int Rq = 0; Rq < 4; ++Rq) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s <= Rq / 2; ++s) {
-                const V8 a = frag8<E>(sKGT + (16 * ct + ln) * L::LT + 32 * s + 8 * g);
-                const V8 b = frag8<E>(sTL + (16 * Rq + ln) * L::LT + 32 * s + 8 * g);
-                acc = mma32(a, b, acc);
-            }
             V4 w;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[i]);
+            for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[Rq][i]);
             const int r = 16 * Rq + ln;
-            store_vec(out.W + (chh * CHUNK + r) * DK + perm_index(16 * ct + 4 * g), w);
+            store_vec(out.W + r * DK + perm_index(16 * ct + 4 * g), w);
         }
     }
     for (int ct = wave; ct < DV / 16; ct += 4) {
+        V8 a[4][2], b[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) b[s] = frag8<E>(sVT + (16 * ct + ln) * L::LT + 32 * s + 8 * g);
+#pragma unroll
+        for (int Rq = 0; Rq < 4; ++Rq)
+#pragma unroll
+            for (int s = 0; s <= Rq / 2; ++s) a[Rq][s] = frag8<E>(sTL + (16 * Rq + ln) * L::LT + 32 * s + 8 * g);
+        f32x4 acc[4];
+#pragma unroll
+        for (int Rq = 0; Rq < 4; ++Rq) acc[Rq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int Rq = 2 * s; Rq < 4; ++Rq) acc[Rq] = mma32(a[Rq][s], b[s], acc[Rq]);
 #pragma unroll
         for (int Rq = 0; Rq < 4; ++Rq) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s <= Rq / 2; ++s) {
-                const V8 a = frag8<E>(sTL + (16 * Rq + ln) * L::LT + 32 * s + 8 * g);
-                const V8 b = frag8<E>(sVT + (16 * ct + ln) * L::LT + 32 * s + 8 * g);
-                acc = mma32(a, b, acc);
-            }
             V4 w;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[i]);
-            store_vec(out.Ut + (chh * DV + 16 * ct + ln) * CHUNK + 16 * Rq + 4 * g, w);
+            for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[Rq][i]);
+            store_vec(out.Ut + (16 * ct + ln) * CHUNK + 16 * Rq + 4 * g, w);
         }
     }
 }
@@ -444,25 +477,24 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
 template <typename E, int DK, int DV>
 static hipError_t launch_intra_t(const void* q, const void* k, const void* v, const float* la,
                                  const float* beta, const ChunkInfo* chunks,
-                                 const int32_t* n_chunks, int max_chunks, int H, void* const* bufs,
+                                 const int32_t* n_chunks, int max_chunks, int H, void* rec,
                                  hipStream_t stream)
 {
-    ChunkBufs<E> b{(E*)bufs[0], (E*)bufs[1], (E*)bufs[2], (E*)bufs[3], (E*)bufs[4], (float*)bufs[5]};
     hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV>), dim3(max_chunks, H), dim3(256), 0, stream,
-                       (const E*)q, (const E*)k, (const E*)v, la, beta, chunks, n_chunks, H, b);
+                       (const E*)q, (const E*)k, (const E*)v, la, beta, chunks, n_chunks, H,
+                       (unsigned char*)rec);
     return hipGetLastError();
 }
 
-// bufs: W, Qg, Kh, Aqk, Ut, gC
 hipError_t launch_prefill_intra(const void* q, const void* k, const void* v, const float* la,
                                 const float* beta, const ChunkInfo* chunks,
                                 const int32_t* n_chunks, int max_chunks, int H, int dk, int dv,
-                                bool bf16_io, void* const* bufs, hipStream_t stream)
+                                bool bf16_io, void* rec, hipStream_t stream)
 {
 #define KDA_INTRA_CASE(E, DK_, DV_)                                                               \
     if (dk == DK_ && dv == DV_)                                                                  \
         return launch_intra_t<E, DK_, DV_>(q, k, v, la, beta, chunks, n_chunks, max_chunks, H,   \
-                                           bufs, stream);
+                                           rec, stream);
     if (bf16_io) {
         KDA_INTRA_CASE(bf16, 128, 128)
         KDA_INTRA_CASE(bf16, 64, 64)

@@ -10,10 +10,17 @@
 //
 // One workgroup per (sequence, head, 16 value columns): the columns of S evolve
 // independently, so a head's state is split over DV/16 workgroups that never
-// communicate.  Wave 0 computes; it keeps the fp32 state tile (DK x 16) in MFMA
-// accumulator registers for the whole sequence.  Waves 1-3 stage the next
-// chunk's operands into an LDS double buffer while wave 0 works on the current
-// one, so the serial loop never waits on HBM/L2 latency.
+// communicate.  Roles inside the workgroup:
+//   wave 0   the serial chain N, then S; it keeps the fp32 state tile (DK x 16)
+//            in MFMA accumulator registers for the whole sequence;
+//   wave 1   the output O of the same chunk, from the chunk-start state and N
+//            that wave 0 hands over through a small LDS area;
+//   wave 2   stages W into an LDS double buffer and touches the operands a
+//            few chunks ahead so they sit in L2.
+// Waves 0 and 1 load their other operand fragments straight from L2 into
+// registers one chunk ahead (two register sets, loop unrolled by two).  The
+// split keeps every wave under the 63 vector-memory operations one wave may
+// have in flight, so loads for the next chunk never stall the current one.
 //
 // Every product takes its register-resident operand (S or N) straight from
 // accumulator tiles: a 16x16 tile gives lane group g rows 4g..4g+3, the slot
@@ -22,130 +29,98 @@
 
 namespace kda {
 
-template <typename E>
-struct ChunkBufsC {
-    const E* W;
-    const E* Qg;
-    const E* Kh;
-    const E* Aqk;
-    const E* Ut;
-    const float* gC;
-};
+constexpr int PREFETCH_DIST = 3;   // chunks between the L2 touch and the register load
 
-// LDS image of one chunk's operands.  Rows are XOR-swizzled in 16-byte units
-// so that the 16 rows a ds_read_b128 touches fall in distinct banks.
 template <typename E, int DK, int DV>
-struct StateLayout {
+struct StateCfg {
     static constexpr int ES = sizeof(E);
-    static constexpr int W_RB = DK * ES;                    // row bytes of W / Qg
-    static constexpr int K_RB = CHUNK * ES;                 // row bytes of Khat^T / A_qk / U^T
-    static constexpr int OFF_W = 0;
-    static constexpr int OFF_Q = OFF_W + CHUNK * W_RB;
-    static constexpr int OFF_K = OFF_Q + CHUNK * W_RB;
-    static constexpr int OFF_A = OFF_K + DK * K_RB;
-    static constexpr int OFF_U = OFF_A + CHUNK * K_RB;      // this slice's 16 rows of U^T
-    static constexpr int OFF_G = OFF_U + 16 * K_RB;
-    static constexpr int BYTES = OFF_G + DK * 4;
-    static constexpr int NBUF = 2 * BYTES <= 150 * 1024 ? 2 : 1;
-    static constexpr int UNITS = BYTES / 16;
-    static constexpr int LOADERS = 3;                       // waves 1..3
-    static constexpr int PER_LANE = (UNITS + 64 * LOADERS - 1) / (64 * LOADERS);
+    static constexpr int KS = DK / 32;   // contraction steps over key channels
+    static constexpr int KT = DK / 16;   // accumulator tiles of S
+    static constexpr int NSL = DV / 16;  // value slices per head
+    static constexpr int FRAG = 8 * ES;  // bytes of one operand fragment per lane
+    static constexpr int XFER = (KS + 2) * 64 * FRAG;   // chunk-start S and N
+    static constexpr int W_RS = DK * ES + 16;           // padded LDS row stride of W
+    static constexpr int W_BYTES = CHUNK * W_RS;
+    static constexpr int W_UNITS = CHUNK * DK * ES / 16;
+    static constexpr int W_PER_LANE = W_UNITS / 64;     // 16-byte units per loader lane
+    static constexpr RecLayout RL = rec_layout(ES, DK, DV);
+    static constexpr int LINES = (int)((RL.bytes + 127) / 128);
+    // Two register sets of operands (load one chunk ahead) unless that would
+    // spill: fp32 operands at dk = 128 use one set loaded at the chunk start.
+    static constexpr bool TWO_SETS = ES == 2 || DK == 64;
 };
 
-__device__ __forceinline__ int swz(int row, int unit, int row_bytes) {
-    const int units = row_bytes / 16;
-    const int rows_per_256 = row_bytes >= 256 ? 1 : 256 / row_bytes;
-    return row * row_bytes + 16 * (unit ^ ((row / rows_per_256) % units));
-}
-
-// 16-byte units of one chunk's operands, in LDS-image order:
-// unit x -> (global source, LDS byte offset).
-template <typename E, int DK, int DV>
-__device__ __forceinline__ void unit_map(int x, const ChunkBufsC<E>& cb, size_t chh, int j0,
-                                         const unsigned char*& src, int& dst)
-{
-    using L = StateLayout<E, DK, DV>;
-    constexpr int UW = CHUNK * L::W_RB / 16, UK = DK * L::K_RB / 16, UA = CHUNK * L::K_RB / 16;
-    constexpr int UU = 16 * L::K_RB / 16;
-    if (x < UW) {
-        src = (const unsigned char*)(cb.W + chh * CHUNK * DK) + 16 * x;
-        dst = L::OFF_W + swz(x / (L::W_RB / 16), x % (L::W_RB / 16), L::W_RB);
-    } else if ((x -= UW) < UW) {
-        src = (const unsigned char*)(cb.Qg + chh * CHUNK * DK) + 16 * x;
-        dst = L::OFF_Q + swz(x / (L::W_RB / 16), x % (L::W_RB / 16), L::W_RB);
-    } else if ((x -= UW) < UK) {
-        src = (const unsigned char*)(cb.Kh + chh * DK * CHUNK) + 16 * x;
-        dst = L::OFF_K + swz(x / (L::K_RB / 16), x % (L::K_RB / 16), L::K_RB);
-    } else if ((x -= UK) < UA) {
-        src = (const unsigned char*)(cb.Aqk + chh * CHUNK * CHUNK) + 16 * x;
-        dst = L::OFF_A + swz(x / (L::K_RB / 16), x % (L::K_RB / 16), L::K_RB);
-    } else if ((x -= UA) < UU) {
-        src = (const unsigned char*)(cb.Ut + (chh * DV + j0) * CHUNK) + 16 * x;
-        dst = L::OFF_U + 16 * x;
-    } else {
-        x -= UU;
-        src = (const unsigned char*)(cb.gC + chh * DK) + 16 * x;
-        dst = L::OFF_G + 16 * x;
-    }
-}
-
-template <typename E, int DK, int DV>
-struct Stager {
-    using L = StateLayout<E, DK, DV>;
-    f32x4 reg[L::PER_LANE];
-    int dst[L::PER_LANE];
-
-    __device__ __forceinline__ void issue(const ChunkBufsC<E>& cb, size_t chh, int j0, int lt) {
-#pragma unroll
-        for (int i = 0; i < L::PER_LANE; ++i) {
-            const int x = lt + 64 * L::LOADERS * i;
-            dst[i] = -1;
-            if (x < L::UNITS) {
-                const unsigned char* src;
-                unit_map<E, DK, DV>(x, cb, chh, j0, src, dst[i]);
-                reg[i] = *reinterpret_cast<const f32x4*>(src);
-            }
-        }
-    }
-    __device__ __forceinline__ void commit(unsigned char* buf) {
-#pragma unroll
-        for (int i = 0; i < L::PER_LANE; ++i)
-            if (dst[i] >= 0) *reinterpret_cast<f32x4*>(buf + dst[i]) = reg[i];
-    }
+// Operands of one chunk as seen by the serial wave (this lane's fragments).
+template <typename E, int DK>
+struct SerialOps {
+    typename Vec<E>::v8 k[DK / 16][2];   // Khat^T rows 16t + ln
+    f32x4 gc[DK / 16];                   // gamma_C rows 16t + 4g .. +3
+    typename Vec<E>::v4 u[4];            // U^T[j0 + ln][16R + 4g .. +3]
 };
 
-// 8 operand elements at (row, element offset) of a swizzled LDS matrix
-template <typename E>
-__device__ __forceinline__ typename Vec<E>::v8 lds_frag(const unsigned char* base, int row,
-                                                        int elem, int row_bytes)
+// Operands of one chunk as seen by the output wave.
+template <typename E, int DK>
+struct OutputOps {
+    typename Vec<E>::v8 q[4][DK / 32];   // Qg rows 16R + ln
+    typename Vec<E>::v8 a[4][2];         // A_qk rows 16R + ln (steps ks <= R/2)
+    int start, len;
+};
+
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void load_serial(SerialOps<E, DK>& op, const unsigned char* r, int g,
+                                            int ln, int j0)
 {
+    using C = StateCfg<E, DK, DV>;
     using V8 = typename Vec<E>::v8;
-    if constexpr (sizeof(E) == 2) {
-        return *reinterpret_cast<const V8*>(base + swz(row, elem * 2 / 16, row_bytes));
-    } else {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(base + swz(row, elem * 4 / 16, row_bytes));
-        const f32x4 b = *reinterpret_cast<const f32x4*>(base + swz(row, elem * 4 / 16 + 1, row_bytes));
-        return V8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    using V4 = typename Vec<E>::v4;
+    const E* K = reinterpret_cast<const E*>(r + C::RL.k);
+    const float* G = reinterpret_cast<const float*>(r + C::RL.g);
+    const E* U = reinterpret_cast<const E*>(r + C::RL.u);
+#pragma unroll
+    for (int t = 0; t < C::KT; ++t) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) op.k[t][ks] = load_vec<V8>(K + (16 * t + ln) * CHUNK + 32 * ks + 8 * g);
+        op.gc[t] = load_vec<f32x4>(G + 16 * t + 4 * g);
     }
+#pragma unroll
+    for (int R = 0; R < 4; ++R) op.u[R] = load_vec<V4>(U + (j0 + ln) * CHUNK + 16 * R + 4 * g);
+}
+
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void load_output(OutputOps<E, DK>& op, const unsigned char* r,
+                                            const ChunkInfo* ci, int g, int ln)
+{
+    using C = StateCfg<E, DK, DV>;
+    using V8 = typename Vec<E>::v8;
+    const E* Q = reinterpret_cast<const E*>(r + C::RL.q);
+    const E* A = reinterpret_cast<const E*>(r + C::RL.a);
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) op.q[R][ks] = load_vec<V8>(Q + (16 * R + ln) * DK + 32 * ks + 8 * g);
+#pragma unroll
+        for (int ks = 0; ks <= R / 2; ++ks) op.a[R][ks] = load_vec<V8>(A + (16 * R + ln) * CHUNK + 32 * ks + 8 * g);
+    }
+    op.start = ci->start;
+    op.len = ci->len;
 }
 
 // Workgroups are grouped so that the DV/16 slices of one (sequence, head)
 // have block indices congruent mod 8: blocks are dispatched round-robin over
 // the 8 XCDs, so the slices that read the same chunk operands share one L2.
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void prefill_state_kernel(
-    ChunkBufsC<E> cb, const int32_t* __restrict__ seq_chunk_start,
+__global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_state_kernel(
+    const unsigned char* __restrict__ rec, const int32_t* __restrict__ seq_chunk_start,
     const ChunkInfo* __restrict__ chunks, const float* __restrict__ S0,
     float* __restrict__ S_final, E* __restrict__ o, int H, int n_pairs)
 {
-    using L = StateLayout<E, DK, DV>;
+    using C = StateCfg<E, DK, DV>;
     using V4 = typename Vec<E>::v4;
     using V8 = typename Vec<E>::v8;
-    constexpr int NSL = DV / 16;  // value slices per head
-    constexpr int KT = DK / 16;   // accumulator tiles of S
-    constexpr int KS = DK / 32;   // contraction steps over key channels
+    constexpr int KS = C::KS, KT = C::KT, NSL = C::NSL;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[L::NBUF * L::BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char xfer[C::XFER];
+    __shared__ __attribute__((aligned(16))) unsigned char wbuf[2 * C::W_BYTES];
 
     const int b = blockIdx.x;
     const int xcd = b & 7, q8 = b >> 3;
@@ -158,21 +133,15 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(
     const int j0 = slice * 16;
     const int c_begin = seq_chunk_start[s], c_end = seq_chunk_start[s + 1];
     const size_t sbase = (size_t)pair * DK * DV;
+    auto record = [&](int cid) { return rec + ((size_t)cid * H + h) * C::RL.bytes; };
+    E* xS = reinterpret_cast<E*>(xfer);                      // [KS][64 lanes][8]
+    E* xN = reinterpret_cast<E*>(xfer + KS * 64 * C::FRAG);  // [2][64 lanes][8]
 
-    Stager<E, DK, DV> stage;
-    const int lt = tid - 64;  // loader lane index 0..191
-    if (wave > 0 && c_begin < c_end) {
-        stage.issue(cb, (size_t)c_begin * H + h, j0, lt);
-        stage.commit(smem);
-    }
-
-    // S tile t: lane holds S[16t + 4g + i][j0 + ln], i = 0..3 (wave 0 only)
-    f32x4 S[KT];
     if (wave == 0) {
+        // ------------------------------------------------ serial wave
+        f32x4 S[KT];
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[t][i] = 0.f;
+        for (int t = 0; t < KT; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (S0) {
 #pragma unroll
             for (int t = 0; t < KT; ++t)
@@ -180,125 +149,200 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(
                 for (int i = 0; i < 4; ++i)
                     S[t][i] = S0[sbase + (size_t)(16 * t + 4 * g + i) * DV + j0 + ln];
         }
-    }
-    __syncthreads();
+        SerialOps<E, DK> opA, opB;
+        if (C::TWO_SETS && c_begin < c_end) load_serial<E, DK, DV>(opA, record(c_begin), g, ln, j0);
+        __syncthreads();   // W of the first chunk is in LDS
 
-    for (int cid = c_begin; cid < c_end; ++cid) {
-        const int it = cid - c_begin;
-        const unsigned char* buf = smem + (it % L::NBUF) * L::BYTES;
-        if (wave == 0) {
-            const ChunkInfo ci = chunks[cid];
+        auto step = [&](SerialOps<E, DK>& cur, SerialOps<E, DK>& nxt, int cid) {
+            // The next chunk's loads are unconditional (the last chunk reloads
+            // itself) so no branch makes the wait counters conservative.
+            __builtin_amdgcn_sched_barrier(0);   // keep each chunk's work inside its step
+            if constexpr (!C::TWO_SETS) load_serial<E, DK, DV>(cur, record(cid), g, ln, j0);
+            else load_serial<E, DK, DV>(nxt, record(min(cid + 1, c_end - 1)), g, ln, j0);
             // S as an MFMA operand: slots of step ks = rows {32ks+4g..+3, 32ks+16+4g..+3}
             V8 Sf[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     Sf[ks][i] = from_f32<E>(S[2 * ks][i]);
                     Sf[ks][4 + i] = from_f32<E>(S[2 * ks + 1][i]);
                 }
-
+                store_vec(xS + (ks * 64 + l) * 8, Sf[ks]);
+            }
             // N = U - W S   (N tile R: lane holds N[16R + 4g + i][j0 + ln])
-            f32x4 N[4];
+            const unsigned char* wb = wbuf + ((cid - c_begin) & 1) * C::W_BYTES + ln * C::W_RS + 8 * g * C::ES;
+            V8 wf[4][KS];
 #pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int R = 0; R < 4; ++R)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    acc = mma32(lds_frag<E>(buf + L::OFF_W, 16 * R + ln, 32 * ks + 8 * g, L::W_RB),
-                                Sf[ks], acc);
-                const V4 u = *reinterpret_cast<const V4*>(buf + L::OFF_U + ln * L::K_RB +
-                                                         (16 * R + 4 * g) * L::ES);
+                    wf[R][ks] = load_vec<V8>(reinterpret_cast<const E*>(wb + 16 * R * C::W_RS + 32 * ks * C::ES));
+            f32x4 N[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) N[R][i] = to_f32(u[i]) - acc[i];
-            }
+            for (int R = 0; R < 4; ++R) N[R] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int R = 0; R < 4; ++R) N[R] = mma32(wf[R][ks], Sf[ks], N[R]);
             V8 Nf[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    Nf[ks][i] = from_f32<E>(to_f32(cur.u[2 * ks][i]) - N[2 * ks][i]);
+                    Nf[ks][4 + i] = from_f32<E>(to_f32(cur.u[2 * ks + 1][i]) - N[2 * ks + 1][i]);
+                }
+                store_vec(xN + (ks * 64 + l) * 8, Nf[ks]);
+            }
+            __syncthreads();   // A: chunk-start S and N handed to the output wave
+            // S = Diag(gamma_C) S + Khat^T N
+#pragma unroll
+            for (int t = 0; t < KT; ++t) S[t] *= cur.gc[t];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    Nf[ks][i] = from_f32<E>(N[2 * ks][i]);
-                    Nf[ks][4 + i] = from_f32<E>(N[2 * ks + 1][i]);
-                }
-
-            // S = Diag(gamma_C) S + Khat^T N   (the serial dependency: issue first)
-#pragma unroll
-            for (int t = 0; t < KT; ++t) {
-                const f32x4 gc = *reinterpret_cast<const f32x4*>(buf + L::OFF_G + (16 * t + 4 * g) * 4);
-                f32x4 acc = S[t] * gc;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    acc = mma32(lds_frag<E>(buf + L::OFF_K, 16 * t + ln, 32 * ks + 8 * g, L::K_RB),
-                                Nf[ks], acc);
-                S[t] = acc;
+                for (int t = 0; t < KT; ++t) S[t] = mma32(cur.k[t][ks], Nf[ks], S[t]);
+            __syncthreads();   // B: the hand-over area is free again
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        int cid = c_begin;
+        if constexpr (C::TWO_SETS) {
+            for (; cid + 1 < c_end; cid += 2) {
+                step(opA, opB, cid);
+                step(opB, opA, cid + 1);
             }
+        }
+        for (; cid < c_end; ++cid) step(opA, opB, cid);
 
-            // O^T = S0^T Qg^T + N^T A_qk^T with S0 the chunk-start state (held in Sf)
+        if (S_final) {
+#pragma unroll
+            for (int t = 0; t < KT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S_final[sbase + (size_t)(16 * t + 4 * g + i) * DV + j0 + ln] = S[t][i];
+        }
+    } else if (wave == 1) {
+        // ------------------------------------------------ output wave
+        OutputOps<E, DK> opA, opB;
+        if (C::TWO_SETS && c_begin < c_end) load_output<E, DK, DV>(opA, record(c_begin), chunks + c_begin, g, ln);
+        __syncthreads();   // W of the first chunk is in LDS
+
+        auto step = [&](OutputOps<E, DK>& cur, OutputOps<E, DK>& nxt, int cid) {
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!C::TWO_SETS) load_output<E, DK, DV>(cur, record(cid), chunks + cid, g, ln);
+            else {
+                const int nx = min(cid + 1, c_end - 1);
+                load_output<E, DK, DV>(nxt, record(nx), chunks + nx, g, ln);
+            }
+            __syncthreads();   // A
+            V8 Sf[KS], Nf[2];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) Sf[ks] = load_vec<V8>(xS + (ks * 64 + l) * 8);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) Nf[ks] = load_vec<V8>(xN + (ks * 64 + l) * 8);
+            __syncthreads();   // B
+            // O^T = S_start^T Qg^T + N^T A_qk^T   (tile R: lane holds O[16R + ln][j0 + 4g + i])
+            f32x4 O[4];
+#pragma unroll
+            for (int R = 0; R < 4; ++R) O[R] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int R = 0; R < 4; ++R) O[R] = mma32(Sf[ks], cur.q[R][ks], O[R]);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int R = 2 * ks; R < 4; ++R) O[R] = mma32(Nf[ks], cur.a[R][ks], O[R]);
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    acc = mma32(Sf[ks], lds_frag<E>(buf + L::OFF_Q, 16 * R + ln, 32 * ks + 8 * g, L::W_RB),
-                                acc);
-#pragma unroll
-                for (int ks = 0; ks <= R / 2; ++ks)
-                    acc = mma32(Nf[ks], lds_frag<E>(buf + L::OFF_A, 16 * R + ln, 32 * ks + 8 * g, L::K_RB),
-                                acc);
                 const int r = 16 * R + ln;
-                if (r < ci.len) {
+                if (r < cur.len) {
                     V4 w;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[i]);
-                    store_vec(o + ((size_t)(ci.start + r) * H + h) * DV + j0 + 4 * g, w);
+                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(O[R][i]);
+                    store_vec(o + ((size_t)(cur.start + r) * H + h) * DV + j0 + 4 * g, w);
                 }
             }
-        } else if (L::NBUF == 2 && cid + 1 < c_end) {
-            stage.issue(cb, (size_t)(cid + 1) * H + h, j0, lt);
-            stage.commit(smem + ((it + 1) % 2) * L::BYTES);
-        }
-        __syncthreads();
-        if (L::NBUF == 1 && cid + 1 < c_end) {
-            if (wave > 0) {
-                stage.issue(cb, (size_t)(cid + 1) * H + h, j0, lt);
-                stage.commit(smem);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        int cid = c_begin;
+        if constexpr (C::TWO_SETS) {
+            for (; cid + 1 < c_end; cid += 2) {
+                step(opA, opB, cid);
+                step(opB, opA, cid + 1);
             }
-            __syncthreads();
         }
-    }
-
-    if (wave == 0 && S_final) {
+        for (; cid < c_end; ++cid) step(opA, opB, cid);
+    } else {
+        // ------------------------------------------------ W stager / L2 prefetch wave
+        // W of chunk c sits in wbuf[c & 1] from barrier B of chunk c-1 on; the
+        // stager holds chunk c+1 in registers and commits it during chunk c.
+        // Each of the NSL slices of a head also touches every NSL-th 128-byte
+        // line of the record PREFETCH_DIST chunks ahead; together they cover it.
+        f32x4 wr[C::W_PER_LANE];
+        auto wload = [&](int cid) {
+            const f32x4* src = reinterpret_cast<const f32x4*>(record(cid) + C::RL.w);
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
+            for (int i = 0; i < C::W_PER_LANE; ++i) wr[i] = src[l + 64 * i];
+        };
+        auto wcommit = [&](int it) {
+            unsigned char* dst = wbuf + (it & 1) * C::W_BYTES;
+            constexpr int UPR = DK * C::ES / 16;   // 16-byte units per row
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S_final[sbase + (size_t)(16 * t + 4 * g + i) * DV + j0 + ln] = S[t][i];
+            for (int i = 0; i < C::W_PER_LANE; ++i) {
+                const int x = l + 64 * i;
+                *reinterpret_cast<f32x4*>(dst + (x / UPR) * C::W_RS + 16 * (x % UPR)) = wr[i];
+            }
+        };
+        if (c_begin < c_end) {
+            wload(c_begin);
+            wcommit(0);
+            wload(min(c_begin + 1, c_end - 1));
+        }
+        __syncthreads();   // W of the first chunk is in LDS
+        uint32_t sink = 0;
+        for (int cid = c_begin; cid < c_end; ++cid) {
+            const int it = cid - c_begin;
+            const int pf = cid + PREFETCH_DIST;
+            if (pf < c_end) {
+                const unsigned char* r = record(pf);
+                for (int line = slice + NSL * l; line < C::LINES; line += NSL * 64)
+                    sink ^= *reinterpret_cast<const uint32_t*>(r + 128 * line);
+            }
+            __syncthreads();   // A
+            if (cid + 1 < c_end) {
+                wcommit(it + 1);                       // buffer freed by barrier B of chunk c-1
+                wload(min(cid + 2, c_end - 1));
+            }
+            __syncthreads();   // B
+        }
+        if (n_pairs < 0) o[0] = from_f32<E>((float)sink);   // keeps the touches alive; never taken
     }
 }
 
 template <typename E, int DK, int DV>
-static hipError_t launch_state_t(void* const* bufs, const int32_t* seq_chunk_start,
+static hipError_t launch_state_t(const void* rec, const int32_t* seq_chunk_start,
                                  const ChunkInfo* chunks, const float* S0, float* S_final,
                                  void* o, int N, int H, hipStream_t stream)
 {
     const int n_pairs = N * H;
     const int groups = (n_pairs + 7) / 8;
     const long long blocks = (long long)groups * 8 * (DV / 16);
-    ChunkBufsC<E> cb{(const E*)bufs[0], (const E*)bufs[1], (const E*)bufs[2],
-                     (const E*)bufs[3], (const E*)bufs[4], (const float*)bufs[5]};
-    hipLaunchKernelGGL((prefill_state_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(256), 0,
-                       stream, cb, seq_chunk_start, chunks, S0, S_final, (E*)o, H, n_pairs);
+    hipLaunchKernelGGL((prefill_state_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(192), 0,
+                       stream, (const unsigned char*)rec, seq_chunk_start, chunks, S0, S_final,
+                       (E*)o, H, n_pairs);
     return hipGetLastError();
 }
 
-hipError_t launch_prefill_state(void* const* bufs, const int32_t* seq_chunk_start,
+hipError_t launch_prefill_state(const void* rec, const int32_t* seq_chunk_start,
                                 const ChunkInfo* chunks, const float* S0, float* S_final,
                                 void* o, int N, int H, int dk, int dv, bool bf16_io,
                                 hipStream_t stream)
 {
 #define KDA_STATE_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
-        return launch_state_t<E, DK_, DV_>(bufs, seq_chunk_start, chunks, S0, S_final, o, N, H, stream);
+        return launch_state_t<E, DK_, DV_>(rec, seq_chunk_start, chunks, S0, S_final, o, N, H, stream);
     if (bf16_io) {
         KDA_STATE_CASE(bf16, 128, 128)
         KDA_STATE_CASE(bf16, 64, 64)
