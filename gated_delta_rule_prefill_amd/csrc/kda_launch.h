@@ -18,26 +18,27 @@ struct ChunkInfo {
 };
 
 // Per-(chunk, head) record of the chunk intermediates in the workspace
-// (byte offsets; es = element size of q/k/v, 2 or 4).  One contiguous
-// record lets the state kernel stage a chunk with loop-invariant offsets.
-//   W    [64][dk]   e^g-decayed keys through the UT transform, channels perm32
-//   Qg   [64][dk]   e^g-decayed queries, channels perm32
-//   Kh   [dk][64]   (e^{g_C - g} k)^T, tokens perm32
-//   Aqk  [64][64]   intra-chunk query-key weights, key tokens perm32
+// (byte offsets; es = element size of q/k/v, 2 or 4).  With entry state S,
+// a chunk's state update and output are
+//     S_next = Diag(gC) S + PM S + Hc,      O = QM S + OI
+// (the chunk's transition and read-out folded in by the intra kernel):
+//   PM   [dk][dk]   -Khat^T W, columns in perm32 order
+//   HCt  [dv][dk]   (Khat^T U)^T, natural order
+//   QM   [64][dk]   Qg - A_qk W, columns in perm32 order
+//   OI   [64][dv]   A_qk U, natural order
 //   gC   [dk] fp32  e^{g_C}
-//   Ut   [dv][64]   U^T, natural token order
 struct RecLayout {
-    size_t w, q, k, a, g, u, bytes;
+    size_t pm, hc, qm, oi, g, bytes;
 };
 constexpr RecLayout rec_layout(int es, int dk, int dv) {
     return RecLayout{0,
-                     (size_t)CHUNK * dk * es,
-                     (size_t)2 * CHUNK * dk * es,
-                     (size_t)3 * CHUNK * dk * es,
-                     (size_t)3 * CHUNK * dk * es + (size_t)CHUNK * CHUNK * es,
-                     (size_t)3 * CHUNK * dk * es + (size_t)CHUNK * CHUNK * es + (size_t)dk * 4,
-                     ((size_t)3 * CHUNK * dk * es + (size_t)CHUNK * CHUNK * es + (size_t)dk * 4 +
-                      (size_t)dv * CHUNK * es + 255) & ~(size_t)255};
+                     (size_t)dk * dk * es,
+                     (size_t)dk * dk * es + (size_t)dv * dk * es,
+                     (size_t)dk * dk * es + (size_t)dv * dk * es + (size_t)CHUNK * dk * es,
+                     (size_t)dk * dk * es + (size_t)dv * dk * es + (size_t)CHUNK * dk * es +
+                         (size_t)CHUNK * dv * es,
+                     ((size_t)dk * dk * es + (size_t)dv * dk * es + (size_t)CHUNK * dk * es +
+                      (size_t)CHUNK * dv * es + (size_t)dk * 4 + 255) & ~(size_t)255};
 }
 
 hipError_t launch_chunk_table(const int32_t* cu, int64_t T, int N, int32_t* seq_chunk_start,

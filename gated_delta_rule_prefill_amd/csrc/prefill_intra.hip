@@ -2,23 +2,28 @@
 //
 // One workgroup (4 waves) per (chunk, head); chunks are independent, so the
 // grid covers the whole batch at once.  For a chunk of C = 64 tokens
-// r = 0..63 (rows past the sequence end are zero-padded, which makes every
-// quantity below vanish for them) it computes, from the recurrence
-// S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
-// (Kimi Linear paper notes, section 2) folded over the chunk (section 3:
-// WY/UT-style W and U, inter plus intra output; the listed chunk
-// intermediates g_cumsum, Akk, Aqk, w, u, qg, kg):
+// r = 0..63 (only log_alpha and beta are zeroed past the sequence end, which
+// makes every quantity below vanish or go unused for those rows) it computes,
+// from the recurrence S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} +
+// beta_t k_t v_t^T, o_t = S_t^T q_t (Kimi Linear paper notes, section 2)
+// folded over the chunk (section 3: WY/UT-style W and U, inter- plus
+// intra-chunk output, only the fixed-size state passed between chunks):
 //
 //   g_r       = sum_{j<=r} log alpha_j             per channel (cumulative log-decay)
 //   A_kk[r,i] = beta_r sum_c k_rc k_ic e^{g_rc - g_ic}, i < r
 //   A_qk[r,i] =        sum_c q_rc k_ic e^{g_rc - g_ic}, i <= r
 //   T         = (I + A_kk)^{-1} Diag(beta)         blocked substitution in LDS
 //   W         = T (e^g * K),   U = T V             MFMA
-//   Khat      = e^{g_C - g} * K,  Qg = e^g * Q,  gamma_C = e^{g_C}
+//   Khat      = e^{g_C - g} * K,   Qg = e^g * Q,   gamma_C = e^{g_C}
 //
-// and stores W, U, Khat^T, Qg, A_qk and gamma_C (one record per chunk and
-// head) for the sequential state kernel.  The state kernel then needs, per chunk, only
-//   N = U - W S,  O = Qg S + A_qk N,  S <- Diag(gamma_C) S + Khat^T N.
+// With entry state S the chunk gives N = U - W S, O = Qg S + A_qk N and
+// S' = Diag(gamma_C) S + Khat^T N.  This kernel folds W and U into the
+// chunk's transition and read-out, so the sequential kernel only applies
+//
+//   S' = Diag(gamma_C) S + PM S + Hc,   O = QM S + OI
+//   PM = -Khat^T W,  Hc = Khat^T U,  QM = Qg - A_qk W,  OI = A_qk U
+//
+// and writes PM, Hc^T, QM, OI and gamma_C as one record per chunk and head.
 //
 // The inverse of the unit lower-triangular I + A_kk is built blockwise: the
 // four 16x16 diagonal blocks by forward substitution (one lane per column),
@@ -41,17 +46,27 @@ struct IntraLayout {
     static constexpr int LK = DK + PAD;              // row stride of [64][DK] arrays
     static constexpr int LT = CHUNK + PAD;           // row stride of [d][64] / [64][64] arrays
     static constexpr int LA = CHUNK + 4;             // row stride of the fp32 A / X array
-    // phase 1 (A tiles): KP|QP and KD;  phase 3+ (W, U): kgT and vT in the same bytes
+    // region U1: phase 1 KP|QP and KD; phase 3-4 kgT and vT; phase 5 QA (fp32 A_qk W)
     static constexpr int P1_BYTES = 2 * CHUNK * LK * ES;
     static constexpr int P2_BYTES = (DK + DV) * LT * ES;
-    static constexpr int U1_BYTES = P1_BYTES > P2_BYTES ? P1_BYTES : P2_BYTES;
+    static constexpr int P5_BYTES = CHUNK * (DK + 4) * 4;
+    static constexpr int U1_A = P1_BYTES > P2_BYTES ? P1_BYTES : P2_BYTES;
+    static constexpr int U1_BYTES = U1_A > P5_BYTES ? U1_A : P5_BYTES;
     static constexpr int OFF_KP = 0;                         // also QP
     static constexpr int OFF_KD = CHUNK * LK * ES;
     static constexpr int OFF_KGT = 0;
     static constexpr int OFF_VT = DK * LT * ES;
+    static constexpr int OFF_QA = 0;
+    static constexpr int LQA = DK + 4;                       // row stride of QA (fp32)
+    // region U2: A_kk / X (fp32) until T is formed, then Khat^T (perm32 token order)
+    static constexpr int AL_BYTES = CHUNK * LA * 4;
+    static constexpr int KHT_BYTES = DK * LT * ES;
     static constexpr int OFF_AL = (U1_BYTES + 255) & ~255;
-    static constexpr int OFF_TL = OFF_AL + CHUNK * LA * 4;
-    static constexpr int OFF_TAU = OFF_TL + ((CHUNK * LT * ES + 15) & ~15);
+    static constexpr int OFF_KHT = OFF_AL;
+    static constexpr int U2_BYTES = AL_BYTES > KHT_BYTES ? AL_BYTES : KHT_BYTES;
+    static constexpr int OFF_TL = OFF_AL + ((U2_BYTES + 15) & ~15);
+    static constexpr int OFF_AQ = OFF_TL + ((CHUNK * LT * ES + 15) & ~15);   // A_qk, perm32 keys
+    static constexpr int OFF_TAU = OFF_AQ + ((CHUNK * LT * ES + 15) & ~15);
     static constexpr int OFF_ETAB = OFF_TAU + 4 * DK * 4;
     static constexpr int OFF_BETA = OFF_ETAB + 6 * DK * 4;
     static constexpr int BYTES = OFF_BETA + CHUNK * 4;
@@ -60,21 +75,19 @@ struct IntraLayout {
 // Pointers into one (chunk, head) record of the workspace (see rec_layout).
 template <typename E, int DK, int DV>
 struct ChunkOut {
-    E* W;
-    E* Qg;
-    E* Kh;
-    E* Aqk;
+    E* PM;
+    E* HCt;
+    E* QM;
+    E* OI;
     float* gC;
-    E* Ut;
     __device__ ChunkOut(unsigned char* rec, size_t chh) {
         constexpr RecLayout RL = rec_layout(sizeof(E), DK, DV);
         unsigned char* base = rec + chh * RL.bytes;
-        W = reinterpret_cast<E*>(base + RL.w);
-        Qg = reinterpret_cast<E*>(base + RL.q);
-        Kh = reinterpret_cast<E*>(base + RL.k);
-        Aqk = reinterpret_cast<E*>(base + RL.a);
+        PM = reinterpret_cast<E*>(base + RL.pm);
+        HCt = reinterpret_cast<E*>(base + RL.hc);
+        QM = reinterpret_cast<E*>(base + RL.qm);
+        OI = reinterpret_cast<E*>(base + RL.oi);
         gC = reinterpret_cast<float*>(base + RL.g);
-        Ut = reinterpret_cast<E*>(base + RL.u);
     }
 };
 
@@ -106,6 +119,20 @@ __device__ __forceinline__ void load_row(const E* p, float (&out)[CPT]) {
     } else {
         out[0] = to_f32(p[0]);
     }
+}
+
+// An MFMA operand over 32 tokens (step s) from two stacked 16-token
+// accumulator tiles: lane group g holds rows 4g..4g+3 of each, i.e. the
+// perm32 slot order.
+template <typename E>
+__device__ __forceinline__ typename Vec<E>::v8 tiles_to_frag(const f32x4& lo, const f32x4& hi) {
+    typename Vec<E>::v8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i] = from_f32<E>(lo[i]);
+        f[4 + i] = from_f32<E>(hi[i]);
+    }
+    return f;
 }
 
 // Pairs (R, I) of 16-token blocks with I <= R, spread over the 4 waves; the
@@ -156,7 +183,7 @@ __device__ __forceinline__ void x_block(float* sAL, int R, int I, int g, int ln)
 }
 
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void prefill_intra_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_intra_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const ChunkInfo* __restrict__ chunks, const int32_t* __restrict__ n_chunks_ptr, int H,
@@ -168,14 +195,19 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     constexpr int CPT = DK / 64;   // key channels per thread in the row-block mapping
     constexpr int CPTV = DV / 64;  // value channels per thread
     constexpr int KS = DK / 32;    // contraction steps over key channels
+    constexpr int NWB = (DK / 16 + 3) / 4;   // key-column blocks per wave
+    constexpr int NUB = (DV / 16 + 3) / 4;   // value-column blocks per wave
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
     E* sKP = reinterpret_cast<E*>(smem + L::OFF_KP);   // k*e^{g-B}  (phase 1a), then q*e^{g-B} (1b)
     E* sKD = reinterpret_cast<E*>(smem + L::OFF_KD);   // k*e^{B-g}
-    E* sKGT = reinterpret_cast<E*>(smem + L::OFF_KGT); // (e^g * k)^T   (phase 3+)
-    E* sVT = reinterpret_cast<E*>(smem + L::OFF_VT);   // v^T           (phase 3+)
+    E* sKGT = reinterpret_cast<E*>(smem + L::OFF_KGT); // (e^g * k)^T   (phase 3-4)
+    E* sVT = reinterpret_cast<E*>(smem + L::OFF_VT);   // v^T           (phase 3-4)
+    float* sQA = reinterpret_cast<float*>(smem + L::OFF_QA);  // A_qk W (phase 5-6)
     float* sAL = reinterpret_cast<float*>(smem + L::OFF_AL);
+    E* sKHT = reinterpret_cast<E*>(smem + L::OFF_KHT);  // Khat^T (phase 4+)
     E* sTL = reinterpret_cast<E*>(smem + L::OFF_TL);
+    E* sAQ = reinterpret_cast<E*>(smem + L::OFF_AQ);
     float* sTau = reinterpret_cast<float*>(smem + L::OFF_TAU);
     float* sEtab = reinterpret_cast<float*>(smem + L::OFF_ETAB);
     float* sBeta = reinterpret_cast<float*>(smem + L::OFF_BETA);
@@ -195,7 +227,7 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     const int c0 = lane * CPT;
     const int cv0 = lane * CPTV;
 
-    // ---- phase 0: unconditional loads (rows past the end clamp, then zero) ----
+    // ---- phase 0: unconditional loads (rows past the end re-read the last row) -
     float la[16][CPT], kr[16][CPT], qr[16][CPT], vr[16][CPTV];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -208,7 +240,8 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     }
     float bt = 0.f;
     if (wave == 0) bt = beta[((size_t)ci.start + (lane < ci.len ? lane : ci.len - 1)) * H + h];
-    // cumulative log-decay inside each 16-token block (zero past the end)
+    // cumulative log-decay inside each 16-token block; padded rows add nothing
+    // (with beta = 0 there, their k, q, v never reach a stored result).
     float ell[16][CPT];
     {
         float run[CPT];
@@ -221,11 +254,7 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
             for (int e = 0; e < CPT; ++e) {
                 run[e] += valid ? la[r][e] : 0.f;
                 ell[r][e] = run[e];
-                kr[r][e] = valid ? kr[r][e] : 0.f;
-                qr[r][e] = valid ? qr[r][e] : 0.f;
             }
-#pragma unroll
-            for (int e = 0; e < CPTV; ++e) vr[r][e] = valid ? vr[r][e] : 0.f;
         }
 #pragma unroll
         for (int e = 0; e < CPT; ++e) sTau[R * DK + c0 + e] = run[e];
@@ -262,23 +291,14 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
             const float iP = fast_exp(fminf(-ell[r][e], 80.f));    // e^{B_R - g_r}
             sKP[row * L::LK + c0 + e] = from_f32<E>(kr[r][e] * P);
             sKD[row * L::LK + c0 + e] = from_f32<E>(kr[r][e] * iP);
-            const float kh = kr[r][e] * iP * eTE[e];               // k e^{g_C - g_r}
-            kr[r][e] *= P * eB[e];                                 // now e^{g_r} k  (for W)
+            ell[r][e] = kr[r][e] * iP * eTE[e];                    // Khat: k e^{g_C - g_r}
+            kr[r][e] *= P * eB[e];                                 // e^{g_r} k  (for W)
             qr[r][e] *= P;                                         // q e^{g_r - B_R}
-            ell[r][e] = kh;                                        // reuse: Khat value
         }
     }
+    if (R == 0) {
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-        E* dst = out.Kh + (c0 + e) * CHUNK;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            V4 w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(ell[4 * r4 + i][e]);
-            store_vec(dst + perm_index(16 * R + 4 * r4), w);
-        }
-        if (R == 0) out.gC[c0 + e] = eTE[e];
+        for (int e = 0; e < CPT; ++e) out.gC[c0 + e] = eTE[e];
     }
     __syncthreads();
 
@@ -311,23 +331,20 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
     }
     __syncthreads();   // sKP no longer read
 
-    // ---- phase 1b: queries -> q e^{g - B} (LDS) and Qg = q e^{g} (workspace) ----
+    // ---- phase 1b: queries -> q e^{g - B} (LDS); qr becomes Qg = q e^{g} --------
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = 16 * R + r;
-        typename Vec<E>::v2 qg2;
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
             sKP[row * L::LK + c0 + e] = from_f32<E>(qr[r][e]);
-            const E val = from_f32<E>(qr[r][e] * eB[e]);
-            if constexpr (CPT == 2) qg2[e] = val;
-            else out.Qg[row * DK + perm_index(c0 + e)] = val;
+            qr[r][e] *= eB[e];
         }
-        if constexpr (CPT == 2) store_vec(out.Qg + row * DK + perm_index(c0), qg2);
     }
     __syncthreads();
 
     // ---- phase 1c: A_qk^T tiles (rows i of block I, columns r of block R) -------
+    // stored as A_qk[r][perm32(i)] in LDS for the read-out products
     for (int p = wave; p < 10; p += 4) {
         const int PR = kPairR[p], PI = kPairI[p];
         const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
@@ -349,14 +366,14 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
             const int col = 16 * PI + 4 * g + i;
             w[i] = from_f32<E>(r >= col ? acc[i] : 0.f);
         }
-        store_vec(out.Aqk + r * CHUNK + perm_index(16 * PI + 4 * g), w);
+        store_vec(sAQ + r * L::LT + perm_index(16 * PI + 4 * g), w);
     }
     for (int u = wave - 2; u >= 0 && u < 6; u += 2) {
         const int UR = kUpperR[u], UI = kUpperI[u];
         V4 z;
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = from_f32<E>(0.f);
-        store_vec(out.Aqk + (16 * UR + ln) * CHUNK + perm_index(16 * UI + 4 * g), z);
+        store_vec(sAQ + (16 * UR + ln) * L::LT + perm_index(16 * UI + 4 * g), z);
     }
     __syncthreads();   // sKP / sKD dead: their bytes become kgT and vT
 
@@ -421,56 +438,141 @@ __global__ __launch_bounds__(256) void prefill_intra_kernel(
         const int r = idx >> 6, c = idx & 63;
         sTL[r * L::LT + c] = from_f32<E>(x_elem<L::LA>(sAL, r, c) * sBeta[c]);
     }
-    __syncthreads();
+    __syncthreads();   // X dead: its bytes become Khat^T
 
-    // ---- phase 4: W^T = (e^g K)^T T^T and U = T V on MFMA ---------------------
-    // T is lower triangular, so output block R' only needs key tokens < 16R'+16.
-    for (int ct = wave; ct < DK / 16; ct += 4) {
-        V8 a[2], b[4][2];
+    // ---- phase 3f: Khat^T with tokens in perm32 order ---------------------------
 #pragma unroll
-        for (int s = 0; s < 2; ++s) a[s] = frag8<E>(sKGT + (16 * ct + ln) * L::LT + 32 * s + 8 * g);
+    for (int e = 0; e < CPT; ++e) {
 #pragma unroll
-        for (int Rq = 0; Rq < 4; ++Rq)
-#pragma unroll
-            for (int s = 0; s <= Rq / 2; ++s) b[Rq][s] = frag8<E>(sTL + (16 * Rq + ln) * L::LT + 32 * s + 8 * g);
-        f32x4 acc[4];
-#pragma unroll
-        for (int Rq = 0; Rq < 4; ++Rq) acc[Rq] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int Rq = 2 * s; Rq < 4; ++Rq) acc[Rq] = mma32(a[s], b[Rq][s], acc[Rq]);
-#pragma unroll
-        for (int Rq = 0; Rq < 4; ++Rq) {
+        for (int r4 = 0; r4 < 4; ++r4) {
             V4 w;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[Rq][i]);
-            const int r = 16 * Rq + ln;
-            store_vec(out.W + r * DK + perm_index(16 * ct + 4 * g), w);
+            for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(ell[4 * r4 + i][e]);
+            store_vec(sKHT + (c0 + e) * L::LT + perm_index(16 * R + 4 * r4), w);
         }
     }
-    for (int ct = wave; ct < DV / 16; ct += 4) {
-        V8 a[4][2], b[2];
+
+    // ---- phase 4: W = T (e^g K) and U = T V on MFMA, kept in registers ---------
+    // tile (Rq, column block): lane holds rows 16Rq + 4g + i, column 16cb + ln.
+    // T is lower triangular, so token block Rq only needs key tokens < 16Rq+16.
+    f32x4 Wt[NWB][4], Ut[NUB][4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) b[s] = frag8<E>(sVT + (16 * ct + ln) * L::LT + 32 * s + 8 * g);
+    for (int bw = 0; bw < NWB; ++bw) {
+        const int ct = wave + 4 * bw;
+        if (ct < DK / 16) {
+            V8 a[4][2], b[2];
 #pragma unroll
-        for (int Rq = 0; Rq < 4; ++Rq)
+            for (int s = 0; s < 2; ++s) b[s] = frag8<E>(sKGT + (16 * ct + ln) * L::LT + 32 * s + 8 * g);
 #pragma unroll
-            for (int s = 0; s <= Rq / 2; ++s) a[Rq][s] = frag8<E>(sTL + (16 * Rq + ln) * L::LT + 32 * s + 8 * g);
-        f32x4 acc[4];
+            for (int Rq = 0; Rq < 4; ++Rq)
 #pragma unroll
-        for (int Rq = 0; Rq < 4; ++Rq) acc[Rq] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s <= Rq / 2; ++s) a[Rq][s] = frag8<E>(sTL + (16 * Rq + ln) * L::LT + 32 * s + 8 * g);
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+            for (int Rq = 0; Rq < 4; ++Rq) Wt[bw][Rq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int Rq = 2 * s; Rq < 4; ++Rq) acc[Rq] = mma32(a[Rq][s], b[s], acc[Rq]);
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int Rq = 0; Rq < 4; ++Rq) {
-            V4 w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[Rq][i]);
-            store_vec(out.Ut + (16 * ct + ln) * CHUNK + 16 * Rq + 4 * g, w);
+                for (int Rq = 2 * s; Rq < 4; ++Rq) Wt[bw][Rq] = mma32(a[Rq][s], b[s], Wt[bw][Rq]);
         }
+    }
+#pragma unroll
+    for (int bu = 0; bu < NUB; ++bu) {
+        const int ct = wave + 4 * bu;
+        if (ct < DV / 16) {
+            V8 a[4][2], b[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) b[s] = frag8<E>(sVT + (16 * ct + ln) * L::LT + 32 * s + 8 * g);
+#pragma unroll
+            for (int Rq = 0; Rq < 4; ++Rq)
+#pragma unroll
+                for (int s = 0; s <= Rq / 2; ++s) a[Rq][s] = frag8<E>(sTL + (16 * Rq + ln) * L::LT + 32 * s + 8 * g);
+#pragma unroll
+            for (int Rq = 0; Rq < 4; ++Rq) Ut[bu][Rq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int Rq = 2 * s; Rq < 4; ++Rq) Ut[bu][Rq] = mma32(a[Rq][s], b[s], Ut[bu][Rq]);
+        }
+    }
+    __syncthreads();   // kgT / vT dead: the region holds A_qk W from here on
+
+    // ---- phase 5: transition and read-out products -------------------------
+    //   PM^T (c', c) = -(W^T Khat)   Hc (c, j) = Khat^T U
+    //   (A_qk W)^T (c', r)            OI^T (j, r) = U^T A_qk^T
+    // W and U enter as operands straight from their accumulator tiles.
+#pragma unroll
+    for (int bw = 0; bw < NWB; ++bw) {
+        const int ct = wave + 4 * bw;
+        if (ct < DK / 16) {
+            const V8 wf[2] = {tiles_to_frag<E>(Wt[bw][0], Wt[bw][1]), tiles_to_frag<E>(Wt[bw][2], Wt[bw][3])};
+            // PM rows c = 16a + ln, columns c' = 16ct + 4g + i (4 consecutive: one store)
+#pragma unroll
+            for (int a = 0; a < DK / 16; ++a) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    acc = mma32(wf[s], frag8<E>(sKHT + (16 * a + ln) * L::LT + 32 * s + 8 * g), acc);
+                V4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(-acc[i]);
+                store_vec(out.PM + (16 * a + ln) * DK + perm_index(16 * ct + 4 * g), w);
+            }
+            // (A_qk W)[r][c'] for r = 16Rr + ln, c' = 16ct + 4g + i  (A_qk is causal)
+#pragma unroll
+            for (int Rr = 0; Rr < 4; ++Rr) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s <= Rr / 2; ++s)
+                    acc = mma32(wf[s], frag8<E>(sAQ + (16 * Rr + ln) * L::LT + 32 * s + 8 * g), acc);
+                *reinterpret_cast<f32x4*>(sQA + (16 * Rr + ln) * L::LQA + 16 * ct + 4 * g) = acc;
+            }
+        }
+    }
+#pragma unroll
+    for (int bu = 0; bu < NUB; ++bu) {
+        const int ct = wave + 4 * bu;
+        if (ct < DV / 16) {
+            const V8 uf[2] = {tiles_to_frag<E>(Ut[bu][0], Ut[bu][1]), tiles_to_frag<E>(Ut[bu][2], Ut[bu][3])};
+            // Hc rows c = 16a + 4g + i, column j = 16ct + ln -> Hc^T[j][c..c+3]
+#pragma unroll
+            for (int a = 0; a < DK / 16; ++a) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    acc = mma32(frag8<E>(sKHT + (16 * a + ln) * L::LT + 32 * s + 8 * g), uf[s], acc);
+                V4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[i]);
+                store_vec(out.HCt + (16 * ct + ln) * DK + 16 * a + 4 * g, w);
+            }
+            // OI[r][j..j+3] for r = 16Rr + ln, j = 16ct + 4g
+#pragma unroll
+            for (int Rr = 0; Rr < 4; ++Rr) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s <= Rr / 2; ++s)
+                    acc = mma32(uf[s], frag8<E>(sAQ + (16 * Rr + ln) * L::LT + 32 * s + 8 * g), acc);
+                V4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[i]);
+                store_vec(out.OI + (16 * Rr + ln) * DV + 16 * ct + 4 * g, w);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 6: QM = Qg - A_qk W in the row mapping ------------------------
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = 16 * R + r;
+        typename Vec<E>::v2 w2;
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+            const E val = from_f32<E>(qr[r][e] - sQA[row * L::LQA + c0 + e]);
+            if constexpr (CPT == 2) w2[e] = val;
+            else out.QM[row * DK + perm_index(c0 + e)] = val;
+        }
+        if constexpr (CPT == 2) store_vec(out.QM + row * DK + perm_index(c0), w2);
     }
 }
 

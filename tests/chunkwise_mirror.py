@@ -22,6 +22,12 @@ r = 1..C entering with state S0:
     O     = (exp(g) * Q) S0 + A_qk N               (inter + intra)
     S_C   = Diag(exp(g_C)) S0 + (exp(g_C - g) * K)^T N
 
+Folding W and U into the chunk gives the equivalent transition / read-out
+form used by the GPU's sequential pass:
+
+    S_C = Diag(exp(g_C)) S0 + PM S0 + Hc,     O = QM S0 + OI
+    PM = -Khat^T W,  Hc = Khat^T U,  QM = Qg - A_qk W,  OI = A_qk U
+
 This module is test infrastructure: it is not the oracle (the oracle is the
 token-by-token recurrence) and it shares no code with the GPU library.  The
 pins check it against the oracle for several chunk sizes; GPU stage tests
@@ -68,7 +74,24 @@ def head_sequence(q, k, v, la, beta, S0, C):
     return O, S
 
 
-def prefill(x: "gen.KDAInputs", C: int):
+def head_sequence_transition(q, k, v, la, beta, S0, C):
+    """The same chunks in transition / read-out form.  Returns (O, S_final)."""
+    T = q.shape[0]
+    S = S0.copy()
+    O = np.zeros((T, v.shape[1]))
+    for c0 in range(0, T, C):
+        sl = slice(c0, min(c0 + C, T))
+        t = chunk_terms(q[sl], k[sl], v[sl], la[sl], beta[sl])
+        PM = -t["Khat"].T @ t["W"]
+        Hc = t["Khat"].T @ t["U"]
+        QM = t["Qg"] - t["Aqk"] @ t["W"]
+        OI = t["Aqk"] @ t["U"]
+        O[sl] = QM @ S + OI
+        S = t["gC"][:, None] * S + PM @ S + Hc
+    return O, S
+
+
+def prefill(x: "gen.KDAInputs", C: int, transition: bool = False):
     """The whole packed batch in chunks of C tokens (fp64)."""
     q, k, v = (gen.as_f32(a).astype(np.float64) for a in (x.q, x.k, x.v))
     la = x.log_alpha.astype(np.float64)
@@ -82,6 +105,7 @@ def prefill(x: "gen.KDAInputs", C: int):
         for h in range(x.H):
             S0 = np.zeros((x.dk, x.dv)) if x.initial_state is None else \
                 x.initial_state[s, h].astype(np.float64)
-            O[a:b, h], F[s, h] = head_sequence(q[a:b, h], k[a:b, h], v[a:b, h], la[a:b, h],
-                                               be[a:b, h], S0, C)
+            fn = head_sequence_transition if transition else head_sequence
+            O[a:b, h], F[s, h] = fn(q[a:b, h], k[a:b, h], v[a:b, h], la[a:b, h], be[a:b, h],
+                                    S0, C)
     return O, F

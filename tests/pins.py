@@ -258,6 +258,17 @@ def pin_chunkwise_algebra(orc):
         assert rel_err(mS, fin) < 1e-11, C
 
 
+def pin_chunk_transition_form(orc):
+    """Folding W and U into each chunk's transition (S' = Diag(gamma_C) S + PM S
+    + Hc) and read-out (O = QM S + OI) reproduces the recurrence."""
+    x = _case(26, 0, 2, 8, 6, mu=2.0, lengths=[150, 64, 37])
+    o, fin = orc.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.initial_state, x.cu_seqlens)
+    for C in (1, 5, 16, 64):
+        mo, mS = chunkwise_mirror.prefill(x, C, transition=True)
+        assert rel_err(mo, o) < 1e-11, (C, rel_err(mo, o))
+        assert rel_err(mS, fin) < 1e-11, C
+
+
 def pin_packing(orc):
     """A packed batch equals separate calls per sequence; equal rows equal cu_seqlens."""
     x = _case(20, 0, 2, 5, 4, lengths=[7, 0, 13, 1])
@@ -321,5 +332,6 @@ def pin_non_expansive(orc):
 
 ALL_PINS = [pin_transition_product, pin_exact_rational, pin_identity_no_write, pin_pure_decay,
             pin_deltanet, pin_gated_deltanet, pin_exact_recall, pin_one_hot_linear_attention,
-            pin_one_hot_rows, pin_single_token, pin_chunkwise_algebra, pin_packing,
+            pin_one_hot_rows, pin_single_token, pin_chunkwise_algebra, pin_chunk_transition_form,
+            pin_packing,
             pin_decode_matches_prefill, pin_linearity, pin_non_expansive]
