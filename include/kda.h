@@ -62,10 +62,12 @@ typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
 
 /*
  * Device workspace kda_prefill needs for these sizes (bytes, 256-aligned).
- * It holds the per-chunk intermediates of the chunkwise form: decayed keys
- * and queries, the UT-transformed W and U, the intra-chunk A_qk and the
- * chunk-end decay (paper notes, section 3 and its list of chunk
- * intermediates).  Returns 0 for invalid sizes.
+ * It holds one record per (chunk, head) built from the chunk intermediates of
+ * the chunkwise form (paper notes, section 3 and its list of chunk
+ * intermediates: g, A_qk, A_kk, w, u, decayed q and k): the chunk's state
+ * transition and read-out with W and U folded in, in the dtype of q/k/v, plus
+ * the chunk-end decay in fp32; and the chunk table of the batch.  Returns 0
+ * for invalid sizes.
  */
 size_t kda_prefill_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H,
                                    int32_t dk, int32_t dv, kda_dtype dtype);

@@ -58,3 +58,18 @@ def test_decode_config5_sampled():
     eo, es = run_decode(c["seed"], c["N"], c["H"], c["dk"], c["dv"], c["steps"], c["dtype"], sample)
     print(f"[parity] decode config 5: worst step o={eo:.3e} state after 128={es:.3e}", flush=True)
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_hand_worked_example():
+    """The two-token example of tests/golden/ as two decode steps."""
+    import torch
+    import gated_delta_rule_prefill_amd as kda
+    from golden_case import load
+    x, o_ref, fin_ref = load(d=64, H=2)
+    state = torch.zeros((1, 2, 64, 64), dtype=torch.float32, device="cuda")
+    for t in range(2):
+        o = kda.decode_step(state, dev_qkv(x.q[t:t + 1]), dev_qkv(x.k[t:t + 1]),
+                            dev_qkv(x.v[t:t + 1]), dev_f32(x.log_alpha[t:t + 1]),
+                            dev_f32(x.beta[t:t + 1]))
+        assert np.abs(host(o)[0] - o_ref[t]).max() < 1e-5
+    assert np.abs(host(state) - fin_ref).max() < 1e-5

@@ -26,6 +26,16 @@ def test_small_ragged(dtype, dk, dv):
     check_prefill(x, label=f"small {dk}x{dv}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_hand_worked_example(d):
+    """The two-token example of tests/golden/, worked by hand, in d channels."""
+    from golden_case import load
+    x, o_ref, fin_ref = load(d=d, H=3)
+    o, fin = gpu_prefill(x)
+    assert np.abs(host(o) - o_ref).max() < 1e-5
+    assert np.abs(host(fin) - fin_ref).max() < 1e-5
+
+
 def test_config1_tiny_fp32():
     x = gen.config_prefill(1)
     check_prefill(x, label="config 1")
