@@ -23,9 +23,9 @@ struct ChunkInfo {
 //     S_next = Diag(gC) S + PM S + Hc,      O = QM S + OI
 // (the chunk's transition and read-out folded in by the intra kernel):
 //   PM   [dk][dk]   -Khat^T W, columns in perm32 order
-//   HCt  [dv][dk]   (Khat^T U)^T, natural order
+//   HCt  [dv][dk]   (Khat^T U)^T, columns in perm32 order
 //   QM   [64][dk]   Qg - A_qk W, columns in perm32 order
-//   OI   [64][dv]   A_qk U, natural order
+//   OI   [64][dv]   A_qk U, columns in perm32 order
 //   gC   [dk] fp32  e^{g_C}
 struct RecLayout {
     size_t pm, hc, qm, oi, g, bytes;

@@ -458,7 +458,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     f32x4 Wt[NWB][4], Ut[NUB][4];
 #pragma unroll
     for (int bw = 0; bw < NWB; ++bw) {
-        const int ct = wave + 4 * bw;
+        const int ct = NWB * wave + bw;
         if (ct < DK / 16) {
             V8 a[4][2], b[2];
 #pragma unroll
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
 #pragma unroll
     for (int bu = 0; bu < NUB; ++bu) {
-        const int ct = wave + 4 * bu;
+        const int ct = NUB * wave + bu;
         if (ct < DV / 16) {
             V8 a[4][2], b[2];
 #pragma unroll
@@ -499,63 +499,128 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // ---- phase 5: transition and read-out products -------------------------
     //   PM^T (c', c) = -(W^T Khat)   Hc (c, j) = Khat^T U
     //   (A_qk W)^T (c', r)            OI^T (j, r) = U^T A_qk^T
-    // W and U enter as operands straight from their accumulator tiles.
+    // W and U enter as operands straight from their accumulator tiles.  A wave
+    // owns adjacent column tiles 2w, 2w + 1; in perm32 order their columns
+    // 4g..4g+3 and 16+4g..16+4g+3 are the 8 consecutive slots 8g..8g+7 of the
+    // 32-column block, so each lane writes 16 contiguous bytes.
+    {
+        static_assert(NWB == 1 || NWB == 2, "column tiles per wave");
+        V8 wf[NWB][2];
 #pragma unroll
-    for (int bw = 0; bw < NWB; ++bw) {
-        const int ct = wave + 4 * bw;
-        if (ct < DK / 16) {
-            const V8 wf[2] = {tiles_to_frag<E>(Wt[bw][0], Wt[bw][1]), tiles_to_frag<E>(Wt[bw][2], Wt[bw][3])};
-            // PM rows c = 16a + ln, columns c' = 16ct + 4g + i (4 consecutive: one store)
+        for (int bw = 0; bw < NWB; ++bw) {
+            wf[bw][0] = tiles_to_frag<E>(Wt[bw][0], Wt[bw][1]);
+            wf[bw][1] = tiles_to_frag<E>(Wt[bw][2], Wt[bw][3]);
+        }
+        const int ct0 = NWB * wave;
+        if (ct0 < DK / 16) {
+            // PM rows c = 16a + ln; columns 16 ct0 + 4g + i (and 16 (ct0 + 1) + 4g + i)
 #pragma unroll
             for (int a = 0; a < DK / 16; ++a) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                V8 kf[2];
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    acc = mma32(wf[s], frag8<E>(sKHT + (16 * a + ln) * L::LT + 32 * s + 8 * g), acc);
-                V4 w;
+                for (int s = 0; s < 2; ++s) kf[s] = frag8<E>(sKHT + (16 * a + ln) * L::LT + 32 * s + 8 * g);
+                f32x4 acc[NWB];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(-acc[i]);
-                store_vec(out.PM + (16 * a + ln) * DK + perm_index(16 * ct + 4 * g), w);
+                for (int bw = 0; bw < NWB; ++bw) {
+                    acc[bw] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) acc[bw] = mma32(wf[bw][s], kf[s], acc[bw]);
+                }
+                E* dst = out.PM + (16 * a + ln) * DK + perm_index(16 * ct0 + 4 * g);
+                if constexpr (NWB == 2) {
+                    V8 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        w[i] = from_f32<E>(-acc[0][i]);
+                        w[4 + i] = from_f32<E>(-acc[1][i]);
+                    }
+                    store_vec(dst, w);
+                } else {
+                    V4 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(-acc[0][i]);
+                    store_vec(dst, w);
+                }
             }
             // (A_qk W)[r][c'] for r = 16Rr + ln, c' = 16ct + 4g + i  (A_qk is causal)
 #pragma unroll
             for (int Rr = 0; Rr < 4; ++Rr) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                V8 af[2];
 #pragma unroll
-                for (int s = 0; s <= Rr / 2; ++s)
-                    acc = mma32(wf[s], frag8<E>(sAQ + (16 * Rr + ln) * L::LT + 32 * s + 8 * g), acc);
-                *reinterpret_cast<f32x4*>(sQA + (16 * Rr + ln) * L::LQA + 16 * ct + 4 * g) = acc;
+                for (int s = 0; s <= Rr / 2; ++s) af[s] = frag8<E>(sAQ + (16 * Rr + ln) * L::LT + 32 * s + 8 * g);
+#pragma unroll
+                for (int bw = 0; bw < NWB; ++bw) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s <= Rr / 2; ++s) acc = mma32(wf[bw][s], af[s], acc);
+                    *reinterpret_cast<f32x4*>(sQA + (16 * Rr + ln) * L::LQA + 16 * (ct0 + bw) + 4 * g) = acc;
+                }
             }
         }
     }
+    {
+        static_assert(NUB == 1 || NUB == 2, "value tiles per wave");
+        V8 uf[NUB][2];
 #pragma unroll
-    for (int bu = 0; bu < NUB; ++bu) {
-        const int ct = wave + 4 * bu;
-        if (ct < DV / 16) {
-            const V8 uf[2] = {tiles_to_frag<E>(Ut[bu][0], Ut[bu][1]), tiles_to_frag<E>(Ut[bu][2], Ut[bu][3])};
-            // Hc rows c = 16a + 4g + i, column j = 16ct + ln -> Hc^T[j][c..c+3]
+        for (int bu = 0; bu < NUB; ++bu) {
+            uf[bu][0] = tiles_to_frag<E>(Ut[bu][0], Ut[bu][1]);
+            uf[bu][1] = tiles_to_frag<E>(Ut[bu][2], Ut[bu][3]);
+        }
+        const int ct0 = NUB * wave;
+        if (ct0 < DV / 16) {
+            // Hc rows c = 16a + 4g + i, column j = 16ct + ln  ->  Hc^T[j][perm(c)]:
+            // row tiles a = 2m and 2m + 1 fill slots 32m + 8g .. +7
 #pragma unroll
-            for (int a = 0; a < DK / 16; ++a) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int bu = 0; bu < NUB; ++bu) {
+                const int ct = ct0 + bu;
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    acc = mma32(frag8<E>(sKHT + (16 * a + ln) * L::LT + 32 * s + 8 * g), uf[s], acc);
-                V4 w;
+                for (int m = 0; m < DK / 32; ++m) {
+                    f32x4 acc[2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[i]);
-                store_vec(out.HCt + (16 * ct + ln) * DK + 16 * a + 4 * g, w);
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int a = 2 * m + h2;
+                        acc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s = 0; s < 2; ++s)
+                            acc[h2] = mma32(frag8<E>(sKHT + (16 * a + ln) * L::LT + 32 * s + 8 * g), uf[bu][s], acc[h2]);
+                    }
+                    V8 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        w[i] = from_f32<E>(acc[0][i]);
+                        w[4 + i] = from_f32<E>(acc[1][i]);
+                    }
+                    store_vec(out.HCt + (16 * ct + ln) * DK + 32 * m + 8 * g, w);
+                }
             }
-            // OI[r][j..j+3] for r = 16Rr + ln, j = 16ct + 4g
+            // OI[r][perm(j)] for r = 16Rr + ln, j = 16ct + 4g + i
 #pragma unroll
             for (int Rr = 0; Rr < 4; ++Rr) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                V8 af[2];
 #pragma unroll
-                for (int s = 0; s <= Rr / 2; ++s)
-                    acc = mma32(uf[s], frag8<E>(sAQ + (16 * Rr + ln) * L::LT + 32 * s + 8 * g), acc);
-                V4 w;
+                for (int s = 0; s <= Rr / 2; ++s) af[s] = frag8<E>(sAQ + (16 * Rr + ln) * L::LT + 32 * s + 8 * g);
+                f32x4 acc[NUB];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[i]);
-                store_vec(out.OI + (16 * Rr + ln) * DV + 16 * ct + 4 * g, w);
+                for (int bu = 0; bu < NUB; ++bu) {
+                    acc[bu] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s <= Rr / 2; ++s) acc[bu] = mma32(uf[bu][s], af[s], acc[bu]);
+                }
+                E* dst = out.OI + (16 * Rr + ln) * DV + perm_index(16 * ct0 + 4 * g);
+                if constexpr (NUB == 2) {
+                    V8 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        w[i] = from_f32<E>(acc[0][i]);
+                        w[4 + i] = from_f32<E>(acc[1][i]);
+                    }
+                    store_vec(dst, w);
+                } else {
+                    V4 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[0][i]);
+                    store_vec(dst, w);
+                }
             }
         }
     }
