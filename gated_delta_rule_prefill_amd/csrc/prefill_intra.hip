@@ -135,14 +135,15 @@ __device__ __forceinline__ typename Vec<E>::v8 tiles_to_frag(const f32x4& lo, co
     return f;
 }
 
-// Pairs (R, I) of 16-token blocks with I <= R, spread over the 4 waves; the
-// index of an off-diagonal pair in the decay-factor table is R(R-1)/2 + I.
-__device__ __constant__ const int8_t kPairR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__device__ __constant__ const int8_t kPairI[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-__device__ __constant__ const int8_t kUpperR[6] = {0, 0, 0, 1, 1, 2};
-__device__ __constant__ const int8_t kUpperI[6] = {1, 2, 3, 2, 3, 3};
-__device__ __constant__ const int8_t kOffR[6] = {1, 2, 2, 3, 3, 3};
-__device__ __constant__ const int8_t kOffI[6] = {0, 0, 1, 0, 1, 2};
+// Pairs (R, I) of 16-token blocks, enumerated arithmetically (a table would be
+// read from memory inside the loops).  All pairs with I <= R in the order
+// (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...:
+__device__ __forceinline__ int pair_r(int p) { return (p >= 1) + (p >= 3) + (p >= 6); }
+__device__ __forceinline__ int pair_i(int p) { const int r = pair_r(p); return p - r * (r + 1) / 2; }
+// the six pairs with I < R in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2); the
+// index of pair (R, I) is R(R-1)/2 + I, which is also its slot in the decay table
+__device__ __forceinline__ int off_r(int p) { return 1 + (p >= 1) + (p >= 3); }
+__device__ __forceinline__ int off_i(int p) { const int r = off_r(p); return p - r * (r - 1) / 2; }
 
 // Element (r, c) of X = (I + A_kk)^{-1}: unit lower triangular, its strictly
 // lower part stored transposed in the (otherwise zero) upper triangle of sAL.
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
     const int t = threadIdx.x;
     const int lane = t & 63;
-    const int wave = t >> 6;     // also the 16-token block handled in the row mapping
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // also the 16-token block of the row mapping
     const int R = wave;
     const int g = lane >> 4, ln = lane & 15;
     const int c0 = lane * CPT;
@@ -279,7 +280,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int idx = t; idx < 6 * DK; idx += 256) {
         const int p = idx / DK, c = idx % DK;
         float d = 0.f;
-        for (int Rp = kOffI[p]; Rp < kOffR[p]; ++Rp) d += sTau[Rp * DK + c];
+        for (int Rp = off_i(p); Rp < off_r(p); ++Rp) d += sTau[Rp * DK + c];
         sEtab[idx] = fast_exp(d);
     }
 #pragma unroll
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // ---- phase 1a: A_kk tiles (rows r of block R, columns i of block I) --------
     // A operand k_r e^{g_r - B_R}; B operand k_i e^{B_I - g_i} * e^{B_R - B_I}.
     for (int p = wave; p < 10; p += 4) {
-        const int PR = kPairR[p], PI = kPairI[p];
+        const int PR = pair_r(p), PI = pair_i(p);
         const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
         V8 a[KS], b[KS];
 #pragma unroll
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
     }
     for (int u = wave - 2; u >= 0 && u < 6; u += 2) {   // waves 2 and 3 zero the upper tiles
-        const int UR = kUpperR[u], UI = kUpperI[u];
+        const int UR = off_i(u), UI = off_r(u);   // the transposed (upper) tile
 #pragma unroll
         for (int i = 0; i < 4; ++i) sAL[(16 * UR + 4 * g + i) * L::LA + 16 * UI + ln] = 0.f;
     }
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // ---- phase 1c: A_qk^T tiles (rows i of block I, columns r of block R) -------
     // stored as A_qk[r][perm32(i)] in LDS for the read-out products
     for (int p = wave; p < 10; p += 4) {
-        const int PR = kPairR[p], PI = kPairI[p];
+        const int PR = pair_r(p), PI = pair_i(p);
         const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
         V8 a[KS], b[KS];
 #pragma unroll
@@ -369,7 +370,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         store_vec(sAQ + r * L::LT + perm_index(16 * PI + 4 * g), w);
     }
     for (int u = wave - 2; u >= 0 && u < 6; u += 2) {
-        const int UR = kUpperR[u], UI = kUpperI[u];
+        const int UR = off_i(u), UI = off_r(u);   // the transposed (upper) tile
         V4 z;
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = from_f32<E>(0.f);

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int pair = grp * 8 + xcd;
     if (pair >= n_pairs) return;
     const int s = pair / H, h = pair % H;
-    const int tid = threadIdx.x, wave = tid >> 6;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, g = l >> 4, ln = l & 15;
     const int j0 = slice * 16;
     const int c_begin = seq_chunk_start[s];
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int pair = grp * 8 + xcd;
     if (pair >= n_pairs) return;
     const int s = pair / H, h = pair % H;
-    const int tid = threadIdx.x, wave = tid >> 6;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, g = l >> 4, ln = l & 15;
     const int j0 = slice * 16;
     const int c_begin = seq_chunk_start[s];
