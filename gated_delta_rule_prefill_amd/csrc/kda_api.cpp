@@ -26,10 +26,13 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Workspace layout of one prefill call: one record per (chunk, head) slot,
+// then (with the output pass) one chunk-start state per (chunk, head) slot,
 // then the chunk table.
 struct Plan {
     int64_t max_chunks = 0;
     size_t rec_bytes = 0;   // bytes of one (chunk, head) record
+    bool output_pass = false;
+    size_t off_states = 0;  // chunk-start states [max_chunks * H] (output pass only)
     size_t off_seq = 0;     // seq_chunk_start [N+1]
     size_t off_chunks = 0;  // ChunkInfo [max_chunks]
     size_t total = 0;
@@ -41,7 +44,11 @@ bool make_plan(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtyp
     const int es = dtype == KDA_DTYPE_BF16 ? 2 : 4;
     p.max_chunks = (T + kda::CHUNK - 1) / kda::CHUNK + N;
     p.rec_bytes = kda::rec_layout(es, dk, dv).bytes;
+    p.output_pass = kda::uses_output_pass(dtype == KDA_DTYPE_BF16, dk);
     size_t at = align256((size_t)p.max_chunks * (size_t)H * p.rec_bytes);
+    p.off_states = at;
+    if (p.output_pass)
+        at += align256((size_t)p.max_chunks * (size_t)H * kda::chunk_state_bytes(es, dk, dv));
     p.off_seq = at;
     at += align256(((size_t)N + 1) * 4);
     p.off_chunks = at;
@@ -181,12 +188,20 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
                                   "intra-chunk kernel", stream);
                 timer.mark("prefill_intra");
             }
+            void* states = plan.output_pass ? (void*)(ws + plan.off_states) : nullptr;
             if (st == KDA_OK) {
                 st = check_launch(kda::launch_prefill_state(ws, seq_start, chunks, initial_state,
-                                                            final_state, o, num_seqs, H, dk, dv,
-                                                            bf16, stream),
+                                                            final_state, o, states, num_seqs, H,
+                                                            dk, dv, bf16, stream),
                                   "state kernel", stream);
                 timer.mark("prefill_state");
+            }
+            if (st == KDA_OK && plan.output_pass && total_tokens > 0) {
+                st = check_launch(kda::launch_prefill_output(ws, states, chunks, seq_start + num_seqs,
+                                                             (int)plan.max_chunks, H, dk, dv, bf16,
+                                                             o, stream),
+                                  "output kernel", stream);
+                timer.mark("prefill_output");
             }
         }
         if (owned) {

@@ -50,10 +50,26 @@ hipError_t launch_prefill_intra(const void* q, const void* k, const void* v, con
                                 const int32_t* n_chunks, int max_chunks, int H, int dk, int dv,
                                 bool bf16_io, void* rec, hipStream_t stream);
 
+// Sequential inter-chunk pass.  With the output pass (uses_output_pass) it
+// stores every chunk-start state into `states` and leaves o to
+// launch_prefill_output; otherwise it writes o itself and ignores `states`.
 hipError_t launch_prefill_state(const void* rec, const int32_t* seq_chunk_start,
                                 const ChunkInfo* chunks, const float* S0, float* S_final,
-                                void* o, int N, int H, int dk, int dv, bool bf16_io,
+                                void* o, void* states, int N, int H, int dk, int dv, bool bf16_io,
                                 hipStream_t stream);
+
+// Whether a configuration runs the chain-only sequential kernel followed by the
+// parallel output pass (its LDS ring fits), or the fused register-staged one.
+constexpr bool uses_output_pass(bool bf16_io, int dk) { return bf16_io || dk == 64; }
+
+// Bytes of one (chunk, head) chunk-start state: dk x dv in the q/k/v dtype, laid
+// out as MFMA operand slots [dv/16 slices][dk/32 steps][64 lanes][8].
+constexpr size_t chunk_state_bytes(int es, int dk, int dv) { return (size_t)dk * dv * es; }
+
+// Parallel output pass: O = QM S_c + OI for every (chunk, head).
+hipError_t launch_prefill_output(const void* rec, const void* states, const ChunkInfo* chunks,
+                                 const int32_t* n_chunks, int max_chunks, int H, int dk, int dv,
+                                 bool bf16_io, void* o, hipStream_t stream);
 
 hipError_t launch_decode_step(float* state, const void* q, const void* k, const void* v,
                               const float* la, const float* beta, void* o, int units, int dk,

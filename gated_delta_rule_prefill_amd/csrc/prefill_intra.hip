@@ -214,9 +214,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     float* sBeta = reinterpret_cast<float*>(smem + L::OFF_BETA);
 
     const int cid = blockIdx.x;
-    if (cid >= *n_chunks_ptr) return;
-    const int h = blockIdx.y;
+    // Both reads are issued together (the table holds gridDim.x entries, so
+    // chunks[cid] is in bounds even for a block that then exits).
+    const int n_chunks = *n_chunks_ptr;
     const ChunkInfo ci = chunks[cid];
+    if (cid >= n_chunks) return;
+    const int h = blockIdx.y;
     const size_t chh = (size_t)cid * H + h;
     const ChunkOut<E, DK, DV> out(rec, chh);
 
@@ -229,16 +232,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int cv0 = lane * CPTV;
 
     // ---- phase 0: unconditional loads (rows past the end re-read the last row) -
+    // Issued tensor by tensor in the order they are first needed: a wave's
+    // loads complete in order, so the prefix sum waits only for log_alpha, the
+    // decayed keys only for k, and v stays in flight until the transposes.
     float la[16][CPT], kr[16][CPT], qr[16][CPT], vr[16][CPTV];
+    size_t rowoff[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = 16 * R + r;
-        const size_t tok = (size_t)ci.start + (row < ci.len ? row : ci.len - 1);
-        load_row<CPT>(log_alpha + (tok * H + h) * DK + c0, la[r]);
-        load_row<CPT>(k + (tok * H + h) * DK + c0, kr[r]);
-        load_row<CPT>(q + (tok * H + h) * DK + c0, qr[r]);
-        load_row<CPTV>(v + (tok * H + h) * DV + cv0, vr[r]);
+        rowoff[r] = ((size_t)ci.start + (row < ci.len ? row : ci.len - 1)) * H + h;
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) load_row<CPT>(log_alpha + rowoff[r] * DK + c0, la[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) load_row<CPT>(k + rowoff[r] * DK + c0, kr[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) load_row<CPT>(q + rowoff[r] * DK + c0, qr[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) load_row<CPTV>(v + rowoff[r] * DV + cv0, vr[r]);
     float bt = 0.f;
     if (wave == 0) bt = beta[((size_t)ci.start + (lane < ci.len ? lane : ci.len - 1)) * H + h];
     // cumulative log-decay inside each 16-token block; padded rows add nothing
@@ -294,9 +305,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             sKD[row * L::LK + c0 + e] = from_f32<E>(kr[r][e] * iP);
             ell[r][e] = kr[r][e] * iP * eTE[e];                    // Khat: k e^{g_C - g_r}
             kr[r][e] *= P * eB[e];                                 // e^{g_r} k  (for W)
-            qr[r][e] *= P;                                         // q e^{g_r - B_R}
+            la[r][e] = P;                                          // log_alpha is dead here
         }
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) qr[r][e] *= la[r][e];        // q e^{g_r - B_R}
     if (R == 0) {
 #pragma unroll
         for (int e = 0; e < CPT; ++e) out.gC[c0 + e] = eTE[e];

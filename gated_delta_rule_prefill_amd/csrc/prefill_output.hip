@@ -1,0 +1,122 @@
+// prefill_output.hip -- output pass of the chunkwise KDA prefill.
+//
+// The output of a chunk is its read-out of the chunk-start state plus its
+// intra-chunk term (Kimi Linear paper notes, section 3: inter- plus
+// intra-chunk output).  With the chunk folded by the intra kernel,
+//
+//     O = QM S_c + OI,
+//
+// where S_c is the state entering the chunk, stored by the sequential kernel
+// as bf16 (or fp32) MFMA operand slots.  Every (chunk, head) is independent,
+// so the pass is one workgroup per (chunk, head), like the intra kernel.
+#include "kda_common.h"
+
+namespace kda {
+
+// Wave w owns value slices SPW*w .. SPW*w + SPW - 1 (16 columns each) for all
+// 64 rows; with two slices per wave their columns 4g..4g+3 are the 8
+// consecutive perm32 slots 8g..8g+7 of OI.
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void prefill_output_kernel(
+    const unsigned char* __restrict__ rec, const E* __restrict__ states,
+    const ChunkInfo* __restrict__ chunks, const int32_t* __restrict__ n_chunks_ptr, int H,
+    E* __restrict__ o)
+{
+    using V4 = typename Vec<E>::v4;
+    using V8 = typename Vec<E>::v8;
+    constexpr int KS = DK / 32, NSL = DV / 16, SPW = NSL / 4;
+    static_assert(SPW == 1 || SPW == 2, "value slices per wave");
+    constexpr RecLayout RL = rec_layout(sizeof(E), DK, DV);
+
+    const int cid = blockIdx.x;
+    // both reads are issued together (the table holds gridDim.x entries)
+    const int n_chunks = *n_chunks_ptr;
+    const ChunkInfo ci = chunks[cid];
+    if (cid >= n_chunks) return;
+    const int h = blockIdx.y;
+    const size_t chh = (size_t)cid * H + h;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = threadIdx.x & 63, g = l >> 4, ln = l & 15;
+    const E* QM = reinterpret_cast<const E*>(rec + chh * RL.bytes + RL.qm);
+    const E* OI = reinterpret_cast<const E*>(rec + chh * RL.bytes + RL.oi);
+    const E* St = states + chh * DK * DV;
+
+    V8 sf[SPW][KS];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sf[sp][ks] = load_vec<V8>(St + (((SPW * wave + sp) * KS + ks) * 64 + l) * 8);
+    V8 q[4][KS];
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) q[R][ks] = load_vec<V8>(QM + (16 * R + ln) * DK + 32 * ks + 8 * g);
+    // OI[16R + ln][columns j0 + 4g .. +3 of each owned slice] (perm32 slots)
+    float oi[4][SPW][4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+        const E* src = OI + (16 * R + ln) * DV + perm_index(16 * SPW * wave + 4 * g);
+        if constexpr (SPW == 2) {
+            const V8 v = load_vec<V8>(src);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                oi[R][0][i] = to_f32(v[i]);
+                oi[R][1][i] = to_f32(v[4 + i]);
+            }
+        } else {
+            const V4 v = load_vec<V4>(src);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oi[R][0][i] = to_f32(v[i]);
+        }
+    }
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+        const int r = 16 * R + ln;
+#pragma unroll
+        for (int sp = 0; sp < SPW; ++sp) {
+            // O^T tile: lane holds O[16R + ln][j0 + 4g + i]
+            f32x4 acc = {oi[R][sp][0], oi[R][sp][1], oi[R][sp][2], oi[R][sp][3]};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc = mma32(sf[sp][ks], q[R][ks], acc);
+            if (r < ci.len) {
+                V4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[i]);
+                const int j0 = 16 * (SPW * wave + sp);
+                store_vec(o + ((size_t)(ci.start + r) * H + h) * DV + j0 + 4 * g, w);
+            }
+        }
+    }
+}
+
+template <typename E, int DK, int DV>
+static hipError_t launch_output_t(const void* rec, const void* states, const ChunkInfo* chunks,
+                                  const int32_t* n_chunks, int max_chunks, int H, void* o,
+                                  hipStream_t stream)
+{
+    hipLaunchKernelGGL((prefill_output_kernel<E, DK, DV>), dim3(max_chunks, H), dim3(256), 0, stream,
+                       (const unsigned char*)rec, (const E*)states, chunks, n_chunks, H, (E*)o);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_output(const void* rec, const void* states, const ChunkInfo* chunks,
+                                 const int32_t* n_chunks, int max_chunks, int H, int dk, int dv,
+                                 bool bf16_io, void* o, hipStream_t stream)
+{
+#define KDA_OUT_CASE(E, DK_, DV_)   \
+    if (dk == DK_ && dv == DV_)       \
+        return launch_output_t<E, DK_, DV_>(rec, states, chunks, n_chunks, max_chunks, H, o, stream);
+    if (bf16_io) {
+        KDA_OUT_CASE(bf16, 128, 128)
+        KDA_OUT_CASE(bf16, 64, 64)
+        KDA_OUT_CASE(bf16, 128, 64)
+        KDA_OUT_CASE(bf16, 64, 128)
+    } else {
+        KDA_OUT_CASE(float, 64, 64)
+        KDA_OUT_CASE(float, 64, 128)
+    }
+#undef KDA_OUT_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

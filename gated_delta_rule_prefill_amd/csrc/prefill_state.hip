@@ -126,6 +126,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int c_begin = seq_chunk_start[s];
     const int n = seq_chunk_start[s + 1] - c_begin;   // chunks of this sequence
     const size_t sbase = (size_t)pair * DK * DV;
+    if (n == 0) {   // empty sequence: the final state is the initial one (or zero)
+        if (S_final)
+            for (int x = tid; x < DK * 16; x += blockDim.x) {
+                const size_t at = sbase + (size_t)(x >> 4) * DV + j0 + (x & 15);
+                S_final[at] = S0 ? S0[at] : 0.f;
+            }
+        return;   // uniform over the workgroup: no barrier is skipped by part of it
+    }
     auto record = [&](int it) { return rec + ((size_t)(c_begin + it) * H + h) * C::RL.bytes; };
     auto xslot = [&](int it) { return reinterpret_cast<E*>(xfer + (it & 1) * C::XSLOT); };
 
@@ -286,46 +294,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------------------
-// LDS-ring variant.  Same roles and barrier schedule as above, but the operands
-// of the serial chain (PM, this slice's Hc^T rows and gamma_C) reach LDS by
-// direct global->LDS loads (global_load_lds_dwordx4: no registers, no commit
-// step) into a ring of three slots, two chunks ahead of their use:
-//   wave 0  serial chain (reads PM, Hc, gamma_C of chunk it from slot it % 3)
-//   wave 1  output one chunk behind; QM and OI come straight from global
-//           memory into registers two chunks ahead (three register sets)
-//   wave 2  the direct loads of chunk it + 2, then waits for chunk it + 1
-//   wave 3  touches every line of chunk it + TOUCH_DIST so that the loads of
-//           the other waves hit L2.  It is the only wave with loads whose
-//           latency nobody waits for: a wave's vector-memory counter completes
-//           in order, so touches issued by a loading wave would make that
-//           wave's next wait cover them.
-// A slot is written only after the barrier that ends the chunk which last
-// read it, so every LDS hand-over is ordered by the one barrier per chunk.
+// LDS-ring variant, for every configuration whose ring fits in LDS.  It runs
+// only the sequential chain; the outputs come from a separate parallel pass
+// over the chunk-start states this kernel stores.
+//
+// One workgroup per (sequence, head, 16 value columns), DK/32 + 5 waves:
+//   serial waves w < DK/32  own rows 32w..32w+31 of the fp32 state tile; per
+//       chunk each applies S' = Diag(gamma_C) S + Hc + PM S to its rows (8
+//       MFMAs), reading the whole chunk-start state as bf16 operand slots from
+//       LDS and writing its own rows' slots for the next chunk, to LDS and to
+//       the chunk-state buffer.  A 16x16 accumulator tile gives lane group g
+//       rows 4g..4g+3, so the two tiles of rows 32w.. are exactly operand
+//       step w of the next product;
+//   touch wave  touches every line of chunk it + TOUCH_DIST so that the direct
+//       loads hit L2 (plain loads, folded into a value three chunks later);
+//   stager waves (4)  move PM, this slice's Hc^T rows and gamma_C into a
+//       three-slot LDS ring by direct global->LDS loads
+//       (global_load_lds_dwordx4), two chunks ahead, each a quarter of them
+//       (one wave issues such a load only every ~70 cycles).
+// Every wave passes one barrier per chunk.  A ring slot or state slot is
+// written only after the barrier that ends the chunk which last read it.
 template <typename E, int DK, int DV>
 struct RingCfg {
     static constexpr int ES = sizeof(E);
     static constexpr int KS = DK / 32, KT = DK / 16, NSL = DV / 16;
+    static constexpr int NSER = KS;                  // serial waves
+    static constexpr int NSTG = 4;                   // stager waves
+    static constexpr int WAVES = NSER + 1 + NSTG;    // + the touch wave
     static constexpr int FRAG = 8 * ES;
-    static constexpr int XSLOT = KS * 64 * FRAG;
+    static constexpr int XSLOT = KS * 64 * FRAG;     // one chunk-start state (operand slots)
+    static constexpr int NX = 2;                     // state slots: it (read), it + 1 (written)
     static constexpr int RW = DK * ES / 16;          // 16-byte units per PM / Hc^T row
     static constexpr int RS = (RW + 1) * 16;         // padded LDS row stride (bytes)
     static constexpr int PM_UNITS = DK * (RW + 1);
     static constexpr int HC_UNITS = 16 * (RW + 1);
     static constexpr int G_UNITS = DK / 4;
     static constexpr int UNITS = PM_UNITS + HC_UNITS + G_UNITS;
-    static constexpr int LOADS = (UNITS + 63) / 64;  // direct loads per chunk (one wave)
+    static constexpr int LOADS = (UNITS + 63) / 64;  // direct loads per chunk
+    static constexpr int LOADS_W = (LOADS + NSTG - 1) / NSTG;   // per stager wave
+    static constexpr int LOADS_LAST = LOADS - (NSTG - 1) * LOADS_W;   // the last stager's share
     static constexpr int SLOT = LOADS * 1024;
     static constexpr int OFF_HC = PM_UNITS * 16;
     static constexpr int OFF_G = OFF_HC + HC_UNITS * 16;
     static constexpr int NSLOT = 3;
-    static constexpr int LDS_BYTES = NSLOT * SLOT + 2 * XSLOT + 256;
+    static constexpr int LDS_BYTES = NSLOT * SLOT + NX * XSLOT;
     static constexpr RecLayout RL = rec_layout(ES, DK, DV);
-    static constexpr int LINES = (int)(RL.bytes / 128);
-    static constexpr int TOUCH_PER_LANE = (LINES + 64 * NSL - 1) / (64 * NSL);
-    static_assert(LOADS <= 56, "direct loads of one chunk must fit the vector-memory counter");
+    static constexpr int TOUCH_LINES = DK * DK * ES / 128 / NSL + 16 * DK * ES / 128 + DK * 4 / 128;
+    static constexpr int TOUCH_PER_LANE = (TOUCH_LINES + 63) / 64;
+    static_assert(2 * LOADS_W <= 60, "two chunks of one stager's direct loads must fit its counter");
+    static_assert(LOADS_LAST > 0 && LOADS_LAST <= LOADS_W, "stager split");
 };
 
-constexpr int TOUCH_DIST = 5;   // chunks between the L2 touch and the first direct load
+constexpr int TOUCH_DIST = 6;   // chunks between the L2 touch and the first direct load
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (lgkm and exp counters left free).
@@ -334,12 +354,13 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 typedef __attribute__((address_space(1))) void global_void;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Workgroup barrier for the waves that only issue direct global->LDS loads.
-// __syncthreads() carries a workgroup release fence, which makes the wave wait
+// Workgroup barrier for waves without LDS accesses of their own.
+// __syncthreads() carries a workgroup release fence, which makes a wave wait
 // for every outstanding direct load (they write LDS) -- including those meant
-// for later chunks.  These waves order their LDS writes themselves with an
-// explicit vector-memory wait, so they take a bare s_barrier; the empty asm
-// statements only stop the compiler from moving memory accesses across it.
+// for later chunks.  The stager waves order their LDS writes themselves with
+// an explicit vector-memory wait, so they (and the touch wave) take a bare
+// s_barrier; the empty asm statements only stop the compiler from moving
+// memory accesses across it.
 __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -347,19 +368,18 @@ __device__ __forceinline__ void bare_barrier() {
 }
 
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_state_ring_kernel(
+__global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
     const unsigned char* __restrict__ rec, const int32_t* __restrict__ seq_chunk_start,
-    const ChunkInfo* __restrict__ chunks, const float* __restrict__ S0,
-    float* __restrict__ S_final, E* __restrict__ o, int H, int n_pairs)
+    const float* __restrict__ S0, float* __restrict__ S_final, E* __restrict__ states,
+    int H, int n_pairs)
 {
     using C = RingCfg<E, DK, DV>;
     using V4 = typename Vec<E>::v4;
     using V8 = typename Vec<E>::v8;
-    constexpr int KS = C::KS, KT = C::KT, NSL = C::NSL;
+    constexpr int KS = C::KS, NSL = C::NSL, NSER = C::NSER;
 
     __shared__ __attribute__((aligned(1024))) unsigned char ring[C::NSLOT * C::SLOT];
-    __shared__ __attribute__((aligned(16))) unsigned char xfer[2 * C::XSLOT];
-    __shared__ __attribute__((aligned(16))) unsigned char dump[256];   // touch destination, never read
+    __shared__ __attribute__((aligned(16))) unsigned char xfer[C::NX * C::XSLOT];
 
     const int b = blockIdx.x;
     const int xcd = b & 7, q8 = b >> 3;
@@ -373,120 +393,145 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int c_begin = seq_chunk_start[s];
     const int n = seq_chunk_start[s + 1] - c_begin;   // chunks of this sequence
     const size_t sbase = (size_t)pair * DK * DV;
+    if (n == 0) {   // empty sequence: the final state is the initial one (or zero)
+        if (S_final)
+            for (int x = tid; x < DK * 16; x += blockDim.x) {
+                const size_t at = sbase + (size_t)(x >> 4) * DV + j0 + (x & 15);
+                S_final[at] = S0 ? S0[at] : 0.f;
+            }
+        return;   // uniform over the workgroup: no barrier is skipped by part of it
+    }
     auto record = [&](int it) { return rec + ((size_t)(c_begin + it) * H + h) * C::RL.bytes; };
     auto slot = [&](int it) { return ring + (it % C::NSLOT) * C::SLOT; };
-    auto xslot = [&](int it) { return reinterpret_cast<E*>(xfer + (it & 1) * C::XSLOT); };
+    auto xslot = [&](int it) { return reinterpret_cast<E*>(xfer + (it % C::NX) * C::XSLOT); };
 
-    if (wave == 0) {
-        // ------------------------------------------------ serial wave
-        f32x4 S[KT];   // tile t: lane holds S[16t + 4g + i][j0 + ln]
+    if (wave < NSER) {
+        // ------------------------------------------------ serial waves
+        const int w = wave;
+        f32x4 S[2];   // S[h2]: lane holds S[32w + 16 h2 + 4g + i][j0 + ln]
 #pragma unroll
-        for (int t = 0; t < KT; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h2 = 0; h2 < 2; ++h2) S[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (S0) {
 #pragma unroll
-            for (int t = 0; t < KT; ++t)
+            for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S[t][i] = S0[sbase + (size_t)(16 * t + 4 * g + i) * DV + j0 + ln];
+                    S[h2][i] = S0[sbase + (size_t)(32 * w + 16 * h2 + 4 * g + i) * DV + j0 + ln];
         }
+        // chunk-start state of chunk it, this wave's operand step, to LDS and to
+        // the chunk-state buffer ([chunk, head][slice][step][lane][8])
+        auto put = [&](int it) {
+            V8 f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f[i] = from_f32<E>(S[0][i]);
+                f[4 + i] = from_f32<E>(S[1][i]);
+            }
+            store_vec(xslot(it) + (w * 64 + l) * 8, f);
+            if (it < n)
+                store_vec(states + ((size_t)(c_begin + it) * H + h) * DK * DV +
+                              ((size_t)(slice * KS + w) * 64 + l) * 8, f);
+        };
+        put(0);
         __syncthreads();
         for (int it = 0; it < n; ++it) {
-            __builtin_amdgcn_sched_barrier(0);
             const unsigned char* sl = slot(it);
-            const unsigned char* pm = sl + ln * C::RS + 8 * g * sizeof(E);
-            V8 pf[KT][KS];
+            const E* xs = xslot(it);
+            V8 Sf[KS];
 #pragma unroll
-            for (int t = 0; t < KT; ++t)
+            for (int ks = 0; ks < KS; ++ks) Sf[ks] = load_vec<V8>(xs + (ks * 64 + l) * 8);
+            V8 pf[2][KS];
+            V4 hc[2];
+            f32x4 gc[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int t = 2 * w + h2;
+                const unsigned char* pm = sl + (16 * t + ln) * C::RS + 8 * g * sizeof(E);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    pf[t][ks] = load_vec<V8>(reinterpret_cast<const E*>(pm + 16 * t * C::RS + 32 * ks * sizeof(E)));
-            V4 hc[KT];
-            f32x4 gc[KT];
-#pragma unroll
-            for (int t = 0; t < KT; ++t) {
-                hc[t] = load_vec<V4>(reinterpret_cast<const E*>(sl + C::OFF_HC + ln * C::RS) + perm_index(16 * t + 4 * g));
-                gc[t] = load_vec<f32x4>(reinterpret_cast<const float*>(sl + C::OFF_G) + 16 * t + 4 * g);
-            }
-            // chunk-start state as MFMA operand slots {32ks+4g..+3, 32ks+16+4g..+3}
-            V8 Sf[KS];
-            E* xs = xslot(it);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    Sf[ks][i] = from_f32<E>(S[2 * ks][i]);
-                    Sf[ks][4 + i] = from_f32<E>(S[2 * ks + 1][i]);
-                }
-                store_vec(xs + (ks * 64 + l) * 8, Sf[ks]);
+                    pf[h2][ks] = load_vec<V8>(reinterpret_cast<const E*>(pm + 32 * ks * sizeof(E)));
+                hc[h2] = load_vec<V4>(reinterpret_cast<const E*>(sl + C::OFF_HC + ln * C::RS) + perm_index(16 * t + 4 * g));
+                gc[h2] = load_vec<f32x4>(reinterpret_cast<const float*>(sl + C::OFF_G) + 16 * t + 4 * g);
             }
             // S' = Diag(gamma_C) S + Hc + PM S
 #pragma unroll
-            for (int t = 0; t < KT; ++t)
+            for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[t][i] = S[t][i] * gc[t][i] + to_f32(hc[t][i]);
+                for (int i = 0; i < 4; ++i) S[h2][i] = S[h2][i] * gc[h2][i] + to_f32(hc[h2][i]);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int t = 0; t < KT; ++t) S[t] = mma32(pf[t][ks], Sf[ks], S[t]);
+                for (int h2 = 0; h2 < 2; ++h2) S[h2] = mma32(pf[h2][ks], Sf[ks], S[h2]);
+            if (it + 1 < n) put(it + 1);
             __syncthreads();
         }
-        __syncthreads();   // iteration n: only the output wave works
         if (S_final) {
 #pragma unroll
-            for (int t = 0; t < KT; ++t)
+            for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S_final[sbase + (size_t)(16 * t + 4 * g + i) * DV + j0 + ln] = S[t][i];
+                    S_final[sbase + (size_t)(32 * w + 16 * h2 + 4 * g + i) * DV + j0 + ln] = S[h2][i];
         }
-    } else if (wave == 1) {
-        // ------------------------------------------------ output wave (one chunk behind)
-        OutputOps<E, DK> op0, op1, op2;
-        if (n > 0) load_output<E, DK, DV>(op0, record(0), chunks + c_begin, g, ln, j0);
-        __syncthreads();
-        // iteration it: load chunk it + 1 into set (it + 1) % 3, output chunk it - 1
-        auto step = [&](OutputOps<E, DK>& cur, OutputOps<E, DK>& nxt, int it) {
-            __builtin_amdgcn_sched_barrier(0);
-            const int nx = min(it + 1, n - 1);
-            load_output<E, DK, DV>(nxt, record(nx), chunks + c_begin + nx, g, ln, j0);
-            if (it > 0) {
-                const E* xs = xslot(it - 1);
-                V8 Sf[KS];
+    } else if (wave == NSER) {
+        // ------------------------------------------------ touch wave
+        // Plain loads whose values are folded into `sink` three chunks later;
+        // unconditional (clamped chunk index) so that each load writes its own
+        // registers and the compiler has no reason to wait for it early.
+        // Lines touched per chunk: 1/NSL of PM (shared by the slices of a head),
+        // this slice's 16 rows of Hc^T, and gamma_C; QM and OI are not read here.
+        using TouchSet = uint32_t[C::TOUCH_PER_LANE];
+        uint32_t toff[C::TOUCH_PER_LANE];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) Sf[ks] = load_vec<V8>(xs + (ks * 64 + l) * 8);
-                f32x4 O[4];   // O^T tile R: lane holds O[16R + ln][j0 + 4g + i];  O = QM S + OI
+        for (int k = 0; k < C::TOUCH_PER_LANE; ++k) {
+            const int u = l + 64 * k;
+            constexpr int PM_LINES = DK * DK * (int)sizeof(E) / 128;
+            constexpr int HC_LINES = 16 * DK * (int)sizeof(E) / 128;
+            constexpr int PM_MINE = PM_LINES / NSL;
+            size_t x;
+            if (u < PM_MINE) x = C::RL.pm + 128 * (size_t)(slice + NSL * u);
+            else if (u < PM_MINE + HC_LINES) x = C::RL.hc + (size_t)j0 * DK * sizeof(E) + 128 * (size_t)(u - PM_MINE);
+            else x = C::RL.g + 128 * (size_t)((u - PM_MINE - HC_LINES) % (DK * 4 / 128));
+            toff[k] = (uint32_t)x;
+        }
+        auto touch = [&](TouchSet& tv, int c) {
+            const unsigned char* r = record(c);
 #pragma unroll
-                for (int R = 0; R < 4; ++R)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) O[R][i] = to_f32(cur.oi[R][i]);
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int R = 0; R < 4; ++R) O[R] = mma32(Sf[ks], cur.q[R][ks], O[R]);
-#pragma unroll
-                for (int R = 0; R < 4; ++R) {
-                    const int r = 16 * R + ln;
-                    if (r < cur.len) {
-                        V4 w;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(O[R][i]);
-                        store_vec(o + ((size_t)(cur.start + r) * H + h) * DV + j0 + 4 * g, w);
-                    }
-                }
-            }
-            __syncthreads();
+            for (int k = 0; k < C::TOUCH_PER_LANE; ++k) tv[k] = *reinterpret_cast<const uint32_t*>(r + toff[k]);
         };
-        // sets rotate: chunk c lives in set c % 3; iteration it outputs chunk it - 1
-        for (int it = 0; it <= n; it += 3) {
-            step(op2, op1, it);                         // outputs chunk it - 1 (set 2), loads it + 1
-            if (it + 1 <= n) step(op0, op2, it + 1);    // outputs chunk it (set 0), loads it + 2
-            if (it + 2 <= n) step(op1, op0, it + 2);    // outputs chunk it + 1 (set 1), loads it + 3
-        }
-    } else if (wave == 2) {
-        // ------------------------------------------------ direct loads into the ring
-        int off[C::LOADS];   // this lane's byte offset inside a record, per load
+        uint32_t sink = 0;
+        TouchSet tv0, tv1, tv2;
+        auto fold = [&](TouchSet& tv) {
 #pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) {
-            const int u = 64 * i + l;
+            for (int k = 0; k < C::TOUCH_PER_LANE; ++k) sink ^= tv[k];
+        };
+        touch(tv0, min(TOUCH_DIST - 3, n - 1));
+        touch(tv1, min(TOUCH_DIST - 2, n - 1));
+        touch(tv2, min(TOUCH_DIST - 1, n - 1));
+        bare_barrier();
+        auto step = [&](TouchSet& tv, int it) {
+            fold(tv);   // issued three chunks ago
+            touch(tv, min(it + TOUCH_DIST, n - 1));
+            bare_barrier();
+        };
+        for (int it = 0; it < n; it += 3) {
+            step(tv0, it);
+            if (it + 1 < n) step(tv1, it + 1);
+            if (it + 2 < n) step(tv2, it + 2);
+        }
+        fold(tv0);
+        fold(tv1);
+        fold(tv2);
+        if (n_pairs < 0) states[0] = from_f32<E>((float)sink);   // keeps the touches; never taken
+    } else {
+        // ------------------------------------------------ stager waves: direct loads into the ring
+        const int sw = wave - NSER - 1;
+        const int i0 = sw * C::LOADS_W;
+        const int cnt = min(C::LOADS_W, C::LOADS - i0);
+        // This lane's byte offset inside a record, per load.
+        uint32_t off[C::LOADS_W];
+#pragma unroll
+        for (int k = 0; k < C::LOADS_W; ++k) {
+            const int u = 64 * (i0 + k) + l;
             int x;
             if (u < C::PM_UNITS) {
                 const int row = u / (C::RW + 1), col = u % (C::RW + 1);
@@ -500,63 +545,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             } else {
                 x = (int)C::RL.g;   // past the slot's data: lands in the slot's tail padding
             }
-            off[i] = x;
+            off[k] = (uint32_t)x;
         }
         auto issue = [&](int c) {
             const unsigned char* r = record(c);
-            unsigned char* dst = slot(c);
+            unsigned char* dst = slot(c) + 1024 * i0;
+            // all addresses first, then the loads: each load keeps its own address
+            // registers, so no address is rewritten while a queued load still reads it
+            const unsigned char* src[C::LOADS_W];
 #pragma unroll
-            for (int i = 0; i < C::LOADS; ++i)
-                __builtin_amdgcn_global_load_lds((global_void*)(r + off[i]), (lds_void*)(dst + 1024 * i),
-                                                 16, 0, 0);
+            for (int k = 0; k < C::LOADS_W; ++k) src[k] = r + off[k];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < C::LOADS_W; ++k)
+                if (k < cnt)
+                    __builtin_amdgcn_global_load_lds((global_void*)src[k], (lds_void*)(dst + 1024 * k), 16, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         };
-        if (n > 0) {
-            issue(0);
-            issue(min(1, n - 1));
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS));   // chunk 0 has landed
-        }
+        // wait until only the chunk issued last is in flight (cnt loads)
+        auto wait_one_in_flight = [&]() {
+            if (cnt == C::LOADS_W) __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS_W));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS_LAST));
+        };
+        issue(0);
+        issue(min(1, n - 1));
+        wait_one_in_flight();   // chunk 0 has landed
         bare_barrier();
-        for (int it = 0; it <= n; ++it) {
+        for (int it = 0; it < n; ++it) {
             if (it + 2 < n) {
                 issue(it + 2);   // its slot was last read in iteration it - 1
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS));   // chunk it + 1 has landed
+                wait_one_in_flight();   // chunk it + 1 has landed
             } else {
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
             bare_barrier();
         }
-    } else {
-        // ------------------------------------------------ L2 touches
-        auto touch = [&](int c) {
-            const unsigned char* r = record(c);
-#pragma unroll
-            for (int k = 0; k < C::TOUCH_PER_LANE; ++k) {
-                const int line = slice + NSL * (l + 64 * k);
-                if (line < C::LINES)
-                    __builtin_amdgcn_global_load_lds((global_void*)(r + 128 * line), (lds_void*)dump, 4, 0, 0);
-            }
-        };
-        for (int c = 2; c < min(TOUCH_DIST, n); ++c) touch(c);
-        bare_barrier();
-        for (int it = 0; it <= n; ++it) {
-            if (it + TOUCH_DIST < n) touch(it + TOUCH_DIST);
-            bare_barrier();
-        }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no load may land after the workgroup ends
     }
 }
 
 template <typename E, int DK, int DV>
 static hipError_t launch_state_ring_t(const void* rec, const int32_t* seq_chunk_start,
-                                      const ChunkInfo* chunks, const float* S0, float* S_final,
-                                      void* o, int N, int H, hipStream_t stream)
+                                      const float* S0, float* S_final, void* states, int N, int H,
+                                      hipStream_t stream)
 {
+    using C = RingCfg<E, DK, DV>;
     const int n_pairs = N * H;
     const int groups = (n_pairs + 7) / 8;
     const long long blocks = (long long)groups * 8 * (DV / 16);
-    hipLaunchKernelGGL((prefill_state_ring_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(256), 0,
-                       stream, (const unsigned char*)rec, seq_chunk_start, chunks, S0, S_final,
-                       (E*)o, H, n_pairs);
+    hipLaunchKernelGGL((prefill_state_ring_kernel<E, DK, DV>), dim3((unsigned)blocks),
+                       dim3(64 * C::WAVES), 0, stream, (const unsigned char*)rec, seq_chunk_start,
+                       S0, S_final, (E*)states, H, n_pairs);
     return hipGetLastError();
 }
 
@@ -576,27 +614,28 @@ static hipError_t launch_state_t(const void* rec, const int32_t* seq_chunk_start
 
 hipError_t launch_prefill_state(const void* rec, const int32_t* seq_chunk_start,
                                 const ChunkInfo* chunks, const float* S0, float* S_final,
-                                void* o, int N, int H, int dk, int dv, bool bf16_io,
+                                void* o, void* states, int N, int H, int dk, int dv, bool bf16_io,
                                 hipStream_t stream)
 {
 #define KDA_RING_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
-        return launch_state_ring_t<E, DK_, DV_>(rec, seq_chunk_start, chunks, S0, S_final, o, N, H, stream);
+        return launch_state_ring_t<E, DK_, DV_>(rec, seq_chunk_start, S0, S_final, states, N, H, stream);
 #define KDA_STATE_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
         return launch_state_t<E, DK_, DV_>(rec, seq_chunk_start, chunks, S0, S_final, o, N, H, stream);
-    // The ring needs three slots of (PM + 16 rows of Hc^T + gamma_C) in LDS; with
-    // fp32 operands and dk = 128 they do not fit, and the register-staged kernel runs.
-    if (bf16_io) {
-        KDA_RING_CASE(bf16, 128, 128)
-        KDA_RING_CASE(bf16, 64, 64)
-        KDA_RING_CASE(bf16, 128, 64)
-        KDA_RING_CASE(bf16, 64, 128)
+    if (uses_output_pass(bf16_io, dk)) {
+        if (bf16_io) {
+            KDA_RING_CASE(bf16, 128, 128)
+            KDA_RING_CASE(bf16, 64, 64)
+            KDA_RING_CASE(bf16, 128, 64)
+            KDA_RING_CASE(bf16, 64, 128)
+        } else {
+            KDA_RING_CASE(float, 64, 64)
+            KDA_RING_CASE(float, 64, 128)
+        }
     } else {
         KDA_STATE_CASE(float, 128, 128)
-        KDA_RING_CASE(float, 64, 64)
         KDA_STATE_CASE(float, 128, 64)
-        KDA_RING_CASE(float, 64, 128)
     }
 #undef KDA_RING_CASE
 #undef KDA_STATE_CASE
