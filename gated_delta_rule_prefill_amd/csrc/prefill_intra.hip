@@ -121,6 +121,19 @@ __device__ __forceinline__ void load_row(const E* p, float (&out)[CPT]) {
     }
 }
 
+// CPT consecutive elements to LDS (one store)
+template <int CPT, typename E>
+__device__ __forceinline__ void store_row(E* p, const E (&v)[CPT]) {
+    if constexpr (CPT == 2) {
+        typename Vec<E>::v2 w;
+        w[0] = v[0];
+        w[1] = v[1];
+        *reinterpret_cast<typename Vec<E>::v2*>(p) = w;
+    } else {
+        p[0] = v[0];
+    }
+}
+
 // An MFMA operand over 32 tokens (step s) from two stacked 16-token
 // accumulator tiles: lane group g holds rows 4g..4g+3 of each, i.e. the
 // perm32 slot order.
@@ -297,16 +310,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = 16 * R + r;
+        E kp[CPT], kd[CPT];
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
             const float P = fast_exp(ell[r][e]);                   // e^{g_r - B_R} <= 1
             const float iP = fast_exp(fminf(-ell[r][e], 80.f));    // e^{B_R - g_r}
-            sKP[row * L::LK + c0 + e] = from_f32<E>(kr[r][e] * P);
-            sKD[row * L::LK + c0 + e] = from_f32<E>(kr[r][e] * iP);
+            kp[e] = from_f32<E>(kr[r][e] * P);
+            kd[e] = from_f32<E>(kr[r][e] * iP);
             ell[r][e] = kr[r][e] * iP * eTE[e];                    // Khat: k e^{g_C - g_r}
             kr[r][e] *= P * eB[e];                                 // e^{g_r} k  (for W)
             la[r][e] = P;                                          // log_alpha is dead here
         }
+        store_row<CPT>(sKP + row * L::LK + c0, kp);
+        store_row<CPT>(sKD + row * L::LK + c0, kd);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r)
@@ -320,24 +336,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
     // ---- phase 1a: A_kk tiles (rows r of block R, columns i of block I) --------
     // A operand k_r e^{g_r - B_R}; B operand k_i e^{B_I - g_i} * e^{B_R - B_I}.
-    for (int p = wave; p < 10; p += 4) {
-        const int PR = pair_r(p), PI = pair_i(p);
-        const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
-        V8 a[KS], b[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int cb = 32 * s + 8 * g;
-            a[s] = frag8<E>(sKP + (16 * PR + ln) * L::LK + cb);
-            b[s] = PR == PI ? frag8<E>(sKD + (16 * PI + ln) * L::LK + cb)
-                            : frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f + cb);
-        }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k3 = 0; k3 < 3; ++k3) {
+        const int p = wave + 4 * k3;
+        if (p < 10) {
+            const int PR = pair_r(p), PI = pair_i(p);
+            const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
+            V8 a[KS], b[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) acc = mma32(a[s], b[s], acc);
+            for (int s = 0; s < KS; ++s) {
+                const int cb = 32 * s + 8 * g;
+                a[s] = frag8<E>(sKP + (16 * PR + ln) * L::LK + cb);
+                b[s] = PR == PI ? frag8<E>(sKD + (16 * PI + ln) * L::LK + cb)
+                                : frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f + cb);
+            }
+            const f32x4 bt4 = *reinterpret_cast<const f32x4*>(sBeta + 16 * PR + 4 * g);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * PR + 4 * g + i, col = 16 * PI + ln;
-            sAL[r * L::LA + col] = r > col ? sBeta[r] * acc[i] : 0.f;
+            for (int s = 0; s < KS; ++s) acc = mma32(a[s], b[s], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * PR + 4 * g + i, col = 16 * PI + ln;
+                sAL[r * L::LA + col] = r > col ? bt4[i] * acc[i] : 0.f;
+            }
         }
     }
     for (int u = wave - 2; u >= 0 && u < 6; u += 2) {   // waves 2 and 3 zero the upper tiles
@@ -351,17 +372,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = 16 * R + r;
+        E qp[CPT];
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
-            sKP[row * L::LK + c0 + e] = from_f32<E>(qr[r][e]);
+            qp[e] = from_f32<E>(qr[r][e]);
             qr[r][e] *= eB[e];
         }
+        store_row<CPT>(sKP + row * L::LK + c0, qp);
     }
     __syncthreads();
 
     // ---- phase 1c: A_qk^T tiles (rows i of block I, columns r of block R) -------
     // stored as A_qk[r][perm32(i)] in LDS for the read-out products
-    for (int p = wave; p < 10; p += 4) {
+#pragma unroll
+    for (int k3 = 0; k3 < 3; ++k3) {
+        const int p = wave + 4 * k3;
+        if (p >= 10) continue;
         const int PR = pair_r(p), PI = pair_i(p);
         const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
         V8 a[KS], b[KS];
@@ -450,9 +476,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     __syncthreads();
 
     // ---- phase 3e: T = X Diag(beta) in the operand dtype ----------------------
-    for (int idx = t; idx < CHUNK * CHUNK; idx += 256) {
-        const int r = idx >> 6, c = idx & 63;
-        sTL[r * L::LT + c] = from_f32<E>(x_elem<L::LA>(sAL, r, c) * sBeta[c]);
+    // lane = row r, wave w: column groups 2w, 2w + 1 (8 columns each, one
+    // 16-byte store); X[r][c] for r > c sits transposed at sAL[c][r], so the
+    // 64 lanes of one read touch 64 consecutive words.
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+        const int r = lane, c0 = 8 * (2 * wave + k2);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(sBeta + c0);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(sBeta + c0 + 4);
+        float xv[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) xv[m] = sAL[(c0 + m) * L::LA + r];
+        V8 w;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int c = c0 + m;
+            const float x = r > c ? xv[m] : (r == c ? 1.f : 0.f);
+            w[m] = from_f32<E>(x * (m < 4 ? b0[m] : b1[m - 4]));
+        }
+        store_vec(sTL + r * L::LT + c0, w);
     }
     __syncthreads();   // X dead: its bytes become Khat^T
 

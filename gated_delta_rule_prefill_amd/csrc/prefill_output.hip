@@ -13,20 +13,43 @@
 
 namespace kda {
 
+typedef __attribute__((address_space(1))) void out_global_void;
+typedef __attribute__((address_space(3))) void out_lds_void;
+
+// LDS staging of one (chunk, head): the chunk-start state exactly as stored
+// (operand slots, lane-contiguous) and QM with 16-byte padded rows.
+template <typename E, int DK, int DV>
+struct OutCfg {
+    static constexpr int ES = sizeof(E);
+    static constexpr int KS = DK / 32, NSL = DV / 16, SPW = NSL / 4;
+    static constexpr int ST_UNITS = DK * DV * ES / 16;        // state, 16-byte units
+    static constexpr int RW = DK * ES / 16;                   // units per QM row
+    static constexpr int QM_UNITS = 64 * (RW + 1);            // padded rows
+    static constexpr int UNITS = ST_UNITS + QM_UNITS;
+    static constexpr int LOADS = (UNITS + 63) / 64;           // direct loads per block
+    static constexpr int LOADS_W = (LOADS + 3) / 4;           // per wave
+    static constexpr int OFF_QM = ST_UNITS * 16;
+    static constexpr int QRS = (RW + 1) * 16;                 // padded QM row stride
+    static constexpr int LDS_BYTES = LOADS_W * 4 * 1024;
+};
+
 // Wave w owns value slices SPW*w .. SPW*w + SPW - 1 (16 columns each) for all
 // 64 rows; with two slices per wave their columns 4g..4g+3 are the 8
-// consecutive perm32 slots 8g..8g+7 of OI.
+// consecutive perm32 slots 8g..8g+7 of OI.  The state and QM are moved into
+// LDS once per workgroup by direct global->LDS loads, a quarter per wave.
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void prefill_output_kernel(
     const unsigned char* __restrict__ rec, const E* __restrict__ states,
     const ChunkInfo* __restrict__ chunks, const int32_t* __restrict__ n_chunks_ptr, int H,
     E* __restrict__ o)
 {
+    using C = OutCfg<E, DK, DV>;
     using V4 = typename Vec<E>::v4;
     using V8 = typename Vec<E>::v8;
-    constexpr int KS = DK / 32, NSL = DV / 16, SPW = NSL / 4;
+    constexpr int KS = C::KS, SPW = C::SPW;
     static_assert(SPW == 1 || SPW == 2, "value slices per wave");
     constexpr RecLayout RL = rec_layout(sizeof(E), DK, DV);
+    __shared__ __attribute__((aligned(1024))) unsigned char sm[C::LDS_BYTES];
 
     const int cid = blockIdx.x;
     // both reads are issued together (the table holds gridDim.x entries)
@@ -37,22 +60,33 @@ __global__ __launch_bounds__(256) void prefill_output_kernel(
     const size_t chh = (size_t)cid * H + h;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63, g = l >> 4, ln = l & 15;
-    const E* QM = reinterpret_cast<const E*>(rec + chh * RL.bytes + RL.qm);
-    const E* OI = reinterpret_cast<const E*>(rec + chh * RL.bytes + RL.oi);
-    const E* St = states + chh * DK * DV;
+    const unsigned char* R0 = rec + chh * RL.bytes;
+    const unsigned char* St = reinterpret_cast<const unsigned char*>(states + chh * DK * DV);
 
-    V8 sf[SPW][KS];
+    // direct loads: units [0, ST_UNITS) copy the state, the rest fill QM's padded rows
+    {
+        const unsigned char* src[C::LOADS_W];
 #pragma unroll
-    for (int sp = 0; sp < SPW; ++sp)
+        for (int k = 0; k < C::LOADS_W; ++k) {
+            const int u = 64 * (C::LOADS_W * wave + k) + l;
+            if (u < C::ST_UNITS) {
+                src[k] = St + 16 * (size_t)u;
+            } else {
+                const int v = u < C::UNITS ? u - C::ST_UNITS : 0;
+                const int row = v / (C::RW + 1), col = v % (C::RW + 1);
+                src[k] = R0 + RL.qm + (size_t)row * DK * sizeof(E) + (col < C::RW ? col : 0) * 16;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sf[sp][ks] = load_vec<V8>(St + (((SPW * wave + sp) * KS + ks) * 64 + l) * 8);
-    V8 q[4][KS];
-#pragma unroll
-    for (int R = 0; R < 4; ++R)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) q[R][ks] = load_vec<V8>(QM + (16 * R + ln) * DK + 32 * ks + 8 * g);
+        for (int k = 0; k < C::LOADS_W; ++k)
+            if (C::LOADS_W * wave + k < C::LOADS)
+                __builtin_amdgcn_global_load_lds((out_global_void*)src[k],
+                                                 (out_lds_void*)(sm + 1024 * (C::LOADS_W * wave + k)), 16, 0, 0);
+    }
     // OI[16R + ln][columns j0 + 4g .. +3 of each owned slice] (perm32 slots)
     float oi[4][SPW][4];
+    const E* OI = reinterpret_cast<const E*>(R0 + RL.oi);
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
         const E* src = OI + (16 * R + ln) * DV + perm_index(16 * SPW * wave + 4 * g);
@@ -69,15 +103,27 @@ __global__ __launch_bounds__(256) void prefill_output_kernel(
             for (int i = 0; i < 4; ++i) oi[R][0][i] = to_f32(v[i]);
         }
     }
+    __syncthreads();   // the workgroup's direct loads have landed
+
+    const E* sst = reinterpret_cast<const E*>(sm);
+    V8 sf[SPW][KS];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sf[sp][ks] = load_vec<V8>(sst + (((SPW * wave + sp) * KS + ks) * 64 + l) * 8);
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
+        V8 q[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            q[ks] = load_vec<V8>(reinterpret_cast<const E*>(sm + C::OFF_QM + (16 * R + ln) * C::QRS) + 32 * ks + 8 * g);
         const int r = 16 * R + ln;
 #pragma unroll
         for (int sp = 0; sp < SPW; ++sp) {
             // O^T tile: lane holds O[16R + ln][j0 + 4g + i]
             f32x4 acc = {oi[R][sp][0], oi[R][sp][1], oi[R][sp][2], oi[R][sp][3]};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc = mma32(sf[sp][ks], q[R][ks], acc);
+            for (int ks = 0; ks < KS; ++ks) acc = mma32(sf[sp][ks], q[ks], acc);
             if (r < ci.len) {
                 V4 w;
 #pragma unroll
