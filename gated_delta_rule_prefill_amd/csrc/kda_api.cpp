@@ -176,13 +176,18 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
         kda_status st = KDA_OK;
         {
             Timer timer(stream);
-            st = check_launch(kda::launch_chunk_table(cu_seqlens, total_tokens, num_seqs, seq_start,
-                                                      chunks, (int)plan.max_chunks, stream),
-                              "chunk table kernel", stream);
-            timer.mark("chunk_table");
+            // N equal rows need no chunk table: the kernels derive their chunks
+            kda::ChunkSrc src{chunks, seq_start, cu_seqlens ? -1 : (int)(total_tokens / num_seqs),
+                              num_seqs};
+            if (cu_seqlens) {
+                st = check_launch(kda::launch_chunk_table(cu_seqlens, total_tokens, num_seqs,
+                                                          seq_start, chunks, (int)plan.max_chunks,
+                                                          stream),
+                                  "chunk table kernel", stream);
+                timer.mark("chunk_table");
+            }
             if (st == KDA_OK && total_tokens > 0) {
-                st = check_launch(kda::launch_prefill_intra(q, k, v, log_alpha, beta, chunks,
-                                                            seq_start + num_seqs,
+                st = check_launch(kda::launch_prefill_intra(q, k, v, log_alpha, beta, src,
                                                             (int)plan.max_chunks, H, dk, dv, bf16,
                                                             ws, stream),
                                   "intra-chunk kernel", stream);
@@ -190,16 +195,14 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
             }
             void* states = plan.output_pass ? (void*)(ws + plan.off_states) : nullptr;
             if (st == KDA_OK) {
-                st = check_launch(kda::launch_prefill_state(ws, seq_start, chunks, initial_state,
-                                                            final_state, o, states, num_seqs, H,
-                                                            dk, dv, bf16, stream),
+                st = check_launch(kda::launch_prefill_state(ws, src, initial_state, final_state, o,
+                                                            states, H, dk, dv, bf16, stream),
                                   "state kernel", stream);
                 timer.mark("prefill_state");
             }
             if (st == KDA_OK && plan.output_pass && total_tokens > 0) {
-                st = check_launch(kda::launch_prefill_output(ws, states, chunks, seq_start + num_seqs,
-                                                             (int)plan.max_chunks, H, dk, dv, bf16,
-                                                             o, stream),
+                st = check_launch(kda::launch_prefill_output(ws, states, src, (int)plan.max_chunks,
+                                                             H, dk, dv, bf16, o, stream),
                                   "output kernel", stream);
                 timer.mark("prefill_output");
             }

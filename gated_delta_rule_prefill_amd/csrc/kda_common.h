@@ -90,4 +90,51 @@ __device__ __forceinline__ void store_vec<f32x8, float>(float* p, f32x8 v) {
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
+// Chunks of a batch (see ChunkSrc): from the table, or arithmetically for N
+// equal sequences of src.rows tokens.
+__device__ __forceinline__ int chunks_per_row(int rows) { return (rows + CHUNK - 1) / CHUNK; }
+
+// Number of chunks and the descriptor of chunk cid (cid < gridDim.x entries of
+// the table, so the table read is in bounds even past the last chunk; both
+// table reads are issued together).
+__device__ __forceinline__ void chunk_of(const ChunkSrc& src, int cid, int& n_chunks, ChunkInfo& ci) {
+    if (src.rows >= 0) {
+        const int cps = chunks_per_row(src.rows);
+        n_chunks = src.N * cps;
+        const int sq = cps > 0 ? cid / cps : 0, k = cps > 0 ? cid - sq * cps : 0;
+        ci.seq = sq;
+        ci.start = sq * src.rows + CHUNK * k;
+        ci.len = min(CHUNK, src.rows - CHUNK * k);
+        ci.pad = 0;
+    } else {
+        n_chunks = src.seq_chunk_start[src.N];
+        ci = src.chunks[cid];
+    }
+}
+
+// Descriptor of chunk cid (cid must be a valid chunk).
+__device__ __forceinline__ ChunkInfo chunk_desc(const ChunkSrc& src, int cid) {
+    if (src.rows < 0) return src.chunks[cid];
+    const int cps = chunks_per_row(src.rows);
+    const int sq = cid / cps, k = cid - sq * cps;
+    ChunkInfo ci;
+    ci.seq = sq;
+    ci.start = sq * src.rows + CHUNK * k;
+    ci.len = min(CHUNK, src.rows - CHUNK * k);
+    ci.pad = 0;
+    return ci;
+}
+
+// First chunk and chunk count of sequence s.
+__device__ __forceinline__ void seq_chunks(const ChunkSrc& src, int s, int& c_begin, int& n) {
+    if (src.rows >= 0) {
+        const int cps = chunks_per_row(src.rows);
+        c_begin = s * cps;
+        n = cps;
+    } else {
+        c_begin = src.seq_chunk_start[s];
+        n = src.seq_chunk_start[s + 1] - c_begin;
+    }
+}
+
 }  // namespace kda

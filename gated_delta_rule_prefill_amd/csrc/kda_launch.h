@@ -17,6 +17,16 @@ struct ChunkInfo {
     int32_t pad;
 };
 
+// Where the kernels find the chunks of a batch: the chunk table (packed
+// batches, rows < 0), or N equal sequences of `rows` tokens each, whose chunks
+// follow arithmetically (no table, no extra kernel).
+struct ChunkSrc {
+    const ChunkInfo* chunks;          // [max_chunks], table mode
+    const int32_t* seq_chunk_start;   // [N + 1], table mode
+    int rows;                         // >= 0: tokens per sequence; < 0: table mode
+    int N;
+};
+
 // Per-(chunk, head) record of the chunk intermediates in the workspace
 // (byte offsets; es = element size of q/k/v, 2 or 4).  With entry state S,
 // a chunk's state update and output are
@@ -46,16 +56,14 @@ hipError_t launch_chunk_table(const int32_t* cu, int64_t T, int N, int32_t* seq_
 
 // rec: [max_chunks * H] records of rec_layout() bytes
 hipError_t launch_prefill_intra(const void* q, const void* k, const void* v, const float* la,
-                                const float* beta, const ChunkInfo* chunks,
-                                const int32_t* n_chunks, int max_chunks, int H, int dk, int dv,
-                                bool bf16_io, void* rec, hipStream_t stream);
+                                const float* beta, ChunkSrc src, int max_chunks, int H, int dk,
+                                int dv, bool bf16_io, void* rec, hipStream_t stream);
 
 // Sequential inter-chunk pass.  With the output pass (uses_output_pass) it
 // stores every chunk-start state into `states` and leaves o to
 // launch_prefill_output; otherwise it writes o itself and ignores `states`.
-hipError_t launch_prefill_state(const void* rec, const int32_t* seq_chunk_start,
-                                const ChunkInfo* chunks, const float* S0, float* S_final,
-                                void* o, void* states, int N, int H, int dk, int dv, bool bf16_io,
+hipError_t launch_prefill_state(const void* rec, ChunkSrc src, const float* S0, float* S_final,
+                                void* o, void* states, int H, int dk, int dv, bool bf16_io,
                                 hipStream_t stream);
 
 // Whether a configuration runs the chain-only sequential kernel followed by the
@@ -67,9 +75,9 @@ constexpr bool uses_output_pass(bool bf16_io, int dk) { return bf16_io || dk == 
 constexpr size_t chunk_state_bytes(int es, int dk, int dv) { return (size_t)dk * dv * es; }
 
 // Parallel output pass: O = QM S_c + OI for every (chunk, head).
-hipError_t launch_prefill_output(const void* rec, const void* states, const ChunkInfo* chunks,
-                                 const int32_t* n_chunks, int max_chunks, int H, int dk, int dv,
-                                 bool bf16_io, void* o, hipStream_t stream);
+hipError_t launch_prefill_output(const void* rec, const void* states, ChunkSrc src,
+                                 int max_chunks, int H, int dk, int dv, bool bf16_io, void* o,
+                                 hipStream_t stream);
 
 hipError_t launch_decode_step(float* state, const void* q, const void* k, const void* v,
                               const float* la, const float* beta, void* o, int units, int dk,

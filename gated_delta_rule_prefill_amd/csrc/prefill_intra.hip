@@ -200,7 +200,7 @@ template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_intra_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    const ChunkInfo* __restrict__ chunks, const int32_t* __restrict__ n_chunks_ptr, int H,
+    const ChunkSrc src, int H,
     unsigned char* __restrict__ rec)
 {
     using L = IntraLayout<E, DK, DV>;
@@ -227,10 +227,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     float* sBeta = reinterpret_cast<float*>(smem + L::OFF_BETA);
 
     const int cid = blockIdx.x;
-    // Both reads are issued together (the table holds gridDim.x entries, so
-    // chunks[cid] is in bounds even for a block that then exits).
-    const int n_chunks = *n_chunks_ptr;
-    const ChunkInfo ci = chunks[cid];
+    int n_chunks;
+    ChunkInfo ci;
+    chunk_of(src, cid, n_chunks, ci);
     if (cid >= n_chunks) return;
     const int h = blockIdx.y;
     const size_t chh = (size_t)cid * H + h;
@@ -701,25 +700,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
 template <typename E, int DK, int DV>
 static hipError_t launch_intra_t(const void* q, const void* k, const void* v, const float* la,
-                                 const float* beta, const ChunkInfo* chunks,
-                                 const int32_t* n_chunks, int max_chunks, int H, void* rec,
+                                 const float* beta, ChunkSrc src, int max_chunks, int H, void* rec,
                                  hipStream_t stream)
 {
     hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV>), dim3(max_chunks, H), dim3(256), 0, stream,
-                       (const E*)q, (const E*)k, (const E*)v, la, beta, chunks, n_chunks, H,
+                       (const E*)q, (const E*)k, (const E*)v, la, beta, src, H,
                        (unsigned char*)rec);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_intra(const void* q, const void* k, const void* v, const float* la,
-                                const float* beta, const ChunkInfo* chunks,
-                                const int32_t* n_chunks, int max_chunks, int H, int dk, int dv,
-                                bool bf16_io, void* rec, hipStream_t stream)
+                                const float* beta, ChunkSrc src, int max_chunks, int H, int dk,
+                                int dv, bool bf16_io, void* rec, hipStream_t stream)
 {
 #define KDA_INTRA_CASE(E, DK_, DV_)                                                               \
     if (dk == DK_ && dv == DV_)                                                                  \
-        return launch_intra_t<E, DK_, DV_>(q, k, v, la, beta, chunks, n_chunks, max_chunks, H,   \
-                                           rec, stream);
+        return launch_intra_t<E, DK_, DV_>(q, k, v, la, beta, src, max_chunks, H, rec, stream);
     if (bf16_io) {
         KDA_INTRA_CASE(bf16, 128, 128)
         KDA_INTRA_CASE(bf16, 64, 64)

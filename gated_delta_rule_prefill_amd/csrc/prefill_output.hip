@@ -40,8 +40,7 @@ struct OutCfg {
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void prefill_output_kernel(
     const unsigned char* __restrict__ rec, const E* __restrict__ states,
-    const ChunkInfo* __restrict__ chunks, const int32_t* __restrict__ n_chunks_ptr, int H,
-    E* __restrict__ o)
+    const ChunkSrc src, int H, E* __restrict__ o)
 {
     using C = OutCfg<E, DK, DV>;
     using V4 = typename Vec<E>::v4;
@@ -52,9 +51,9 @@ __global__ __launch_bounds__(256) void prefill_output_kernel(
     __shared__ __attribute__((aligned(1024))) unsigned char sm[C::LDS_BYTES];
 
     const int cid = blockIdx.x;
-    // both reads are issued together (the table holds gridDim.x entries)
-    const int n_chunks = *n_chunks_ptr;
-    const ChunkInfo ci = chunks[cid];
+    int n_chunks;
+    ChunkInfo ci;
+    chunk_of(src, cid, n_chunks, ci);
     if (cid >= n_chunks) return;
     const int h = blockIdx.y;
     const size_t chh = (size_t)cid * H + h;
@@ -136,22 +135,21 @@ __global__ __launch_bounds__(256) void prefill_output_kernel(
 }
 
 template <typename E, int DK, int DV>
-static hipError_t launch_output_t(const void* rec, const void* states, const ChunkInfo* chunks,
-                                  const int32_t* n_chunks, int max_chunks, int H, void* o,
-                                  hipStream_t stream)
+static hipError_t launch_output_t(const void* rec, const void* states, ChunkSrc src, int max_chunks,
+                                  int H, void* o, hipStream_t stream)
 {
     hipLaunchKernelGGL((prefill_output_kernel<E, DK, DV>), dim3(max_chunks, H), dim3(256), 0, stream,
-                       (const unsigned char*)rec, (const E*)states, chunks, n_chunks, H, (E*)o);
+                       (const unsigned char*)rec, (const E*)states, src, H, (E*)o);
     return hipGetLastError();
 }
 
-hipError_t launch_prefill_output(const void* rec, const void* states, const ChunkInfo* chunks,
-                                 const int32_t* n_chunks, int max_chunks, int H, int dk, int dv,
-                                 bool bf16_io, void* o, hipStream_t stream)
+hipError_t launch_prefill_output(const void* rec, const void* states, ChunkSrc src,
+                                 int max_chunks, int H, int dk, int dv, bool bf16_io, void* o,
+                                 hipStream_t stream)
 {
 #define KDA_OUT_CASE(E, DK_, DV_)   \
     if (dk == DK_ && dv == DV_)       \
-        return launch_output_t<E, DK_, DV_>(rec, states, chunks, n_chunks, max_chunks, H, o, stream);
+        return launch_output_t<E, DK_, DV_>(rec, states, src, max_chunks, H, o, stream);
     if (bf16_io) {
         KDA_OUT_CASE(bf16, 128, 128)
         KDA_OUT_CASE(bf16, 64, 64)

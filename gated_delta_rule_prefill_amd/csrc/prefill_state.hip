@@ -80,7 +80,7 @@ __device__ __forceinline__ void load_serial(SerialOps<E, DK>& op, const unsigned
 
 template <typename E, int DK, int DV>
 __device__ __forceinline__ void load_output(OutputOps<E, DK>& op, const unsigned char* r,
-                                            const ChunkInfo* ci, int g, int ln, int j0)
+                                            const ChunkInfo ci, int g, int ln, int j0)
 {
     using C = StateCfg<E, DK, DV>;
     using V8 = typename Vec<E>::v8;
@@ -93,8 +93,8 @@ __device__ __forceinline__ void load_output(OutputOps<E, DK>& op, const unsigned
         for (int ks = 0; ks < C::KS; ++ks) op.q[R][ks] = load_vec<V8>(QM + (16 * R + ln) * DK + 32 * ks + 8 * g);
         op.oi[R] = load_vec<V4>(OI + (16 * R + ln) * DV + perm_index(j0 + 4 * g));
     }
-    op.start = ci->start;
-    op.len = ci->len;
+    op.start = ci.start;
+    op.len = ci.len;
 }
 
 // Workgroups are grouped so that the DV/16 slices of one (sequence, head)
@@ -102,8 +102,7 @@ __device__ __forceinline__ void load_output(OutputOps<E, DK>& op, const unsigned
 // the 8 XCDs, so the slices that read the same chunk records share one L2.
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_state_kernel(
-    const unsigned char* __restrict__ rec, const int32_t* __restrict__ seq_chunk_start,
-    const ChunkInfo* __restrict__ chunks, const float* __restrict__ S0,
+    const unsigned char* __restrict__ rec, const ChunkSrc src, const float* __restrict__ S0,
     float* __restrict__ S_final, E* __restrict__ o, int H, int n_pairs)
 {
     using C = StateCfg<E, DK, DV>;
@@ -123,8 +122,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, g = l >> 4, ln = l & 15;
     const int j0 = slice * 16;
-    const int c_begin = seq_chunk_start[s];
-    const int n = seq_chunk_start[s + 1] - c_begin;   // chunks of this sequence
+    int c_begin, n;   // first chunk and chunk count of this sequence
+    seq_chunks(src, s, c_begin, n);
     const size_t sbase = (size_t)pair * DK * DV;
     if (n == 0) {   // empty sequence: the final state is the initial one (or zero)
         if (S_final)
@@ -209,14 +208,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     } else if (wave == 1) {
         // ------------------------------------------------ output wave (one chunk behind)
         OutputOps<E, DK> opA, opB;
-        if (n > 0) load_output<E, DK, DV>(opA, record(0), chunks + c_begin, g, ln, j0);
+        if (n > 0) load_output<E, DK, DV>(opA, record(0), chunk_desc(src, c_begin), g, ln, j0);
         __syncthreads();
         __syncthreads();   // iteration 0: the serial wave hands over chunk 0's start state
 
         auto step = [&](OutputOps<E, DK>& cur, OutputOps<E, DK>& nxt, int it) {
             __builtin_amdgcn_sched_barrier(0);
             const int nx = min(it + 1, n - 1);
-            load_output<E, DK, DV>(nxt, record(nx), chunks + c_begin + nx, g, ln, j0);
+            load_output<E, DK, DV>(nxt, record(nx), chunk_desc(src, c_begin + nx), g, ln, j0);
             const E* xs = xslot(it);
             V8 Sf[KS];
 #pragma unroll
@@ -369,9 +368,8 @@ __device__ __forceinline__ void bare_barrier() {
 
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
-    const unsigned char* __restrict__ rec, const int32_t* __restrict__ seq_chunk_start,
-    const float* __restrict__ S0, float* __restrict__ S_final, E* __restrict__ states,
-    int H, int n_pairs)
+    const unsigned char* __restrict__ rec, const ChunkSrc src, const float* __restrict__ S0,
+    float* __restrict__ S_final, E* __restrict__ states, int H, int n_pairs)
 {
     using C = RingCfg<E, DK, DV>;
     using V4 = typename Vec<E>::v4;
@@ -390,8 +388,8 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, g = l >> 4, ln = l & 15;
     const int j0 = slice * 16;
-    const int c_begin = seq_chunk_start[s];
-    const int n = seq_chunk_start[s + 1] - c_begin;   // chunks of this sequence
+    int c_begin, n;   // first chunk and chunk count of this sequence
+    seq_chunks(src, s, c_begin, n);
     const size_t sbase = (size_t)pair * DK * DV;
     if (n == 0) {   // empty sequence: the final state is the initial one (or zero)
         if (S_final)
@@ -584,45 +582,41 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
 }
 
 template <typename E, int DK, int DV>
-static hipError_t launch_state_ring_t(const void* rec, const int32_t* seq_chunk_start,
-                                      const float* S0, float* S_final, void* states, int N, int H,
-                                      hipStream_t stream)
+static hipError_t launch_state_ring_t(const void* rec, ChunkSrc src, const float* S0, float* S_final,
+                                      void* states, int H, hipStream_t stream)
 {
     using C = RingCfg<E, DK, DV>;
-    const int n_pairs = N * H;
+    const int n_pairs = src.N * H;
     const int groups = (n_pairs + 7) / 8;
     const long long blocks = (long long)groups * 8 * (DV / 16);
     hipLaunchKernelGGL((prefill_state_ring_kernel<E, DK, DV>), dim3((unsigned)blocks),
-                       dim3(64 * C::WAVES), 0, stream, (const unsigned char*)rec, seq_chunk_start,
-                       S0, S_final, (E*)states, H, n_pairs);
+                       dim3(64 * C::WAVES), 0, stream, (const unsigned char*)rec, src, S0, S_final,
+                       (E*)states, H, n_pairs);
     return hipGetLastError();
 }
 
 template <typename E, int DK, int DV>
-static hipError_t launch_state_t(const void* rec, const int32_t* seq_chunk_start,
-                                 const ChunkInfo* chunks, const float* S0, float* S_final,
-                                 void* o, int N, int H, hipStream_t stream)
+static hipError_t launch_state_t(const void* rec, ChunkSrc src, const float* S0, float* S_final,
+                                 void* o, int H, hipStream_t stream)
 {
-    const int n_pairs = N * H;
+    const int n_pairs = src.N * H;
     const int groups = (n_pairs + 7) / 8;
     const long long blocks = (long long)groups * 8 * (DV / 16);
     hipLaunchKernelGGL((prefill_state_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(256), 0,
-                       stream, (const unsigned char*)rec, seq_chunk_start, chunks, S0, S_final,
-                       (E*)o, H, n_pairs);
+                       stream, (const unsigned char*)rec, src, S0, S_final, (E*)o, H, n_pairs);
     return hipGetLastError();
 }
 
-hipError_t launch_prefill_state(const void* rec, const int32_t* seq_chunk_start,
-                                const ChunkInfo* chunks, const float* S0, float* S_final,
-                                void* o, void* states, int N, int H, int dk, int dv, bool bf16_io,
+hipError_t launch_prefill_state(const void* rec, ChunkSrc src, const float* S0, float* S_final,
+                                void* o, void* states, int H, int dk, int dv, bool bf16_io,
                                 hipStream_t stream)
 {
 #define KDA_RING_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
-        return launch_state_ring_t<E, DK_, DV_>(rec, seq_chunk_start, S0, S_final, states, N, H, stream);
+        return launch_state_ring_t<E, DK_, DV_>(rec, src, S0, S_final, states, H, stream);
 #define KDA_STATE_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
-        return launch_state_t<E, DK_, DV_>(rec, seq_chunk_start, chunks, S0, S_final, o, N, H, stream);
+        return launch_state_t<E, DK_, DV_>(rec, src, S0, S_final, o, H, stream);
     if (uses_output_pass(bf16_io, dk)) {
         if (bf16_io) {
             KDA_RING_CASE(bf16, 128, 128)
