@@ -254,6 +254,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         const int row = 16 * R + r;
         rowoff[r] = ((size_t)ci.start + (row < ci.len ? row : ci.len - 1)) * H + h;
     }
+    // beta first: it is needed before the first barrier, and a wave's loads
+    // complete in order, so a late beta load would make that barrier wait for
+    // every input row (every wave loads it; wave 0 keeps it)
+    const float bt = beta[((size_t)ci.start + (lane < ci.len ? lane : ci.len - 1)) * H + h];
 #pragma unroll
     for (int r = 0; r < 16; ++r) load_row<CPT>(log_alpha + rowoff[r] * DK + c0, la[r]);
 #pragma unroll
@@ -262,8 +266,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int r = 0; r < 16; ++r) load_row<CPT>(q + rowoff[r] * DK + c0, qr[r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) load_row<CPTV>(v + rowoff[r] * DV + cv0, vr[r]);
-    float bt = 0.f;
-    if (wave == 0) bt = beta[((size_t)ci.start + (lane < ci.len ? lane : ci.len - 1)) * H + h];
     // cumulative log-decay inside each 16-token block; padded rows add nothing
     // (with beta = 0 there, their k, q, v never reach a stored result).
     float ell[16][CPT];
