@@ -146,11 +146,13 @@ def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def make_prefill(seed: int, lengths: Sequence[int], H: int, dk: int, dv: int,
                  dtype: str = "bf16", mu: float = 3.0, state_std: float = 0.0,
-                 packed: Optional[bool] = None) -> KDAInputs:
+                 packed: Optional[bool] = None, raw: bool = False) -> KDAInputs:
     """Inputs for one prefill call over sequences of the given lengths.
 
     ``packed`` (default: more than one distinct length) selects cu_seqlens;
-    otherwise the batch is N equal rows and cu_seqlens is None.
+    otherwise the batch is N equal rows and cu_seqlens is None.  ``raw`` draws
+    the layer's inputs before its own preprocessing: q and k rows N(0, 1) with
+    a per-row scale 2^U(-3, 3) (not normalised) and beta as a N(0, 1) logit.
     """
     lengths = [int(x) for x in lengths]
     N = len(lengths)
@@ -159,11 +161,17 @@ def make_prefill(seed: int, lengths: Sequence[int], H: int, dk: int, dv: int,
         packed = len(set(lengths)) > 1
     if not packed and len(set(lengths)) > 1:
         raise ValueError("unequal lengths need a packed batch")
-    q = _unit_rows(_normal(rng(seed, Q), (T, H, dk)))
-    k = _unit_rows(_normal(rng(seed, K), (T, H, dk)))
+    if raw:
+        g = rng(seed, Q, 1)
+        q = _normal(rng(seed, Q), (T, H, dk)) * np.exp2(g.uniform(-3, 3, (T, H, 1))).astype(np.float32)
+        k = _normal(rng(seed, K), (T, H, dk)) * np.exp2(g.uniform(-3, 3, (T, H, 1))).astype(np.float32)
+        beta = _normal(rng(seed, BETA), (T, H))
+    else:
+        q = _unit_rows(_normal(rng(seed, Q), (T, H, dk)))
+        k = _unit_rows(_normal(rng(seed, K), (T, H, dk)))
+        beta = _sigmoid(_normal(rng(seed, BETA), (T, H)))
     v = _normal(rng(seed, V), (T, H, dv))
     la = _log_sigmoid(_normal(rng(seed, LOG_ALPHA), (T, H, dk), loc=mu))
-    beta = _sigmoid(_normal(rng(seed, BETA), (T, H)))
     s0 = None
     if state_std:
         s0 = (np.float32(state_std) * _normal(rng(seed, STATE), (N, H, dk, dv))).astype(np.float32)

@@ -52,6 +52,9 @@ class Oracle:
         lib.oracle_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
                                        i32, vp, vp, i32]
         lib.oracle_prefill.restype = ctypes.c_int
+        lib.oracle_prefill_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
+                                          i32, i32, i32, vp, vp, vp, i32]
+        lib.oracle_prefill_ex.restype = ctypes.c_int
         lib.oracle_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                            vp, i32]
         lib.oracle_decode_step.restype = ctypes.c_int
@@ -65,6 +68,9 @@ class Oracle:
 
     def decode_step(self, *args, **kwargs):
         return _decode_step(self.lib, *args, **kwargs)
+
+    def decode_tokens(self, *args, **kwargs):
+        return _decode_tokens(self.lib, *args, **kwargs)
 
 
 _default: Optional[Oracle] = None
@@ -127,17 +133,31 @@ def decode_step(*args, **kwargs) -> np.ndarray:
     return _decode_step(_load(), *args, **kwargs)
 
 
+def decode_tokens(*args, **kwargs) -> np.ndarray:
+    """Recurrent tokens of a packed batch on pooled states (see ``_decode_tokens``)."""
+    return _decode_tokens(_load(), *args, **kwargs)
+
+
+# option bits of oracle_prefill_ex
+L2NORM_QK, BETA_LOGIT = 1, 2
+
+
 def _prefill(lib, q: np.ndarray, k: np.ndarray, v: np.ndarray, log_alpha: np.ndarray,
              beta: np.ndarray, initial_state: Optional[np.ndarray] = None,
              cu_seqlens: Optional[np.ndarray] = None, num_seqs: Optional[int] = None,
-             nthreads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+             nthreads: Optional[int] = None, l2norm_qk: bool = False,
+             beta_logit: bool = False, states_every: int = 0):
     """Token-by-token fp64 recurrence over a packed batch.
 
     q, k: [T, H, dk]; v: [T, H, dv] -- float32, or uint16 holding bf16 bits.
-    log_alpha: [T, H, dk] float32; beta: [T, H] float32.
-    initial_state: [N, H, dk, dv] float32 or None (zeros).
+    log_alpha: [T, H, dk] float32; beta: [T, H] float32 (a logit if beta_logit).
+    initial_state: [N, H, dk, dv] float32 or float64, or None (zeros).
     cu_seqlens: [N+1] int32 offsets, or None for N equal rows (num_seqs, default 1).
-    Returns (o [T, H, dv] float64, final_state [N, H, dk, dv] float64).
+    l2norm_qk: L2-normalise q and k per (token, head) first (with 1e-6 added
+    to the squared norm); beta_logit: beta = sigmoid(given value).
+    Returns (o [T, H, dv] float64, final_state [N, H, dk, dv] float64), and
+    with states_every = C > 0 also the state entering every C-th token of each
+    sequence, [sum_s ceil(len_s / C), H, dk, dv] float64, in sequence order.
     """
     dtype = _qkv_dtype(q)
     assert k.dtype == q.dtype and v.dtype == q.dtype
@@ -154,18 +174,35 @@ def _prefill(lib, q: np.ndarray, k: np.ndarray, v: np.ndarray, log_alpha: np.nda
     q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
     la = np.ascontiguousarray(log_alpha, dtype=np.float32)
     be = np.ascontiguousarray(beta, dtype=np.float32)
-    s0 = None
+    s0 = s64 = None
     if initial_state is not None:
-        s0 = np.ascontiguousarray(initial_state, dtype=np.float32)
-        assert s0.shape == (N, H, dk, dv)
+        if initial_state.dtype == np.float64:
+            s64 = np.ascontiguousarray(initial_state)
+        else:
+            s0 = np.ascontiguousarray(initial_state, dtype=np.float32)
+        assert initial_state.shape == (N, H, dk, dv)
     o = np.zeros((T, H, dv), dtype=np.float64)
     fin = np.zeros((N, H, dk, dv), dtype=np.float64)
-    rc = lib.oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(s0),
-                            _ptr(cu), T, N, H, dk, dv, dtype, _ptr(o), _ptr(fin),
-                            int(nthreads or default_threads()))
+    flags = (L2NORM_QK if l2norm_qk else 0) | (BETA_LOGIT if beta_logit else 0)
+    if flags == 0 and states_every == 0 and s64 is None:
+        rc = lib.oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(s0),
+                                _ptr(cu), T, N, H, dk, dv, dtype, _ptr(o), _ptr(fin),
+                                int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle_prefill rejected its arguments")
+        return o, fin
+    snaps = None
+    if states_every > 0:
+        lens = np.diff(cu) if cu is not None else np.full(N, T // N)
+        n_snap = int(sum((int(n) + states_every - 1) // states_every for n in lens))
+        snaps = np.zeros((n_snap, H, dk, dv), dtype=np.float64)
+    rc = lib.oracle_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(s0),
+                               _ptr(s64), _ptr(cu), T, N, H, dk, dv, dtype, flags,
+                               int(states_every), _ptr(snaps), _ptr(o), _ptr(fin),
+                               int(nthreads or default_threads()))
     if rc != 0:
-        raise ValueError("oracle_prefill rejected its arguments")
-    return o, fin
+        raise ValueError("oracle_prefill_ex rejected its arguments")
+    return (o, fin) if snaps is None else (o, fin, snaps)
 
 
 def _decode_step(lib, state: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
@@ -187,4 +224,37 @@ def _decode_step(lib, state: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.nda
                                 int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError("oracle_decode_step rejected its arguments")
+    return o
+
+
+def _decode_tokens(lib, pool: np.ndarray, slots: Optional[np.ndarray], q: np.ndarray,
+                   k: np.ndarray, v: np.ndarray, log_alpha: np.ndarray, beta: np.ndarray,
+                   cu_seqlens: Optional[np.ndarray] = None, num_seqs: Optional[int] = None,
+                   nthreads: Optional[int] = None, l2norm_qk: bool = False,
+                   beta_logit: bool = False) -> np.ndarray:
+    """Recurrent tokens of a packed batch, each sequence starting from and
+    returning to its slot of a state pool (float64 [P, H, dk, dv], updated in
+    place).  slots: [N] int32 slot per sequence (None = slot s for sequence s);
+    a slot outside [0, P) marks a padding sequence: its output rows are zero
+    and no state is read or written.  Returns o [T, H, dv] float64."""
+    assert pool.dtype == np.float64 and pool.flags.c_contiguous
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        N = cu.shape[0] - 1
+    else:
+        N = int(num_seqs or 1)
+        cu = np.arange(N + 1, dtype=np.int32) * (T // N)
+    sl = np.arange(N, dtype=np.int64) if slots is None else np.asarray(slots, dtype=np.int64)
+    assert sl.shape == (N,)
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    for s in range(N):
+        if not 0 <= sl[s] < pool.shape[0]:
+            continue
+        a, b = int(cu[s]), int(cu[s + 1])
+        os_, fs = _prefill(lib, q[a:b], k[a:b], v[a:b], log_alpha[a:b], beta[a:b],
+                           pool[sl[s]][None].copy(), None, 1, nthreads, l2norm_qk, beta_logit)
+        o[a:b] = os_
+        pool[sl[s]] = fs[0]
     return o

@@ -95,28 +95,63 @@ static int set_threads(int nthreads)
 /* Number of OpenMP threads a parallel region will use (for reporting). */
 int oracle_max_threads(int nthreads) { return set_threads(nthreads); }
 
+/* Optional preprocessing of the inputs (the options a caller may ask the
+ * library to apply in-kernel; Kimi Linear paper notes, section 3 on the FLA
+ * implementation: q/k L2 normalisation and the beta sigmoid):
+ *   ORACLE_L2NORM_QK   q_t <- q_t / sqrt(q_t . q_t + 1e-6), the same for k_t
+ *                      (per token and head, over the dk key channels)
+ *   ORACLE_BETA_LOGIT  beta is given as a logit x: beta = 1 / (1 + exp(-x)) */
+enum { ORACLE_L2NORM_QK = 1, ORACLE_BETA_LOGIT = 2 };
+
+static void l2_normalise(double *x, int d)
+{
+    double ss = 0.0;
+    for (int c = 0; c < d; ++c)
+        ss += x[c] * x[c];
+    double inv = 1.0 / sqrt(ss + 1e-6);
+    for (int c = 0; c < d; ++c)
+        x[c] *= inv;
+}
+
 /*
- * Prefill over a packed batch.
+ * Prefill over a packed batch, with options.
  *   q,k: [T,H,dk]   v: [T,H,dv]    (dtype: 0 = fp32, 1 = bf16 bit patterns)
- *   log_alpha: [T,H,dk] fp32       beta: [T,H] fp32
- *   initial_state: [N,H,dk,dv] fp32, or NULL = zeros
+ *   log_alpha: [T,H,dk] fp32       beta: [T,H] fp32 (a logit with ORACLE_BETA_LOGIT)
+ *   initial state: s0_f32 or s0_f64 [N,H,dk,dv] (at most one), or both NULL = zeros
  *   cu_seqlens: host [N+1] int32 offsets, or NULL = N equal rows of T/N
+ *   flags: ORACLE_* bits above
+ *   every, states: if every > 0 and states != NULL, the state entering token
+ *      t0 + every*c of each sequence (c = 0 .. ceil(len/every) - 1, i.e. after
+ *      every*c of its tokens) is written to states[(base_s + c)*H + h] with
+ *      base_s = sum over earlier sequences of ceil(len/every): [NS,H,dk,dv] fp64
  *   o: [T,H,dv] fp64 out            final_state: [N,H,dk,dv] fp64 out or NULL
  * Returns 0, or -1 on bad arguments.
  */
-int oracle_prefill(const void *q, const void *k, const void *v,
-                   const float *log_alpha, const float *beta,
-                   const float *initial_state, const int32_t *cu_seqlens,
-                   int64_t total_tokens, int32_t num_seqs, int32_t H,
-                   int32_t dk, int32_t dv, int32_t dtype,
-                   double *o, double *final_state, int32_t nthreads)
+int oracle_prefill_ex(const void *q, const void *k, const void *v,
+                      const float *log_alpha, const float *beta,
+                      const float *s0_f32, const double *s0_f64, const int32_t *cu_seqlens,
+                      int64_t total_tokens, int32_t num_seqs, int32_t H,
+                      int32_t dk, int32_t dv, int32_t dtype, int32_t flags,
+                      int32_t every, double *states,
+                      double *o, double *final_state, int32_t nthreads)
 {
-    if (num_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0 || total_tokens < 0)
+    if (num_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0 || total_tokens < 0 || every < 0)
         return -1;
     if (!cu_seqlens && total_tokens % num_seqs != 0)
         return -1;
+    if (s0_f32 && s0_f64)
+        return -1;
     set_threads(nthreads);
     const int64_t units = (int64_t)num_seqs * H;
+    /* first snapshot row of every sequence */
+    int64_t *snap_base = (int64_t *)calloc((size_t)num_seqs + 1, sizeof(int64_t));
+    if (!snap_base)
+        return -1;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        int64_t len = cu_seqlens ? (int64_t)cu_seqlens[s + 1] - cu_seqlens[s]
+                                 : total_tokens / num_seqs;
+        snap_base[s + 1] = snap_base[s] + (every > 0 && len > 0 ? (len + every - 1) / every : 0);
+    }
     int bad = 0;
 
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
@@ -144,12 +179,17 @@ int oracle_prefill(const void *q, const void *k, const void *v,
             continue;
         }
         double *kv = qv + dk, *lv = kv + dk, *vv = lv + dk, *ov = vv + dv, *y = ov + dv;
-        if (initial_state) {
-            const float *S0 = initial_state + ((int64_t)s * H + h) * dk * dv;
+        if (s0_f32) {
+            const float *S0 = s0_f32 + ((int64_t)s * H + h) * dk * dv;
             for (int64_t i = 0; i < (int64_t)dk * dv; ++i)
                 S[i] = (double)S0[i];
+        } else if (s0_f64) {
+            memcpy(S, s0_f64 + ((int64_t)s * H + h) * dk * dv, sizeof(double) * (size_t)dk * dv);
         }
         for (int64_t t = t0; t < t1; ++t) {
+            if (every > 0 && states && (t - t0) % every == 0)
+                memcpy(states + ((snap_base[s] + (t - t0) / every) * H + h) * dk * dv, S,
+                       sizeof(double) * (size_t)dk * dv);
             const int64_t rk = (t * H + h) * dk, rv = (t * H + h) * dv;
             for (int c = 0; c < dk; ++c) {
                 qv[c] = widen(q, rk + c, dtype);
@@ -158,7 +198,14 @@ int oracle_prefill(const void *q, const void *k, const void *v,
             }
             for (int j = 0; j < dv; ++j)
                 vv[j] = widen(v, rv + j, dtype);
-            kda_step(S, dk, dv, qv, kv, vv, lv, (double)beta[t * H + h], ov, y);
+            if (flags & ORACLE_L2NORM_QK) {
+                l2_normalise(qv, dk);
+                l2_normalise(kv, dk);
+            }
+            double b = (double)beta[t * H + h];
+            if (flags & ORACLE_BETA_LOGIT)
+                b = 1.0 / (1.0 + exp(-b));
+            kda_step(S, dk, dv, qv, kv, vv, lv, b, ov, y);
             memcpy(o + rv, ov, sizeof(double) * (size_t)dv);
         }
         if (final_state)
@@ -167,7 +214,21 @@ int oracle_prefill(const void *q, const void *k, const void *v,
         free(S);
         free(qv);
     }
+    free(snap_base);
     return bad ? -1 : 0;
+}
+
+/* Prefill without options (fp32 initial state, no snapshots). */
+int oracle_prefill(const void *q, const void *k, const void *v,
+                   const float *log_alpha, const float *beta,
+                   const float *initial_state, const int32_t *cu_seqlens,
+                   int64_t total_tokens, int32_t num_seqs, int32_t H,
+                   int32_t dk, int32_t dv, int32_t dtype,
+                   double *o, double *final_state, int32_t nthreads)
+{
+    return oracle_prefill_ex(q, k, v, log_alpha, beta, initial_state, NULL, cu_seqlens,
+                             total_tokens, num_seqs, H, dk, dv, dtype, 0, 0, NULL,
+                             o, final_state, nthreads);
 }
 
 /*

@@ -38,10 +38,10 @@ def rel_err(x, ref) -> float:
     return float(num / den) if den > 0 else float(num)
 
 
-def _case(seed, T, H, dk, dv, dtype="f32", mu=1.0, state_std=0.3, lengths=None):
+def _case(seed, T, H, dk, dv, dtype="f32", mu=1.0, state_std=0.3, lengths=None, raw=False):
     lengths = lengths or [T]
     return gen.make_prefill(seed, lengths, H=H, dk=dk, dv=dv, dtype=dtype, mu=mu,
-                            state_std=state_std, packed=len(lengths) > 1 or None)
+                            state_std=state_std, packed=len(lengths) > 1 or None, raw=raw)
 
 
 def _f64(x):
@@ -330,8 +330,106 @@ def pin_non_expansive(orc):
         assert np.all(after <= bound * (1 + 1e-6))
 
 
+# --------------------------------------------------------------------------
+# options: state snapshots, in-call q/k normalisation and beta logits, pools
+# --------------------------------------------------------------------------
+def pin_state_snapshots(orc):
+    """The state entering every C-th token of a sequence is the final state of
+    the same sequence cut after that many tokens (the initial state at 0);
+    rows follow the sequences in order, ceil(len / C) per sequence."""
+    x = _case(27, 0, 2, 5, 4, lengths=[13, 0, 8, 1, 17])
+    C = 4
+    _, _, snaps = orc.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.initial_state,
+                              x.cu_seqlens, states_every=C)
+    row = 0
+    for s, n in enumerate(x.lengths()):
+        y = x.select_seqs([s])
+        for c in range((n + C - 1) // C):
+            if c == 0:
+                expect = y.initial_state[0].astype(np.float64)
+            else:
+                _, f = orc.prefill(y.q[:C * c], y.k[:C * c], y.v[:C * c], y.log_alpha[:C * c],
+                                   y.beta[:C * c], y.initial_state)
+                expect = f[0]
+            assert np.array_equal(snaps[row], expect), (s, c)
+            row += 1
+    assert row == snaps.shape[0]
+
+
+def pin_qk_l2_normalisation(orc):
+    """In-call L2 normalisation of q and k (per token and head, over dk):
+    power-of-two rescaling of any row changes nothing but the regulariser's
+    share; rows that are unit vectors already give the plain result; and with
+    beta = 1 and q_t parallel to k_t the read-out recalls v_t exactly."""
+    x = _case(28, 24, 2, 8, 5, raw=True)
+    be = gen.as_f32(x.beta)
+    q, k = x.q * np.float32(8), x.k * np.float32(8)        # exact; rows have |x|^2 >= 1e-2
+    o1, f1 = orc.prefill(q, k, x.v, x.log_alpha, be, x.initial_state, l2norm_qk=True)
+    g = np.random.default_rng(28)
+    sq = np.exp2(g.integers(0, 7, (x.T, x.H, 1))).astype(np.float32)
+    sk = np.exp2(g.integers(0, 7, (x.T, x.H, 1))).astype(np.float32)
+    o2, f2 = orc.prefill(q * sq, k * sk, x.v, x.log_alpha, be, x.initial_state,
+                         l2norm_qk=True)
+    # the regulariser moves a row by at most 1e-6 / (2 |x|^2) relative
+    bound = 1e-6 / min(np.einsum("thc,thc->th", q, q).min(), np.einsum("thc,thc->th", k, k).min())
+    assert rel_err(o2, o1) < 4 * bound and rel_err(f2, f1) < 4 * bound, bound
+    # unit rows: only the 1e-6 regulariser separates the two calls
+    u = _case(29, 24, 2, 8, 5)
+    o3, f3 = orc.prefill(u.q, u.k, u.v, u.log_alpha, u.beta, u.initial_state, l2norm_qk=True)
+    o4, f4 = orc.prefill(u.q, u.k, u.v, u.log_alpha, u.beta, u.initial_state)
+    assert rel_err(o3, o4) < 2e-6 and rel_err(f3, f4) < 2e-6
+    # recall: |k|^2 ~ 1e4, so the normalised key has |k|^2 = 1 - 1e-10
+    k = (x.k * np.float32(30.0)).astype(np.float32)
+    o5, _ = orc.prefill((k * np.float32(0.5)).astype(np.float32), k, x.v, x.log_alpha,
+                        np.ones_like(be), x.initial_state, l2norm_qk=True)
+    assert rel_err(o5, _f64(x.v)) < 1e-8
+
+
+def pin_beta_logit(orc):
+    """beta given as a logit x: beta = sigmoid(x), so x = ln(p / (1 - p)) gives
+    the plain call with beta = p."""
+    x = _case(30, 20, 2, 6, 4)
+    g = np.random.default_rng(30)
+    p = g.choice([0.2, 0.25, 0.5, 0.75, 0.8], size=x.beta.shape)
+    logit = np.log(p / (1.0 - p)).astype(np.float32)
+    o1, f1 = orc.prefill(x.q, x.k, x.v, x.log_alpha, logit, x.initial_state, beta_logit=True)
+    o2, f2 = orc.prefill(x.q, x.k, x.v, x.log_alpha, p.astype(np.float32), x.initial_state)
+    # the logit is rounded to fp32: beta moves by ~1e-8
+    assert rel_err(o1, o2) < 1e-6 and rel_err(f1, f2) < 1e-6
+
+
+def pin_pooled_tokens(orc):
+    """Recurrent tokens on a state pool: each sequence starts from its slot's
+    state and leaves its final state there; a slot outside the pool marks a
+    padding sequence (zero output, pool untouched).  Checked against
+    token-by-token decode steps on copies of the slots."""
+    x = _case(31, 0, 2, 5, 4, lengths=[4, 3, 0, 2, 5])
+    P = 6
+    g = np.random.default_rng(31)
+    pool = 0.3 * g.standard_normal((P, x.H, x.dk, x.dv))
+    slots = np.array([3, -1, 0, 7, 2], dtype=np.int32)
+    got = pool.copy()
+    o = orc.decode_tokens(got, slots, x.q, x.k, x.v, x.log_alpha, x.beta, x.cu_seqlens)
+    ref = pool.copy()
+    cu = x.cu_seqlens
+    for s in range(x.num_seqs):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if not 0 <= slots[s] < P:
+            assert not np.any(o[a:b])
+            continue
+        S = ref[slots[s]][None].copy()
+        for t in range(a, b):
+            ot = orc.decode_step(S, x.q[t][None], x.k[t][None], x.v[t][None],
+                                 x.log_alpha[t][None], x.beta[t][None])
+            assert rel_err(ot[0], o[t]) < 1e-13, (s, t)
+        ref[slots[s]] = S[0]
+    assert rel_err(got, ref) < 1e-13
+    assert np.array_equal(got[[1, 4, 5]], pool[[1, 4, 5]])   # slots no sequence names
+
+
 ALL_PINS = [pin_transition_product, pin_exact_rational, pin_identity_no_write, pin_pure_decay,
             pin_deltanet, pin_gated_deltanet, pin_exact_recall, pin_one_hot_linear_attention,
             pin_one_hot_rows, pin_single_token, pin_chunkwise_algebra, pin_chunk_transition_form,
             pin_packing,
-            pin_decode_matches_prefill, pin_linearity, pin_non_expansive]
+            pin_decode_matches_prefill, pin_linearity, pin_non_expansive,
+            pin_state_snapshots, pin_qk_l2_normalisation, pin_beta_logit, pin_pooled_tokens]

@@ -25,6 +25,12 @@ MUTANTS = [
     ("packed offset", "t0 = cu_seqlens[s];", "t0 = cu_seqlens[s] + (s > 0 && cu_seqlens[s] < cu_seqlens[s + 1]);"),
     ("scalar decay", "lv[c] = (double)log_alpha[rk + c];", "lv[c] = (double)log_alpha[rk];"),
     ("decode beta", "(double)beta[u]", "(double)beta[0]"),
+    ("q not normalised", "l2_normalise(qv, dk);", ";"),
+    ("k not normalised", "l2_normalise(kv, dk);", ";"),
+    ("norm over half the channels", "l2_normalise(kv, dk);", "l2_normalise(kv, dk / 2);"),
+    ("sigmoid sign", "b = 1.0 / (1.0 + exp(-b));", "b = 1.0 / (1.0 + exp(b));"),
+    ("snapshot one token late", "(t - t0) % every == 0", "(t - t0) % every == 1 % every"),
+    ("snapshot rows", "snap_base[s + 1] = snap_base[s] +", "snap_base[s + 1] = snap_base[s] * 0 +"),
 ]
 
 
