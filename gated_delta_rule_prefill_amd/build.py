@@ -18,7 +18,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 ARCH = "gfx950"
 KERNEL_SOURCES = ["chunk_table.hip", "prefill_intra.hip", "prefill_state.hip", "prefill_output.hip",
-                  "decode.hip"]
+                  "decode.hip", "recurrent.hip"]
 HOST_SOURCES = ["kda_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", CSRC, "-I", INCLUDE]

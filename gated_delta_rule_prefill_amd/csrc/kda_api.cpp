@@ -59,6 +59,13 @@ bool make_plan(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtyp
 
 bool supported_dim(int32_t d) { return d == 64 || d == 128; }
 
+constexpr uint32_t kFlagMask = KDA_FLAG_L2NORM_QK | KDA_FLAG_BETA_SIGMOID;
+
+unsigned pre_flags(uint32_t flags) {
+    return ((flags & KDA_FLAG_L2NORM_QK) ? kda::PRE_L2NORM_QK : 0u) |
+           ((flags & KDA_FLAG_BETA_SIGMOID) ? kda::PRE_BETA_LOGIT : 0u);
+}
+
 // -- optional kernel timing ---------------------------------------------------
 constexpr int kMaxTimed = 8;
 std::mutex g_timing_mu;
@@ -127,9 +134,21 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
                        int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk, int32_t dv,
                        kda_dtype dtype, void* o, float* final_state, void* workspace,
                        size_t workspace_bytes, void* stream_ptr) {
+    return kda_prefill_ex(q, k, v, log_alpha, beta, initial_state, cu_seqlens, total_tokens,
+                          num_seqs, H, dk, dv, dtype, 0u, o, final_state, nullptr, workspace,
+                          workspace_bytes, stream_ptr);
+}
+
+kda_status kda_prefill_ex(const void* q, const void* k, const void* v, const float* log_alpha,
+                          const float* beta, const float* initial_state,
+                          const int32_t* cu_seqlens, int64_t total_tokens, int32_t num_seqs,
+                          int32_t H, int32_t dk, int32_t dv, kda_dtype dtype, uint32_t flags,
+                          void* o, float* final_state, float* chunk_states, void* workspace,
+                          size_t workspace_bytes, void* stream_ptr) {
     try {
         if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
             return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_DTYPE_F32 or KDA_DTYPE_BF16");
+        if (flags & ~kFlagMask) return fail(KDA_ERR_INVALID_ARGUMENT, "unknown flag bits");
         if (num_seqs <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1");
         if (H <= 0 || H > 65535) return fail(KDA_ERR_INVALID_ARGUMENT, "H must be in [1, 65535]");
         if (total_tokens < 0 || total_tokens >= ((int64_t)1 << 31) - 2 * kda::CHUNK)
@@ -142,7 +161,7 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
         if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
             return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, log_alpha, beta and o must be non-NULL");
         const void* ptrs[] = {q, k, v, log_alpha, beta, initial_state, cu_seqlens, o,
-                              final_state, workspace};
+                              final_state, chunk_states, workspace};
         for (const void* p : ptrs)
             if (p && !aligned16(p))
                 return fail(KDA_ERR_INVALID_ARGUMENT, "every pointer must be 16-byte aligned");
@@ -189,14 +208,15 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
             if (st == KDA_OK && total_tokens > 0) {
                 st = check_launch(kda::launch_prefill_intra(q, k, v, log_alpha, beta, src,
                                                             (int)plan.max_chunks, H, dk, dv, bf16,
-                                                            ws, stream),
+                                                            pre_flags(flags), ws, stream),
                                   "intra-chunk kernel", stream);
                 timer.mark("prefill_intra");
             }
             void* states = plan.output_pass ? (void*)(ws + plan.off_states) : nullptr;
             if (st == KDA_OK) {
                 st = check_launch(kda::launch_prefill_state(ws, src, initial_state, final_state, o,
-                                                            states, H, dk, dv, bf16, stream),
+                                                            states, chunk_states, H, dk, dv, bf16,
+                                                            stream),
                                   "state kernel", stream);
                 timer.mark("prefill_state");
             }
@@ -215,6 +235,48 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
         return st;
     } catch (...) {
         return fail(KDA_ERR_HIP, "unexpected C++ exception inside kda_prefill");
+    }
+}
+
+kda_status kda_decode_tokens(float* state_pool, int32_t num_slots, const int32_t* state_indices,
+                             const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, const int32_t* cu_seqlens, int64_t total_tokens,
+                             int32_t num_seqs, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype,
+                             uint32_t flags, void* o, void* stream_ptr) {
+    try {
+        if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_DTYPE_F32 or KDA_DTYPE_BF16");
+        if (flags & ~kFlagMask) return fail(KDA_ERR_INVALID_ARGUMENT, "unknown flag bits");
+        if (num_seqs <= 0 || H <= 0 || num_slots <= 0)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs, H and num_slots must be >= 1");
+        if (total_tokens < 0 || total_tokens > 0x7fffffffLL)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "total_tokens must be in [0, 2^31)");
+        const long long blocks = (long long)num_seqs * H * (dv > 64 ? dv / 64 : 1);
+        if (blocks > 0x7fffffffLL || (long long)num_slots * H > 0x7fffffffLL)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs * H or num_slots * H too large");
+        if (!supported_dim(dk) || !supported_dim(dv))
+            return fail(KDA_ERR_UNSUPPORTED, "dk and dv must each be 64 or 128");
+        if (!cu_seqlens && total_tokens % num_seqs != 0)
+            return fail(KDA_ERR_INVALID_ARGUMENT,
+                        "without cu_seqlens, total_tokens must be a multiple of num_seqs");
+        if (!state_indices && num_slots < num_seqs)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "without state_indices, num_slots must be >= num_seqs");
+        if (!state_pool) return fail(KDA_ERR_INVALID_ARGUMENT, "state_pool must be non-NULL");
+        if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, log_alpha, beta and o must be non-NULL");
+        const void* ptrs[] = {state_pool, state_indices, q, k, v, log_alpha, beta, cu_seqlens, o};
+        for (const void* p : ptrs)
+            if (p && !aligned16(p))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "every pointer must be 16-byte aligned");
+        hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+        const int rows = cu_seqlens ? -1 : (int)(total_tokens / num_seqs);
+        return check_launch(kda::launch_recurrent(state_pool, num_slots, state_indices, q, k, v,
+                                                  log_alpha, beta, cu_seqlens, rows, num_seqs, H,
+                                                  dk, dv, dtype == KDA_DTYPE_BF16,
+                                                  pre_flags(flags), o, stream),
+                            "recurrent kernel", stream);
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected C++ exception inside kda_decode_tokens");
     }
 }
 

@@ -90,6 +90,57 @@ __device__ __forceinline__ void store_vec<f32x8, float>(float* p, f32x8 v) {
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
+// -- options of the layer's own input preprocessing ----------------------------
+// In-call L2 normalisation of q and k (per token and head over the key
+// channels, 1e-6 added to the squared norm) and beta given as a logit.
+constexpr float L2NORM_EPS = 1e-6f;
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// Wave-wide sums of 16 values per lane at once (a transposing butterfly: 15
+// lane exchanges instead of 16 x 6).  Lane l receives the total of
+// a[row_of_lane(l)] over all 64 lanes, row_of_lane(l) = 8 b5 + 4 b4 + 2 b3 + b2
+// with b_i bit i of l; row_lane(r) is a lane that holds row r's total.
+__host__ __device__ constexpr int row_lane(int r) {
+    return (((r >> 3) & 1) << 5) | (((r >> 2) & 1) << 4) | (((r >> 1) & 1) << 3) | ((r & 1) << 2);
+}
+__device__ __forceinline__ float wave_sum16(const float (&a)[16], int lane) {
+    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8, h2 = lane & 4;
+    float b[8], c[4], d[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[j] = (h5 ? a[8 + j] : a[j]) + __shfl_xor(h5 ? a[j] : a[8 + j], 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = (h4 ? b[4 + j] : b[j]) + __shfl_xor(h4 ? b[j] : b[4 + j], 16);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) d[j] = (h3 ? c[2 + j] : c[j]) + __shfl_xor(h3 ? c[j] : c[2 + j], 8);
+    float e = (h2 ? d[1] : d[0]) + __shfl_xor(h2 ? d[0] : d[1], 4);
+    e += __shfl_xor(e, 2);
+    e += __shfl_xor(e, 1);
+    return e;
+}
+__device__ __forceinline__ float read_lane(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// L2-normalise 16 rows held by a wave, CPT channels per lane (the lanes
+// together hold every channel of each row).
+template <int CPT>
+__device__ __forceinline__ void l2_normalise_rows(float (&x)[16][CPT], int lane) {
+    float a[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        a[r] = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) a[r] += x[r][e] * x[r][e];
+    }
+    const float inv = rsqrtf(wave_sum16(a, lane) + L2NORM_EPS);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const float sr = read_lane(inv, row_lane(r));
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) x[r][e] *= sr;
+    }
+}
+
 // Chunks of a batch (see ChunkSrc): from the table, or arithmetically for N
 // equal sequences of src.rows tokens.
 __device__ __forceinline__ int chunks_per_row(int rows) { return (rows + CHUNK - 1) / CHUNK; }

@@ -51,20 +51,26 @@ constexpr RecLayout rec_layout(int es, int dk, int dv) {
                       (size_t)CHUNK * dv * es + (size_t)dk * 4 + 255) & ~(size_t)255};
 }
 
+// Input preprocessing options (bits): L2-normalise q and k per (token, head);
+// beta arrives as a logit and goes through a sigmoid.
+constexpr unsigned PRE_L2NORM_QK = 1u, PRE_BETA_LOGIT = 2u;
+
 hipError_t launch_chunk_table(const int32_t* cu, int64_t T, int N, int32_t* seq_chunk_start,
                               ChunkInfo* chunks, int max_chunks, hipStream_t stream);
 
 // rec: [max_chunks * H] records of rec_layout() bytes
 hipError_t launch_prefill_intra(const void* q, const void* k, const void* v, const float* la,
                                 const float* beta, ChunkSrc src, int max_chunks, int H, int dk,
-                                int dv, bool bf16_io, void* rec, hipStream_t stream);
+                                int dv, bool bf16_io, unsigned flags, void* rec,
+                                hipStream_t stream);
 
 // Sequential inter-chunk pass.  With the output pass (uses_output_pass) it
 // stores every chunk-start state into `states` and leaves o to
 // launch_prefill_output; otherwise it writes o itself and ignores `states`.
+// chunk_states (or NULL): every chunk-start state in fp32, [chunk][H][dk][dv].
 hipError_t launch_prefill_state(const void* rec, ChunkSrc src, const float* S0, float* S_final,
-                                void* o, void* states, int H, int dk, int dv, bool bf16_io,
-                                hipStream_t stream);
+                                void* o, void* states, float* chunk_states, int H, int dk, int dv,
+                                bool bf16_io, hipStream_t stream);
 
 // Whether a configuration runs the chain-only sequential kernel followed by the
 // parallel output pass (its LDS ring fits), or the fused register-staged one.
@@ -78,6 +84,12 @@ constexpr size_t chunk_state_bytes(int es, int dk, int dv) { return (size_t)dk *
 hipError_t launch_prefill_output(const void* rec, const void* states, ChunkSrc src,
                                  int max_chunks, int H, int dk, int dv, bool bf16_io, void* o,
                                  hipStream_t stream);
+
+// Recurrent tokens of a packed batch on pooled states (see kda_decode_tokens).
+hipError_t launch_recurrent(float* pool, int num_slots, const int32_t* slots, const void* q,
+                            const void* k, const void* v, const float* la, const float* beta,
+                            const int32_t* cu, int rows, int N, int H, int dk, int dv,
+                            bool bf16_io, unsigned flags, void* o, hipStream_t stream);
 
 hipError_t launch_decode_step(float* state, const void* q, const void* k, const void* v,
                               const float* la, const float* beta, void* o, int units, int dk,

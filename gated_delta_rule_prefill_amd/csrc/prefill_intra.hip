@@ -196,11 +196,12 @@ __device__ __forceinline__ void x_block(float* sAL, int R, int I, int g, int ln)
     for (int i = 0; i < 4; ++i) sAL[(16 * I + ln) * LA + 16 * R + 4 * g + i] = x[i];
 }
 
-template <typename E, int DK, int DV>
+// NORM: L2-normalise q and k rows first; beta_logit: beta arrives as a logit.
+template <typename E, int DK, int DV, bool NORM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_intra_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    const ChunkSrc src, int H,
+    const ChunkSrc src, int H, int beta_logit,
     unsigned char* __restrict__ rec)
 {
     using L = IntraLayout<E, DK, DV>;
@@ -284,11 +285,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
 #pragma unroll
         for (int e = 0; e < CPT; ++e) sTau[R * DK + c0 + e] = run[e];
-        if (wave == 0) sBeta[lane] = lane < ci.len ? bt : 0.f;
+        if (wave == 0) sBeta[lane] = lane < ci.len ? (beta_logit ? sigmoid(bt) : bt) : 0.f;
     }
     __syncthreads();
 
     // ---- phase 0b: block references, decay table, decayed keys ---------------
+    if constexpr (NORM) l2_normalise_rows<CPT>(kr, lane);
     float eB[CPT], eTE[CPT];   // e^{B_R} (g before block R);  e^{g_C - B_R}
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
@@ -325,6 +327,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         store_row<CPT>(sKP + row * L::LK + c0, kp);
         store_row<CPT>(sKD + row * L::LK + c0, kd);
     }
+    if constexpr (NORM) l2_normalise_rows<CPT>(qr, lane);
 #pragma unroll
     for (int r = 0; r < 16; ++r)
 #pragma unroll
@@ -702,22 +705,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
 template <typename E, int DK, int DV>
 static hipError_t launch_intra_t(const void* q, const void* k, const void* v, const float* la,
-                                 const float* beta, ChunkSrc src, int max_chunks, int H, void* rec,
-                                 hipStream_t stream)
+                                 const float* beta, ChunkSrc src, int max_chunks, int H,
+                                 unsigned flags, void* rec, hipStream_t stream)
 {
-    hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV>), dim3(max_chunks, H), dim3(256), 0, stream,
-                       (const E*)q, (const E*)k, (const E*)v, la, beta, src, H,
-                       (unsigned char*)rec);
+    const int beta_logit = (flags & PRE_BETA_LOGIT) ? 1 : 0;
+    if (flags & PRE_L2NORM_QK)
+        hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, true>), dim3(max_chunks, H), dim3(256), 0,
+                           stream, (const E*)q, (const E*)k, (const E*)v, la, beta, src, H,
+                           beta_logit, (unsigned char*)rec);
+    else
+        hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, false>), dim3(max_chunks, H), dim3(256), 0,
+                           stream, (const E*)q, (const E*)k, (const E*)v, la, beta, src, H,
+                           beta_logit, (unsigned char*)rec);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_intra(const void* q, const void* k, const void* v, const float* la,
                                 const float* beta, ChunkSrc src, int max_chunks, int H, int dk,
-                                int dv, bool bf16_io, void* rec, hipStream_t stream)
+                                int dv, bool bf16_io, unsigned flags, void* rec, hipStream_t stream)
 {
 #define KDA_INTRA_CASE(E, DK_, DV_)                                                               \
     if (dk == DK_ && dv == DV_)                                                                  \
-        return launch_intra_t<E, DK_, DV_>(q, k, v, la, beta, src, max_chunks, H, rec, stream);
+        return launch_intra_t<E, DK_, DV_>(q, k, v, la, beta, src, max_chunks, H, flags, rec, stream);
     if (bf16_io) {
         KDA_INTRA_CASE(bf16, 128, 128)
         KDA_INTRA_CASE(bf16, 64, 64)

@@ -103,7 +103,8 @@ __device__ __forceinline__ void load_output(OutputOps<E, DK>& op, const unsigned
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_state_kernel(
     const unsigned char* __restrict__ rec, const ChunkSrc src, const float* __restrict__ S0,
-    float* __restrict__ S_final, E* __restrict__ o, int H, int n_pairs)
+    float* __restrict__ S_final, E* __restrict__ o, float* __restrict__ chunk_states, int H,
+    int n_pairs)
 {
     using C = StateCfg<E, DK, DV>;
     using V4 = typename Vec<E>::v4;
@@ -161,6 +162,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             __builtin_amdgcn_sched_barrier(0);
             // the next chunk's loads are unconditional (the last chunk reloads itself)
             load_serial<E, DK, DV>(nxt, record(min(it + 1, n - 1)), g, ln, j0);
+            if (chunk_states) {   // the chunk-start state, fp32 [chunk][H][DK][DV]
+                float* cs = chunk_states + ((size_t)(c_begin + it) * H + h) * DK * DV + j0 + ln;
+#pragma unroll
+                for (int t = 0; t < KT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) cs[(size_t)(16 * t + 4 * g + i) * DV] = S[t][i];
+            }
             // chunk-start state as MFMA operand slots {32ks+4g..+3, 32ks+16+4g..+3}
             V8 Sf[KS];
             E* xs = xslot(it);
@@ -369,7 +377,8 @@ __device__ __forceinline__ void bare_barrier() {
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
     const unsigned char* __restrict__ rec, const ChunkSrc src, const float* __restrict__ S0,
-    float* __restrict__ S_final, E* __restrict__ states, int H, int n_pairs)
+    float* __restrict__ S_final, E* __restrict__ states, float* __restrict__ chunk_states, int H,
+    int n_pairs)
 {
     using C = RingCfg<E, DK, DV>;
     using V4 = typename Vec<E>::v4;
@@ -429,6 +438,14 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
             if (it < n)
                 store_vec(states + ((size_t)(c_begin + it) * H + h) * DK * DV +
                               ((size_t)(slice * KS + w) * 64 + l) * 8, f);
+            if (chunk_states && it < n) {   // fp32 [chunk][H][DK][DV]
+                float* cs = chunk_states + ((size_t)(c_begin + it) * H + h) * DK * DV + j0 + ln;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        cs[(size_t)(32 * w + 16 * h2 + 4 * g + i) * DV] = S[h2][i];
+            }
         };
         put(0);
         __syncthreads();
@@ -583,7 +600,7 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
 
 template <typename E, int DK, int DV>
 static hipError_t launch_state_ring_t(const void* rec, ChunkSrc src, const float* S0, float* S_final,
-                                      void* states, int H, hipStream_t stream)
+                                      void* states, float* chunk_states, int H, hipStream_t stream)
 {
     using C = RingCfg<E, DK, DV>;
     const int n_pairs = src.N * H;
@@ -591,32 +608,33 @@ static hipError_t launch_state_ring_t(const void* rec, ChunkSrc src, const float
     const long long blocks = (long long)groups * 8 * (DV / 16);
     hipLaunchKernelGGL((prefill_state_ring_kernel<E, DK, DV>), dim3((unsigned)blocks),
                        dim3(64 * C::WAVES), 0, stream, (const unsigned char*)rec, src, S0, S_final,
-                       (E*)states, H, n_pairs);
+                       (E*)states, chunk_states, H, n_pairs);
     return hipGetLastError();
 }
 
 template <typename E, int DK, int DV>
 static hipError_t launch_state_t(const void* rec, ChunkSrc src, const float* S0, float* S_final,
-                                 void* o, int H, hipStream_t stream)
+                                 void* o, float* chunk_states, int H, hipStream_t stream)
 {
     const int n_pairs = src.N * H;
     const int groups = (n_pairs + 7) / 8;
     const long long blocks = (long long)groups * 8 * (DV / 16);
     hipLaunchKernelGGL((prefill_state_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(256), 0,
-                       stream, (const unsigned char*)rec, src, S0, S_final, (E*)o, H, n_pairs);
+                       stream, (const unsigned char*)rec, src, S0, S_final, (E*)o, chunk_states, H,
+                       n_pairs);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_state(const void* rec, ChunkSrc src, const float* S0, float* S_final,
-                                void* o, void* states, int H, int dk, int dv, bool bf16_io,
-                                hipStream_t stream)
+                                void* o, void* states, float* chunk_states, int H, int dk, int dv,
+                                bool bf16_io, hipStream_t stream)
 {
 #define KDA_RING_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
-        return launch_state_ring_t<E, DK_, DV_>(rec, src, S0, S_final, states, H, stream);
+        return launch_state_ring_t<E, DK_, DV_>(rec, src, S0, S_final, states, chunk_states, H, stream);
 #define KDA_STATE_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
-        return launch_state_t<E, DK_, DV_>(rec, src, S0, S_final, o, H, stream);
+        return launch_state_t<E, DK_, DV_>(rec, src, S0, S_final, o, chunk_states, H, stream);
     if (uses_output_pass(bf16_io, dk)) {
         if (bf16_io) {
             KDA_RING_CASE(bf16, 128, 128)

@@ -61,6 +61,17 @@ typedef enum {
 typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
 
 /*
+ * Input preprocessing the layer may leave to the kernels (Kimi Linear paper
+ * notes, section 3 on the FLA implementation: the layer L2-normalises q and
+ * k and passes beta through a sigmoid, optionally inside the kernel).  Flags
+ * for kda_prefill_ex and kda_decode_tokens; any other bit is rejected.
+ *   KDA_FLAG_L2NORM_QK    q_t <- q_t / sqrt(q_t . q_t + 1e-6) per (token,
+ *                         head) over the dk channels, the same for k_t
+ *   KDA_FLAG_BETA_SIGMOID beta holds logits x; beta_t = 1 / (1 + exp(-x))
+ */
+enum { KDA_FLAG_L2NORM_QK = 1u, KDA_FLAG_BETA_SIGMOID = 2u };
+
+/*
  * Device workspace kda_prefill needs for these sizes (bytes, 256-aligned).
  * It holds one record per (chunk, head) built from the chunk intermediates of
  * the chunkwise form (paper notes, section 3 and its list of chunk
@@ -101,6 +112,27 @@ kda_status kda_prefill(const void *q, const void *k, const void *v,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_prefill with options.  The extra arguments:
+ *   flags         KDA_FLAG_* bits (0 = kda_prefill)
+ *   chunk_states  fp32 [NC,H,dk,dv] (device, written), or NULL: the state
+ *                 entering every 64-token chunk of every sequence, i.e. after
+ *                 64c of its tokens for c = 0 .. ceil(len/64) - 1 (c = 0 is
+ *                 the initial state).  Rows run over the sequences in order,
+ *                 ceil(len_s/64) rows for sequence s (none for an empty one):
+ *                 NC = sum_s ceil(len_s/64) <= ceil(T/64) + N.  With
+ *                 final_state, a caller can roll back to any 64-token boundary
+ *                 of a sequence and prefill again from there (paper notes,
+ *                 section 3: the chunk states h of the chunkwise form).
+ */
+kda_status kda_prefill_ex(const void *q, const void *k, const void *v,
+                          const float *log_alpha, const float *beta,
+                          const float *initial_state, const int32_t *cu_seqlens,
+                          int64_t total_tokens, int32_t num_seqs, int32_t H,
+                          int32_t dk, int32_t dv, kda_dtype dtype, uint32_t flags,
+                          void *o, float *final_state, float *chunk_states,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent token for each of N sequences (fused recurrent decode,
  * paper notes, section 3; the state is the only memory a KDA layer keeps per
  * sequence).  The state is updated in place:
@@ -114,6 +146,35 @@ kda_status kda_decode_step(float *state, const void *q, const void *k, const voi
                            const float *log_alpha, const float *beta,
                            int32_t num_seqs, int32_t H, int32_t dk, int32_t dv,
                            kda_dtype dtype, void *o, void *stream);
+
+/*
+ * The recurrent form over a few tokens per sequence, on pooled states
+ * (paper notes, section 3: FLA's fused recurrent mode, used for short inputs
+ * and decoding; one fixed-size state per sequence).  Each sequence s runs
+ * its tokens in order starting from state_pool[slot_s] and leaves its final
+ * state there; the state never leaves the registers in between.
+ *
+ *   state_pool     [num_slots,H,dk,dv] fp32 (device, read and written)
+ *   num_slots      >= 1
+ *   state_indices  [N] int32 slot per sequence (device), or NULL = slot s for
+ *                  sequence s (then num_slots >= N).  A slot outside
+ *                  [0, num_slots) marks a padding sequence: its o rows are
+ *                  zeroed and no state is read or written.  Sequences must
+ *                  name distinct slots (overlapping ones race).
+ *   q, k, v, log_alpha, beta, cu_seqlens, total_tokens, num_seqs, flags:
+ *                  as for kda_prefill_ex (tokens packed, cu_seqlens NULL = N
+ *                  equal rows)
+ *   o              [T,H,dv] dtype (device, written)
+ * Meant for short runs (speculative verification, chunked decoding): the
+ * tokens of one sequence are processed serially.  kda_decode_step is the
+ * one-token, identity-slot case without options.
+ */
+kda_status kda_decode_tokens(float *state_pool, int32_t num_slots, const int32_t *state_indices,
+                             const void *q, const void *k, const void *v,
+                             const float *log_alpha, const float *beta,
+                             const int32_t *cu_seqlens, int64_t total_tokens, int32_t num_seqs,
+                             int32_t H, int32_t dk, int32_t dv, kda_dtype dtype,
+                             uint32_t flags, void *o, void *stream);
 
 /* Static description of a status code. */
 const char *kda_status_string(kda_status status);

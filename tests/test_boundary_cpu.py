@@ -118,3 +118,52 @@ def test_product_path_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "kda_oracle" not in text and "liboracle" not in text, f
+
+
+def _prefill_ex(flags=0, cs=None, **kw):
+    args = dict(q=A, k=A, v=A, la=A, beta=A, s0=None, cu=None, T=128, N=1, H=2, dk=64, dv=64,
+                dtype=kda.KDA_DTYPE_BF16, o=A, fin=None, ws=A, wsb=1 << 40, stream=None)
+    args.update(kw)
+    return kda.lib().kda_prefill_ex(args["q"], args["k"], args["v"], args["la"], args["beta"],
+                                    args["s0"], args["cu"], args["T"], args["N"], args["H"],
+                                    args["dk"], args["dv"], args["dtype"], flags, args["o"],
+                                    args["fin"], cs, args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=4), kda.KDA_ERR_INVALID_ARGUMENT),        # unknown option bit
+    (dict(flags=1 << 31), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(cs=A + 8), kda.KDA_ERR_INVALID_ARGUMENT),       # misaligned chunk states
+    (dict(flags=3, dk=32), kda.KDA_ERR_UNSUPPORTED),
+    (dict(flags=3, wsb=100), kda.KDA_ERR_WORKSPACE),
+])
+def test_prefill_ex_rejects_before_any_hip_call(kw, status):
+    assert _prefill_ex(**kw) == status
+
+
+def _decode_tokens(**kw):
+    args = dict(pool=A, slots=A, q=A, k=A, v=A, la=A, beta=A, cu=None, T=8, N=2, H=2, dk=64,
+                dv=64, P=4, dtype=kda.KDA_DTYPE_BF16, flags=0, o=A, stream=None)
+    args.update(kw)
+    return kda.lib().kda_decode_tokens(args["pool"], args["P"], args["slots"], args["q"], args["k"],
+                                       args["v"], args["la"], args["beta"], args["cu"], args["T"],
+                                       args["N"], args["H"], args["dk"], args["dv"],
+                                       args["dtype"], args["flags"], args["o"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(N=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(T=7), kda.KDA_ERR_INVALID_ARGUMENT),           # unequal rows need cu_seqlens
+    (dict(slots=None, P=1), kda.KDA_ERR_INVALID_ARGUMENT),   # identity slots need P >= N
+    (dict(pool=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(slots=A + 4), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(flags=8), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=3), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dv=32), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_decode_tokens_rejects_before_any_hip_call(kw, status):
+    assert _decode_tokens(**kw) == status
