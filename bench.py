@@ -12,6 +12,8 @@ One JSON line on stdout:
            when the committed measurement matches the current kernel source;
   path     the whole prefill path against its HBM roofline (1540 B per token-head);
   decode   the batched decode workload (256 seqs x 32 heads, 128 steps) in GB/s;
+  options  the optional paths: chunk-state export, in-kernel preprocessing and
+           the pooled multi-token recurrent path;
   cpu_baseline  the fp64 oracle on the host cores, same inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -90,6 +92,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-options", action="store_true",
+                    help="skip the optional paths (chunk states, preprocessing, pooled tokens)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -216,6 +220,85 @@ def main():
         log(f"[bench] decode: {us:.1f} us/step, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak)")
         del state
 
+    # ---------------- optional paths ----------------
+    options = None
+    if not args.no_options:
+        options = {}
+        ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+        def timed(fn, reps):
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record()
+            for i in range(reps):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / reps
+
+        reps = max(20, min(args.steps, 100))
+        base_us = timed(step, reps)
+        # chunk-state export: fp32 state entering each of the 64 chunks, per head
+        nc = kdalib.num_chunk_states(T, 1)
+        cs = torch.empty((nc, H, dk, dv), dtype=torch.float32, device=dev)
+
+        def step_cs(i):
+            s = sets[i % args.sets]
+            kdalib.prefill(s["q"], s["k"], s["v"], s["la"], s["beta"], None, None, num_seqs=1,
+                           final_state=fin, out=out[i % args.sets], workspace=ws, chunk_states=cs)
+        cs_us = timed(step_cs, reps)
+        cs_bytes = nc * H * dk * dv * 4
+        options["chunk_states"] = {
+            "workload": "the prefill workload, also writing the fp32 state entering each of "
+                        "its 64 chunks", "us_per_step": round(cs_us, 2),
+            "extra_us": round(cs_us - base_us, 2), "extra_bytes": cs_bytes,
+            "tokens_per_s": round(T / (cs_us * 1e-6), 1)}
+        # in-kernel q/k normalisation and beta sigmoid on raw inputs
+        r = gen.make_prefill(2, [T], H=H, dk=dk, dv=dv, dtype="bf16", raw=True)
+        raw = dict(q=dq(r.q), k=dq(r.k), v=dq(r.v), la=torch.from_numpy(r.log_alpha).to(dev),
+                   beta=torch.from_numpy(r.beta).to(dev))
+
+        def step_pre(i):
+            kdalib.prefill(raw["q"], raw["k"], raw["v"], raw["la"], raw["beta"], None, None,
+                           num_seqs=1, final_state=fin, out=out[0], workspace=ws,
+                           l2norm_qk=True, beta_sigmoid=True)
+
+        def step_plain_same_buffers(i):
+            kdalib.prefill(raw["q"], raw["k"], raw["v"], raw["la"], raw["beta"], None, None,
+                           num_seqs=1, final_state=fin, out=out[0], workspace=ws)
+        pre_us = timed(step_pre, reps)
+        plain_us = timed(step_plain_same_buffers, reps)
+        options["preprocessing"] = {
+            "workload": "the prefill workload from raw q/k and beta logits, L2 normalisation "
+                        "and sigmoid in the kernels (one input set, cache-warm)",
+            "us_per_step": round(pre_us, 2), "us_per_step_without": round(plain_us, 2)}
+        # pooled recurrent tokens: 256 sequences x 8 tokens (speculative verification)
+        Nr, Tr, Hr = 256, 8, H
+        rr = gen.make_prefill(9, [Tr] * Nr, H=Hr, dk=dk, dv=dv, dtype="bf16")
+        pool = torch.from_numpy(gen.decode_state(9, Nr, Hr, dk, dv)).to(dev)
+        slots = torch.from_numpy(np.random.default_rng(9).permutation(Nr).astype(np.int32)).to(dev)
+        rin = dict(q=dq(rr.q), k=dq(rr.k), v=dq(rr.v), la=torch.from_numpy(rr.log_alpha).to(dev),
+                   beta=torch.from_numpy(rr.beta).to(dev))
+        o_r = torch.empty((Nr * Tr, Hr, dv), dtype=torch.bfloat16, device=dev)
+
+        def step_rec(i):
+            kdalib.decode_tokens(pool, rin["q"], rin["k"], rin["v"], rin["la"], rin["beta"],
+                                 state_indices=slots, num_seqs=Nr, out=o_r)
+        rec_us = timed(step_rec, reps)
+        rec_bytes = Nr * Hr * (2 * dk * dv * 4 + Tr * PATH_BYTES_PER_TOKEN_HEAD)
+        rec_gbs = rec_bytes / (rec_us * 1e-6) / 1e9
+        options["decode_tokens"] = {
+            "workload": "pooled recurrent tokens: 256 seqs x 8 tokens, H=32, dk=dv=128, bf16, "
+                        "fp32 states in permuted slots", "us_per_call": round(rec_us, 2),
+            "algorithmic_bytes": rec_bytes, "achieved_GBs": round(rec_gbs, 1),
+            "frac_of_hbm_peak": round(rec_gbs / HBM_PEAK_GBS, 4)}
+        log(f"[bench] options: chunk states {cs_us:.1f} us (+{cs_us - base_us:.1f}), "
+            f"preprocessing {pre_us:.1f} us (plain {plain_us:.1f}), "
+            f"decode_tokens 256x8 {rec_us:.1f} us = {rec_gbs:.0f} GB/s")
+        del pool, cs
+
     if args.copy_calib:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -252,7 +335,8 @@ def main():
                                   "bf16 q/k/v, fp32 log_alpha/beta/state, chunk 64",
                       "global_batch": 1, "seq_len": T, "heads": H, "head_dim": dk,
                       "parallelism": "single GPU"},
-           "roofline": roofline, "path": path, "decode": decode, "cpu_baseline": cpu}
+           "roofline": roofline, "path": path, "decode": decode, "options": options,
+           "cpu_baseline": cpu}
     print(json.dumps(rec), flush=True)
 
 

@@ -170,8 +170,8 @@ kda_status kda_prefill_ex(const void* q, const void* k, const void* v, const flo
         Plan plan;
         if (!make_plan(total_tokens, num_seqs, H, dk, dv, dtype, plan))
             return fail(KDA_ERR_INVALID_ARGUMENT, "invalid sizes");
-        if (plan.max_chunks > 0x7fffffffLL / 2)
-            return fail(KDA_ERR_INVALID_ARGUMENT, "too many chunks");
+        if (plan.max_chunks > 0x7fffffffLL / 2 || plan.max_chunks * H > 0x7fffffffLL)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "too many chunks (chunks * H must be < 2^31)");
         if (workspace && workspace_bytes < plan.total)
             return fail(KDA_ERR_WORKSPACE, "workspace too small: need " +
                                                std::to_string(plan.total) + " bytes");

@@ -176,6 +176,27 @@ __device__ __forceinline__ ChunkInfo chunk_desc(const ChunkSrc& src, int cid) {
     return ci;
 }
 
+// Workgroup -> (chunk, head) of the per-chunk kernels (one-dimensional grid
+// of max_chunks * H workgroups).  Workgroups are dispatched round-robin over
+// the 8 XCDs, and the sequential kernel reads head h's records on XCD h % 8
+// (for H a multiple of 8): here too, so a head's records are written, read
+// and re-read through one L2.  `descending` walks the chunks from the last:
+// the intra kernel writes chunk 0 last, so the sequential kernel, which
+// starts from chunk 0, finds the most recently written records first.
+__device__ __forceinline__ void chunk_head_of_block(int H, bool descending, int& cid, int& h) {
+    const int L = blockIdx.x, n = gridDim.x / H;
+    int q;
+    if ((H & 7) == 0) {
+        const int hg = H >> 3;
+        q = (L >> 3) / hg;
+        h = (L & 7) + 8 * ((L >> 3) % hg);
+    } else {
+        q = L / H;
+        h = L % H;
+    }
+    cid = descending ? n - 1 - q : q;
+}
+
 // First chunk and chunk count of sequence s.
 __device__ __forceinline__ void seq_chunks(const ChunkSrc& src, int s, int& c_begin, int& n) {
     if (src.rows >= 0) {

@@ -109,15 +109,16 @@ __device__ __forceinline__ typename Vec<E>::v8 frag8_scaled(const E* p, const fl
     return v;
 }
 
-// CPT consecutive elements as floats (one vector load)
+// CPT consecutive elements as floats (one vector load).  The inputs are read
+// once: streaming loads keep them from displacing the records in the caches.
 template <int CPT, typename E>
 __device__ __forceinline__ void load_row(const E* p, float (&out)[CPT]) {
     if constexpr (CPT == 2) {
-        const typename Vec<E>::v2 v = *reinterpret_cast<const typename Vec<E>::v2*>(p);
+        const typename Vec<E>::v2 v = __builtin_nontemporal_load(reinterpret_cast<const typename Vec<E>::v2*>(p));
         out[0] = to_f32(v[0]);
         out[1] = to_f32(v[1]);
     } else {
-        out[0] = to_f32(p[0]);
+        out[0] = to_f32(__builtin_nontemporal_load(p));
     }
 }
 
@@ -227,12 +228,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     float* sEtab = reinterpret_cast<float*>(smem + L::OFF_ETAB);
     float* sBeta = reinterpret_cast<float*>(smem + L::OFF_BETA);
 
-    const int cid = blockIdx.x;
+    int cid, h;
+    chunk_head_of_block(H, true, cid, h);
     int n_chunks;
     ChunkInfo ci;
     chunk_of(src, cid, n_chunks, ci);
     if (cid >= n_chunks) return;
-    const int h = blockIdx.y;
     const size_t chh = (size_t)cid * H + h;
     const ChunkOut<E, DK, DV> out(rec, chh);
 
@@ -710,11 +711,11 @@ static hipError_t launch_intra_t(const void* q, const void* k, const void* v, co
 {
     const int beta_logit = (flags & PRE_BETA_LOGIT) ? 1 : 0;
     if (flags & PRE_L2NORM_QK)
-        hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, true>), dim3(max_chunks, H), dim3(256), 0,
+        hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, true>), dim3(max_chunks * H), dim3(256), 0,
                            stream, (const E*)q, (const E*)k, (const E*)v, la, beta, src, H,
                            beta_logit, (unsigned char*)rec);
     else
-        hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, false>), dim3(max_chunks, H), dim3(256), 0,
+        hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, false>), dim3(max_chunks * H), dim3(256), 0,
                            stream, (const E*)q, (const E*)k, (const E*)v, la, beta, src, H,
                            beta_logit, (unsigned char*)rec);
     return hipGetLastError();

@@ -43,12 +43,12 @@ __global__ __launch_bounds__(256) void prefill_output_kernel(
     constexpr RecLayout RL = rec_layout(sizeof(E), DK, DV);
     __shared__ __attribute__((aligned(1024))) unsigned char sm[C::LOADS_W * 4 * 1024];
 
-    const int cid = blockIdx.x;
+    int cid, h;
+    chunk_head_of_block(H, false, cid, h);
     int n_chunks;
     ChunkInfo ci;
     chunk_of(src, cid, n_chunks, ci);
     if (cid >= n_chunks) return;
-    const int h = blockIdx.y;
     const size_t chh = (size_t)cid * H + h;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63, g = l >> 4, ln = l & 15;
@@ -107,7 +107,7 @@ template <typename E, int DK, int DV>
 static hipError_t launch_output_t(const void* rec, const void* states, ChunkSrc src, int max_chunks,
                                   int H, void* o, hipStream_t stream)
 {
-    hipLaunchKernelGGL((prefill_output_kernel<E, DK, DV>), dim3(max_chunks, H), dim3(256), 0, stream,
+    hipLaunchKernelGGL((prefill_output_kernel<E, DK, DV>), dim3(max_chunks * H), dim3(256), 0, stream,
                        (const unsigned char*)rec, (const E*)states, src, H, (E*)o);
     return hipGetLastError();
 }

@@ -387,6 +387,10 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
 
     __shared__ __attribute__((aligned(1024))) unsigned char ring[C::NSLOT * C::SLOT];
     __shared__ __attribute__((aligned(16))) unsigned char xfer[C::NX * C::XSLOT];
+    // fp32 chunk-start states for the chunk_states output, column-major
+    // [slot][16 columns][DK rows (+4 padding)]; written by the serial waves with
+    // 16-byte LDS stores, sent to memory row-major by the touch wave
+    __shared__ __attribute__((aligned(16))) float cst[C::NX][16][DK + 4];
 
     const int b = blockIdx.x;
     const int xcd = b & 7, q8 = b >> 3;
@@ -438,13 +442,10 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
             if (it < n)
                 store_vec(states + ((size_t)(c_begin + it) * H + h) * DK * DV +
                               ((size_t)(slice * KS + w) * 64 + l) * 8, f);
-            if (chunk_states && it < n) {   // fp32 [chunk][H][DK][DV]
-                float* cs = chunk_states + ((size_t)(c_begin + it) * H + h) * DK * DV + j0 + ln;
+            if (chunk_states) {
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        cs[(size_t)(32 * w + 16 * h2 + 4 * g + i) * DV] = S[h2][i];
+                    *reinterpret_cast<f32x4*>(&cst[it % C::NX][ln][32 * w + 16 * h2 + 4 * g]) = S[h2];
             }
         };
         put(0);
@@ -523,9 +524,23 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
         touch(tv1, min(TOUCH_DIST - 2, n - 1));
         touch(tv2, min(TOUCH_DIST - 1, n - 1));
         bare_barrier();
+        // chunk-start state `it` (in cst since the barrier that ended chunk it - 1;
+        // rewritten only after the barrier that ends chunk it) to chunk_states,
+        // fp32 [chunk][H][DK][DV]: 16-byte stores of 4 columns of a row
+        auto send_state = [&](int it) {
+            float* cs = chunk_states + ((size_t)(c_begin + it) * H + h) * DK * DV + j0;
+#pragma unroll
+            for (int k = 0; k < DK * 4 / 64; ++k) {
+                const int u = l + 64 * k, row = u >> 2, qd = u & 3;
+                const f32x4 val = {cst[it % C::NX][4 * qd][row], cst[it % C::NX][4 * qd + 1][row],
+                                   cst[it % C::NX][4 * qd + 2][row], cst[it % C::NX][4 * qd + 3][row]};
+                *reinterpret_cast<f32x4*>(cs + (size_t)row * DV + 4 * qd) = val;
+            }
+        };
         auto step = [&](TouchSet& tv, int it) {
             fold(tv);   // issued three chunks ago
             touch(tv, min(it + TOUCH_DIST, n - 1));
+            if (chunk_states) send_state(it);
             bare_barrier();
         };
         for (int it = 0; it < n; it += 3) {
