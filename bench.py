@@ -86,8 +86,8 @@ def traffic_for(kernel: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--sets", type=int, default=3, help="rotated input sets (defeat the MALL)")
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")

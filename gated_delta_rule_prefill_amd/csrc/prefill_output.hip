@@ -64,7 +64,8 @@ __global__ __launch_bounds__(256) void prefill_output_kernel(
         for (int k = 0; k < C::LOADS_W; ++k)
             if (C::LOADS_W * wave + k < C::LOADS)
                 __builtin_amdgcn_global_load_lds((out_global_void*)srcp[k],
-                                                 (out_lds_void*)(sm + 1024 * (C::LOADS_W * wave + k)), 16, 0, 0);
+                                                 (out_lds_void*)(sm + 1024 * (C::LOADS_W * wave + k)), 16, 0,
+                                                 2 /* non-temporal: the state's only reader */);
     }
     const int r = 16 * wave + ln;   // this lane's row of the chunk
     const E* QM = reinterpret_cast<const E*>(R0 + RL.qm);
