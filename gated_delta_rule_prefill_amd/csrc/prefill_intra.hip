@@ -27,8 +27,9 @@
 //
 // The inverse of the unit lower-triangular I + A_kk is built blockwise: the
 // four 16x16 diagonal blocks by forward substitution (one lane per column),
-// then the off-diagonal blocks on fp32 MFMA, one block diagonal at a time,
-// stored transposed in the unused upper triangle of A_kk.
+// then the off-diagonal blocks on fp32 MFMA, each wave walking down one
+// column block with the blocks above it in registers, stored transposed in
+// the unused upper triangle of A_kk.
 //
 // Decay factors never form 1/gamma over a whole chunk: the chunk is cut into
 // four 16-token blocks with reference log-decays B_R (g just before block R).
@@ -67,6 +68,9 @@ struct IntraLayout {
     static constexpr int OFF_TL = OFF_AL + ((U2_BYTES + 15) & ~15);
     static constexpr int OFF_AQ = OFF_TL + ((CHUNK * LT * ES + 15) & ~15);   // A_qk, perm32 keys
     static constexpr int OFF_TAU = OFF_AQ + ((CHUNK * LT * ES + 15) & ~15);
+    // phase 0b-1: q e^{g - B} ([64][LK]) over the T and A_qk areas, free until then
+    static constexpr int OFF_QP = OFF_TL;
+    static_assert(OFF_QP + CHUNK * LK * ES <= OFF_TAU, "q operand area");
     static constexpr int OFF_ETAB = OFF_TAU + 4 * DK * 4;
     static constexpr int OFF_BETA = OFF_ETAB + 6 * DK * 4;
     static constexpr int BYTES = OFF_BETA + CHUNK * 4;
@@ -166,35 +170,38 @@ __device__ __forceinline__ float x_elem(const float* sAL, int r, int c) {
     return r == c ? 1.f : (r > c ? sAL[c * LA + r] : 0.f);
 }
 
-// X block (R, I), R > I (NJ = R - I), by one wave on fp32 MFMA:
-//   X_RI = -X_RR * sum_{J=I}^{R-1} A_RJ X_JI
-// The first product's accumulator feeds the second as its B operand:
-// slot (g, m) carries contraction index 4g + m in both.
-template <int LA, int NJ>
-__device__ __forceinline__ void x_block(float* sAL, int R, int I, int g, int ln) {
-    float a[NJ][4], b[NJ][4], xr[4];
+// Column block I of X below the diagonal, by one wave on fp32 MFMA:
+//   X_RI = -X_RR * sum_{J=I}^{R-1} A_RJ X_JI,   R = I+1 .. 3,
+// each block feeding the next from registers: an accumulator tile (lane
+// group g holding rows 4g..4g+3) is the B operand whose slot (g, m) carries
+// contraction index 4g + m.  Only the diagonal inverses X_RR and A come
+// from LDS; the results go to the upper triangle of sAL, transposed.
+template <int LA, int I>
+__device__ __forceinline__ void x_column(float* sAL, int g, int ln) {
+    f32x4 xc[4];
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-        const int J = I + jj;
+    for (int m = 0; m < 4; ++m) xc[I][m] = x_elem<LA>(sAL, 16 * I + 4 * g + m, 16 * I + ln);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int kk = 4 * g + m;
-            a[jj][m] = sAL[(16 * R + ln) * LA + 16 * J + kk];
-            b[jj][m] = x_elem<LA>(sAL, 16 * J + kk, 16 * I + ln);
-        }
+    for (int R = I + 1; R < 4; ++R) {
+        float a[R - I][4], xr[4];
+#pragma unroll
+        for (int J = I; J < R; ++J)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) a[J - I][m] = sAL[(16 * R + ln) * LA + 16 * J + 4 * g + m];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) xr[m] = -x_elem<LA>(sAL, 16 * R + ln, 16 * R + 4 * g + m);
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = I; J < R; ++J)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) z = __builtin_amdgcn_mfma_f32_16x16x4f32(a[J - I][m], xc[J][m], z, 0, 0, 0);
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) x = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[m], z[m], x, 0, 0, 0);
+        xc[R] = x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sAL[(16 * I + ln) * LA + 16 * R + 4 * g + i] = x[i];
     }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) xr[m] = -x_elem<LA>(sAL, 16 * R + ln, 16 * R + 4 * g + m);
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) z = __builtin_amdgcn_mfma_f32_16x16x4f32(a[jj][m], b[jj][m], z, 0, 0, 0);
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 4; ++m) x = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[m], z[m], x, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sAL[(16 * I + ln) * LA + 16 * R + 4 * g + i] = x[i];
 }
 
 // NORM: L2-normalise q and k rows first; beta_logit: beta arrives as a logit.
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     constexpr int NUB = (DV / 16 + 3) / 4;   // value-column blocks per wave
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
-    E* sKP = reinterpret_cast<E*>(smem + L::OFF_KP);   // k*e^{g-B}  (phase 1a), then q*e^{g-B} (1b)
+    E* sKP = reinterpret_cast<E*>(smem + L::OFF_KP);   // k*e^{g-B}  (phase 0b-1)
     E* sKD = reinterpret_cast<E*>(smem + L::OFF_KD);   // k*e^{B-g}
     E* sKGT = reinterpret_cast<E*>(smem + L::OFF_KGT); // (e^g * k)^T   (phase 3-4)
     E* sVT = reinterpret_cast<E*>(smem + L::OFF_VT);   // v^T           (phase 3-4)
@@ -224,6 +231,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     E* sKHT = reinterpret_cast<E*>(smem + L::OFF_KHT);  // Khat^T (phase 4+)
     E* sTL = reinterpret_cast<E*>(smem + L::OFF_TL);
     E* sAQ = reinterpret_cast<E*>(smem + L::OFF_AQ);
+    E* sQP = reinterpret_cast<E*>(smem + L::OFF_QP);   // q*e^{g-B} (phase 0b-1)
     float* sTau = reinterpret_cast<float*>(smem + L::OFF_TAU);
     float* sEtab = reinterpret_cast<float*>(smem + L::OFF_ETAB);
     float* sBeta = reinterpret_cast<float*>(smem + L::OFF_BETA);
@@ -290,8 +298,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
     __syncthreads();
 
-    // ---- phase 0b: block references, decay table, decayed keys ---------------
-    if constexpr (NORM) l2_normalise_rows<CPT>(kr, lane);
+    // ---- phase 0b: block references, decay table, decayed keys and queries ----
+    if constexpr (NORM) {
+        l2_normalise_rows<CPT>(kr, lane);
+        l2_normalise_rows<CPT>(qr, lane);
+    }
     float eB[CPT], eTE[CPT];   // e^{B_R} (g before block R);  e^{g_C - B_R}
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
@@ -314,56 +325,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = 16 * R + r;
-        E kp[CPT], kd[CPT];
+        E kp[CPT], kd[CPT], qp[CPT];
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
             const float P = fast_exp(ell[r][e]);                   // e^{g_r - B_R} <= 1
             const float iP = fast_exp(fminf(-ell[r][e], 80.f));    // e^{B_R - g_r}
             kp[e] = from_f32<E>(kr[r][e] * P);
             kd[e] = from_f32<E>(kr[r][e] * iP);
+            qp[e] = from_f32<E>(qr[r][e] * P);
             ell[r][e] = kr[r][e] * iP * eTE[e];                    // Khat: k e^{g_C - g_r}
             kr[r][e] *= P * eB[e];                                 // e^{g_r} k  (for W)
-            la[r][e] = P;                                          // log_alpha is dead here
+            qr[r][e] *= P * eB[e];                                 // Qg = e^{g_r} q
         }
         store_row<CPT>(sKP + row * L::LK + c0, kp);
         store_row<CPT>(sKD + row * L::LK + c0, kd);
+        store_row<CPT>(sQP + row * L::LK + c0, qp);
     }
-    if constexpr (NORM) l2_normalise_rows<CPT>(qr, lane);
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) qr[r][e] *= la[r][e];        // q e^{g_r - B_R}
     if (R == 0) {
 #pragma unroll
         for (int e = 0; e < CPT; ++e) out.gC[c0 + e] = eTE[e];
     }
     __syncthreads();
 
-    // ---- phase 1a: A_kk tiles (rows r of block R, columns i of block I) --------
-    // A operand k_r e^{g_r - B_R}; B operand k_i e^{B_I - g_i} * e^{B_R - B_I}.
+    // ---- phase 1: A_kk and A_qk^T tiles of each block pair (R, I), I <= R ----
+    // A_kk: A operand k_r e^{g_r - B_R}, B operand k_i e^{B_I - g_i} e^{B_R - B_I};
+    // A_qk^T: that same key operand as A, q_r e^{g_r - B_R} as B.  The decay
+    // scaling of the key fragments is done once for both products, and the
+    // diagonal test once per tile, so each path is straight code.  A_qk
+    // tiles stay in registers until the barrier: their LDS area holds q.
+    auto pair_tiles = [&](const int PR, const int PI, const bool diag) {
+        const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
+        V8 a[KS], b[KS], qf[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int cb = 32 * s + 8 * g;
+            a[s] = frag8<E>(sKP + (16 * PR + ln) * L::LK + cb);
+            b[s] = diag ? frag8<E>(sKD + (16 * PI + ln) * L::LK + cb)
+                        : frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f + cb);
+            qf[s] = frag8<E>(sQP + (16 * PR + ln) * L::LK + cb);
+        }
+        const f32x4 bt4 = *reinterpret_cast<const f32x4*>(sBeta + 16 * PR + 4 * g);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            acc = mma32(a[s], b[s], acc);
+            aq = mma32(b[s], qf[s], aq);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * PR + 4 * g + i, col = 16 * PI + ln;
+            sAL[r * L::LA + col] = r > col ? bt4[i] * acc[i] : 0.f;
+        }
+        // A_qk^T tile: lane holds A_qk[16 PR + ln][16 PI + 4g + i] (causal mask)
+        V4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = from_f32<E>(16 * PR + ln >= 16 * PI + 4 * g + i ? aq[i] : 0.f);
+        return w;
+    };
+    V4 qk[3];
 #pragma unroll
     for (int k3 = 0; k3 < 3; ++k3) {
         const int p = wave + 4 * k3;
         if (p < 10) {
             const int PR = pair_r(p), PI = pair_i(p);
-            const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
-            V8 a[KS], b[KS];
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int cb = 32 * s + 8 * g;
-                a[s] = frag8<E>(sKP + (16 * PR + ln) * L::LK + cb);
-                b[s] = PR == PI ? frag8<E>(sKD + (16 * PI + ln) * L::LK + cb)
-                                : frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f + cb);
-            }
-            const f32x4 bt4 = *reinterpret_cast<const f32x4*>(sBeta + 16 * PR + 4 * g);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) acc = mma32(a[s], b[s], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * PR + 4 * g + i, col = 16 * PI + ln;
-                sAL[r * L::LA + col] = r > col ? bt4[i] * acc[i] : 0.f;
-            }
+            qk[k3] = PR == PI ? pair_tiles(PR, PI, true) : pair_tiles(PR, PI, false);
         }
     }
     for (int u = wave - 2; u >= 0 && u < 6; u += 2) {   // waves 2 and 3 zero the upper tiles
@@ -371,49 +397,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
         for (int i = 0; i < 4; ++i) sAL[(16 * UR + 4 * g + i) * L::LA + 16 * UI + ln] = 0.f;
     }
-    __syncthreads();   // sKP no longer read
+    __syncthreads();   // kp, kd, q operands dead: U1 becomes kgT / vT, the q area A_qk
 
-    // ---- phase 1b: queries -> q e^{g - B} (LDS); qr becomes Qg = q e^{g} --------
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 16 * R + r;
-        E qp[CPT];
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-            qp[e] = from_f32<E>(qr[r][e]);
-            qr[r][e] *= eB[e];
-        }
-        store_row<CPT>(sKP + row * L::LK + c0, qp);
-    }
-    __syncthreads();
-
-    // ---- phase 1c: A_qk^T tiles (rows i of block I, columns r of block R) -------
-    // stored as A_qk[r][perm32(i)] in LDS for the read-out products
+    // A_qk[r][perm32(i)] for the read-out products; the upper tiles are zero
 #pragma unroll
     for (int k3 = 0; k3 < 3; ++k3) {
         const int p = wave + 4 * k3;
-        if (p >= 10) continue;
-        const int PR = pair_r(p), PI = pair_i(p);
-        const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
-        V8 a[KS], b[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int cb = 32 * s + 8 * g;
-            a[s] = PR == PI ? frag8<E>(sKD + (16 * PI + ln) * L::LK + cb)
-                            : frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f + cb);
-            b[s] = frag8<E>(sKP + (16 * PR + ln) * L::LK + cb);
+        if (p < 10) {
+            const int PR = pair_r(p), PI = pair_i(p);
+            store_vec(sAQ + (16 * PR + ln) * L::LT + perm_index(16 * PI + 4 * g), qk[k3]);
         }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) acc = mma32(a[s], b[s], acc);
-        const int r = 16 * PR + ln;
-        V4 w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int col = 16 * PI + 4 * g + i;
-            w[i] = from_f32<E>(r >= col ? acc[i] : 0.f);
-        }
-        store_vec(sAQ + r * L::LT + perm_index(16 * PI + 4 * g), w);
     }
     for (int u = wave - 2; u >= 0 && u < 6; u += 2) {
         const int UR = off_i(u), UI = off_r(u);   // the transposed (upper) tile
@@ -422,7 +415,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         for (int i = 0; i < 4; ++i) z[i] = from_f32<E>(0.f);
         store_vec(sAQ + (16 * UR + ln) * L::LT + perm_index(16 * UI + 4 * g), z);
     }
-    __syncthreads();   // sKP / sKD dead: their bytes become kgT and vT
 
     // ---- phase 3a: (e^g k)^T and v^T in LDS; diagonal 16x16 inverses ----------
 #pragma unroll
@@ -472,12 +464,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
     __syncthreads();
 
-    // ---- phase 3b-d: off-diagonal blocks of X, one block-diagonal at a time ----
-    if (wave < 3) x_block<L::LA, 1>(sAL, wave + 1, wave, g, ln);          // (1,0) (2,1) (3,2)
-    __syncthreads();
-    if (wave < 2) x_block<L::LA, 2>(sAL, wave + 2, wave, g, ln);          // (2,0) (3,1)
-    __syncthreads();
-    if (wave == 0) x_block<L::LA, 3>(sAL, 3, 0, g, ln);                   // (3,0)
+    // ---- phase 3b: off-diagonal blocks of X, wave w down column block w ------
+    if (wave == 0) x_column<L::LA, 0>(sAL, g, ln);
+    else if (wave == 1) x_column<L::LA, 1>(sAL, g, ln);
+    else if (wave == 2) x_column<L::LA, 2>(sAL, g, ln);
     __syncthreads();
 
     // ---- phase 3e: T = X Diag(beta) in the operand dtype ----------------------
