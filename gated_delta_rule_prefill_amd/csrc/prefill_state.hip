@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int t = 0; t < KT; ++t)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) cs[(size_t)(16 * t + 4 * g + i) * DV] = S[t][i];
+                    for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(S[t][i], cs + (size_t)(16 * t + 4 * g + i) * DV);
             }
             // chunk-start state as MFMA operand slots {32ks+4g..+3, 32ks+16+4g..+3}
             V8 Sf[KS];
@@ -534,7 +534,8 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
                 const int u = l + 64 * k, row = u >> 2, qd = u & 3;
                 const f32x4 val = {cst[it % C::NX][4 * qd][row], cst[it % C::NX][4 * qd + 1][row],
                                    cst[it % C::NX][4 * qd + 2][row], cst[it % C::NX][4 * qd + 3][row]};
-                *reinterpret_cast<f32x4*>(cs + (size_t)row * DV + 4 * qd) = val;
+                // streaming stores: the records this kernel still has to read stay cached
+                __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(cs + (size_t)row * DV + 4 * qd));
             }
         };
         auto step = [&](TouchSet& tv, int it) {
