@@ -58,6 +58,9 @@ class Oracle:
         lib.oracle_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                            vp, i32]
         lib.oracle_decode_step.restype = ctypes.c_int
+        lib.oracle_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32,
+                                        vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        lib.oracle_backward.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = [ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -71,6 +74,9 @@ class Oracle:
 
     def decode_tokens(self, *args, **kwargs):
         return _decode_tokens(self.lib, *args, **kwargs)
+
+    def backward(self, *args, **kwargs):
+        return _backward(self.lib, *args, **kwargs)
 
 
 _default: Optional[Oracle] = None
@@ -136,6 +142,11 @@ def decode_step(*args, **kwargs) -> np.ndarray:
 def decode_tokens(*args, **kwargs) -> np.ndarray:
     """Recurrent tokens of a packed batch on pooled states (see ``_decode_tokens``)."""
     return _decode_tokens(_load(), *args, **kwargs)
+
+
+def backward(*args, **kwargs):
+    """Gradients of the recurrence for given output gradients (see ``_backward``)."""
+    return _backward(_load(), *args, **kwargs)
 
 
 # option bits of oracle_prefill_ex
@@ -258,3 +269,43 @@ def _decode_tokens(lib, pool: np.ndarray, slots: Optional[np.ndarray], q: np.nda
         o[a:b] = os_
         pool[sl[s]] = fs[0]
     return o
+
+
+def _backward(lib, q: np.ndarray, k: np.ndarray, v: np.ndarray, log_alpha: np.ndarray,
+              beta: np.ndarray, initial_state: Optional[np.ndarray], cu_seqlens: Optional[np.ndarray],
+              d_o: np.ndarray, d_final: Optional[np.ndarray] = None,
+              num_seqs: Optional[int] = None, nthreads: Optional[int] = None) -> dict:
+    """Reverse-mode gradients of the token-by-token recurrence.
+
+    Inputs as for ``prefill``; d_o [T, H, dv] and d_final [N, H, dk, dv] (or
+    None) are the gradients of the loss with respect to o and the final state.
+    Returns float64 arrays: dq, dk [T, H, dk]; dv [T, H, dv]; dlog_alpha
+    [T, H, dk]; dbeta [T, H]; dinitial_state [N, H, dk, dv].
+    """
+    dtype = _qkv_dtype(q)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        N = cu.shape[0] - 1
+    else:
+        cu = None
+        N = int(num_seqs or 1)
+    q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
+    la = np.ascontiguousarray(log_alpha, dtype=np.float32)
+    be = np.ascontiguousarray(beta, dtype=np.float32)
+    s0 = None if initial_state is None else np.ascontiguousarray(initial_state, dtype=np.float32)
+    do = np.ascontiguousarray(d_o, dtype=np.float64)
+    df = None if d_final is None else np.ascontiguousarray(d_final, dtype=np.float64)
+    assert do.shape == (T, H, dv)
+    out = dict(dq=np.zeros((T, H, dk)), dk=np.zeros((T, H, dk)), dv=np.zeros((T, H, dv)),
+               dlog_alpha=np.zeros((T, H, dk)), dbeta=np.zeros((T, H)),
+               dinitial_state=np.zeros((N, H, dk, dv)))
+    rc = lib.oracle_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(s0), _ptr(cu),
+                             T, N, H, dk, dv, dtype, _ptr(do), _ptr(df), _ptr(out["dq"]),
+                             _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]),
+                             _ptr(out["dbeta"]), _ptr(out["dinitial_state"]),
+                             int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_backward rejected its arguments")
+    return out

@@ -270,3 +270,185 @@ int oracle_decode_step(double *state, const void *q, const void *k, const void *
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * Gradients of the recurrence (reverse mode, written out step by step).
+ *
+ * For a loss L whose gradients with respect to the outputs are d_o [T,H,dv]
+ * and d_final [N,H,dk,dv] (NULL = 0), this returns dL/dq, dL/dk, dL/dv,
+ * dL/dlog_alpha, dL/dbeta and dL/dinitial_state (the pages give no backward
+ * pass; this is the chain rule applied to the three lines of kda_step in
+ * reverse order, and a finite-difference test pins it to the forward above).
+ *
+ * One forward step is  X = Diag(a) S;  y = X^T k;  S' = X + beta k (v - y)^T;
+ * o = S'^T q.  With G the gradient of S' (plus q do^T from the read-out):
+ *   dq   = S' do
+ *   dX   = G;   dk += beta G (v - y);   dbeta = k^T G (v - y);
+ *   dv   = beta G^T k;   dy = -beta G^T k
+ *   dX  += k dy^T;   dk += X dy
+ *   dS   = Diag(a) dX;   dlog_alpha_c = sum_j dX[c,j] X[c,j]
+ * States are recomputed forward from checkpoints every 64 tokens (the same
+ * operations in the same order, so the recomputed states are the forward's).
+ *
+ * Outputs (fp64): dq, dk [T,H,dk]; dv [T,H,dv]; dla [T,H,dk]; dbeta [T,H];
+ * ds0 [N,H,dk,dv] or NULL.  Returns 0, or -1 on bad arguments.
+ */
+enum { ORACLE_CKPT = 64 };
+
+int oracle_backward(const void *q, const void *k, const void *v,
+                    const float *log_alpha, const float *beta,
+                    const float *initial_state, const int32_t *cu_seqlens,
+                    int64_t total_tokens, int32_t num_seqs, int32_t H,
+                    int32_t dk, int32_t dv, int32_t dtype,
+                    const double *d_o, const double *d_final,
+                    double *dq, double *dk_out, double *dv_out, double *dla, double *dbeta,
+                    double *ds0, int32_t nthreads)
+{
+    if (num_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0 || total_tokens < 0 || !d_o)
+        return -1;
+    if (!cu_seqlens && total_tokens % num_seqs != 0)
+        return -1;
+    set_threads(nthreads);
+    const int64_t units = (int64_t)num_seqs * H;
+    const int64_t SZ = (int64_t)dk * dv;
+    int bad = 0;
+
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t u = 0; u < units; ++u) {
+        const int32_t s = (int32_t)(u / H), h = (int32_t)(u % H);
+        int64_t t0, t1;
+        if (cu_seqlens) {
+            t0 = cu_seqlens[s];
+            t1 = cu_seqlens[s + 1];
+        } else {
+            int64_t len = total_tokens / num_seqs;
+            t0 = (int64_t)s * len;
+            t1 = t0 + len;
+        }
+        if (t0 < 0 || t1 < t0 || t1 > total_tokens) {
+            bad |= 1;
+            continue;
+        }
+        const int64_t len = t1 - t0;
+        const int64_t nck = (len + ORACLE_CKPT - 1) / ORACLE_CKPT;
+        /* ckpt[c]: state before token t0 + 64c;  seg[i]: state before token i of a segment */
+        double *ckpt = (double *)malloc(sizeof(double) * (size_t)((nck + 1) * SZ));
+        double *seg = (double *)malloc(sizeof(double) * (size_t)((ORACLE_CKPT + 1) * SZ));
+        double *G = (double *)calloc((size_t)SZ, sizeof(double));
+        double *X = (double *)malloc(sizeof(double) * (size_t)SZ);
+        double *vec = (double *)malloc(sizeof(double) * (size_t)(4 * dk + 6 * dv));
+        if (!ckpt || !seg || !G || !X || !vec) {
+            free(ckpt); free(seg); free(G); free(X); free(vec);
+            bad |= 1;
+            continue;
+        }
+        double *qv = vec, *kv = qv + dk, *lv = kv + dk, *av = lv + dk;
+        double *vv = av + dk, *ov = vv + dv, *y = ov + dv, *dov = y + dv, *gk = dov + dv, *dy = gk + dv;
+
+        /* the token's inputs, widened exactly */
+        #define KDA_LOAD_TOKEN(t)                                              \
+            do {                                                               \
+                const int64_t rk_ = ((t) * H + h) * dk, rv_ = ((t) * H + h) * dv; \
+                for (int c = 0; c < dk; ++c) {                                 \
+                    qv[c] = widen(q, rk_ + c, dtype);                          \
+                    kv[c] = widen(k, rk_ + c, dtype);                          \
+                    lv[c] = (double)log_alpha[rk_ + c];                        \
+                    av[c] = exp(lv[c]);                                        \
+                }                                                              \
+                for (int j = 0; j < dv; ++j)                                   \
+                    vv[j] = widen(v, rv_ + j, dtype);                          \
+            } while (0)
+
+        /* forward: checkpoints */
+        double *S = ckpt;
+        memset(S, 0, sizeof(double) * (size_t)SZ);
+        if (initial_state) {
+            const float *S0 = initial_state + ((int64_t)s * H + h) * SZ;
+            for (int64_t i = 0; i < SZ; ++i)
+                S[i] = (double)S0[i];
+        }
+        for (int64_t c = 0; c < nck; ++c) {
+            double *Sc = ckpt + c * SZ, *Sn = ckpt + (c + 1) * SZ;
+            memcpy(Sn, Sc, sizeof(double) * (size_t)SZ);
+            const int64_t a = t0 + c * ORACLE_CKPT, b = a + ORACLE_CKPT < t1 ? a + ORACLE_CKPT : t1;
+            for (int64_t t = a; t < b; ++t) {
+                KDA_LOAD_TOKEN(t);
+                kda_step(Sn, dk, dv, qv, kv, vv, lv, (double)beta[t * H + h], ov, y);
+            }
+        }
+        /* reverse */
+        if (d_final)
+            memcpy(G, d_final + ((int64_t)s * H + h) * SZ, sizeof(double) * (size_t)SZ);
+        for (int64_t c = nck - 1; c >= 0; --c) {
+            const int64_t a = t0 + c * ORACLE_CKPT, b = a + ORACLE_CKPT < t1 ? a + ORACLE_CKPT : t1;
+            memcpy(seg, ckpt + c * SZ, sizeof(double) * (size_t)SZ);
+            for (int64_t t = a; t < b; ++t) {
+                double *Sn = seg + (t - a + 1) * SZ;
+                memcpy(Sn, seg + (t - a) * SZ, sizeof(double) * (size_t)SZ);
+                KDA_LOAD_TOKEN(t);
+                kda_step(Sn, dk, dv, qv, kv, vv, lv, (double)beta[t * H + h], ov, y);
+            }
+            for (int64_t t = b - 1; t >= a; --t) {
+                const double *Sprev = seg + (t - a) * SZ, *Snew = seg + (t - a + 1) * SZ;
+                const int64_t rk = (t * H + h) * dk, rv = (t * H + h) * dv;
+                const double bt = (double)beta[t * H + h];
+                KDA_LOAD_TOKEN(t);
+                for (int j = 0; j < dv; ++j)
+                    dov[j] = d_o[rv + j];
+                /* X = Diag(a) S_prev;  y = X^T k */
+                for (int c2 = 0; c2 < dk; ++c2)
+                    for (int j = 0; j < dv; ++j)
+                        X[(int64_t)c2 * dv + j] = av[c2] * Sprev[(int64_t)c2 * dv + j];
+                for (int j = 0; j < dv; ++j) {
+                    y[j] = 0.0;
+                    for (int c2 = 0; c2 < dk; ++c2)
+                        y[j] += kv[c2] * X[(int64_t)c2 * dv + j];
+                }
+                /* read-out: dq = S' do;  G += q do^T */
+                for (int c2 = 0; c2 < dk; ++c2) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        acc += Snew[(int64_t)c2 * dv + j] * dov[j];
+                        G[(int64_t)c2 * dv + j] += qv[c2] * dov[j];
+                    }
+                    dq[rk + c2] = acc;
+                }
+                /* write: gk = G^T k;  dv = beta gk;  dy = -beta gk;  dbeta = gk . (v - y) */
+                double db = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    gk[j] = 0.0;
+                    for (int c2 = 0; c2 < dk; ++c2)
+                        gk[j] += G[(int64_t)c2 * dv + j] * kv[c2];
+                    dv_out[rv + j] = bt * gk[j];
+                    dy[j] = -bt * gk[j];
+                    db += gk[j] * (vv[j] - y[j]);
+                }
+                dbeta[t * H + h] = db;
+                /* dk = beta G (v - y) + X dy;  dX = G + k dy^T */
+                for (int c2 = 0; c2 < dk; ++c2) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        acc += bt * G[(int64_t)c2 * dv + j] * (vv[j] - y[j]);
+                        acc += X[(int64_t)c2 * dv + j] * dy[j];
+                        G[(int64_t)c2 * dv + j] += kv[c2] * dy[j];
+                    }
+                    dk_out[rk + c2] = acc;
+                }
+                /* decay: dlog_alpha = sum_j dX X;  dS = Diag(a) dX */
+                for (int c2 = 0; c2 < dk; ++c2) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        acc += G[(int64_t)c2 * dv + j] * X[(int64_t)c2 * dv + j];
+                        G[(int64_t)c2 * dv + j] *= av[c2];
+                    }
+                    dla[rk + c2] = acc;
+                }
+            }
+        }
+        #undef KDA_LOAD_TOKEN
+        if (ds0)
+            memcpy(ds0 + ((int64_t)s * H + h) * SZ, G, sizeof(double) * (size_t)SZ);
+        free(ckpt); free(seg); free(G); free(X); free(vec);
+    }
+    return bad ? -1 : 0;
+}

@@ -21,6 +21,7 @@ Every pin is also run against deliberately broken copies of the oracle
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 from fractions import Fraction
 
@@ -427,9 +428,62 @@ def pin_pooled_tokens(orc):
     assert np.array_equal(got[[1, 4, 5]], pool[[1, 4, 5]])   # slots no sequence names
 
 
+# --------------------------------------------------------------------------
+# gradients: reverse mode against finite differences and an exact identity
+# --------------------------------------------------------------------------
+def _loss(orc, x, d_o, d_fin, **over):
+    a = dict(q=x.q, k=x.k, v=x.v, log_alpha=x.log_alpha, beta=x.beta,
+             initial_state=x.initial_state)
+    a.update(over)
+    o, fin = orc.prefill(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["initial_state"],
+                         x.cu_seqlens, num_seqs=x.num_seqs)
+    return float(np.sum(d_o * o) + np.sum(d_fin * fin))
+
+
+def pin_backward_finite_differences(orc):
+    """Every gradient entry of L = <dO, o> + <dS, S_T> against a central
+    difference of the forward oracle (fp32 inputs perturbed by 2^-12; the
+    step actually taken after fp32 rounding is the denominator)."""
+    x = _case(32, 0, 1, 4, 3, mu=1.0, lengths=[5, 3])
+    x = dataclasses.replace(x, v=(x.v * np.float32(0.5)).astype(np.float32))
+    g = np.random.default_rng(32)
+    d_o = g.standard_normal((x.T, x.H, x.dv))
+    d_fin = g.standard_normal((x.num_seqs, x.H, x.dk, x.dv))
+    gr = orc.backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.initial_state, x.cu_seqlens, d_o, d_fin)
+    h = 2.0 ** -12
+    for name, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_alpha", "dlog_alpha"),
+                      ("beta", "dbeta"), ("initial_state", "dinitial_state")):
+        base = getattr(x, name)
+        fd = np.zeros(base.shape)
+        for idx in np.ndindex(base.shape):
+            plus, minus = base.copy(), base.copy()
+            plus[idx] = np.float32(base[idx] + h)
+            minus[idx] = np.float32(base[idx] - h)
+            step = float(plus[idx]) - float(minus[idx])
+            fd[idx] = (_loss(orc, x, d_o, d_fin, **{name: plus}) -
+                       _loss(orc, x, d_o, d_fin, **{name: minus})) / step
+        assert rel_err(gr[key], fd) < 1e-5, (name, rel_err(gr[key], fd))
+
+
+def pin_backward_linear_part(orc):
+    """o and S_T are linear in (S0, V) for fixed q, k, alpha, beta, so
+    L(S0, V) = <dL/dS0, S0> + <dL/dV, V> exactly (Euler's identity)."""
+    x = _case(33, 0, 2, 6, 5, mu=1.0, lengths=[9, 0, 14])
+    g = np.random.default_rng(33)
+    d_o = g.standard_normal((x.T, x.H, x.dv))
+    d_fin = g.standard_normal((x.num_seqs, x.H, x.dk, x.dv))
+    gr = orc.backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.initial_state, x.cu_seqlens, d_o, d_fin)
+    L = _loss(orc, x, d_o, d_fin)
+    euler = float(np.sum(gr["dinitial_state"] * x.initial_state) + np.sum(gr["dv"] * x.v))
+    assert abs(L - euler) <= 1e-12 * max(1.0, abs(L)), (L, euler)
+    # an empty sequence passes its final-state gradient straight through
+    assert np.array_equal(gr["dinitial_state"][1], d_fin[1])
+
+
 ALL_PINS = [pin_transition_product, pin_exact_rational, pin_identity_no_write, pin_pure_decay,
             pin_deltanet, pin_gated_deltanet, pin_exact_recall, pin_one_hot_linear_attention,
             pin_one_hot_rows, pin_single_token, pin_chunkwise_algebra, pin_chunk_transition_form,
             pin_packing,
             pin_decode_matches_prefill, pin_linearity, pin_non_expansive,
-            pin_state_snapshots, pin_qk_l2_normalisation, pin_beta_logit, pin_pooled_tokens]
+            pin_state_snapshots, pin_qk_l2_normalisation, pin_beta_logit, pin_pooled_tokens,
+            pin_backward_finite_differences, pin_backward_linear_part]

@@ -31,6 +31,14 @@ MUTANTS = [
     ("sigmoid sign", "b = 1.0 / (1.0 + exp(-b));", "b = 1.0 / (1.0 + exp(b));"),
     ("snapshot one token late", "(t - t0) % every == 0", "(t - t0) % every == 1 % every"),
     ("snapshot rows", "snap_base[s + 1] = snap_base[s] +", "snap_base[s + 1] = snap_base[s] * 0 +"),
+    ("backward: key term of the correction dropped", "acc += X[(int64_t)c2 * dv + j] * dy[j];", "acc += 0.0 * dy[j];"),
+    ("backward: decay gradient from the undecayed state", "acc += G[(int64_t)c2 * dv + j] * X[(int64_t)c2 * dv + j];",
+     "acc += G[(int64_t)c2 * dv + j] * Sprev[(int64_t)c2 * dv + j];"),
+    ("backward: decay not applied to the carried gradient", "G[(int64_t)c2 * dv + j] *= av[c2];", "G[(int64_t)c2 * dv + j] *= 1.0;"),
+    ("backward: correction sign", "dy[j] = -bt * gk[j];", "dy[j] = bt * gk[j];"),
+    ("backward: read-out from the pre-update state", "acc += Snew[(int64_t)c2 * dv + j] * dov[j];",
+     "acc += Sprev[(int64_t)c2 * dv + j] * dov[j];"),
+    ("backward: beta gradient without the prediction", "db += gk[j] * (vv[j] - y[j]);", "db += gk[j] * vv[j];"),
 ]
 
 
