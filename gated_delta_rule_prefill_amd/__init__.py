@@ -4,8 +4,10 @@ decode behind the C ABI of ``include/kda.h`` (libkda.so, HIP for gfx950).
 ``prefill``, ``decode_step`` and ``decode_tokens`` marshal torch tensors to the library; the
 library must be built (``python -m gated_delta_rule_prefill_amd.build``).
 """
-from .kda import (KDAError, decode_step, decode_tokens, num_chunk_states,  # noqa: F401
-                  prefill, prefill_kernel_times, set_kernel_timing, workspace_bytes)
+from .kda import (KDAError, backward, backward_workspace_bytes, decode_step,  # noqa: F401
+                  decode_tokens, num_chunk_states, prefill, prefill_kernel_times,
+                  set_kernel_timing, workspace_bytes)
 
-__all__ = ["prefill", "decode_step", "decode_tokens", "num_chunk_states", "workspace_bytes",
-           "KDAError", "set_kernel_timing", "prefill_kernel_times"]
+__all__ = ["prefill", "decode_step", "decode_tokens", "backward", "num_chunk_states",
+           "workspace_bytes", "backward_workspace_bytes", "KDAError", "set_kernel_timing",
+           "prefill_kernel_times"]

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 ARCH = "gfx950"
 KERNEL_SOURCES = ["chunk_table.hip", "prefill_intra.hip", "prefill_state.hip", "prefill_output.hip",
-                  "decode.hip", "recurrent.hip"]
+                  "decode.hip", "recurrent.hip", "backward.hip"]
 HOST_SOURCES = ["kda_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", CSRC, "-I", INCLUDE]
@@ -35,10 +35,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: libkda needs the ROCm toolchain")
 
 
+# Per-source extra flags.  backward.hip: with packed fp32 switched off, the
+# SLP vectoriser's v2f32 conversions trip instruction selection (a compiler
+# crash); that file's kernels gain nothing from it anyway.
+EXTRA = {"backward.hip": ["-fno-slp-vectorize"]}
+
+
 def _compile(src: str, device: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [hipcc()] + COMMON + (DEVICE + ["-x", "hip"] if device else []) + \
-        ["-c", os.path.join(CSRC, src), "-o", obj]
+        EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

@@ -59,6 +59,34 @@ bool make_plan(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtyp
 
 bool supported_dim(int32_t d) { return d == 64 || d == 128; }
 
+// Workspace of one backward call: the forward plan (chunk table, records and
+// chunk-start operand states for a recomputation), then the recomputed fp32
+// chunk states, an output scratch for the recomputation, the per-slice
+// partial gradients and the per-workgroup scratch.
+struct BwdPlan {
+    Plan fwd;
+    size_t off_cs = 0, off_o = 0, off_part = 0, off_scratch = 0, total = 0;
+};
+
+bool make_bwd_plan(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype,
+                   BwdPlan& b) {
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return false;
+    if (!make_plan(T, N, H, dk, dv, dtype, b.fwd)) return false;
+    if (!supported_dim(dk) || !supported_dim(dv)) return false;
+    const int es = dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    size_t at = b.fwd.total;
+    b.off_cs = at;
+    at += align256((size_t)b.fwd.max_chunks * H * dk * dv * 4);
+    b.off_o = at;
+    at += align256((size_t)T * H * dv * es);
+    b.off_part = at;
+    at += align256(kda::backward_partial_bytes(T, H, dk, dv));
+    b.off_scratch = at;
+    at += align256(kda::backward_scratch_bytes(N, H, dk, dv));
+    b.total = at;
+    return true;
+}
+
 constexpr uint32_t kFlagMask = KDA_FLAG_L2NORM_QK | KDA_FLAG_BETA_SIGMOID;
 
 unsigned pre_flags(uint32_t flags) {
@@ -235,6 +263,111 @@ kda_status kda_prefill_ex(const void* q, const void* k, const void* v, const flo
         return st;
     } catch (...) {
         return fail(KDA_ERR_HIP, "unexpected C++ exception inside kda_prefill");
+    }
+}
+
+size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                    int32_t dk, int32_t dv, kda_dtype dtype) {
+    BwdPlan b;
+    if (!make_bwd_plan(total_tokens, num_seqs, H, dk, dv, dtype, b)) return 0;
+    return b.total;
+}
+
+kda_status kda_backward(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                        int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk, int32_t dv,
+                        kda_dtype dtype, const void* d_o, const float* d_final_state,
+                        const float* chunk_states, void* dq, void* dk_out, void* dv_out,
+                        float* dlog_alpha, float* dbeta, float* d_initial_state, void* workspace,
+                        size_t workspace_bytes, void* stream_ptr) {
+    try {
+        if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_DTYPE_F32 or KDA_DTYPE_BF16");
+        if (num_seqs <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1");
+        if (H <= 0 || H > 65535) return fail(KDA_ERR_INVALID_ARGUMENT, "H must be in [1, 65535]");
+        if (total_tokens < 0 || total_tokens >= ((int64_t)1 << 31) - 2 * kda::CHUNK)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "total_tokens must be in [0, 2^31 - 128)");
+        if (!supported_dim(dk) || !supported_dim(dv))
+            return fail(KDA_ERR_UNSUPPORTED, "dk and dv must each be 64 or 128");
+        if (!cu_seqlens && total_tokens % num_seqs != 0)
+            return fail(KDA_ERR_INVALID_ARGUMENT,
+                        "without cu_seqlens, total_tokens must be a multiple of num_seqs");
+        if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !d_o || !dq || !dk_out ||
+                                 !dv_out || !dlog_alpha || !dbeta))
+            return fail(KDA_ERR_INVALID_ARGUMENT,
+                        "inputs, d_o and the gradient outputs must be non-NULL");
+        const void* ptrs[] = {q, k, v, log_alpha, beta, initial_state, cu_seqlens, d_o,
+                              d_final_state, chunk_states, dq, dk_out, dv_out, dlog_alpha, dbeta,
+                              d_initial_state, workspace};
+        for (const void* p : ptrs)
+            if (p && !aligned16(p))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "every pointer must be 16-byte aligned");
+        if (!workspace && workspace_bytes != 0)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "workspace_bytes given without a workspace");
+        BwdPlan b;
+        if (!make_bwd_plan(total_tokens, num_seqs, H, dk, dv, dtype, b))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "invalid sizes");
+        const Plan& plan = b.fwd;
+        if (plan.max_chunks > 0x7fffffffLL / 2 || plan.max_chunks * H > 0x7fffffffLL ||
+            (long long)num_seqs * H * (dv / 16) > 0x7fffffffLL)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "sizes too large");
+        if (workspace && workspace_bytes < b.total)
+            return fail(KDA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(b.total) +
+                                               " bytes");
+
+        hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+        const bool bf16 = dtype == KDA_DTYPE_BF16;
+        unsigned char* ws = static_cast<unsigned char*>(workspace);
+        bool owned = false;
+        if (!ws) {
+            hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), b.total, stream);
+            if (e != hipSuccess)
+                return fail(KDA_ERR_HIP, std::string("hipMallocAsync: ") + hipGetErrorString(e));
+            owned = true;
+        }
+        int32_t* seq_start = reinterpret_cast<int32_t*>(ws + plan.off_seq);
+        kda::ChunkInfo* chunks = reinterpret_cast<kda::ChunkInfo*>(ws + plan.off_chunks);
+        kda::ChunkSrc src{chunks, seq_start, cu_seqlens ? -1 : (int)(total_tokens / num_seqs),
+                          num_seqs};
+        kda_status st = KDA_OK;
+        if (cu_seqlens)
+            st = check_launch(kda::launch_chunk_table(cu_seqlens, total_tokens, num_seqs, seq_start,
+                                                      chunks, (int)plan.max_chunks, stream),
+                              "chunk table kernel", stream);
+        const float* cs = chunk_states;
+        if (st == KDA_OK && !cs && total_tokens > 0) {
+            // forward recomputation: records, then the chain with its chunk states
+            float* own_cs = reinterpret_cast<float*>(ws + b.off_cs);
+            void* o_scratch = ws + b.off_o;
+            void* states = plan.output_pass ? (void*)(ws + plan.off_states) : nullptr;
+            st = check_launch(kda::launch_prefill_intra(q, k, v, log_alpha, beta, src,
+                                                        (int)plan.max_chunks, H, dk, dv, bf16, 0u,
+                                                        ws, stream),
+                              "intra-chunk kernel", stream);
+            if (st == KDA_OK)
+                st = check_launch(kda::launch_prefill_state(ws, src, initial_state, nullptr,
+                                                            o_scratch, states, own_cs, H, dk, dv,
+                                                            bf16, stream),
+                                  "state kernel", stream);
+            cs = own_cs;
+        }
+        if (st == KDA_OK)
+            st = check_launch(kda::launch_backward(q, k, v, log_alpha, beta, src, cs, d_o,
+                                                   d_final_state, H, total_tokens, dk, dv, bf16, dq,
+                                                   dk_out, dv_out, dlog_alpha, dbeta,
+                                                   d_initial_state,
+                                                   reinterpret_cast<float*>(ws + b.off_part),
+                                                   reinterpret_cast<float*>(ws + b.off_scratch),
+                                                   stream),
+                              "backward kernels", stream);
+        if (owned) {
+            hipError_t e = hipFreeAsync(ws, stream);
+            if (st == KDA_OK && e != hipSuccess)
+                st = fail(KDA_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
+        }
+        return st;
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected C++ exception inside kda_backward");
     }
 }
 

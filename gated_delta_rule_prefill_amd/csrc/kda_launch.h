@@ -91,6 +91,18 @@ hipError_t launch_recurrent(float* pool, int num_slots, const int32_t* slots, co
                             const int32_t* cu, int rows, int N, int H, int dk, int dv,
                             bool bf16_io, unsigned flags, void* o, hipStream_t stream);
 
+// Gradients of the recurrence (see backward.hip).  chunk_states: the fp32
+// state entering every chunk, as kda_prefill_ex exports them.  part: the
+// backward_partial_bytes() area; scratch: backward_scratch_bytes().
+size_t backward_partial_bytes(int64_t T, int H, int dk, int dv);
+size_t backward_scratch_bytes(int N, int H, int dk, int dv);
+hipError_t launch_backward(const void* q, const void* k, const void* v, const float* la,
+                           const float* beta, ChunkSrc src, const float* chunk_states,
+                           const void* d_o, const float* d_final, int H, int64_t T, int dk, int dv,
+                           bool bf16_io, void* dq, void* dk_out, void* dv_out, float* dla,
+                           float* dbeta, float* d_initial, float* part, float* scratch,
+                           hipStream_t stream);
+
 hipError_t launch_decode_step(float* state, const void* q, const void* k, const void* v,
                               const float* la, const float* beta, void* o, int units, int dk,
                               int dv, bool bf16_io, hipStream_t stream);

@@ -33,6 +33,10 @@ SIGNATURES = {
     "kda_decode_tokens": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                          _i32, _i32, _i32, _i32, ctypes.c_int, ctypes.c_uint32,
                                          _vp, _vp]),
+    "kda_backward_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, ctypes.c_int]),
+    "kda_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                    _i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _vp, _sz, _vp]),
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_last_error_message": (ctypes.c_char_p, []),
     "kda_version": (_i32, []),
@@ -251,6 +255,65 @@ def decode_tokens(state_pool, q, k, v, log_alpha, beta, state_indices=None, cu_s
                                  H, dk, dv, _dtype_code(q), _flags(l2norm_qk, beta_sigmoid),
                                  _ptr(out), _stream(dev, stream))
     _check(st, "kda_decode_tokens")
+    return out
+
+
+def backward_workspace_bytes(total_tokens: int, num_seqs: int, H: int, dk: int, dv: int,
+                             bf16: bool) -> int:
+    return int(lib().kda_backward_workspace_bytes(int(total_tokens), int(num_seqs), int(H),
+                                                  int(dk), int(dv),
+                                                  KDA_DTYPE_BF16 if bf16 else KDA_DTYPE_F32))
+
+
+def backward(q, k, v, log_alpha, beta, d_o, initial_state=None, cu_seqlens=None,
+             num_seqs: Optional[int] = None, d_final_state=None, chunk_states=None,
+             need_initial_state_grad: bool = True, workspace=None, stream=None) -> dict:
+    """Gradients of ``prefill`` (``kda_backward``): for dL/do = d_o and
+    dL/dfinal_state = d_final_state (or zero) returns dq, dk, dv (q/k/v dtype),
+    dlog_alpha, dbeta and dinitial_state (fp32).  chunk_states: the forward's
+    exported chunk states, or None to recompute them."""
+    import torch
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is not None:
+        _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1, "cu_seqlens: int32 [N+1]")
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = int(num_seqs or 1)
+    dev = q.device
+    for name, t, shape, dt in (("k", k, (T, H, dk), q.dtype), ("v", v, (T, H, dv), q.dtype),
+                               ("log_alpha", log_alpha, (T, H, dk), torch.float32),
+                               ("beta", beta, (T, H), torch.float32),
+                               ("d_o", d_o, (T, H, dv), q.dtype)):
+        _require(tuple(t.shape) == shape, f"{name}: expected shape {shape}, got {tuple(t.shape)}")
+        _require(t.dtype == dt, f"{name}: expected dtype {dt}, got {t.dtype}")
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _require(tuple(t.shape) == (N, H, dk, dv) and t.dtype == torch.float32,
+                     f"{name}: fp32 [N, H, dk, dv]")
+    if chunk_states is not None:
+        _require(chunk_states.dtype == torch.float32 and
+                 chunk_states.numel() >= num_chunk_states(T, N, cu_seqlens) * H * dk * dv,
+                 "chunk_states: fp32 [NC, H, dk, dv]")
+    for t in (q, k, v, log_alpha, beta, d_o, initial_state, cu_seqlens, d_final_state, chunk_states):
+        if t is not None:
+            _require(t.device == dev and t.is_contiguous(), "all inputs: contiguous, on one device")
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dlog_alpha=torch.empty_like(log_alpha), dbeta=torch.empty_like(beta),
+               dinitial_state=torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+               if need_initial_state_grad else None)
+    need = backward_workspace_bytes(T, N, H, dk, dv, q.dtype == torch.bfloat16)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _require(workspace.numel() * workspace.element_size() >= need, "workspace too small")
+    st = lib().kda_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                            _ptr(initial_state), _ptr(cu_seqlens), T, N, H, dk, dv,
+                            _dtype_code(q), _ptr(d_o), _ptr(d_final_state), _ptr(chunk_states),
+                            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                            _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]),
+                            _ptr(out["dinitial_state"]), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    _check(st, "kda_backward")
     return out
 
 

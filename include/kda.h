@@ -176,6 +176,50 @@ kda_status kda_decode_tokens(float *state_pool, int32_t num_slots, const int32_t
                              int32_t H, int32_t dk, int32_t dv, kda_dtype dtype,
                              uint32_t flags, void *o, void *stream);
 
+/*
+ * Device workspace kda_backward needs for these sizes (bytes, 256-aligned;
+ * 0 for invalid sizes).  It covers a forward recomputation of the chunk
+ * states (used when the caller passes none), per-slice partial gradients and
+ * per-workgroup scratch.
+ */
+size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                    int32_t dk, int32_t dv, kda_dtype dtype);
+
+/*
+ * Gradients of kda_prefill (the recurrence of paper notes section 2; the
+ * FLA implementation the pages describe trains through the chunkwise form
+ * with a backward pass, section 3).  For a loss L with dL/do = d_o and
+ * dL/dfinal_state = d_final_state it writes dL/dq, dL/dk, dL/dv, dL/dlog_alpha,
+ * dL/dbeta and dL/dinitial_state.
+ *
+ *   q, k, v, log_alpha, beta, initial_state, cu_seqlens, total_tokens,
+ *   num_seqs, H, dk, dv, dtype   as for kda_prefill (the forward's inputs;
+ *                 no preprocessing flags: the gradients are with respect to
+ *                 the q, k and beta the recurrence sees)
+ *   d_o           [T,H,dv] dtype (device, read)
+ *   d_final_state [N,H,dk,dv] fp32, or NULL = zero
+ *   chunk_states  the forward's chunk states as kda_prefill_ex writes them
+ *                 ([NC,H,dk,dv] fp32), or NULL: recomputed here
+ *   dq, dk_out    [T,H,dk] dtype; dv_out [T,H,dv] dtype (device, written)
+ *   dlog_alpha    [T,H,dk] fp32; dbeta [T,H] fp32 (device, written)
+ *   d_initial_state [N,H,dk,dv] fp32 (device, written), or NULL
+ *   workspace     at least kda_backward_workspace_bytes(), or NULL with 0
+ *                 (then allocated stream-ordered on `stream`)
+ * Outputs must not alias inputs.  The result is deterministic.  The state is
+ * walked token by token backwards (recomputed forward from the chunk states,
+ * 8 tokens at a time): sequences are processed in parallel, their tokens in
+ * order.
+ */
+kda_status kda_backward(const void *q, const void *k, const void *v,
+                        const float *log_alpha, const float *beta,
+                        const float *initial_state, const int32_t *cu_seqlens,
+                        int64_t total_tokens, int32_t num_seqs, int32_t H,
+                        int32_t dk, int32_t dv, kda_dtype dtype,
+                        const void *d_o, const float *d_final_state, const float *chunk_states,
+                        void *dq, void *dk_out, void *dv_out, float *dlog_alpha, float *dbeta,
+                        float *d_initial_state, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
 /* Static description of a status code. */
 const char *kda_status_string(kda_status status);
 

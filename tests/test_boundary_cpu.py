@@ -167,3 +167,35 @@ def _decode_tokens(**kw):
 ])
 def test_decode_tokens_rejects_before_any_hip_call(kw, status):
     assert _decode_tokens(**kw) == status
+
+
+def _backward(**kw):
+    args = dict(q=A, k=A, v=A, la=A, beta=A, s0=None, cu=None, T=128, N=1, H=2, dk=64, dv=64,
+                dtype=kda.KDA_DTYPE_BF16, do=A, dfin=None, cs=None, dq=A, dk_=A, dv_=A, dla=A,
+                db=A, ds0=None, ws=A, wsb=1 << 40, stream=None)
+    args.update(kw)
+    a = args
+    return kda.lib().kda_backward(a["q"], a["k"], a["v"], a["la"], a["beta"], a["s0"], a["cu"],
+                                  a["T"], a["N"], a["H"], a["dk"], a["dv"], a["dtype"], a["do"],
+                                  a["dfin"], a["cs"], a["dq"], a["dk_"], a["dv_"], a["dla"],
+                                  a["db"], a["ds0"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(T=129, N=2), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(do=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dla=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(cs=A + 4), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=5), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(wsb=64), kda.KDA_ERR_WORKSPACE),
+])
+def test_backward_rejects_before_any_hip_call(kw, status):
+    assert _backward(**kw) == status
+
+
+def test_backward_workspace_bytes():
+    w = kda.backward_workspace_bytes(4096, 1, 32, 128, 128, True)
+    assert w >= kda.workspace_bytes(4096, 1, 32, 128, 128, True) and w % 256 == 0
+    assert kda.backward_workspace_bytes(10, 0, 1, 64, 64, False) == 0
