@@ -294,10 +294,30 @@ def main():
                         "fp32 states in permuted slots", "us_per_call": round(rec_us, 2),
             "algorithmic_bytes": rec_bytes, "achieved_GBs": round(rec_gbs, 1),
             "frac_of_hbm_peak": round(rec_gbs / HBM_PEAK_GBS, 4)}
+        # backward of the prefill workload from the exported chunk states
+        g = np.random.default_rng(11)
+        d_o = dq(gen.bf16_bits(g.standard_normal((T, H, dv)).astype(np.float32)))
+        s0set = sets[0]
+        bws = torch.empty(kdalib.backward_workspace_bytes(T, 1, H, dk, dv, True), dtype=torch.uint8,
+                          device=dev)
+        kdalib.prefill(s0set["q"], s0set["k"], s0set["v"], s0set["la"], s0set["beta"], None, None,
+                       num_seqs=1, final_state=fin, out=out[0], workspace=ws, chunk_states=cs)
+
+        def step_bwd(i):
+            kdalib.backward(s0set["q"], s0set["k"], s0set["v"], s0set["la"], s0set["beta"], d_o,
+                            chunk_states=cs, need_initial_state_grad=False, workspace=bws)
+        bwd_us = timed(step_bwd, max(3, reps // 10))
+        bwd_bytes = (PATH_BYTES_PER_TOKEN_HEAD + 768 + 512 + 4) * token_heads
+        options["backward"] = {
+            "workload": "gradients of the prefill workload (T=4096, H=32, d=128, bf16) from its "
+                        "exported chunk states", "us_per_call": round(bwd_us, 1),
+            "tokens_per_s": round(T / (bwd_us * 1e-6), 1),
+            "algorithmic_bytes": bwd_bytes,
+            "achieved_GBs": round(bwd_bytes / (bwd_us * 1e-6) / 1e9, 1)}
         log(f"[bench] options: chunk states {cs_us:.1f} us (+{cs_us - base_us:.1f}), "
             f"preprocessing {pre_us:.1f} us (plain {plain_us:.1f}), "
-            f"decode_tokens 256x8 {rec_us:.1f} us = {rec_gbs:.0f} GB/s")
-        del pool, cs
+            f"decode_tokens 256x8 {rec_us:.1f} us = {rec_gbs:.0f} GB/s, backward {bwd_us:.0f} us")
+        del pool, cs, bws
 
     if args.copy_calib:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -20,59 +20,50 @@
 //
 // One workgroup of 4 waves per (sequence, head, 16 value columns): the
 // columns of S and G evolve independently, so a head splits into DV/16
-// chains.  Wave w owns key rows RW*w .. RW*w + RW - 1 (RW = DK/4); lane l
-// holds row RW*w + l % RW and CPL = RW/4 consecutive columns of group
-// l / RW.  The products over key rows (y, dnu) are reduced across the
-// workgroup every token; the sums over value columns (dq, dk, dlog_alpha,
-// dbeta) are partial per workgroup and summed over the column slices by a
-// second kernel in a fixed order, so the result is deterministic.
+// chains.  Wave w owns 4 of the 16 columns for every key row (lane l: rows
+// RPL*l .. RPL*l + RPL - 1, RPL = DK/64), so the products over key rows
+// (y, dnu) are reduced inside the wave, with no barrier per token.  The sums
+// over value columns (dq, dk, dlog_alpha, dbeta) are combined over the 4
+// waves through LDS once per 8-token piece, giving one partial per
+// workgroup; a second kernel sums the DV/16 partials in a fixed order, so
+// the result is deterministic.
 #include "kda_common.h"
 
 namespace kda {
 
 constexpr int BWD_COLS = 16;   // value columns per workgroup
+constexpr int BWD_CW = 4;      // value columns per wave
 constexpr int BWD_PIECE = 8;   // tokens per recomputed piece
 constexpr int BWD_PIECES = CHUNK / BWD_PIECE;
 
-template <int DK>
-struct BwdCfg {
-    static constexpr int RW = DK / 4;          // key rows per wave
-    static constexpr int GROUPS = 64 / RW;     // column groups per wave
-    static constexpr int CPL = BWD_COLS / GROUPS;   // columns per lane
-    static_assert(CPL * GROUPS == BWD_COLS && CPL == RW / 4, "lane split");
-};
-
-// In-wave sum over the RW lanes of a column group (lane bits below log2(RW))
-// of CPL values at once: lane l ends with the total of value (l >> 2) % CPL.
-template <int RW, int CPL>
-__device__ __forceinline__ float group_col_sum(const float (&a)[CPL], int lane) {
-    float cur[CPL];
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) cur[e] = a[e];
-    int n = CPL;
-#pragma unroll
-    for (int m = RW / 2; m >= 1; m >>= 1) {
-        if (n > 1) {
-            const bool hi = lane & m;
-#pragma unroll
-            for (int j = 0; j < CPL / 2; ++j)
-                if (j < n / 2)
-                    cur[j] = (hi ? cur[n / 2 + j] : cur[j]) + __shfl_xor(hi ? cur[j] : cur[n / 2 + j], m);
-            n >>= 1;
-        } else {
-            cur[0] += __shfl_xor(cur[0], m);
-        }
-    }
-    return cur[0];
+// Value of lane l ^ M: quad permutations and the row rotation by 8 through
+// DPP, xor 4 and 16 through a swizzle, 32 through a permute.
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+    const int v = __builtin_bit_cast(int, x);
+    int r;
+    if constexpr (M == 1) r = __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);        // quad_perm 1,0,3,2
+    else if constexpr (M == 2) r = __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    else if constexpr (M == 8) r = __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false);  // row_ror 8
+    else if constexpr (M == 4 || M == 16) r = __builtin_amdgcn_ds_swizzle(v, 0x1F | (M << 10));
+    else r = __builtin_bit_cast(int, __shfl_xor(x, M));
+    return __builtin_bit_cast(float, r);
 }
 
-// Sum over the column groups of one row (lanes l, l + RW, ...): every lane of
-// the row gets the total.
-template <int RW>
-__device__ __forceinline__ float row_sum(float x) {
+// Totals over the 64 lanes of 4 values per lane (a transposing butterfly:
+// the first two exchanges also halve the values), returned uniform.
+__device__ __forceinline__ void wave_sum4(const float (&a)[4], int lane, float (&t)[4]) {
+    const bool h5 = lane & 32, h4 = lane & 16;
+    const float b0 = (h5 ? a[2] : a[0]) + lane_xor<32>(h5 ? a[0] : a[2]);
+    const float b1 = (h5 ? a[3] : a[1]) + lane_xor<32>(h5 ? a[1] : a[3]);
+    float c = (h4 ? b1 : b0) + lane_xor<16>(h4 ? b0 : b1);
+    c += lane_xor<8>(c);
+    c += lane_xor<4>(c);
+    c += lane_xor<2>(c);
+    c += lane_xor<1>(c);
+    // lane 16 i now holds the total of value i
 #pragma unroll
-    for (int m = RW; m < 64; m <<= 1) x += __shfl_xor(x, m);
-    return x;
+    for (int i = 0; i < 4; ++i) t[i] = read_lane(c, 16 * i);
 }
 
 template <typename E, int DK, int DV>
@@ -84,59 +75,56 @@ __global__ __launch_bounds__(256) void backward_kernel(
     E* __restrict__ dv_out, float* __restrict__ part, float* __restrict__ part_beta,
     float* __restrict__ d_initial, float* __restrict__ scratch)
 {
-    using C = BwdCfg<DK>;
-    constexpr int RW = C::RW, CPL = C::CPL, NSL = DV / BWD_COLS;
+    constexpr int RPL = DK / 64, NSL = DV / BWD_COLS, CW = BWD_CW;
+    constexpr int NV = RPL * CW;   // state values per lane
     __shared__ float sQ[CHUNK][DK], sK[CHUNK][DK], sA[CHUNK][DK];
     __shared__ __attribute__((aligned(16))) float sV[CHUNK][BWD_COLS], sDO[CHUNK][BWD_COLS];
     __shared__ float sB[CHUNK];
-    __shared__ float sNu[BWD_PIECE][BWD_COLS], sY[BWD_PIECE][BWD_COLS];
-    __shared__ float red[2][4][BWD_COLS];
+    __shared__ float comb[BWD_PIECE][4][3][DK];   // per-wave row sums of a piece: dq, dk, dlog_alpha
+    __shared__ float combB[BWD_PIECE][4];
 
     const int slice = blockIdx.x % NSL;
     const int pair = blockIdx.x / NSL;   // sequence * H + head
     const int s = pair / H, h = pair % H;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int row = RW * wave + (lane % RW);
-    const int cg = lane / RW;
-    const int col0 = cg * CPL;              // first column of this lane inside the slice
-    const int j0 = slice * BWD_COLS;        // first value column of the slice
-    const int idx = (lane >> 2) % CPL;      // column this lane's group sums end on
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int r0 = RPL * lane;                 // first key row of this lane
+    const int cw0 = wave * CW;                 // first column of this wave inside the slice
+    const int j0 = slice * BWD_COLS + cw0;     // first value column of this wave
     int c_begin, n;
     seq_chunks(src, s, c_begin, n);
 
     // this workgroup's scratch: [piece][value][thread] (each thread its own values)
-    float* const scr = scratch + (size_t)blockIdx.x * BWD_PIECES * CPL * 256;
-    float G[CPL];
+    float* const scr = scratch + (size_t)blockIdx.x * BWD_PIECES * NV * 256;
+    float G[RPL][CW];
 #pragma unroll
-    for (int e = 0; e < CPL; ++e)
-        G[e] = d_final ? d_final[((size_t)pair * DK + row) * DV + j0 + col0 + e] : 0.f;
+    for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+        for (int e = 0; e < CW; ++e)
+            G[rr][e] = d_final ? d_final[((size_t)pair * DK + r0 + rr) * DV + j0 + e] : 0.f;
 
-    int rb = 0;   // reduction buffer toggle: a buffer is rewritten two reductions later
-    // sum over all key rows of CPL per-lane values; returns the lane's CPL column totals
-    auto col_reduce = [&](const float (&a)[CPL], float (&out)[CPL]) {
-        const float t = group_col_sum<RW, CPL>(a, lane);
-        if ((lane & 3) == 0) red[rb][wave][col0 + idx] = t;
-        __syncthreads();
+    // one forward token (index i of the staged chunk) on S; y and nu (uniform) returned
+    auto fwd = [&](float (&S)[RPL][CW], int i, float (&y)[CW], float (&nu)[CW]) {
+        float pp[CW];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e)
-            out[e] = red[rb][0][col0 + e] + red[rb][1][col0 + e] + red[rb][2][col0 + e] + red[rb][3][col0 + e];
-        rb ^= 1;
-    };
-    // one forward token (index i of the staged chunk) on S; y and nu returned
-    auto fwd = [&](float (&S)[CPL], int i, float (&y)[CPL], float (&nu)[CPL]) {
-        const float a = sA[i][row], kc = sK[i][row];
-        float pp[CPL];
+        for (int e = 0; e < CW; ++e) pp[e] = 0.f;
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            S[e] *= a;
-            pp[e] = kc * S[e];
+        for (int rr = 0; rr < RPL; ++rr) {
+            const float a = sA[i][r0 + rr], kc = sK[i][r0 + rr];
+#pragma unroll
+            for (int e = 0; e < CW; ++e) {
+                S[rr][e] *= a;
+                pp[e] += kc * S[rr][e];
+            }
         }
-        col_reduce(pp, y);
+        wave_sum4(pp, lane, y);
         const float b = sB[i];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            nu[e] = b * (sV[i][col0 + e] - y[e]);
-            S[e] += kc * nu[e];
+        for (int e = 0; e < CW; ++e) nu[e] = b * (sV[i][cw0 + e] - y[e]);
+#pragma unroll
+        for (int rr = 0; rr < RPL; ++rr) {
+            const float kc = sK[i][r0 + rr];
+#pragma unroll
+            for (int e = 0; e < CW; ++e) S[rr][e] += kc * nu[e];
         }
     };
 
@@ -154,7 +142,7 @@ __global__ __launch_bounds__(256) void backward_kernel(
         }
         for (int x = tid; x < CHUNK * BWD_COLS; x += 256) {
             const int i = x / BWD_COLS, j = x % BWD_COLS;
-            const size_t at = ((size_t)(ci.start + min(i, L - 1)) * H + h) * DV + j0 + j;
+            const size_t at = ((size_t)(ci.start + min(i, L - 1)) * H + h) * DV + slice * BWD_COLS + j;
             sV[i][j] = to_f32(v[at]);
             sDO[i][j] = to_f32(d_o[at]);
         }
@@ -164,17 +152,21 @@ __global__ __launch_bounds__(256) void backward_kernel(
         // ---- first sweep: the state entering every piece, to scratch ----
         const int npieces = (L + BWD_PIECE - 1) / BWD_PIECE;
         {
-            float S[CPL];
-            const float* cs = chunk_states + ((size_t)(c_begin + c) * H + h) * DK * DV + (size_t)row * DV + j0 + col0;
+            float S[RPL][CW];
+            const float* cs = chunk_states + ((size_t)(c_begin + c) * H + h) * DK * DV + (size_t)r0 * DV + j0;
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) S[e] = cs[e];
+            for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+                for (int e = 0; e < CW; ++e) S[rr][e] = cs[(size_t)rr * DV + e];
             for (int p = 0; p < npieces; ++p) {
 #pragma unroll
-                for (int e = 0; e < CPL; ++e) scr[(p * CPL + e) * 256 + tid] = S[e];
+                for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+                    for (int e = 0; e < CW; ++e) scr[(p * NV + rr * CW + e) * 256 + tid] = S[rr][e];
                 if (p + 1 < npieces) {   // the last piece's successors are not needed
 #pragma unroll
                     for (int i = 0; i < BWD_PIECE; ++i) {
-                        float y[CPL], nu[CPL];
+                        float y[CW], nu[CW];
                         fwd(S, BWD_PIECE * p + i, y, nu);
                     }
                 }
@@ -184,84 +176,105 @@ __global__ __launch_bounds__(256) void backward_kernel(
         for (int p = npieces - 1; p >= 0; --p) {
             const int i0 = BWD_PIECE * p;
             const int np = min(BWD_PIECE, L - i0);
-            float Sp[BWD_PIECE][CPL];   // state before each token of the piece
+            float Sp[BWD_PIECE][RPL][CW];   // state before each token of the piece
+            float yP[BWD_PIECE][CW], nuP[BWD_PIECE][CW];
             {
-                float S[CPL];
+                float S[RPL][CW];
 #pragma unroll
-                for (int e = 0; e < CPL; ++e) S[e] = scr[(p * CPL + e) * 256 + tid];
+                for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+                    for (int e = 0; e < CW; ++e) S[rr][e] = scr[(p * NV + rr * CW + e) * 256 + tid];
 #pragma unroll
                 for (int i = 0; i < BWD_PIECE; ++i) {
                     if (i < np) {
 #pragma unroll
-                        for (int e = 0; e < CPL; ++e) Sp[i][e] = S[e];
-                        float y[CPL], nu[CPL];
-                        fwd(S, i0 + i, y, nu);
-                        if ((lane % RW) == 0 && wave == 0) {
+                        for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
-                            for (int e = 0; e < CPL; ++e) {
-                                sNu[i][col0 + e] = nu[e];
-                                sY[i][col0 + e] = y[e];
-                            }
-                        }
+                            for (int e = 0; e < CW; ++e) Sp[i][rr][e] = S[rr][e];
+                        fwd(S, i0 + i, yP[i], nuP[i]);
                     }
                 }
             }
-            __syncthreads();   // sNu / sY of the piece visible
 #pragma unroll
             for (int i = BWD_PIECE - 1; i >= 0; --i) {
                 if (i >= np) continue;
                 const int ti = i0 + i;
-                const size_t t = (size_t)ci.start + ti;
-                const float a = sA[ti][row], kc = sK[ti][row], qc = sQ[ti][row], b = sB[ti];
-                float X[CPL], dq = 0.f;
+                const float b = sB[ti];
+                float dov[CW], vr[CW];
 #pragma unroll
-                for (int e = 0; e < CPL; ++e) {
-                    X[e] = a * Sp[i][e];
-                    const float snew = X[e] + kc * sNu[i][col0 + e];
-                    const float d = sDO[ti][col0 + e];
-                    dq += snew * d;
-                    G[e] += qc * d;
+                for (int e = 0; e < CW; ++e) {
+                    dov[e] = sDO[ti][cw0 + e];
+                    vr[e] = sV[ti][cw0 + e] - yP[i][e];   // v - y
                 }
-                float gkp[CPL], gk[CPL];
+                float X[RPL][CW], dq[RPL], gkp[CW];
 #pragma unroll
-                for (int e = 0; e < CPL; ++e) gkp[e] = G[e] * kc;
-                col_reduce(gkp, gk);
-                float dbp = 0.f, dkp = 0.f, dlp = 0.f;
-                float dy[CPL];
+                for (int e = 0; e < CW; ++e) gkp[e] = 0.f;
 #pragma unroll
-                for (int e = 0; e < CPL; ++e) {
-                    const float r = sV[ti][col0 + e] - sY[i][col0 + e];
+                for (int rr = 0; rr < RPL; ++rr) {
+                    const float a = sA[ti][r0 + rr], kc = sK[ti][r0 + rr], qc = sQ[ti][r0 + rr];
+                    dq[rr] = 0.f;
+#pragma unroll
+                    for (int e = 0; e < CW; ++e) {
+                        X[rr][e] = a * Sp[i][rr][e];
+                        dq[rr] += (X[rr][e] + kc * nuP[i][e]) * dov[e];
+                        G[rr][e] += qc * dov[e];
+                        gkp[e] += G[rr][e] * kc;
+                    }
+                }
+                float gk[CW], dy[CW];
+                wave_sum4(gkp, lane, gk);
+                float db = 0.f;
+#pragma unroll
+                for (int e = 0; e < CW; ++e) {
                     dy[e] = -b * gk[e];
-                    dbp += gk[e] * r;
-                    dkp += b * G[e] * r + X[e] * dy[e];
-                    G[e] += kc * dy[e];
-                    dlp += G[e] * X[e];
-                    G[e] *= a;
+                    db += gk[e] * vr[e];
                 }
-                dq = row_sum<RW>(dq);
-                dkp = row_sum<RW>(dkp);
-                dlp = row_sum<RW>(dlp);
-                dbp = row_sum<RW>(dbp);   // every row holds the slice's dbeta partial
-                float* pr = part + (((size_t)slice * T + t) * H + h) * DK;
-                const size_t plane = (size_t)NSL * T * H * DK;
-                if (cg == 0) {
-                    pr[row] = dq;
-                    pr[plane + row] = dkp;
-                    pr[2 * plane + row] = dlp;
-                }
-                if (wave == 0 && lane == 0) part_beta[((size_t)slice * T + t) * H + h] = dbp;
-                if (wave == 0 && (lane % RW) == 0) {
 #pragma unroll
-                    for (int e = 0; e < CPL; ++e)
-                        dv_out[(t * H + h) * DV + j0 + col0 + e] = from_f32<E>(-dy[e]);
+                for (int rr = 0; rr < RPL; ++rr) {
+                    const float a = sA[ti][r0 + rr], kc = sK[ti][r0 + rr];
+                    float dk = 0.f, dl = 0.f;
+#pragma unroll
+                    for (int e = 0; e < CW; ++e) {
+                        dk += b * G[rr][e] * vr[e] + X[rr][e] * dy[e];
+                        G[rr][e] += kc * dy[e];
+                        dl += G[rr][e] * X[rr][e];
+                        G[rr][e] *= a;
+                    }
+                    comb[i][wave][0][r0 + rr] = dq[rr];
+                    comb[i][wave][1][r0 + rr] = dk;
+                    comb[i][wave][2][r0 + rr] = dl;
+                }
+                if (lane == 0) combB[i][wave] = db;
+                if (lane < CW) {
+                    const size_t t = (size_t)ci.start + ti;
+                    // dv = beta dnu = -dy; lane e writes column e
+                    float dve = -dy[0];
+#pragma unroll
+                    for (int e = 1; e < CW; ++e) dve = lane == e ? -dy[e] : dve;
+                    dv_out[(t * H + h) * DV + j0 + lane] = from_f32<E>(dve);
                 }
             }
-            __syncthreads();   // sNu / sY rewritten by the next piece
+            __syncthreads();   // the piece's per-wave row sums are in LDS
+            for (int x = tid; x < np * DK; x += 256) {
+                const int i = x / DK, r = x % DK;
+                const size_t t = (size_t)ci.start + i0 + i;
+                float* pr = part + (((size_t)slice * T + t) * H + h) * DK + r;
+                const size_t plane = (size_t)NSL * T * H * DK;
+#pragma unroll
+                for (int m = 0; m < 3; ++m)
+                    pr[m * plane] = comb[i][0][m][r] + comb[i][1][m][r] + comb[i][2][m][r] + comb[i][3][m][r];
+            }
+            if (tid < np)
+                part_beta[((size_t)slice * T + ci.start + i0 + tid) * H + h] =
+                    combB[tid][0] + combB[tid][1] + combB[tid][2] + combB[tid][3];
+            __syncthreads();   // comb is rewritten by the next piece
         }
     }
     if (d_initial) {
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) d_initial[((size_t)pair * DK + row) * DV + j0 + col0 + e] = G[e];
+        for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+            for (int e = 0; e < CW; ++e) d_initial[((size_t)pair * DK + r0 + rr) * DV + j0 + e] = G[rr][e];
     }
 }
 
