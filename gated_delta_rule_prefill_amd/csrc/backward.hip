@@ -36,20 +36,6 @@ constexpr int BWD_CW = 4;      // value columns per wave
 constexpr int BWD_PIECE = 8;   // tokens per recomputed piece
 constexpr int BWD_PIECES = CHUNK / BWD_PIECE;
 
-// Value of lane l ^ M: quad permutations and the row rotation by 8 through
-// DPP, xor 4 and 16 through a swizzle, 32 through a permute.
-template <int M>
-__device__ __forceinline__ float lane_xor(float x) {
-    const int v = __builtin_bit_cast(int, x);
-    int r;
-    if constexpr (M == 1) r = __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);        // quad_perm 1,0,3,2
-    else if constexpr (M == 2) r = __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
-    else if constexpr (M == 8) r = __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false);  // row_ror 8
-    else if constexpr (M == 4 || M == 16) r = __builtin_amdgcn_ds_swizzle(v, 0x1F | (M << 10));
-    else r = __builtin_bit_cast(int, __shfl_xor(x, M));
-    return __builtin_bit_cast(float, r);
-}
-
 // Totals over the 64 lanes of 4 values per lane (a transposing butterfly:
 // the first two exchanges also halve the values), returned uniform.
 __device__ __forceinline__ void wave_sum4(const float (&a)[4], int lane, float (&t)[4]) {

@@ -103,18 +103,32 @@ __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-
 __host__ __device__ constexpr int row_lane(int r) {
     return (((r >> 3) & 1) << 5) | (((r >> 2) & 1) << 4) | (((r >> 1) & 1) << 3) | ((r & 1) << 2);
 }
+// Value of lane l ^ M: quad permutations and the row rotation by 8 through
+// DPP, xor 4 and 16 through a swizzle (within 32 lanes), 32 through a permute.
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+    const int v = __builtin_bit_cast(int, x);
+    int r;
+    if constexpr (M == 1) r = __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);        // quad_perm 1,0,3,2
+    else if constexpr (M == 2) r = __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    else if constexpr (M == 8) r = __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false);  // row_ror 8
+    else if constexpr (M == 4 || M == 16) r = __builtin_amdgcn_ds_swizzle(v, 0x1F | (M << 10));
+    else r = __builtin_bit_cast(int, __shfl_xor(x, M));
+    return __builtin_bit_cast(float, r);
+}
+
 __device__ __forceinline__ float wave_sum16(const float (&a)[16], int lane) {
     const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8, h2 = lane & 4;
     float b[8], c[4], d[2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = (h5 ? a[8 + j] : a[j]) + __shfl_xor(h5 ? a[j] : a[8 + j], 32);
+    for (int j = 0; j < 8; ++j) b[j] = (h5 ? a[8 + j] : a[j]) + lane_xor<32>(h5 ? a[j] : a[8 + j]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = (h4 ? b[4 + j] : b[j]) + __shfl_xor(h4 ? b[j] : b[4 + j], 16);
+    for (int j = 0; j < 4; ++j) c[j] = (h4 ? b[4 + j] : b[j]) + lane_xor<16>(h4 ? b[j] : b[4 + j]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) d[j] = (h3 ? c[2 + j] : c[j]) + __shfl_xor(h3 ? c[j] : c[2 + j], 8);
-    float e = (h2 ? d[1] : d[0]) + __shfl_xor(h2 ? d[0] : d[1], 4);
-    e += __shfl_xor(e, 2);
-    e += __shfl_xor(e, 1);
+    for (int j = 0; j < 2; ++j) d[j] = (h3 ? c[2 + j] : c[j]) + lane_xor<8>(h3 ? c[j] : c[2 + j]);
+    float e = (h2 ? d[1] : d[0]) + lane_xor<4>(h2 ? d[0] : d[1]);
+    e += lane_xor<2>(e);
+    e += lane_xor<1>(e);
     return e;
 }
 __device__ __forceinline__ float read_lane(float x, int l) {
