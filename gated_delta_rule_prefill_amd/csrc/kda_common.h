@@ -96,12 +96,12 @@ __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 constexpr float L2NORM_EPS = 1e-6f;
 __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
 
-// Wave-wide sums of 16 values per lane at once (a transposing butterfly: 15
-// lane exchanges instead of 16 x 6).  Lane l receives the total of
-// a[row_of_lane(l)] over all 64 lanes, row_of_lane(l) = 8 b5 + 4 b4 + 2 b3 + b2
+// Wave-wide sums of 8 values per lane at once (a transposing butterfly: 10
+// lane exchanges instead of 8 x 6).  Lane l receives the total of
+// a[row_of_lane(l)] over all 64 lanes, row_of_lane(l) = 4 b5 + 2 b4 + b3
 // with b_i bit i of l; row_lane(r) is a lane that holds row r's total.
 __host__ __device__ constexpr int row_lane(int r) {
-    return (((r >> 3) & 1) << 5) | (((r >> 2) & 1) << 4) | (((r >> 1) & 1) << 3) | ((r & 1) << 2);
+    return (((r >> 2) & 1) << 5) | (((r >> 1) & 1) << 4) | ((r & 1) << 3);
 }
 // Value of lane l ^ M: quad permutations and the row rotation by 8 through
 // DPP, xor 4 and 16 through a swizzle (within 32 lanes), 32 through a permute.
@@ -117,38 +117,38 @@ __device__ __forceinline__ float lane_xor(float x) {
     return __builtin_bit_cast(float, r);
 }
 
-__device__ __forceinline__ float wave_sum16(const float (&a)[16], int lane) {
-    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8, h2 = lane & 4;
-    float b[8], c[4], d[2];
+__device__ __forceinline__ float wave_sum8(const float (&a)[8], int lane) {
+    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
+    float b[4], c[2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = (h5 ? a[8 + j] : a[j]) + lane_xor<32>(h5 ? a[j] : a[8 + j]);
+    for (int j = 0; j < 4; ++j) b[j] = (h5 ? a[4 + j] : a[j]) + lane_xor<32>(h5 ? a[j] : a[4 + j]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = (h4 ? b[4 + j] : b[j]) + lane_xor<16>(h4 ? b[j] : b[4 + j]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) d[j] = (h3 ? c[2 + j] : c[j]) + lane_xor<8>(h3 ? c[j] : c[2 + j]);
-    float e = (h2 ? d[1] : d[0]) + lane_xor<4>(h2 ? d[0] : d[1]);
-    e += lane_xor<2>(e);
-    e += lane_xor<1>(e);
-    return e;
+    for (int j = 0; j < 2; ++j) c[j] = (h4 ? b[2 + j] : b[j]) + lane_xor<16>(h4 ? b[j] : b[2 + j]);
+    float d = (h3 ? c[1] : c[0]) + lane_xor<8>(h3 ? c[0] : c[1]);
+    d += lane_xor<4>(d);
+    d += lane_xor<2>(d);
+    d += lane_xor<1>(d);
+    return d;
 }
 __device__ __forceinline__ float read_lane(float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
-// L2-normalise 16 rows held by a wave, CPT channels per lane (the lanes
+// L2-normalise 8 rows held by a wave, CPT channels per lane (the lanes
 // together hold every channel of each row).
-template <int CPT>
-__device__ __forceinline__ void l2_normalise_rows(float (&x)[16][CPT], int lane) {
-    float a[16];
+template <int NR, int CPT>
+__device__ __forceinline__ void l2_normalise_rows(float (&x)[NR][CPT], int lane) {
+    static_assert(NR == 8, "rows per wave");
+    float a[NR];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < NR; ++r) {
         a[r] = 0.f;
 #pragma unroll
         for (int e = 0; e < CPT; ++e) a[r] += x[r][e] * x[r][e];
     }
-    const float inv = rsqrtf(wave_sum16(a, lane) + L2NORM_EPS);
+    const float inv = rsqrtf(wave_sum8(a, lane) + L2NORM_EPS);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < NR; ++r) {
         const float sr = read_lane(inv, row_lane(r));
 #pragma unroll
         for (int e = 0; e < CPT; ++e) x[r][e] *= sr;

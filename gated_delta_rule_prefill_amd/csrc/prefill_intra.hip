@@ -1,6 +1,6 @@
 // prefill_intra.hip -- per-chunk work of the chunkwise KDA prefill.
 //
-// One workgroup (4 waves) per (chunk, head); chunks are independent, so the
+// One workgroup (8 waves) per (chunk, head); chunks are independent, so the
 // grid covers the whole batch at once.  For a chunk of C = 64 tokens
 // r = 0..63 (only log_alpha and beta are zeroed past the sequence end, which
 // makes every quantity below vanish or go unused for those rows) it computes,
@@ -26,10 +26,16 @@
 // and writes PM, Hc^T, QM, OI and gamma_C as one record per chunk and head.
 //
 // The inverse of the unit lower-triangular I + A_kk is built blockwise: the
-// four 16x16 diagonal blocks by forward substitution (one lane per column),
-// then the off-diagonal blocks on fp32 MFMA, each wave walking down one
-// column block with the blocks above it in registers, stored transposed in
-// the unused upper triangle of A_kk.
+// four 16x16 diagonal blocks by forward substitution (one lane per column,
+// by the wave that built the block), then the off-diagonal blocks on fp32
+// MFMA, each wave walking down one column block with the blocks above it in
+// registers, stored transposed in the unused upper triangle of A_kk.
+//
+// Wave w holds tokens 8w .. 8w + 7 in the row mapping (lane l: key channels
+// l*dk/64 ..), so the per-token work of the loads, the decay factors and QM
+// is spread over all eight waves; the MFMA phases split their tiles over
+// the waves.  Eight waves of at most 128 registers, two workgroups per CU,
+// keep 16 waves resident to cover the memory and MFMA latencies.
 //
 // Decay factors never form 1/gamma over a whole chunk: the chunk is cut into
 // four 16-token blocks with reference log-decays B_R (g just before block R).
@@ -39,6 +45,8 @@
 #include "kda_common.h"
 
 namespace kda {
+
+constexpr int INTRA_WAVES = 8;   // waves per workgroup
 
 template <typename E, int DK, int DV>
 struct IntraLayout {
@@ -67,11 +75,12 @@ struct IntraLayout {
     static constexpr int U2_BYTES = AL_BYTES > KHT_BYTES ? AL_BYTES : KHT_BYTES;
     static constexpr int OFF_TL = OFF_AL + ((U2_BYTES + 15) & ~15);
     static constexpr int OFF_AQ = OFF_TL + ((CHUNK * LT * ES + 15) & ~15);   // A_qk, perm32 keys
-    static constexpr int OFF_TAU = OFF_AQ + ((CHUNK * LT * ES + 15) & ~15);
+    // fp32 [8][DK]: log-decay summed over each wave's 8 tokens
+    static constexpr int OFF_HALF = OFF_AQ + ((CHUNK * LT * ES + 15) & ~15);
     // phase 0b-1: q e^{g - B} ([64][LK]) over the T and A_qk areas, free until then
     static constexpr int OFF_QP = OFF_TL;
-    static_assert(OFF_QP + CHUNK * LK * ES <= OFF_TAU, "q operand area");
-    static constexpr int OFF_ETAB = OFF_TAU + 4 * DK * 4;
+    static_assert(OFF_QP + CHUNK * LK * ES <= OFF_HALF, "q operand area");
+    static constexpr int OFF_ETAB = OFF_HALF + 8 * DK * 4;
     static constexpr int OFF_BETA = OFF_ETAB + 6 * DK * 4;
     static constexpr int BYTES = OFF_BETA + CHUNK * 4;
 };
@@ -124,6 +133,20 @@ __device__ __forceinline__ void load_row(const E* p, float (&out)[CPT]) {
     } else {
         out[0] = to_f32(__builtin_nontemporal_load(p));
     }
+}
+
+// CPT consecutive elements as loaded (one streaming load, kept packed), and
+// element e of them.
+template <typename E, int CPT> struct Raw { typedef typename Vec<E>::v2 type; };
+template <typename E> struct Raw<E, 1> { typedef E type; };
+template <int CPT, typename E>
+__device__ __forceinline__ typename Raw<E, CPT>::type load_raw(const E* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const typename Raw<E, CPT>::type*>(p));
+}
+template <int CPT, typename T>
+__device__ __forceinline__ auto raw_get(const T& v, int e) {
+    if constexpr (CPT == 2) return v[e];
+    else return v;
 }
 
 // CPT consecutive elements to LDS (one store)
@@ -204,9 +227,36 @@ __device__ __forceinline__ void x_column(float* sAL, int g, int ln) {
     }
 }
 
+// Inverse of a unit lower-triangular diagonal block of I + A_kk by forward
+// substitution from registers: lane (g, l) holds am = A[4g + i][l], i = 0..3
+// (zero on and above the diagonal), and every lane solves (I + A) x = e_l,
+// the row-r coefficients A[r][i] broadcast from the lane that holds them
+// (v_readlane).  The substitution's only chain is one multiply-add per row.
+// Lanes of group 0 store the strictly lower part of column l transposed,
+// into the block's upper triangle at sX (= sAL + 16 blk LA + 16 blk).
+template <int LA>
+__device__ __forceinline__ void diag_inverse(const f32x4& am, float* sX, int g, int l) {
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float acc = (r == l) ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 0; i < r; ++i) acc -= read_lane(am[r & 3], 16 * (r >> 2) + i) * x[i];
+        x[r] = acc;
+    }
+    if (g == 0) {
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+            if (r > l) sX[l * LA + r] = x[r];
+    }
+}
+
 // NORM: L2-normalise q and k rows first; beta_logit: beta arrives as a logit.
+// bf16 operands fit 128 registers per lane (four waves per SIMD: two
+// workgroups per CU, bounded by LDS); fp32 operands take up to 256.
 template <typename E, int DK, int DV, bool NORM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_intra_kernel(
+__global__ __launch_bounds__(64 * INTRA_WAVES)
+__attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 2))) void prefill_intra_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const ChunkSrc src, int H, int beta_logit,
@@ -215,11 +265,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     using L = IntraLayout<E, DK, DV>;
     using V4 = typename Vec<E>::v4;
     using V8 = typename Vec<E>::v8;
-    constexpr int CPT = DK / 64;   // key channels per thread in the row-block mapping
-    constexpr int CPTV = DV / 64;  // value channels per thread
+    constexpr int CPT = DK / 64;   // key channels per lane in the row mapping
+    constexpr int CPTV = DV / 64;  // value channels per lane
     constexpr int KS = DK / 32;    // contraction steps over key channels
-    constexpr int NWB = (DK / 16 + 3) / 4;   // key-column blocks per wave
-    constexpr int NUB = (DV / 16 + 3) / 4;   // value-column blocks per wave
+    constexpr int NR = CHUNK / INTRA_WAVES;   // token rows per wave
+    constexpr int NWP = DK / 32;   // pairs of 16-column tiles of W
+    constexpr int NUP = DV / 32;   // ... and of U
+    static_assert(NR == 8 && NWP + NUP <= INTRA_WAVES, "work split");
+    using RK = typename Raw<E, CPT>::type;
+    using RV = typename Raw<E, CPTV>::type;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
     E* sKP = reinterpret_cast<E*>(smem + L::OFF_KP);   // k*e^{g-B}  (phase 0b-1)
@@ -232,7 +286,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     E* sTL = reinterpret_cast<E*>(smem + L::OFF_TL);
     E* sAQ = reinterpret_cast<E*>(smem + L::OFF_AQ);
     E* sQP = reinterpret_cast<E*>(smem + L::OFF_QP);   // q*e^{g-B} (phase 0b-1)
-    float* sTau = reinterpret_cast<float*>(smem + L::OFF_TAU);
+    float* sHalf = reinterpret_cast<float*>(smem + L::OFF_HALF);
     float* sEtab = reinterpret_cast<float*>(smem + L::OFF_ETAB);
     float* sBeta = reinterpret_cast<float*>(smem + L::OFF_BETA);
 
@@ -247,45 +301,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
     const int t = threadIdx.x;
     const int lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // also the 16-token block of the row mapping
-    const int R = wave;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int R = wave >> 1;       // 16-token block of the wave's rows
+    const int rb = NR * wave;      // first of the wave's rows
     const int g = lane >> 4, ln = lane & 15;
     const int c0 = lane * CPT;
     const int cv0 = lane * CPTV;
 
     // ---- phase 0: unconditional loads (rows past the end re-read the last row) -
     // Issued tensor by tensor in the order they are first needed: a wave's
-    // loads complete in order, so the prefix sum waits only for log_alpha, the
-    // decayed keys only for k, and v stays in flight until the transposes.
-    float la[16][CPT], kr[16][CPT], qr[16][CPT], vr[16][CPTV];
-    size_t rowoff[16];
+    // loads complete in order, so the prefix sum waits only for log_alpha.
+    // q, k and v stay packed until they are used.
+    float la[NR][CPT];
+    RK kraw[NR], qraw[NR];
+    RV vraw[NR];
+    size_t rowoff[NR];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 16 * R + r;
+    for (int r = 0; r < NR; ++r) {
+        const int row = rb + r;
         rowoff[r] = ((size_t)ci.start + (row < ci.len ? row : ci.len - 1)) * H + h;
     }
     // beta first: it is needed before the first barrier, and a wave's loads
-    // complete in order, so a late beta load would make that barrier wait for
-    // every input row (every wave loads it; wave 0 keeps it)
+    // complete in order (every wave loads it; wave 0 keeps it)
     const float bt = beta[((size_t)ci.start + (lane < ci.len ? lane : ci.len - 1)) * H + h];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) load_row<CPT>(log_alpha + rowoff[r] * DK + c0, la[r]);
+    for (int r = 0; r < NR; ++r) load_row<CPT>(log_alpha + rowoff[r] * DK + c0, la[r]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) load_row<CPT>(k + rowoff[r] * DK + c0, kr[r]);
+    for (int r = 0; r < NR; ++r) kraw[r] = load_raw<CPT>(k + rowoff[r] * DK + c0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) load_row<CPT>(q + rowoff[r] * DK + c0, qr[r]);
+    for (int r = 0; r < NR; ++r) qraw[r] = load_raw<CPT>(q + rowoff[r] * DK + c0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) load_row<CPTV>(v + rowoff[r] * DV + cv0, vr[r]);
-    // cumulative log-decay inside each 16-token block; padded rows add nothing
-    // (with beta = 0 there, their k, q, v never reach a stored result).
-    float ell[16][CPT];
+    for (int r = 0; r < NR; ++r) vraw[r] = load_raw<CPTV>(v + rowoff[r] * DV + cv0);
+    // cumulative log-decay over the wave's rows; padded rows add nothing
+    // (with beta = 0 there, their k, q, v never reach a stored result)
+    float ell[NR][CPT];
     {
         float run[CPT];
 #pragma unroll
         for (int e = 0; e < CPT; ++e) run[e] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const bool valid = 16 * R + r < ci.len;
+        for (int r = 0; r < NR; ++r) {
+            const bool valid = rb + r < ci.len;
 #pragma unroll
             for (int e = 0; e < CPT; ++e) {
                 run[e] += valid ? la[r][e] : 0.f;
@@ -293,15 +349,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             }
         }
 #pragma unroll
-        for (int e = 0; e < CPT; ++e) sTau[R * DK + c0 + e] = run[e];
+        for (int e = 0; e < CPT; ++e) sHalf[wave * DK + c0 + e] = run[e];
         if (wave == 0) sBeta[lane] = lane < ci.len ? (beta_logit ? sigmoid(bt) : bt) : 0.f;
     }
     __syncthreads();
 
     // ---- phase 0b: block references, decay table, decayed keys and queries ----
+    float kr[NR][CPT], qr[NR][CPT];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+            kr[r][e] = to_f32(raw_get<CPT>(kraw[r], e));
+            qr[r][e] = to_f32(raw_get<CPT>(qraw[r], e));
+        }
     if constexpr (NORM) {
-        l2_normalise_rows<CPT>(kr, lane);
-        l2_normalise_rows<CPT>(qr, lane);
+        l2_normalise_rows<NR, CPT>(kr, lane);
+        l2_normalise_rows<NR, CPT>(qr, lane);
     }
     float eB[CPT], eTE[CPT];   // e^{B_R} (g before block R);  e^{g_C - B_R}
 #pragma unroll
@@ -309,22 +373,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         float a = 0.f, b = 0.f;
 #pragma unroll
         for (int Rp = 0; Rp < 4; ++Rp) {
-            const float tv = sTau[Rp * DK + c0 + e];
+            const float tv = sHalf[2 * Rp * DK + c0 + e] + sHalf[(2 * Rp + 1) * DK + c0 + e];
             if (Rp < R) a += tv; else b += tv;
         }
         eB[e] = fast_exp(a);
         eTE[e] = fast_exp(b);
+        if (wave & 1) {   // second half of block R: g_r - B_R includes the first half
+            const float first = sHalf[(wave - 1) * DK + c0 + e];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) ell[r][e] += first;
+        }
     }
     // e^{B_R - B_I} for the six off-diagonal block pairs (all <= 1)
-    for (int idx = t; idx < 6 * DK; idx += 256) {
+    for (int idx = t; idx < 6 * DK; idx += 64 * INTRA_WAVES) {
         const int p = idx / DK, c = idx % DK;
         float d = 0.f;
-        for (int Rp = off_i(p); Rp < off_r(p); ++Rp) d += sTau[Rp * DK + c];
+        for (int Rp = off_i(p); Rp < off_r(p); ++Rp) d += sHalf[2 * Rp * DK + c] + sHalf[(2 * Rp + 1) * DK + c];
         sEtab[idx] = fast_exp(d);
     }
+    V8 kgt[CPT];       // e^g k, the wave's rows of key channel c0 + e  (W operand)
+    V4 kht[CPT][2];    // Khat = k e^{g_C - g}, rows 4m .. 4m + 3
+    RK qg[NR];         // Qg = e^g q in the operand dtype, until QM is formed
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 16 * R + r;
+    for (int r = 0; r < NR; ++r) {
+        const int row = rb + r;
         E kp[CPT], kd[CPT], qp[CPT];
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
@@ -333,15 +405,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             kp[e] = from_f32<E>(kr[r][e] * P);
             kd[e] = from_f32<E>(kr[r][e] * iP);
             qp[e] = from_f32<E>(qr[r][e] * P);
-            ell[r][e] = kr[r][e] * iP * eTE[e];                    // Khat: k e^{g_C - g_r}
-            kr[r][e] *= P * eB[e];                                 // e^{g_r} k  (for W)
-            qr[r][e] *= P * eB[e];                                 // Qg = e^{g_r} q
+            kht[e][r >> 2][r & 3] = from_f32<E>(kr[r][e] * iP * eTE[e]);
+            const float PB = P * eB[e];                           // e^{g_r}
+            kgt[e][r] = from_f32<E>(kr[r][e] * PB);
+            if constexpr (CPT == 2) qg[r][e] = from_f32<E>(qr[r][e] * PB);
+            else qg[r] = from_f32<E>(qr[r][e] * PB);
         }
         store_row<CPT>(sKP + row * L::LK + c0, kp);
         store_row<CPT>(sKD + row * L::LK + c0, kd);
         store_row<CPT>(sQP + row * L::LK + c0, qp);
     }
-    if (R == 0) {
+    V8 vt[CPTV];       // v, the wave's rows of value channel cv0 + e
+#pragma unroll
+    for (int e = 0; e < CPTV; ++e)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) vt[e][r] = raw_get<CPTV>(vraw[r], e);
+    if (wave == 0) {
 #pragma unroll
         for (int e = 0; e < CPT; ++e) out.gC[c0 + e] = eTE[e];
     }
@@ -353,28 +432,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // scaling of the key fragments is done once for both products, and the
     // diagonal test once per tile, so each path is straight code.  A_qk
     // tiles stay in registers until the barrier: their LDS area holds q.
-    auto pair_tiles = [&](const int PR, const int PI, const bool diag) {
+    // Waves 0-3 take the diagonal pairs and invert their block of I + A_kk
+    // right away from the tile's registers; waves 4-7 the six off-diagonal
+    // pairs, whose A_kk tiles go to LDS.
+    auto pair_tiles = [&](const int PR, const int PI, const bool diag, f32x4& am) {
         const float* f = sEtab + (PR * (PR - 1) / 2 + PI) * DK;
-        V8 a[KS], b[KS], qf[KS];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+        // two contraction steps per round of fragment loads (registers)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int cb = 32 * s + 8 * g;
-            a[s] = frag8<E>(sKP + (16 * PR + ln) * L::LK + cb);
-            b[s] = diag ? frag8<E>(sKD + (16 * PI + ln) * L::LK + cb)
-                        : frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f + cb);
-            qf[s] = frag8<E>(sQP + (16 * PR + ln) * L::LK + cb);
+        for (int s0 = 0; s0 < KS; s0 += 2) {
+            V8 a[2], b[2], qf[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int cb = 32 * (s0 + s) + 8 * g;
+                a[s] = frag8<E>(sKP + (16 * PR + ln) * L::LK + cb);
+                b[s] = diag ? frag8<E>(sKD + (16 * PI + ln) * L::LK + cb)
+                            : frag8_scaled<E>(sKD + (16 * PI + ln) * L::LK + cb, f + cb);
+                qf[s] = frag8<E>(sQP + (16 * PR + ln) * L::LK + cb);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                acc = mma32(a[s], b[s], acc);
+                aq = mma32(b[s], qf[s], aq);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         const f32x4 bt4 = *reinterpret_cast<const f32x4*>(sBeta + 16 * PR + 4 * g);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            acc = mma32(a[s], b[s], acc);
-            aq = mma32(b[s], qf[s], aq);
-        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * PR + 4 * g + i, col = 16 * PI + ln;
-            sAL[r * L::LA + col] = r > col ? bt4[i] * acc[i] : 0.f;
+            am[i] = r > col ? bt4[i] * acc[i] : 0.f;
+            if (!diag) sAL[r * L::LA + col] = am[i];
         }
         // A_qk^T tile: lane holds A_qk[16 PR + ln][16 PI + 4g + i] (causal mask)
         V4 w;
@@ -383,168 +471,106 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             w[i] = from_f32<E>(16 * PR + ln >= 16 * PI + 4 * g + i ? aq[i] : 0.f);
         return w;
     };
-    V4 qk[3];
-#pragma unroll
-    for (int k3 = 0; k3 < 3; ++k3) {
-        const int p = wave + 4 * k3;
-        if (p < 10) {
-            const int PR = pair_r(p), PI = pair_i(p);
-            qk[k3] = PR == PI ? pair_tiles(PR, PI, true) : pair_tiles(PR, PI, false);
-        }
-    }
-    for (int u = wave - 2; u >= 0 && u < 6; u += 2) {   // waves 2 and 3 zero the upper tiles
-        const int UR = off_i(u), UI = off_r(u);   // the transposed (upper) tile
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sAL[(16 * UR + 4 * g + i) * L::LA + 16 * UI + ln] = 0.f;
+    // off-diagonal pairs of wave 4 + o: o = 0: 0, 1;  o = 1: 2, 3;  o = 2: 4;  o = 3: 5
+    const int o = wave - 4;
+    const int p0 = o < 2 ? 2 * o : o + 2;
+    V4 qk[2];
+    if (wave < 4) {
+        f32x4 am;
+        qk[0] = pair_tiles(wave, wave, true, am);
+        diag_inverse<L::LA>(am, sAL + 16 * wave * L::LA + 16 * wave, g, ln);
+    } else {
+        f32x4 am;
+        qk[0] = pair_tiles(off_r(p0), off_i(p0), false, am);
+        if (o < 2) qk[1] = pair_tiles(off_r(p0 + 1), off_i(p0 + 1), false, am);
     }
     __syncthreads();   // kp, kd, q operands dead: U1 becomes kgT / vT, the q area A_qk
 
+    // ---- phase 3: A_qk, (e^g k)^T and v^T to LDS; off-diagonal blocks of X ----
     // A_qk[r][perm32(i)] for the read-out products; the upper tiles are zero
+    if (wave < 4) {
+        store_vec(sAQ + (16 * wave + ln) * L::LT + perm_index(16 * wave + 4 * g), qk[0]);
+    } else {
+        store_vec(sAQ + (16 * off_r(p0) + ln) * L::LT + perm_index(16 * off_i(p0) + 4 * g), qk[0]);
+        if (o < 2) {
+            store_vec(sAQ + (16 * off_r(p0 + 1) + ln) * L::LT + perm_index(16 * off_i(p0 + 1) + 4 * g), qk[1]);
+        } else {
+            V4 z;
 #pragma unroll
-    for (int k3 = 0; k3 < 3; ++k3) {
-        const int p = wave + 4 * k3;
-        if (p < 10) {
-            const int PR = pair_r(p), PI = pair_i(p);
-            store_vec(sAQ + (16 * PR + ln) * L::LT + perm_index(16 * PI + 4 * g), qk[k3]);
+            for (int i = 0; i < 4; ++i) z[i] = from_f32<E>(0.f);
+#pragma unroll
+            for (int u = 3 * (o - 2); u < 3 * (o - 1); ++u)   // the transposed (upper) tiles
+                store_vec(sAQ + (16 * off_i(u) + ln) * L::LT + perm_index(16 * off_r(u) + 4 * g), z);
         }
     }
-    for (int u = wave - 2; u >= 0 && u < 6; u += 2) {
-        const int UR = off_i(u), UI = off_r(u);   // the transposed (upper) tile
-        V4 z;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) z[i] = from_f32<E>(0.f);
-        store_vec(sAQ + (16 * UR + ln) * L::LT + perm_index(16 * UI + 4 * g), z);
-    }
-
-    // ---- phase 3a: (e^g k)^T and v^T in LDS; diagonal 16x16 inverses ----------
+    for (int e = 0; e < CPT; ++e) store_vec(sKGT + (c0 + e) * L::LT + rb, kgt[e]);
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-        V8 lo, hi;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            lo[r] = from_f32<E>(kr[r][e]);
-            hi[r] = from_f32<E>(kr[r + 8][e]);
-        }
-        store_vec(sKGT + (c0 + e) * L::LT + 16 * R, lo);
-        store_vec(sKGT + (c0 + e) * L::LT + 16 * R + 8, hi);
-    }
-#pragma unroll
-    for (int e = 0; e < CPTV; ++e) {
-        V8 lo, hi;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            lo[r] = from_f32<E>(vr[r][e]);
-            hi[r] = from_f32<E>(vr[r + 8][e]);
-        }
-        store_vec(sVT + (cv0 + e) * L::LT + 16 * R, lo);
-        store_vec(sVT + (cv0 + e) * L::LT + 16 * R + 8, hi);
-    }
-    if (wave == 0) {
-        // lane (blk, j) solves (I + A_blk) x = e_j on diagonal block blk
-        const int blk = lane >> 4, j = lane & 15;
-        const float* Ab = sAL + 16 * blk * L::LA + 16 * blk;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == j) ? 1.f : 0.f;
-#pragma unroll
-            for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(Ab + r * L::LA + 4 * i4);
-                acc -= a[0] * x[4 * i4] + a[1] * x[4 * i4 + 1] + a[2] * x[4 * i4 + 2] +
-                       a[3] * x[4 * i4 + 3];
-            }
-            x[r] = acc;
-        }
-        float* Xt = sAL + (16 * blk + j) * L::LA + 16 * blk;   // row j of the block, transposed store
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (r > j) Xt[r] = x[r];
-    }
-    __syncthreads();
-
-    // ---- phase 3b: off-diagonal blocks of X, wave w down column block w ------
+    for (int e = 0; e < CPTV; ++e) store_vec(sVT + (cv0 + e) * L::LT + rb, vt[e]);
+    // X_RI for R > I: wave I walks down column block I
     if (wave == 0) x_column<L::LA, 0>(sAL, g, ln);
     else if (wave == 1) x_column<L::LA, 1>(sAL, g, ln);
     else if (wave == 2) x_column<L::LA, 2>(sAL, g, ln);
     __syncthreads();
 
     // ---- phase 3e: T = X Diag(beta) in the operand dtype ----------------------
-    // lane = row r, wave w: column groups 2w, 2w + 1 (8 columns each, one
-    // 16-byte store); X[r][c] for r > c sits transposed at sAL[c][r], so the
-    // 64 lanes of one read touch 64 consecutive words.
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-        const int r = lane, c0 = 8 * (2 * wave + k2);
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(sBeta + c0);
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(sBeta + c0 + 4);
+    // lane = row r, wave w: columns 8w .. 8w + 7 (one 16-byte store); X[r][c]
+    // for r > c sits transposed at sAL[c][r], so the 64 lanes of one read touch
+    // 64 consecutive words.
+    {
+        const int r = lane, cg = 8 * wave;
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(sBeta + cg);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(sBeta + cg + 4);
         float xv[8];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) xv[m] = sAL[(c0 + m) * L::LA + r];
+        for (int m = 0; m < 8; ++m) xv[m] = sAL[(cg + m) * L::LA + r];
         V8 w;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            const int c = c0 + m;
+            const int c = cg + m;
             const float x = r > c ? xv[m] : (r == c ? 1.f : 0.f);
             w[m] = from_f32<E>(x * (m < 4 ? b0[m] : b1[m - 4]));
         }
-        store_vec(sTL + r * L::LT + c0, w);
+        store_vec(sTL + r * L::LT + cg, w);
     }
     __syncthreads();   // X dead: its bytes become Khat^T
 
     // ---- phase 3f: Khat^T with tokens in perm32 order ---------------------------
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) {
+    for (int e = 0; e < CPT; ++e)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            V4 w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(ell[4 * r4 + i][e]);
-            store_vec(sKHT + (c0 + e) * L::LT + perm_index(16 * R + 4 * r4), w);
-        }
-    }
+        for (int m = 0; m < 2; ++m) store_vec(sKHT + (c0 + e) * L::LT + perm_index(rb + 4 * m), kht[e][m]);
 
-    // ---- phase 4: W = T (e^g K) and U = T V on MFMA, kept in registers ---------
-    // tile (Rq, column block): lane holds rows 16Rq + 4g + i, column 16cb + ln.
-    // T is lower triangular, so token block Rq only needs key tokens < 16Rq+16.
-    f32x4 Wt[NWB][4], Ut[NUB][4];
+    // ---- phase 4: W = T (e^g K) or U = T V on MFMA, kept in registers ---------
+    // Waves 0 .. NWP-1 take the W column tiles 2p, 2p + 1, the next NUP waves
+    // the U tiles.  Tile (Rq, column): lane holds rows 16Rq + 4g + i, column
+    // 16ct + ln; T is lower triangular, so token block Rq only needs key tokens
+    // < 16Rq + 16.  The tiles become MFMA operands over the tokens at once.
+    const bool wside = wave < NWP, uside = !wside && wave < NWP + NUP;
+    const int pr = wside ? wave : wave - NWP;   // column-tile pair
+    const int ct0 = 2 * pr;
+    V8 opf[2][2];   // [tile][32-token step]
+    if (wside || uside) {
+        const E* srcT = wside ? sKGT : sVT;
+        V8 a[4][2];
 #pragma unroll
-    for (int bw = 0; bw < NWB; ++bw) {
-        const int ct = NWB * wave + bw;
-        if (ct < DK / 16) {
-            V8 a[4][2], b[2];
+        for (int Rq = 0; Rq < 4; ++Rq)
 #pragma unroll
-            for (int s = 0; s < 2; ++s) b[s] = frag8<E>(sKGT + (16 * ct + ln) * L::LT + 32 * s + 8 * g);
+            for (int s = 0; s <= Rq / 2; ++s) a[Rq][s] = frag8<E>(sTL + (16 * Rq + ln) * L::LT + 32 * s + 8 * g);
 #pragma unroll
-            for (int Rq = 0; Rq < 4; ++Rq)
+        for (int bw = 0; bw < 2; ++bw) {
+            V8 b[2];
 #pragma unroll
-                for (int s = 0; s <= Rq / 2; ++s) a[Rq][s] = frag8<E>(sTL + (16 * Rq + ln) * L::LT + 32 * s + 8 * g);
+            for (int s = 0; s < 2; ++s) b[s] = frag8<E>(srcT + (16 * (ct0 + bw) + ln) * L::LT + 32 * s + 8 * g);
+            f32x4 acc[4];
 #pragma unroll
-            for (int Rq = 0; Rq < 4; ++Rq) Wt[bw][Rq] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int Rq = 2 * s; Rq < 4; ++Rq) Wt[bw][Rq] = mma32(a[Rq][s], b[s], Wt[bw][Rq]);
-        }
-    }
-#pragma unroll
-    for (int bu = 0; bu < NUB; ++bu) {
-        const int ct = NUB * wave + bu;
-        if (ct < DV / 16) {
-            V8 a[4][2], b[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) b[s] = frag8<E>(sVT + (16 * ct + ln) * L::LT + 32 * s + 8 * g);
-#pragma unroll
-            for (int Rq = 0; Rq < 4; ++Rq)
-#pragma unroll
-                for (int s = 0; s <= Rq / 2; ++s) a[Rq][s] = frag8<E>(sTL + (16 * Rq + ln) * L::LT + 32 * s + 8 * g);
-#pragma unroll
-            for (int Rq = 0; Rq < 4; ++Rq) Ut[bu][Rq] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int Rq = 0; Rq < 4; ++Rq) acc[Rq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
-                for (int Rq = 2 * s; Rq < 4; ++Rq) Ut[bu][Rq] = mma32(a[Rq][s], b[s], Ut[bu][Rq]);
+                for (int Rq = 2 * s; Rq < 4; ++Rq) acc[Rq] = mma32(a[Rq][s], b[s], acc[Rq]);
+            opf[bw][0] = tiles_to_frag<E>(acc[0], acc[1]);
+            opf[bw][1] = tiles_to_frag<E>(acc[2], acc[3]);
         }
     }
     __syncthreads();   // kgT / vT dead: the region holds A_qk W from here on
@@ -552,141 +578,106 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // ---- phase 5: transition and read-out products -------------------------
     //   PM^T (c', c) = -(W^T Khat)   Hc (c, j) = Khat^T U
     //   (A_qk W)^T (c', r)            OI^T (j, r) = U^T A_qk^T
-    // W and U enter as operands straight from their accumulator tiles.  A wave
-    // owns adjacent column tiles 2w, 2w + 1; in perm32 order their columns
-    // 4g..4g+3 and 16+4g..16+4g+3 are the 8 consecutive slots 8g..8g+7 of the
-    // 32-column block, so each lane writes 16 contiguous bytes.
-    {
-        static_assert(NWB == 1 || NWB == 2, "column tiles per wave");
-        V8 wf[NWB][2];
+    // In perm32 order the columns 4g..4g+3 and 16+4g..16+4g+3 of a tile pair
+    // are the 8 consecutive slots 8g..8g+7 of its 32-column block, so each
+    // lane writes 16 contiguous bytes.
+    if (wside) {
+        // PM rows c = 16a + ln; columns 16 ct0 + 4g + i and 16 (ct0 + 1) + 4g + i
 #pragma unroll
-        for (int bw = 0; bw < NWB; ++bw) {
-            wf[bw][0] = tiles_to_frag<E>(Wt[bw][0], Wt[bw][1]);
-            wf[bw][1] = tiles_to_frag<E>(Wt[bw][2], Wt[bw][3]);
+        for (int a = 0; a < DK / 16; ++a) {
+            V8 kf[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) kf[s] = frag8<E>(sKHT + (16 * a + ln) * L::LT + 32 * s + 8 * g);
+            f32x4 acc[2];
+#pragma unroll
+            for (int bw = 0; bw < 2; ++bw) {
+                acc[bw] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s) acc[bw] = mma32(opf[bw][s], kf[s], acc[bw]);
+            }
+            V8 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w[i] = from_f32<E>(-acc[0][i]);
+                w[4 + i] = from_f32<E>(-acc[1][i]);
+            }
+            store_vec(out.PM + (16 * a + ln) * DK + perm_index(16 * ct0 + 4 * g), w);
         }
-        const int ct0 = NWB * wave;
-        if (ct0 < DK / 16) {
-            // PM rows c = 16a + ln; columns 16 ct0 + 4g + i (and 16 (ct0 + 1) + 4g + i)
+        // (A_qk W)[r][c'] for r = 16Rr + ln, c' = 16ct + 4g + i  (A_qk is causal)
 #pragma unroll
-            for (int a = 0; a < DK / 16; ++a) {
+        for (int Rr = 0; Rr < 4; ++Rr) {
+            V8 af[2];
+#pragma unroll
+            for (int s = 0; s <= Rr / 2; ++s) af[s] = frag8<E>(sAQ + (16 * Rr + ln) * L::LT + 32 * s + 8 * g);
+#pragma unroll
+            for (int bw = 0; bw < 2; ++bw) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s <= Rr / 2; ++s) acc = mma32(opf[bw][s], af[s], acc);
+                *reinterpret_cast<f32x4*>(sQA + (16 * Rr + ln) * L::LQA + 16 * (ct0 + bw) + 4 * g) = acc;
+            }
+        }
+    } else if (uside) {
+        // Hc rows c = 16a + 4g + i, column j = 16ct + ln  ->  Hc^T[j][perm(c)]:
+        // row tiles a = 2m and 2m + 1 fill slots 32m + 8g .. +7
+#pragma unroll
+        for (int m = 0; m < DK / 32; ++m) {
+            f32x4 acc[2][2];   // [value tile][row tile 2m + h2]
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
                 V8 kf[2];
 #pragma unroll
-                for (int s = 0; s < 2; ++s) kf[s] = frag8<E>(sKHT + (16 * a + ln) * L::LT + 32 * s + 8 * g);
-                f32x4 acc[NWB];
+                for (int s = 0; s < 2; ++s) kf[s] = frag8<E>(sKHT + (16 * (2 * m + h2) + ln) * L::LT + 32 * s + 8 * g);
 #pragma unroll
-                for (int bw = 0; bw < NWB; ++bw) {
-                    acc[bw] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int bu = 0; bu < 2; ++bu) {
+                    acc[bu][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < 2; ++s) acc[bw] = mma32(wf[bw][s], kf[s], acc[bw]);
-                }
-                E* dst = out.PM + (16 * a + ln) * DK + perm_index(16 * ct0 + 4 * g);
-                if constexpr (NWB == 2) {
-                    V8 w;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        w[i] = from_f32<E>(-acc[0][i]);
-                        w[4 + i] = from_f32<E>(-acc[1][i]);
-                    }
-                    store_vec(dst, w);
-                } else {
-                    V4 w;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(-acc[0][i]);
-                    store_vec(dst, w);
+                    for (int s = 0; s < 2; ++s) acc[bu][h2] = mma32(kf[s], opf[bu][s], acc[bu][h2]);
                 }
             }
-            // (A_qk W)[r][c'] for r = 16Rr + ln, c' = 16ct + 4g + i  (A_qk is causal)
 #pragma unroll
-            for (int Rr = 0; Rr < 4; ++Rr) {
-                V8 af[2];
+            for (int bu = 0; bu < 2; ++bu) {
+                V8 w;
 #pragma unroll
-                for (int s = 0; s <= Rr / 2; ++s) af[s] = frag8<E>(sAQ + (16 * Rr + ln) * L::LT + 32 * s + 8 * g);
-#pragma unroll
-                for (int bw = 0; bw < NWB; ++bw) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s <= Rr / 2; ++s) acc = mma32(wf[bw][s], af[s], acc);
-                    *reinterpret_cast<f32x4*>(sQA + (16 * Rr + ln) * L::LQA + 16 * (ct0 + bw) + 4 * g) = acc;
+                for (int i = 0; i < 4; ++i) {
+                    w[i] = from_f32<E>(acc[bu][0][i]);
+                    w[4 + i] = from_f32<E>(acc[bu][1][i]);
                 }
+                store_vec(out.HCt + (16 * (ct0 + bu) + ln) * DK + 32 * m + 8 * g, w);
             }
         }
-    }
-    {
-        static_assert(NUB == 1 || NUB == 2, "value tiles per wave");
-        V8 uf[NUB][2];
+        // OI[r][perm(j)] for r = 16Rr + ln, j = 16ct + 4g + i
 #pragma unroll
-        for (int bu = 0; bu < NUB; ++bu) {
-            uf[bu][0] = tiles_to_frag<E>(Ut[bu][0], Ut[bu][1]);
-            uf[bu][1] = tiles_to_frag<E>(Ut[bu][2], Ut[bu][3]);
-        }
-        const int ct0 = NUB * wave;
-        if (ct0 < DV / 16) {
-            // Hc rows c = 16a + 4g + i, column j = 16ct + ln  ->  Hc^T[j][perm(c)]:
-            // row tiles a = 2m and 2m + 1 fill slots 32m + 8g .. +7
+        for (int Rr = 0; Rr < 4; ++Rr) {
+            V8 af[2];
 #pragma unroll
-            for (int bu = 0; bu < NUB; ++bu) {
-                const int ct = ct0 + bu;
+            for (int s = 0; s <= Rr / 2; ++s) af[s] = frag8<E>(sAQ + (16 * Rr + ln) * L::LT + 32 * s + 8 * g);
+            f32x4 acc[2];
 #pragma unroll
-                for (int m = 0; m < DK / 32; ++m) {
-                    f32x4 acc[2];
+            for (int bu = 0; bu < 2; ++bu) {
+                acc[bu] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const int a = 2 * m + h2;
-                        acc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int s = 0; s < 2; ++s)
-                            acc[h2] = mma32(frag8<E>(sKHT + (16 * a + ln) * L::LT + 32 * s + 8 * g), uf[bu][s], acc[h2]);
-                    }
-                    V8 w;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        w[i] = from_f32<E>(acc[0][i]);
-                        w[4 + i] = from_f32<E>(acc[1][i]);
-                    }
-                    store_vec(out.HCt + (16 * ct + ln) * DK + 32 * m + 8 * g, w);
-                }
+                for (int s = 0; s <= Rr / 2; ++s) acc[bu] = mma32(opf[bu][s], af[s], acc[bu]);
             }
-            // OI[r][perm(j)] for r = 16Rr + ln, j = 16ct + 4g + i
+            V8 w;
 #pragma unroll
-            for (int Rr = 0; Rr < 4; ++Rr) {
-                V8 af[2];
-#pragma unroll
-                for (int s = 0; s <= Rr / 2; ++s) af[s] = frag8<E>(sAQ + (16 * Rr + ln) * L::LT + 32 * s + 8 * g);
-                f32x4 acc[NUB];
-#pragma unroll
-                for (int bu = 0; bu < NUB; ++bu) {
-                    acc[bu] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s <= Rr / 2; ++s) acc[bu] = mma32(uf[bu][s], af[s], acc[bu]);
-                }
-                E* dst = out.OI + (16 * Rr + ln) * DV + perm_index(16 * ct0 + 4 * g);
-                if constexpr (NUB == 2) {
-                    V8 w;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        w[i] = from_f32<E>(acc[0][i]);
-                        w[4 + i] = from_f32<E>(acc[1][i]);
-                    }
-                    store_vec(dst, w);
-                } else {
-                    V4 w;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[0][i]);
-                    store_vec(dst, w);
-                }
+            for (int i = 0; i < 4; ++i) {
+                w[i] = from_f32<E>(acc[0][i]);
+                w[4 + i] = from_f32<E>(acc[1][i]);
             }
+            store_vec(out.OI + (16 * Rr + ln) * DV + perm_index(16 * ct0 + 4 * g), w);
         }
     }
     __syncthreads();
 
     // ---- phase 6: QM = Qg - A_qk W in the row mapping ------------------------
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 16 * R + r;
+    for (int r = 0; r < NR; ++r) {
+        const int row = rb + r;
         typename Vec<E>::v2 w2;
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
-            const E val = from_f32<E>(qr[r][e] - sQA[row * L::LQA + c0 + e]);
+            const E val = from_f32<E>(to_f32(raw_get<CPT>(qg[r], e)) - sQA[row * L::LQA + c0 + e]);
             if constexpr (CPT == 2) w2[e] = val;
             else out.QM[row * DK + perm_index(c0 + e)] = val;
         }
@@ -701,11 +692,11 @@ static hipError_t launch_intra_t(const void* q, const void* k, const void* v, co
 {
     const int beta_logit = (flags & PRE_BETA_LOGIT) ? 1 : 0;
     if (flags & PRE_L2NORM_QK)
-        hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, true>), dim3(max_chunks * H), dim3(256), 0,
+        hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, true>), dim3(max_chunks * H), dim3(64 * INTRA_WAVES), 0,
                            stream, (const E*)q, (const E*)k, (const E*)v, la, beta, src, H,
                            beta_logit, (unsigned char*)rec);
     else
-        hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, false>), dim3(max_chunks * H), dim3(256), 0,
+        hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, false>), dim3(max_chunks * H), dim3(64 * INTRA_WAVES), 0,
                            stream, (const E*)q, (const E*)k, (const E*)v, la, beta, src, H,
                            beta_logit, (unsigned char*)rec);
     return hipGetLastError();
