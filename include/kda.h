@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = 1, /* NULL/misaligned pointer, bad size or dtype */
-    KDA_ERR_UNSUPPORTED = 2,      /* a head size this build has no kernels for */
+    KDA_ERR_UNSUPPORTED = 2,      /* a head size the library has no kernels for */
     KDA_ERR_WORKSPACE = 3,        /* caller workspace smaller than required     */
     KDA_ERR_HIP = 4               /* a HIP runtime call or launch failed        */
 } kda_status;
