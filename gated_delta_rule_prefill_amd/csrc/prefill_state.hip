@@ -305,8 +305,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // only the sequential chain; the outputs come from a separate parallel pass
 // over the chunk-start states this kernel stores.
 //
-// One workgroup per (sequence, head, 16 value columns), DK/32 + 5 waves:
-//   serial waves w < DK/32  own rows 32w..32w+31 of the fp32 state tile; per
+// One workgroup per (sequence, head, 16 SW value columns), SW DK/32 + 5 waves
+// (SW = 2 for batches with more chains than CUs: the slices of a workgroup
+// share the PM it moves through its CU):
+//   serial waves w < SW DK/32  own rows 32w'..32w'+31 (w' = w mod DK/32) of
+//       the fp32 state tile of value slice w / (DK/32); per
 //       chunk each applies S' = Diag(gamma_C) S + Hc + PM S to its rows (8
 //       MFMAs), reading the whole chunk-start state as bf16 operand slots from
 //       LDS and writing its own rows' slots for the next chunk, to LDS and to
@@ -321,20 +324,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 //       (one wave issues such a load only every ~70 cycles).
 // Every wave passes one barrier per chunk.  A ring slot or state slot is
 // written only after the barrier that ends the chunk which last read it.
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, int SW>
 struct RingCfg {
     static constexpr int ES = sizeof(E);
     static constexpr int KS = DK / 32, KT = DK / 16, NSL = DV / 16;
-    static constexpr int NSER = KS;                  // serial waves
+    static constexpr int NWG = NSL / SW;             // workgroups per (sequence, head)
+    static constexpr int NSER = KS * SW;             // serial waves
     static constexpr int NSTG = 4;                   // stager waves
     static constexpr int WAVES = NSER + 1 + NSTG;    // + the touch wave
     static constexpr int FRAG = 8 * ES;
-    static constexpr int XSLOT = KS * 64 * FRAG;     // one chunk-start state (operand slots)
+    static constexpr int XSLOT = SW * KS * 64 * FRAG;   // one chunk-start state (operand slots)
     static constexpr int NX = 2;                     // state slots: it (read), it + 1 (written)
     static constexpr int RW = DK * ES / 16;          // 16-byte units per PM / Hc^T row
     static constexpr int RS = (RW + 1) * 16;         // padded LDS row stride (bytes)
     static constexpr int PM_UNITS = DK * (RW + 1);
-    static constexpr int HC_UNITS = 16 * (RW + 1);
+    static constexpr int HC_UNITS = 16 * SW * (RW + 1);
     static constexpr int G_UNITS = DK / 4;
     static constexpr int UNITS = PM_UNITS + HC_UNITS + G_UNITS;
     static constexpr int LOADS = (UNITS + 63) / 64;  // direct loads per chunk
@@ -346,7 +350,8 @@ struct RingCfg {
     static constexpr int NSLOT = 3;
     static constexpr int LDS_BYTES = NSLOT * SLOT + NX * XSLOT;
     static constexpr RecLayout RL = rec_layout(ES, DK, DV);
-    static constexpr int TOUCH_LINES = DK * DK * ES / 128 / NSL + 16 * DK * ES / 128 + DK * 4 / 128;
+    static constexpr int TOUCH_LINES = DK * DK * ES / 128 / NWG + 16 * SW * DK * ES / 128 + DK * 4 / 128;
+    static constexpr int CST_COLS = SW == 1 ? 16 : 1;   // fp32 state staging (chunk_states; SW = 1 only)
     static constexpr int TOUCH_PER_LANE = (TOUCH_LINES + 63) / 64;
     static_assert(2 * LOADS_W <= 60, "two chunks of one stager's direct loads must fit its counter");
     static_assert(LOADS_LAST > 0 && LOADS_LAST <= LOADS_W, "stager split");
@@ -374,40 +379,40 @@ __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
+template <typename E, int DK, int DV, int SW>
+__global__ __launch_bounds__(64 * (SW * DK / 32 + 5)) void prefill_state_ring_kernel(
     const unsigned char* __restrict__ rec, const ChunkSrc src, const float* __restrict__ S0,
     float* __restrict__ S_final, E* __restrict__ states, float* __restrict__ chunk_states, int H,
     int n_pairs)
 {
-    using C = RingCfg<E, DK, DV>;
+    using C = RingCfg<E, DK, DV, SW>;
     using V4 = typename Vec<E>::v4;
     using V8 = typename Vec<E>::v8;
-    constexpr int KS = C::KS, NSL = C::NSL, NSER = C::NSER;
+    constexpr int KS = C::KS, NWG = C::NWG, NSER = C::NSER;
 
     __shared__ __attribute__((aligned(1024))) unsigned char ring[C::NSLOT * C::SLOT];
     __shared__ __attribute__((aligned(16))) unsigned char xfer[C::NX * C::XSLOT];
     // fp32 chunk-start states for the chunk_states output, column-major
     // [slot][16 columns][DK rows (+4 padding)]; written by the serial waves with
-    // 16-byte LDS stores, sent to memory row-major by the touch wave
-    __shared__ __attribute__((aligned(16))) float cst[C::NX][16][DK + 4];
+    // 16-byte LDS stores, sent to memory row-major by the touch wave (SW = 1)
+    __shared__ __attribute__((aligned(16))) float cst[C::NX][C::CST_COLS][DK + 4];
 
     const int b = blockIdx.x;
     const int xcd = b & 7, q8 = b >> 3;
-    const int grp = q8 / NSL, slice = q8 % NSL;
+    const int grp = q8 / NWG, slice = q8 % NWG;   // slice: 16 SW value columns
     const int pair = grp * 8 + xcd;
     if (pair >= n_pairs) return;
     const int s = pair / H, h = pair % H;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, g = l >> 4, ln = l & 15;
-    const int j0 = slice * 16;
+    const int j0 = slice * 16 * SW;
     int c_begin, n;   // first chunk and chunk count of this sequence
     seq_chunks(src, s, c_begin, n);
     const size_t sbase = (size_t)pair * DK * DV;
     if (n == 0) {   // empty sequence: the final state is the initial one (or zero)
         if (S_final)
-            for (int x = tid; x < DK * 16; x += blockDim.x) {
-                const size_t at = sbase + (size_t)(x >> 4) * DV + j0 + (x & 15);
+            for (int x = tid; x < DK * 16 * SW; x += blockDim.x) {
+                const size_t at = sbase + (size_t)(x / (16 * SW)) * DV + j0 + x % (16 * SW);
                 S_final[at] = S0 ? S0[at] : 0.f;
             }
         return;   // uniform over the workgroup: no barrier is skipped by part of it
@@ -418,8 +423,10 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
 
     if (wave < NSER) {
         // ------------------------------------------------ serial waves
-        const int w = wave;
-        f32x4 S[2];   // S[h2]: lane holds S[32w + 16 h2 + 4g + i][j0 + ln]
+        const int w = wave % KS;        // row group: rows 32w .. 32w + 31
+        const int sub = wave / KS;      // value slice inside the workgroup
+        const int jc = j0 + 16 * sub;   // its first column
+        f32x4 S[2];   // S[h2]: lane holds S[32w + 16 h2 + 4g + i][jc + ln]
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) S[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (S0) {
@@ -427,7 +434,7 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S[h2][i] = S0[sbase + (size_t)(32 * w + 16 * h2 + 4 * g + i) * DV + j0 + ln];
+                    S[h2][i] = S0[sbase + (size_t)(32 * w + 16 * h2 + 4 * g + i) * DV + jc + ln];
         }
         // chunk-start state of chunk it, this wave's operand step, to LDS and to
         // the chunk-state buffer ([chunk, head][slice][step][lane][8])
@@ -438,14 +445,16 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
                 f[i] = from_f32<E>(S[0][i]);
                 f[4 + i] = from_f32<E>(S[1][i]);
             }
-            store_vec(xslot(it) + (w * 64 + l) * 8, f);
+            store_vec(xslot(it) + ((sub * KS + w) * 64 + l) * 8, f);
             if (it < n)
                 store_vec(states + ((size_t)(c_begin + it) * H + h) * DK * DV +
-                              ((size_t)(slice * KS + w) * 64 + l) * 8, f);
-            if (chunk_states) {
+                              ((size_t)((slice * SW + sub) * KS + w) * 64 + l) * 8, f);
+            if constexpr (SW == 1) {
+                if (chunk_states) {
 #pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-                    *reinterpret_cast<f32x4*>(&cst[it % C::NX][ln][32 * w + 16 * h2 + 4 * g]) = S[h2];
+                    for (int h2 = 0; h2 < 2; ++h2)
+                        *reinterpret_cast<f32x4*>(&cst[it % C::NX][ln][32 * w + 16 * h2 + 4 * g]) = S[h2];
+                }
             }
         };
         put(0);
@@ -455,7 +464,7 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
             const E* xs = xslot(it);
             V8 Sf[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) Sf[ks] = load_vec<V8>(xs + (ks * 64 + l) * 8);
+            for (int ks = 0; ks < KS; ++ks) Sf[ks] = load_vec<V8>(xs + ((sub * KS + ks) * 64 + l) * 8);
             V8 pf[2][KS];
             V4 hc[2];
             f32x4 gc[2];
@@ -466,7 +475,7 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
                     pf[h2][ks] = load_vec<V8>(reinterpret_cast<const E*>(pm + 32 * ks * sizeof(E)));
-                hc[h2] = load_vec<V4>(reinterpret_cast<const E*>(sl + C::OFF_HC + ln * C::RS) + perm_index(16 * t + 4 * g));
+                hc[h2] = load_vec<V4>(reinterpret_cast<const E*>(sl + C::OFF_HC + (16 * sub + ln) * C::RS) + perm_index(16 * t + 4 * g));
                 gc[h2] = load_vec<f32x4>(reinterpret_cast<const float*>(sl + C::OFF_G) + 16 * t + 4 * g);
             }
             // S' = Diag(gamma_C) S + Hc + PM S
@@ -486,25 +495,26 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S_final[sbase + (size_t)(32 * w + 16 * h2 + 4 * g + i) * DV + j0 + ln] = S[h2][i];
+                    S_final[sbase + (size_t)(32 * w + 16 * h2 + 4 * g + i) * DV + jc + ln] = S[h2][i];
         }
     } else if (wave == NSER) {
         // ------------------------------------------------ touch wave
         // Plain loads whose values are folded into `sink` three chunks later;
         // unconditional (clamped chunk index) so that each load writes its own
         // registers and the compiler has no reason to wait for it early.
-        // Lines touched per chunk: 1/NSL of PM (shared by the slices of a head),
-        // this slice's 16 rows of Hc^T, and gamma_C; QM and OI are not read here.
+        // Lines touched per chunk: 1/NWG of PM (shared by the workgroups of a
+        // head), this workgroup's 16 SW rows of Hc^T, and gamma_C; QM and OI are
+        // not read here.
         using TouchSet = uint32_t[C::TOUCH_PER_LANE];
         uint32_t toff[C::TOUCH_PER_LANE];
 #pragma unroll
         for (int k = 0; k < C::TOUCH_PER_LANE; ++k) {
             const int u = l + 64 * k;
             constexpr int PM_LINES = DK * DK * (int)sizeof(E) / 128;
-            constexpr int HC_LINES = 16 * DK * (int)sizeof(E) / 128;
-            constexpr int PM_MINE = PM_LINES / NSL;
+            constexpr int HC_LINES = 16 * SW * DK * (int)sizeof(E) / 128;
+            constexpr int PM_MINE = PM_LINES / NWG;
             size_t x;
-            if (u < PM_MINE) x = C::RL.pm + 128 * (size_t)(slice + NSL * u);
+            if (u < PM_MINE) x = C::RL.pm + 128 * (size_t)(slice + NWG * u);
             else if (u < PM_MINE + HC_LINES) x = C::RL.hc + (size_t)j0 * DK * sizeof(E) + 128 * (size_t)(u - PM_MINE);
             else x = C::RL.g + 128 * (size_t)((u - PM_MINE - HC_LINES) % (DK * 4 / 128));
             toff[k] = (uint32_t)x;
@@ -528,14 +538,16 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
         // rewritten only after the barrier that ends chunk it) to chunk_states,
         // fp32 [chunk][H][DK][DV]: 16-byte stores of 4 columns of a row
         auto send_state = [&](int it) {
-            float* cs = chunk_states + ((size_t)(c_begin + it) * H + h) * DK * DV + j0;
+            if constexpr (SW == 1) {
+                float* cs = chunk_states + ((size_t)(c_begin + it) * H + h) * DK * DV + j0;
 #pragma unroll
-            for (int k = 0; k < DK * 4 / 64; ++k) {
-                const int u = l + 64 * k, row = u >> 2, qd = u & 3;
-                const f32x4 val = {cst[it % C::NX][4 * qd][row], cst[it % C::NX][4 * qd + 1][row],
-                                   cst[it % C::NX][4 * qd + 2][row], cst[it % C::NX][4 * qd + 3][row]};
-                // streaming stores: the records this kernel still has to read stay cached
-                __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(cs + (size_t)row * DV + 4 * qd));
+                for (int k = 0; k < DK * 4 / 64; ++k) {
+                    const int u = l + 64 * k, row = u >> 2, qd = u & 3;
+                    const f32x4 val = {cst[it % C::NX][4 * qd][row], cst[it % C::NX][4 * qd + 1][row],
+                                       cst[it % C::NX][4 * qd + 2][row], cst[it % C::NX][4 * qd + 3][row]};
+                    // streaming stores: the records this kernel still has to read stay cached
+                    __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(cs + (size_t)row * DV + 4 * qd));
+                }
             }
         };
         auto step = [&](TouchSet& tv, int it) {
@@ -614,18 +626,45 @@ __global__ __launch_bounds__(64 * (DK / 32 + 5)) void prefill_state_ring_kernel(
     }
 }
 
-template <typename E, int DK, int DV>
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+template <typename E, int DK, int DV, int SW>
 static hipError_t launch_state_ring_t(const void* rec, ChunkSrc src, const float* S0, float* S_final,
                                       void* states, float* chunk_states, int H, hipStream_t stream)
 {
-    using C = RingCfg<E, DK, DV>;
+    using C = RingCfg<E, DK, DV, SW>;
     const int n_pairs = src.N * H;
     const int groups = (n_pairs + 7) / 8;
-    const long long blocks = (long long)groups * 8 * (DV / 16);
-    hipLaunchKernelGGL((prefill_state_ring_kernel<E, DK, DV>), dim3((unsigned)blocks),
+    const long long blocks = (long long)groups * 8 * C::NWG;
+    hipLaunchKernelGGL((prefill_state_ring_kernel<E, DK, DV, SW>), dim3((unsigned)blocks),
                        dim3(64 * C::WAVES), 0, stream, (const unsigned char*)rec, src, S0, S_final,
                        (E*)states, chunk_states, H, n_pairs);
     return hipGetLastError();
+}
+
+// Two value slices per workgroup once the one-slice grid has more chains
+// than the device has CUs (each workgroup takes a CU): a CU then moves each
+// chunk's PM once for both slices.  Not with chunk_states (its fp32 staging
+// is sized for one slice).
+template <typename E, int DK, int DV>
+static hipError_t launch_state_ring(const void* rec, ChunkSrc src, const float* S0, float* S_final,
+                                    void* states, float* chunk_states, int H, hipStream_t stream)
+{
+    const bool wide = !chunk_states && (long long)src.N * H * (DV / 16) > device_cus();
+    return wide ? launch_state_ring_t<E, DK, DV, 2>(rec, src, S0, S_final, states, chunk_states, H, stream)
+                : launch_state_ring_t<E, DK, DV, 1>(rec, src, S0, S_final, states, chunk_states, H, stream);
 }
 
 template <typename E, int DK, int DV>
@@ -647,7 +686,7 @@ hipError_t launch_prefill_state(const void* rec, ChunkSrc src, const float* S0, 
 {
 #define KDA_RING_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
-        return launch_state_ring_t<E, DK_, DV_>(rec, src, S0, S_final, states, chunk_states, H, stream);
+        return launch_state_ring<E, DK_, DV_>(rec, src, S0, S_final, states, chunk_states, H, stream);
 #define KDA_STATE_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
         return launch_state_t<E, DK_, DV_>(rec, src, S0, S_final, o, chunk_states, H, stream);

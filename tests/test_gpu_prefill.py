@@ -50,6 +50,20 @@ def test_varlen_edges(dtype):
     check_prefill(x, label="varlen edges")
 
 
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("bf16", 64, 64), ("bf16", 128, 64),
+                                         ("f32", 64, 128)])
+def test_many_chains(dtype, dk, dv):
+    """More (sequence, head, 16-column) chains than the GPU has CUs, so the
+    sequential kernel takes two value slices per workgroup: a packed batch of
+    40 sequences with an empty and a one-token one, nonzero initial states."""
+    g = np.random.default_rng(33)
+    lens = [int(n) for n in g.integers(0, 150, 40)]
+    lens[3], lens[7] = 0, 1
+    x = gen.make_prefill(33, lens, H=8, dk=dk, dv=dv, dtype=dtype, mu=3.0, state_std=0.02,
+                         packed=True)
+    check_prefill(x, label=f"many chains {dk}x{dv}")
+
+
 def test_config2_single_sequence():
     x = gen.config_prefill(2)
     check_prefill(x, label="config 2")
