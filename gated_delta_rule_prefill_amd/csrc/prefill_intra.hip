@@ -12,7 +12,7 @@
 //   g_r       = sum_{j<=r} log alpha_j             per channel (cumulative log-decay)
 //   A_kk[r,i] = beta_r sum_c k_rc k_ic e^{g_rc - g_ic}, i < r
 //   A_qk[r,i] =        sum_c q_rc k_ic e^{g_rc - g_ic}, i <= r
-//   T         = (I + A_kk)^{-1} Diag(beta)         blocked substitution in LDS
+//   T         = (I + A_kk)^{-1} Diag(beta)         blockwise, see below
 //   W         = T (e^g * K),   U = T V             MFMA
 //   Khat      = e^{g_C - g} * K,   Qg = e^g * Q,   gamma_C = e^{g_C}
 //
@@ -55,7 +55,7 @@ struct IntraLayout {
     static constexpr int LK = DK + PAD;              // row stride of [64][DK] arrays
     static constexpr int LT = CHUNK + PAD;           // row stride of [d][64] / [64][64] arrays
     static constexpr int LA = CHUNK + 4;             // row stride of the fp32 A / X array
-    // region U1: phase 1 KP|QP and KD; phase 3-4 kgT and vT; phase 5 QA (fp32 A_qk W)
+    // region U1: phase 0b-1 KP and KD; phase 3-4 kgT and vT; phase 5-6 QA (fp32 A_qk W)
     static constexpr int P1_BYTES = 2 * CHUNK * LK * ES;
     static constexpr int P2_BYTES = (DK + DV) * LT * ES;
     static constexpr int P5_BYTES = CHUNK * (DK + 4) * 4;
