@@ -384,7 +384,7 @@ kda_status kda_decode_tokens(float* state_pool, int32_t num_slots, const int32_t
             return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs, H and num_slots must be >= 1");
         if (total_tokens < 0 || total_tokens > 0x7fffffffLL)
             return fail(KDA_ERR_INVALID_ARGUMENT, "total_tokens must be in [0, 2^31)");
-        const long long blocks = (long long)num_seqs * H * (dv > 64 ? dv / 64 : 1);
+        const long long blocks = (long long)num_seqs * H;   // one workgroup per (sequence, head)
         if (blocks > 0x7fffffffLL || (long long)num_slots * H > 0x7fffffffLL)
             return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs * H or num_slots * H too large");
         if (!supported_dim(dk) || !supported_dim(dv))
