@@ -16,115 +16,77 @@
 
 namespace kda {
 
-// Value columns per workgroup (measured on MI355X with 256 x 32 heads of
-// 128 x 128 fp32 state: 64 columns beat 128, 32 and 16).
-constexpr int DECODE_COLS = 64;
-
-// One workgroup of 256 threads per (sequence, head, CB value columns): the
-// reductions over key channels are per value column, so column slices of a
-// head are independent.  Thread t owns columns c0 + 4*(t % NQ) .. +3 and key
-// rows rg, rg + RG, ... with rg = t / NQ, so each row of the slice is read by
-// NQ consecutive threads as 16-byte vectors.  Smaller slices mean fewer rows
-// per thread, fewer registers and more workgroups in flight per CU.
-template <typename E, int DK, int DV, int CB>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+// One workgroup per (sequence, head), DV/32 waves: wave w owns value columns
+// 32w .. 32w + 31 for every key row; lane l holds columns 32w + 4(l & 7) .. +3
+// of the DK/8 consecutive rows starting at (DK/8)(l >> 3), so the 8 lanes of
+// a row group read whole 128-byte rows of the state.  Each lane loads its own
+// rows' alpha, k and q, and the sums over key rows (S'^T k, S'^T q for the
+// lane's 4 columns, q . k) stay inside the wave: no LDS and no barrier, so
+// every wave streams its part of the state independently.  Plain loads and
+// streaming stores for the state (measured fastest; an earlier layout with
+// one workgroup per 64 columns and partial sums over four waves reached
+// 5.8 TB/s on the 512 MiB state, this one 6.2).
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(64 * (DV / 32)) void decode_step_kernel(
     float* __restrict__ state, const E* __restrict__ q, const E* __restrict__ k,
     const E* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, E* __restrict__ o)
 {
-    constexpr int NQ = CB / 4;       // column quads of the slice
-    constexpr int RG = 256 / NQ;     // row groups
-    constexpr int RPT = DK / RG;     // rows per thread
-    constexpr int WAVES = 4;
-    constexpr int NPART = DV / CB;   // slices per head
-    static_assert(DK % RG == 0 && RPT >= 1 && DV % CB == 0, "row / column split");
+    constexpr int RPL = DK / 8;   // key rows per lane
+    const int u = blockIdx.x;     // sequence * H + head
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int quad = lane & 7, rg = lane >> 3;
+    const int c0 = 32 * wave + 4 * quad, r0 = RPL * rg;
+    // value index of this lane after the row-group sums: 0..3 -> p, 4..7 -> r
+    const int vi = 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
+    float* S = state + (size_t)u * DK * DV;
 
-    __shared__ float s_q[DK], s_k[DK], s_a[DK];
-    __shared__ f32x4 s_p[WAVES][NQ], s_r[WAVES][NQ];
-    __shared__ float s_qk;
-
-    const int u = blockIdx.x / NPART;         // sequence * H + head
-    const int c0 = (blockIdx.x % NPART) * CB; // first value column of the slice
-    const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    const int jq = t % NQ, rg = t / NQ;
-    float* S = state + (size_t)u * DK * DV + c0;
-
-    // Issue the state loads first: they dominate and do not depend on q/k.
-    // Plain (cached) loads and streaming stores measured fastest: 5.8 TB/s on
-    // the 512 MiB state against 5.5 with streaming loads.
-    f32x4 s[RPT];
+    // the state loads first: they dominate and depend on nothing else
+    f32x4 s[RPL];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int c = rg + RG * m;
-        s[m] = *(reinterpret_cast<const f32x4*>(S + (size_t)c * DV) + jq);
-    }
-
-    for (int c = t; c < DK; c += 256) {
-        s_q[c] = to_f32(q[(size_t)u * DK + c]);
-        s_k[c] = to_f32(k[(size_t)u * DK + c]);
-        s_a[c] = __expf(log_alpha[(size_t)u * DK + c]);
-    }
-    if (wave == 0) {
-        float acc = 0.f;
-        for (int c = lane; c < DK; c += 64)
-            acc += to_f32(q[(size_t)u * DK + c]) * to_f32(k[(size_t)u * DK + c]);
+    for (int m = 0; m < RPL; ++m) s[m] = *reinterpret_cast<const f32x4*>(S + (size_t)(r0 + m) * DV + c0);
+    float la[RPL], kk[RPL], qq[RPL];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        if (lane == 0) s_qk = acc;
-    }
-    __syncthreads();
-
-    f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
+    for (int m4 = 0; m4 < RPL / 4; ++m4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(log_alpha + (size_t)u * DK + r0 + 4 * m4);
+        const typename Vec<E>::v4 k4 = load_vec<typename Vec<E>::v4>(k + (size_t)u * DK + r0 + 4 * m4);
+        const typename Vec<E>::v4 q4 = load_vec<typename Vec<E>::v4>(q + (size_t)u * DK + r0 + 4 * m4);
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int c = rg + RG * m;
-        s[m] *= s_a[c];
-        p += s_k[c] * s[m];
-        r += s_q[c] * s[m];
-    }
-    // Reduce over the row groups inside the wave (lanes that share jq) ...
-#pragma unroll
-    for (int off = NQ; off < 64; off <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[i] += __shfl_xor(p[i], off);
-            r[i] += __shfl_xor(r[i], off);
+        for (int e = 0; e < 4; ++e) {
+            la[4 * m4 + e] = l4[e];
+            kk[4 * m4 + e] = to_f32(k4[e]);
+            qq[4 * m4 + e] = to_f32(q4[e]);
         }
     }
-    // ... then across the four waves.
-    if (lane < NQ) {
-        s_p[wave][jq] = p;
-        s_r[wave][jq] = r;
-    }
-    __syncthreads();
-    p = s_p[0][jq];
-    r = s_r[0][jq];
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w) {
-        p += s_p[w][jq];
-        r += s_r[w][jq];
-    }
-
+    const int jv = 32 * wave + 4 * quad + (vi & 3);   // the column of this lane's sum
+    const float vj = to_f32(v[(size_t)u * DV + jv]);
     const float b = beta[u];
-    const typename Vec<E>::v4 vv = load_vec<typename Vec<E>::v4>(v + (size_t)u * DV + c0 + 4 * jq);
-    f32x4 nu;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) nu[i] = b * (to_f32(vv[i]) - p[i]);
 
-    if (rg == 0) {
-        typename Vec<E>::v4 ov;
+    f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
+    float qk = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = from_f32<E>(r[i] + s_qk * nu[i]);
-        store_vec(o + (size_t)u * DV + c0 + 4 * jq, ov);
+    for (int m = 0; m < RPL; ++m) {
+        s[m] *= __expf(la[m]);
+        p += kk[m] * s[m];
+        r += qq[m] * s[m];
+        qk += qq[m] * kk[m];
     }
-
+    qk += lane_xor<8>(qk);
+    qk += lane_xor<16>(qk);
+    qk += lane_xor<32>(qk);
+    const float part[8] = {p[0], p[1], p[2], p[3], r[0], r[1], r[2], r[3]};
+    const float tot = rowgroup_sum8(part, lane);
+    // lanes with vi < 4 hold p_j and form nu_j; the partner lane (xor 32)
+    // holds r_j and writes o_j = r_j + (q . k) nu_j
+    const float nu = vi < 4 ? b * (vj - tot) : 0.f;
+    const float nu_p = lane_xor<32>(nu);
+    if (vi >= 4) o[(size_t)u * DV + jv] = from_f32<E>(tot + qk * nu_p);
+    f32x4 nu4;   // nu of this lane's 4 columns, from the lanes (quad, vi = 0..3)
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int c = rg + RG * m;
-        f32x4 out = s[m] + s_k[c] * nu;
-        __builtin_nontemporal_store(out, reinterpret_cast<f32x4*>(S + (size_t)c * DV) + jq);
-    }
+    for (int e = 0; e < 4; ++e) nu4[e] = __shfl(nu, quad + 8 * e);
+#pragma unroll
+    for (int m = 0; m < RPL; ++m)
+        __builtin_nontemporal_store(s[m] + kk[m] * nu4, reinterpret_cast<f32x4*>(S + (size_t)(r0 + m) * DV + c0));
 }
 
 template <typename E, int DK, int DV>
@@ -132,9 +94,8 @@ static hipError_t launch_decode(float* state, const void* q, const void* k, cons
                                 const float* la, const float* beta, void* o, int units,
                                 hipStream_t stream)
 {
-    constexpr int CB = DECODE_COLS < DV ? DECODE_COLS : DV;
-    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, CB>), dim3(units * (DV / CB)), dim3(256), 0,
-                       stream, state, (const E*)q, (const E*)k, (const E*)v, la, beta, (E*)o);
+    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV>), dim3(units), dim3(64 * (DV / 32)), 0, stream,
+                       state, (const E*)q, (const E*)k, (const E*)v, la, beta, (E*)o);
     return hipGetLastError();
 }
 

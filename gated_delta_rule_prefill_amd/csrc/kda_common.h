@@ -130,6 +130,19 @@ __device__ __forceinline__ float wave_sum8(const float (&a)[8], int lane) {
     d += lane_xor<1>(d);
     return d;
 }
+// Sums of 8 values over the lanes that share bits 0-2 of the lane index
+// (a transposing butterfly over lane bits 3-5: 7 exchanges).  Lane l gets
+// the total of a[4 b5 + 2 b4 + b3] over its 8 lanes, b_i bit i of l.
+__device__ __forceinline__ float rowgroup_sum8(const float (&a)[8], int lane) {
+    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
+    float b[4], c[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = (h5 ? a[4 + j] : a[j]) + lane_xor<32>(h5 ? a[j] : a[4 + j]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) c[j] = (h4 ? b[2 + j] : b[j]) + lane_xor<16>(h4 ? b[j] : b[2 + j]);
+    return (h3 ? c[1] : c[0]) + lane_xor<8>(h3 ? c[0] : c[1]);
+}
+
 __device__ __forceinline__ float read_lane(float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }

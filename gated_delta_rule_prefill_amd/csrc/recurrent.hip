@@ -25,19 +25,6 @@ namespace kda {
 
 constexpr int REC_TB = 16;     // tokens staged per LDS fill
 
-// Sums of 8 values over the lanes that share bits 0-2 of the lane index
-// (a transposing butterfly over lane bits 3-5: 7 exchanges).  Lane l gets
-// the total of a[4 b5 + 2 b4 + b3] over its 8 lanes, b_i bit i of l.
-__device__ __forceinline__ float rowgroup_sum8(const float (&a)[8], int lane) {
-    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
-    float b[4], c[2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = (h5 ? a[4 + j] : a[j]) + lane_xor<32>(h5 ? a[j] : a[4 + j]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) c[j] = (h4 ? b[2 + j] : b[j]) + lane_xor<16>(h4 ? b[j] : b[2 + j]);
-    return (h3 ? c[1] : c[0]) + lane_xor<8>(h3 ? c[0] : c[1]);
-}
-
 template <typename E, int DK, int DV, bool NORM>
 __global__ __launch_bounds__(64 * (DV / 32)) void recurrent_kernel(
     float* __restrict__ pool, int num_slots, const int32_t* __restrict__ slots,
