@@ -109,3 +109,75 @@ def prefill(x: "gen.KDAInputs", C: int, transition: bool = False):
             O[a:b, h], F[s, h] = fn(q[a:b, h], k[a:b, h], v[a:b, h], la[a:b, h], be[a:b, h],
                                     S0, C)
     return O, F
+
+
+def chunk_backward(q, k, v, la, beta, S, dS, dO):
+    """Reverse mode through one chunk (fp64).  S: state entering the chunk,
+    dS: gradient of the loss with respect to the state leaving it, dO: with
+    respect to the chunk's outputs.  Returns (dq, dk, dv, dla, dbeta, dS_in),
+    dS_in being the gradient with respect to the entering state.
+
+    Every input gradient of a chunk depends only on the chunk, S and dS; the
+    entering-state gradient follows the transpose of the forward transition,
+    dS_in = Diag(gamma_C) dS + Qg^T dO - W^T dN = (Diag(gamma_C) + PM^T) dS + QM^T dO.
+    """
+    n = k.shape[0]
+    t = chunk_terms(q, k, v, la, beta)
+    g, Aqk, Tm, W, U, Khat, Qg = (t[a] for a in ("g", "Aqk", "T", "W", "U", "Khat", "Qg"))
+    gam, gC = np.exp(g), t["gC"]
+    E = np.exp(g[:, None, :] - g[None, :, :])              # E[r, i, c] = exp(g_rc - g_ic)
+    strict = np.tri(n, k=-1, dtype=bool)
+    L = np.where(strict, np.einsum("rc,ic,ric->ri", k, k, E), 0.0)   # A_kk without beta
+    X = np.linalg.inv(np.eye(n) + beta[:, None] * L)
+    N = U - W @ S
+    # through O = Qg S + A_qk N and S_C = Diag(gamma_C) S + Khat^T N
+    dN = Aqk.T @ dO + Khat @ dS
+    dS_in = gC[:, None] * dS + Qg.T @ dO - W.T @ dN
+    dQg = dO @ S.T
+    dAqk = np.tril(dO @ N.T)
+    dKhat = N @ dS.T
+    # through N = U - W S, W = T (e^g K), U = T V, T = X Diag(beta), X = (I + A_kk)^{-1}
+    dW = -dN @ S.T
+    dT = np.tril(dW @ (gam * k).T + dN @ v.T)
+    dKg = Tm.T @ dW
+    dv = Tm.T @ dN
+    dbeta = np.sum(dT * X, axis=0)
+    dA = np.where(strict, -(X.T @ (dT * beta[None, :]) @ X.T), 0.0)
+    dbeta += np.sum(dA * L, axis=1)
+    dL = beta[:, None] * dA
+    # the decayed products M[r, i] = sum_c a_rc b_ic exp(g_rc - g_ic)
+    def through(dM, a, b):
+        da = np.einsum("ri,ic,ric->rc", dM, b, E)
+        db = np.einsum("ri,rc,ric->ic", dM, a, E)
+        return da, db
+    daL, dbL = through(dL, k, k)
+    daQ, dbQ = through(dAqk, q, k)
+    eh = np.exp(g[-1][None, :] - g)                       # exp(g_C - g); gC is exp(g_C)
+    dq = gam * dQg + daQ
+    dk = gam * dKg + eh * dKhat + daL + dbL + dbQ
+    dg = q * gam * dQg + k * gam * dKg - k * eh * dKhat + k * daL - k * dbL + q * daQ - k * dbQ
+    dg[-1] += np.sum(k * eh * dKhat, axis=0) + gC * np.sum(S * dS, axis=1)
+    dla = np.cumsum(dg[::-1], axis=0)[::-1]
+    return dq, dk, dv, dla, dbeta, dS_in
+
+
+def head_backward(q, k, v, la, beta, S0, dO, dSf, C):
+    """One head of one sequence, chunk by chunk in reverse (fp64).  Returns
+    (dq, dk, dv, dla, dbeta, dS0)."""
+    T = q.shape[0]
+    starts = list(range(0, T, C))
+    states, S = [], S0.copy()
+    for c0 in starts:                        # chunk-entry states (forward)
+        sl = slice(c0, min(c0 + C, T))
+        t = chunk_terms(q[sl], k[sl], v[sl], la[sl], beta[sl])
+        states.append(S)
+        S = t["gC"][:, None] * S + t["Khat"].T @ (t["U"] - t["W"] @ S)
+    out = [np.zeros_like(a) for a in (q, k, v, la)] + [np.zeros_like(beta)]
+    dS = dSf.copy()
+    for c0, S in zip(reversed(starts), reversed(states)):
+        sl = slice(c0, min(c0 + C, T))
+        r = chunk_backward(q[sl], k[sl], v[sl], la[sl], beta[sl], S, dS, dO[sl])
+        for o, g in zip(out, r[:5]):
+            o[sl] = g
+        dS = r[5]
+    return (*out, dS)

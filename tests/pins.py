@@ -480,10 +480,39 @@ def pin_backward_linear_part(orc):
     assert np.array_equal(gr["dinitial_state"][1], d_fin[1])
 
 
+def pin_chunkwise_backward(orc):
+    """The reverse mode of the chunkwise form (chunkwise_mirror.chunk_backward:
+    entering-state gradients chained through the transposed chunk
+    transitions, every input gradient chunk-local) gives the oracle's
+    token-by-token gradients, for chunk sizes that do and do not divide the
+    lengths."""
+    x = _case(34, 0, 2, 8, 6, mu=1.0, lengths=[37, 0, 20, 64])
+    g = np.random.default_rng(34)
+    d_o = g.standard_normal((x.T, x.H, x.dv))
+    d_fin = g.standard_normal((x.num_seqs, x.H, x.dk, x.dv))
+    gr = orc.backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.initial_state, x.cu_seqlens, d_o, d_fin)
+    q, k, v = (_f64(a) for a in (x.q, x.k, x.v))
+    la, be = x.log_alpha.astype(np.float64), x.beta.astype(np.float64)
+    offs = np.concatenate([[0], np.cumsum(x.lengths())])
+    for C in (7, 16, 64):
+        got = {n: np.zeros(gr[n].shape) for n in gr}
+        for s in range(x.num_seqs):
+            a, b = offs[s], offs[s + 1]
+            for h in range(x.H):
+                r = chunkwise_mirror.head_backward(q[a:b, h], k[a:b, h], v[a:b, h], la[a:b, h],
+                                                   be[a:b, h], x.initial_state[s, h].astype(np.float64),
+                                                   d_o[a:b, h], d_fin[s, h], C)
+                for n, val in zip(("dq", "dk", "dv", "dlog_alpha", "dbeta"), r[:5]):
+                    got[n][a:b, h] = val
+                got["dinitial_state"][s, h] = r[5]
+        for n in gr:
+            assert rel_err(got[n], gr[n]) < 1e-12, (C, n, rel_err(got[n], gr[n]))
+
+
 ALL_PINS = [pin_transition_product, pin_exact_rational, pin_identity_no_write, pin_pure_decay,
             pin_deltanet, pin_gated_deltanet, pin_exact_recall, pin_one_hot_linear_attention,
             pin_one_hot_rows, pin_single_token, pin_chunkwise_algebra, pin_chunk_transition_form,
             pin_packing,
             pin_decode_matches_prefill, pin_linearity, pin_non_expansive,
             pin_state_snapshots, pin_qk_l2_normalisation, pin_beta_logit, pin_pooled_tokens,
-            pin_backward_finite_differences, pin_backward_linear_part]
+            pin_backward_finite_differences, pin_backward_linear_part, pin_chunkwise_backward]
