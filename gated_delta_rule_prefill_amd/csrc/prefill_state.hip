@@ -312,12 +312,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 //       the fp32 state tile of value slice w / (DK/32); per
 //       chunk each applies S' = Diag(gamma_C) S + Hc + PM S to its rows (8
 //       MFMAs), reading the whole chunk-start state as bf16 operand slots from
-//       LDS and writing its own rows' slots for the next chunk, to LDS and to
-//       the chunk-state buffer.  A 16x16 accumulator tile gives lane group g
-//       rows 4g..4g+3, so the two tiles of rows 32w.. are exactly operand
-//       step w of the next product;
-//   touch wave  touches every line of chunk it + TOUCH_DIST so that the direct
-//       loads hit L2 (plain loads, folded into a value three chunks later);
+//       LDS and writing its own rows' slots for the next chunk to LDS.  A
+//       16x16 accumulator tile gives lane group g rows 4g..4g+3, so the two
+//       tiles of rows 32w.. are exactly operand step w of the next product;
+//   touch wave  copies each chunk-start state slot from LDS to the
+//       chunk-state buffer (keeping those stores off the serial waves'
+//       chain) and, for chains of TOUCH_MIN_CHUNKS or more, touches every
+//       line of chunk it + TOUCH_DIST so that the direct loads hit L2 (plain
+//       loads, folded into a value three chunks later);
 //   stager waves (4)  move PM, this slice's Hc^T rows and gamma_C into a
 //       three-slot LDS ring by direct global->LDS loads
 //       (global_load_lds_dwordx4), two chunks ahead, each a quarter of them
@@ -358,6 +360,10 @@ struct RingCfg {
 };
 
 constexpr int TOUCH_DIST = 6;   // chunks between the L2 touch and the first direct load
+// Chains shorter than this skip the touches: their records are mostly
+// cache-resident already (the intra kernel's grid order), and the touches'
+// own misses delay the workgroup's other loads (a CU returns data in order).
+constexpr int TOUCH_MIN_CHUNKS = 256;
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (lgkm and exp counters left free).
@@ -436,8 +442,8 @@ __global__ __launch_bounds__(64 * (SW * DK / 32 + 5)) void prefill_state_ring_ke
                 for (int i = 0; i < 4; ++i)
                     S[h2][i] = S0[sbase + (size_t)(32 * w + 16 * h2 + 4 * g + i) * DV + jc + ln];
         }
-        // chunk-start state of chunk it, this wave's operand step, to LDS and to
-        // the chunk-state buffer ([chunk, head][slice][step][lane][8])
+        // chunk-start state of chunk it, this wave's operand step, to LDS (the
+        // touch wave copies the slot to the chunk-state buffer)
         auto put = [&](int it) {
             V8 f;
 #pragma unroll
@@ -446,9 +452,6 @@ __global__ __launch_bounds__(64 * (SW * DK / 32 + 5)) void prefill_state_ring_ke
                 f[4 + i] = from_f32<E>(S[1][i]);
             }
             store_vec(xslot(it) + ((sub * KS + w) * 64 + l) * 8, f);
-            if (it < n)
-                store_vec(states + ((size_t)(c_begin + it) * H + h) * DK * DV +
-                              ((size_t)((slice * SW + sub) * KS + w) * 64 + l) * 8, f);
             if constexpr (SW == 1) {
                 if (chunk_states) {
 #pragma unroll
@@ -519,10 +522,12 @@ __global__ __launch_bounds__(64 * (SW * DK / 32 + 5)) void prefill_state_ring_ke
             else x = C::RL.g + 128 * (size_t)((u - PM_MINE - HC_LINES) % (DK * 4 / 128));
             toff[k] = (uint32_t)x;
         }
+        const bool touching = n >= TOUCH_MIN_CHUNKS;   // uniform over the workgroup
         auto touch = [&](TouchSet& tv, int c) {
             const unsigned char* r = record(c);
 #pragma unroll
-            for (int k = 0; k < C::TOUCH_PER_LANE; ++k) tv[k] = *reinterpret_cast<const uint32_t*>(r + toff[k]);
+            for (int k = 0; k < C::TOUCH_PER_LANE; ++k)
+                tv[k] = touching ? *reinterpret_cast<const uint32_t*>(r + toff[k]) : 0u;
         };
         uint32_t sink = 0;
         TouchSet tv0, tv1, tv2;
@@ -550,9 +555,21 @@ __global__ __launch_bounds__(64 * (SW * DK / 32 + 5)) void prefill_state_ring_ke
                 }
             }
         };
+        // chunk-start state `it` as operand slots (in xfer slot it since the barrier
+        // that ended chunk it - 1, rewritten only after the barrier that ends chunk
+        // it + 1) to the chunk-state buffer [chunk, head][slice][step][lane][8]:
+        // the workgroup's slices are one contiguous run of XSLOT bytes
+        auto send_operands = [&](int it) {
+            const f32x4* from = reinterpret_cast<const f32x4*>(xslot(it));
+            f32x4* to = reinterpret_cast<f32x4*>(states + ((size_t)(c_begin + it) * H + h) * DK * DV +
+                                                 (size_t)slice * SW * KS * 64 * 8);
+#pragma unroll
+            for (int k = 0; k < C::XSLOT / 16 / 64; ++k) to[l + 64 * k] = from[l + 64 * k];
+        };
         auto step = [&](TouchSet& tv, int it) {
             fold(tv);   // issued three chunks ago
             touch(tv, min(it + TOUCH_DIST, n - 1));
+            send_operands(it);
             if (chunk_states) send_state(it);
             bare_barrier();
         };
