@@ -88,6 +88,32 @@ __device__ __forceinline__ void store_vec<f32x8, float>(float* p, f32x8 v) {
     *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
+// -- fragment-ordered storage ---------------------------------------------------
+// A matrix that is only ever read as A operands of the 16x16x32 products
+// (the chunk transition PM of the state recursion) is stored fragment by
+// fragment in lane order: fragment (t, ks) -- rows 16t..16t+15, contraction
+// block ks -- takes 512 elements from frag_at(t, ks); inside it lane l's 8
+// slots are the 16 bytes at lane l (bf16), or two 16-byte planes of 64 lanes
+// (fp32: slots 0..3, then 4..7).  Every 16-byte access of a wave then covers
+// 1 KiB contiguously.
+template <int KS>
+__host__ __device__ constexpr int frag_at(int t, int ks) { return (t * KS + ks) * 512; }
+__device__ __forceinline__ bf16x8 load_frag(const bf16* f, int l) {
+    return *reinterpret_cast<const bf16x8*>(f + 8 * l);
+}
+__device__ __forceinline__ f32x8 load_frag(const float* f, int l) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(f + 4 * l);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(f + 256 + 4 * l);
+    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ void store_frag(bf16* f, int l, bf16x8 v) {
+    *reinterpret_cast<bf16x8*>(f + 8 * l) = v;
+}
+__device__ __forceinline__ void store_frag(float* f, int l, f32x8 v) {
+    *reinterpret_cast<f32x4*>(f + 4 * l) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(f + 256 + 4 * l) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
 // -- options of the layer's own input preprocessing ----------------------------

@@ -32,7 +32,8 @@ struct ChunkSrc {
 // a chunk's state update and output are
 //     S_next = Diag(gC) S + PM S + Hc,      O = QM S + OI
 // (the chunk's transition and read-out folded in by the intra kernel):
-//   PM   [dk][dk]   -Khat^T W, columns in perm32 order
+//   PM   dk x dk    -Khat^T W, columns in perm32 order, stored in fragment
+//                   order (frag_at: the A operands of the state product)
 //   HCt  [dv][dk]   (Khat^T U)^T, columns in perm32 order
 //   QM   [64][dk]   Qg - A_qk W, columns in perm32 order
 //   OI   [64][dv]   A_qk U, columns in perm32 order

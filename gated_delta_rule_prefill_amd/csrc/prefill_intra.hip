@@ -601,7 +601,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 2))) void prefill_intra_
                 w[i] = from_f32<E>(-acc[0][i]);
                 w[4 + i] = from_f32<E>(-acc[1][i]);
             }
-            store_vec(out.PM + (16 * a + ln) * DK + perm_index(16 * ct0 + 4 * g), w);
+            store_frag(out.PM + frag_at<DK / 32>(a, pr), lane, w);   // slots 8g .. 8g + 7 of block pr
         }
         // (A_qk W)[r][c'] for r = 16Rr + ln, c' = 16ct + 4g + i  (A_qk is causal)
 #pragma unroll

@@ -39,8 +39,7 @@ struct StateCfg {
     static constexpr int NSL = DV / 16;  // value slices per head
     static constexpr int FRAG = 8 * ES;  // bytes of one operand fragment per lane
     static constexpr int XSLOT = KS * 64 * FRAG;        // one chunk-start state hand-over
-    static constexpr int PM_RS = DK * ES + 16;          // padded LDS row stride of PM
-    static constexpr int PM_BYTES = DK * PM_RS;
+    static constexpr int PM_BYTES = DK * DK * ES;       // fragment order, as in the record
     static constexpr int PM_UNITS = DK * DK * ES / 16;
     static constexpr int STAGERS = 2;                   // waves 2 and 3
     static constexpr int PM_PER_LANE = PM_UNITS / (64 * STAGERS);
@@ -155,7 +154,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         SerialOps<E, DK> opA, opB;
         if (n > 0) load_serial<E, DK, DV>(opA, record(0), g, ln, j0);
-        const unsigned char* pm_lane = pmbuf + ln * C::PM_RS + 8 * g * ES;
         __syncthreads();
 
         auto step = [&](SerialOps<E, DK>& cur, SerialOps<E, DK>& nxt, int it) {
@@ -181,13 +179,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 }
                 store_vec(xs + (ks * 64 + l) * 8, Sf[ks]);
             }
-            const unsigned char* pm = pm_lane + (it & 1) * C::PM_BYTES;
+            const E* pm = reinterpret_cast<const E*>(pmbuf + (it & 1) * C::PM_BYTES);
             V8 pf[KT][KS];
 #pragma unroll
             for (int t = 0; t < KT; ++t)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    pf[t][ks] = load_vec<V8>(reinterpret_cast<const E*>(pm + 16 * t * C::PM_RS + 32 * ks * ES));
+                for (int ks = 0; ks < KS; ++ks) pf[t][ks] = load_frag(pm + frag_at<KS>(t, ks), l);
             // S' = Diag(gamma_C) S + Hc + PM S
 #pragma unroll
             for (int t = 0; t < KT; ++t)
@@ -268,13 +265,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int i = 0; i < C::PM_PER_LANE; ++i) pr[i] = src[sl + 128 * i];
         };
         auto pcommit = [&](int it) {
-            unsigned char* dst = pmbuf + (it & 1) * C::PM_BYTES;
-            constexpr int UPR = DK * ES / 16;   // 16-byte units per row
+            f32x4* dst = reinterpret_cast<f32x4*>(pmbuf + (it & 1) * C::PM_BYTES);
 #pragma unroll
-            for (int i = 0; i < C::PM_PER_LANE; ++i) {
-                const int x = sl + 128 * i;
-                *reinterpret_cast<f32x4*>(dst + (x / UPR) * C::PM_RS + 16 * (x % UPR)) = pr[i];
-            }
+            for (int i = 0; i < C::PM_PER_LANE; ++i) dst[sl + 128 * i] = pr[i];
         };
         if (n > 0) {
             pload(0);
@@ -305,25 +298,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // only the sequential chain; the outputs come from a separate parallel pass
 // over the chunk-start states this kernel stores.
 //
-// One workgroup per (sequence, head, 16 SW value columns), SW DK/32 + 5 waves
-// (SW = 2 for batches with more chains than CUs: the slices of a workgroup
-// share the PM it moves through its CU):
+// One workgroup per (sequence, head, 16 SW value columns), SW DK/32 serial
+// waves, a touch wave and 1 (SW = 1) or 4 (SW = 2) stager waves (SW = 2 for
+// batches with more chains than CUs: the slices of a workgroup share the PM
+// it moves through its CU):
 //   serial waves w < SW DK/32  own rows 32w'..32w'+31 (w' = w mod DK/32) of
 //       the fp32 state tile of value slice w / (DK/32); per
 //       chunk each applies S' = Diag(gamma_C) S + Hc + PM S to its rows (8
 //       MFMAs), reading the whole chunk-start state as bf16 operand slots from
 //       LDS and writing its own rows' slots for the next chunk to LDS.  A
 //       16x16 accumulator tile gives lane group g rows 4g..4g+3, so the two
-//       tiles of rows 32w.. are exactly operand step w of the next product;
+//       tiles of rows 32w.. are exactly operand step w of the next product.
+//       Their PM rows (fragment order in the record, 1 KiB per fragment) come
+//       from the ring slot when SW = 2, else straight from the record into a
+//       register ring PM_DIST - 1 chunks ahead: with one slice nothing shares
+//       them, and the LDS round trip would cost the CU twice the bytes;
 //   touch wave  copies each chunk-start state slot from LDS to the
 //       chunk-state buffer (keeping those stores off the serial waves'
 //       chain) and, for chains of TOUCH_MIN_CHUNKS or more, touches every
-//       line of chunk it + TOUCH_DIST so that the direct loads hit L2 (plain
-//       loads, folded into a value three chunks later);
-//   stager waves (4)  move PM, this slice's Hc^T rows and gamma_C into a
-//       three-slot LDS ring by direct global->LDS loads
-//       (global_load_lds_dwordx4), two chunks ahead, each a quarter of them
-//       (one wave issues such a load only every ~70 cycles).
+//       line of chunk it + TOUCH_DIST so that the loads hit L2 (plain loads,
+//       folded into a value three chunks later);
+//   stager waves  move this slice's Hc^T rows, gamma_C (and PM, SW = 2) into
+//       a three-slot LDS ring by direct global->LDS loads
+//       (global_load_lds_dwordx4), two chunks ahead.
 // Every wave passes one barrier per chunk.  A ring slot or state slot is
 // written only after the barrier that ends the chunk which last read it.
 template <typename E, int DK, int DV, int SW>
@@ -332,14 +329,17 @@ struct RingCfg {
     static constexpr int KS = DK / 32, KT = DK / 16, NSL = DV / 16;
     static constexpr int NWG = NSL / SW;             // workgroups per (sequence, head)
     static constexpr int NSER = KS * SW;             // serial waves
-    static constexpr int NSTG = 4;                   // stager waves
+    // PM through the LDS ring when two slices share it; with one slice each
+    // serial wave loads its own PM rows straight into registers
+    static constexpr bool PM_IN_RING = SW == 2;
+    static constexpr int NSTG = PM_IN_RING ? 4 : 1;  // stager waves
     static constexpr int WAVES = NSER + 1 + NSTG;    // + the touch wave
     static constexpr int FRAG = 8 * ES;
     static constexpr int XSLOT = SW * KS * 64 * FRAG;   // one chunk-start state (operand slots)
     static constexpr int NX = 2;                     // state slots: it (read), it + 1 (written)
     static constexpr int RW = DK * ES / 16;          // 16-byte units per PM / Hc^T row
     static constexpr int RS = (RW + 1) * 16;         // padded LDS row stride (bytes)
-    static constexpr int PM_UNITS = DK * (RW + 1);
+    static constexpr int PM_UNITS = PM_IN_RING ? DK * DK * ES / 16 : 0;   // fragment order: copied as is
     static constexpr int HC_UNITS = 16 * SW * (RW + 1);
     static constexpr int G_UNITS = DK / 4;
     static constexpr int UNITS = PM_UNITS + HC_UNITS + G_UNITS;
@@ -372,6 +372,12 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 typedef __attribute__((address_space(1))) void global_void;
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Register ring of PM fragment sets per serial wave: chunk c's loads are
+// issued while chunk c - PM_DIST + 1 is processed, PM_EARLY of its 2 DK/32
+// fragments before that chunk's MFMAs.
+constexpr int PM_DIST = 3;
+constexpr int PM_EARLY = 4;
+
 // Workgroup barrier for waves without LDS accesses of their own.
 // __syncthreads() carries a workgroup release fence, which makes a wave wait
 // for every outstanding direct load (they write LDS) -- including those meant
@@ -385,8 +391,17 @@ __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Barrier for the serial waves: their own LDS writes complete first, while
+// their PM loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt not waited on
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <typename E, int DK, int DV, int SW>
-__global__ __launch_bounds__(64 * (SW * DK / 32 + 5)) void prefill_state_ring_kernel(
+__global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_state_ring_kernel(
     const unsigned char* __restrict__ rec, const ChunkSrc src, const float* __restrict__ S0,
     float* __restrict__ S_final, E* __restrict__ states, float* __restrict__ chunk_states, int H,
     int n_pairs)
@@ -460,26 +475,54 @@ __global__ __launch_bounds__(64 * (SW * DK / 32 + 5)) void prefill_state_ring_ke
                 }
             }
         };
+        // PM rows 32w .. 32w + 31 of chunk c (clamped): this lane's A fragments
+        // of row tiles 2w, 2w + 1 -- from the ring slot (PM_IN_RING), else
+        // straight from the record into a register ring of PM_DIST sets
+        using PmSet = V8[2][KS];
+        constexpr int NSET = C::PM_IN_RING ? 1 : PM_DIST;
+        // fragments f0 .. f1 - 1 of a set (f: row tile 2w + (f & 1), step f >> 1)
+        auto pm_load = [&](PmSet& pf, int c, int f0, int f1) {
+            const E* pm = reinterpret_cast<const E*>(record(min(c, n - 1)) + C::RL.pm);
+#pragma unroll
+            for (int f = 0; f < 2 * KS; ++f)
+                if (f >= f0 && f < f1) pf[f & 1][f >> 1] = load_frag(pm + frag_at<KS>(2 * w + (f & 1), f >> 1), l);
+        };
+        PmSet pfr[NSET];
+        if constexpr (!C::PM_IN_RING) {
+#pragma unroll
+            for (int u = 0; u < PM_DIST - 1; ++u) pm_load(pfr[u], u, 0, 2 * KS);
+        }
         put(0);
-        __syncthreads();
-        for (int it = 0; it < n; ++it) {
+        lds_barrier();
+        // chunk it: the MFMAs take set pf; in the register ring, set pn (free
+        // since chunk it - 1) takes chunk it + PM_DIST - 1, its loads issued
+        // in two parts so that the CU's load path never holds a whole set of
+        // all serial waves at once: the first while the LDS operands of this
+        // chunk are in flight, the rest after the MFMAs
+        auto step = [&](PmSet& pf, PmSet& pn, int it) {
             const unsigned char* sl = slot(it);
             const E* xs = xslot(it);
             V8 Sf[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) Sf[ks] = load_vec<V8>(xs + ((sub * KS + ks) * 64 + l) * 8);
-            V8 pf[2][KS];
             V4 hc[2];
             f32x4 gc[2];
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const int t = 2 * w + h2;
-                const unsigned char* pm = sl + (16 * t + ln) * C::RS + 8 * g * sizeof(E);
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    pf[h2][ks] = load_vec<V8>(reinterpret_cast<const E*>(pm + 32 * ks * sizeof(E)));
                 hc[h2] = load_vec<V4>(reinterpret_cast<const E*>(sl + C::OFF_HC + (16 * sub + ln) * C::RS) + perm_index(16 * t + 4 * g));
                 gc[h2] = load_vec<f32x4>(reinterpret_cast<const float*>(sl + C::OFF_G) + 16 * t + 4 * g);
+            }
+            if constexpr (C::PM_IN_RING) {
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        pf[h2][ks] = load_frag(reinterpret_cast<const E*>(sl) + frag_at<KS>(2 * w + h2, ks), l);
+            } else {
+                __builtin_amdgcn_sched_barrier(0);   // LDS reads first, then the early loads
+                pm_load(pn, it + PM_DIST - 1, 0, PM_EARLY);
+                __builtin_amdgcn_sched_barrier(0);
             }
             // S' = Diag(gamma_C) S + Hc + PM S
 #pragma unroll
@@ -490,8 +533,23 @@ __global__ __launch_bounds__(64 * (SW * DK / 32 + 5)) void prefill_state_ring_ke
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) S[h2] = mma32(pf[h2][ks], Sf[ks], S[h2]);
+            if constexpr (!C::PM_IN_RING) pm_load(pn, it + PM_DIST - 1, PM_EARLY, 2 * KS);
             if (it + 1 < n) put(it + 1);
-            __syncthreads();
+            lds_barrier();
+        };
+        if constexpr (C::PM_IN_RING) {
+            for (int it = 0; it < n; ++it) step(pfr[0], pfr[0], it);
+        } else {
+            // whole rounds of the register ring without branches (so that each
+            // step waits only for its own set), then the remaining chunks
+            int it0 = 0;
+            for (; it0 + PM_DIST <= n; it0 += PM_DIST) {
+#pragma unroll
+                for (int u = 0; u < NSET; ++u) step(pfr[u], pfr[(u + NSET - 1) % NSET], it0 + u);
+            }
+#pragma unroll
+            for (int u = 0; u < NSET - 1; ++u)
+                if (it0 + u < n) step(pfr[u], pfr[(u + NSET - 1) % NSET], it0 + u);
         }
         if (S_final) {
 #pragma unroll
@@ -594,8 +652,7 @@ __global__ __launch_bounds__(64 * (SW * DK / 32 + 5)) void prefill_state_ring_ke
             const int u = 64 * (i0 + k) + l;
             int x;
             if (u < C::PM_UNITS) {
-                const int row = u / (C::RW + 1), col = u % (C::RW + 1);
-                x = (int)C::RL.pm + row * DK * (int)sizeof(E) + (col < C::RW ? col : 0) * 16;
+                x = (int)C::RL.pm + 16 * u;
             } else if (u < C::PM_UNITS + C::HC_UNITS) {
                 const int v = u - C::PM_UNITS;
                 const int row = v / (C::RW + 1), col = v % (C::RW + 1);
