@@ -109,6 +109,13 @@ __device__ __forceinline__ f32x8 load_frag(const float* f, int l) {
 __device__ __forceinline__ void store_frag(bf16* f, int l, bf16x8 v) {
     *reinterpret_cast<bf16x8*>(f + 8 * l) = v;
 }
+// elements 4h .. 4h + 3 of lane l (h = 0, 1)
+__device__ __forceinline__ bf16x4 load_frag_half(const bf16* f, int l, int h) {
+    return *reinterpret_cast<const bf16x4*>(f + 8 * l + 4 * h);
+}
+__device__ __forceinline__ f32x4 load_frag_half(const float* f, int l, int h) {
+    return *reinterpret_cast<const f32x4*>(f + 256 * h + 4 * l);
+}
 __device__ __forceinline__ void store_frag(float* f, int l, f32x8 v) {
     *reinterpret_cast<f32x4*>(f + 4 * l) = f32x4{v[0], v[1], v[2], v[3]};
     *reinterpret_cast<f32x4*>(f + 256 + 4 * l) = f32x4{v[4], v[5], v[6], v[7]};

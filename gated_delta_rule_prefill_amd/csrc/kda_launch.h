@@ -35,8 +35,9 @@ struct ChunkSrc {
 //   PM   dk x dk    -Khat^T W, columns in perm32 order, stored in fragment
 //                   order (frag_at: the A operands of the state product)
 //   HCt  [dv][dk]   (Khat^T U)^T, columns in perm32 order
-//   QM   [64][dk]   Qg - A_qk W, columns in perm32 order
-//   OI   [64][dv]   A_qk U, columns in perm32 order
+//   QM   [64][dk]   Qg - A_qk W, columns in perm32 order (row-major: it is
+//                   written from the row mapping, where a row is contiguous)
+//   OI   64 x dv    A_qk U, columns in perm32 order, in fragment order
 //   gC   [dk] fp32  e^{g_C}
 struct RecLayout {
     size_t pm, hc, qm, oi, g, bytes;

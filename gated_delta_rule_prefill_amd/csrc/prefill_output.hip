@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void prefill_output_kernel(
     float oi[NSL][4];
 #pragma unroll
     for (int m = 0; m < NSL / 2; ++m) {
-        const V8 v = load_vec<V8>(OI + r * DV + perm_index(32 * m + 4 * g));
+        const V8 v = load_frag(OI + frag_at<DV / 32>(wave, m), l);   // row r, slots 8g .. 8g + 7 of block m
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             oi[2 * m][i] = to_f32(v[i]);

@@ -86,11 +86,13 @@ __device__ __forceinline__ void load_output(OutputOps<E, DK>& op, const unsigned
     using V4 = typename Vec<E>::v4;
     const E* QM = reinterpret_cast<const E*>(r + C::RL.qm);
     const E* OI = reinterpret_cast<const E*>(r + C::RL.oi);
+    const int l = 16 * g + ln;
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) op.q[R][ks] = load_vec<V8>(QM + (16 * R + ln) * DK + 32 * ks + 8 * g);
-        op.oi[R] = load_vec<V4>(OI + (16 * R + ln) * DV + perm_index(j0 + 4 * g));
+        // OI[16R + ln][perm_index(j0 + 4g) ..]: half of fragment (R, j0/32)'s slots 8g .. 8g + 7
+        op.oi[R] = load_frag_half(OI + frag_at<DV / 32>(R, j0 >> 5), l, (j0 >> 4) & 1);
     }
     op.start = ci.start;
     op.len = ci.len;
