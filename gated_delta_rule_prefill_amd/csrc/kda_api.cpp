@@ -248,7 +248,8 @@ kda_status kda_prefill_ex(const void* q, const void* k, const void* v, const flo
                                   "state kernel", stream);
                 timer.mark("prefill_state");
             }
-            if (st == KDA_OK && plan.output_pass && total_tokens > 0) {
+            if (st == KDA_OK && plan.output_pass && total_tokens > 0 &&
+                !kda::state_pass_writes_output(bf16, dk, dv, src.N, H, chunk_states != nullptr)) {
                 st = check_launch(kda::launch_prefill_output(ws, states, src, (int)plan.max_chunks,
                                                              H, dk, dv, bf16, o, stream),
                                   "output kernel", stream);

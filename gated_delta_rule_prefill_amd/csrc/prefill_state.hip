@@ -335,7 +335,10 @@ struct RingCfg {
     // serial wave loads its own PM rows straight into registers
     static constexpr bool PM_IN_RING = SW == 2;
     static constexpr int NSTG = PM_IN_RING ? 4 : 1;  // stager waves
-    static constexpr int WAVES = NSER + 1 + NSTG;    // + the touch wave
+    // with one slice the chunks' outputs are formed here, by NOUT output waves
+    static constexpr bool FUSED_OUT = SW == 1;
+    static constexpr int NOUT = FUSED_OUT ? 2 : 0;
+    static constexpr int WAVES = NSER + 1 + NSTG + NOUT;   // + the touch wave
     static constexpr int FRAG = 8 * ES;
     static constexpr int XSLOT = SW * KS * 64 * FRAG;   // one chunk-start state (operand slots)
     static constexpr int NX = 2;                     // state slots: it (read), it + 1 (written)
@@ -344,13 +347,21 @@ struct RingCfg {
     static constexpr int PM_UNITS = PM_IN_RING ? DK * DK * ES / 16 : 0;   // fragment order: copied as is
     static constexpr int HC_UNITS = 16 * SW * (RW + 1);
     static constexpr int G_UNITS = DK / 4;
-    static constexpr int UNITS = PM_UNITS + HC_UNITS + G_UNITS;
+    // with the outputs formed here: QM rows, padded like Hc^T, and this
+    // slice's OI fragments (R, j0/32), R = 0 .. CHUNK/16 - 1
+    static constexpr int QM_UNITS = FUSED_OUT ? CHUNK * (RW + 1) : 0;
+    static constexpr int OI_FRAG_UNITS = 512 * ES / 16;
+    static constexpr int OI_UNITS = FUSED_OUT ? (CHUNK / 16) * OI_FRAG_UNITS : 0;
+    static constexpr int UNITS = PM_UNITS + HC_UNITS + G_UNITS + QM_UNITS + OI_UNITS;
     static constexpr int LOADS = (UNITS + 63) / 64;  // direct loads per chunk
     static constexpr int LOADS_W = (LOADS + NSTG - 1) / NSTG;   // per stager wave
     static constexpr int LOADS_LAST = LOADS - (NSTG - 1) * LOADS_W;   // the last stager's share
     static constexpr int SLOT = LOADS * 1024;
     static constexpr int OFF_HC = PM_UNITS * 16;
     static constexpr int OFF_G = OFF_HC + HC_UNITS * 16;
+    static constexpr int OFF_QM = OFF_G + G_UNITS * 16;
+    static constexpr int OFF_OI = OFF_QM + QM_UNITS * 16;
+    static constexpr int OUT_RPW = CHUNK / 16 / (NOUT > 0 ? NOUT : 1);   // row tiles per output wave
     static constexpr int NSLOT = 3;
     static constexpr int LDS_BYTES = NSLOT * SLOT + NX * XSLOT;
     static constexpr RecLayout RL = rec_layout(ES, DK, DV);
@@ -405,8 +416,8 @@ __device__ __forceinline__ void lds_barrier() {
 template <typename E, int DK, int DV, int SW>
 __global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_state_ring_kernel(
     const unsigned char* __restrict__ rec, const ChunkSrc src, const float* __restrict__ S0,
-    float* __restrict__ S_final, E* __restrict__ states, float* __restrict__ chunk_states, int H,
-    int n_pairs)
+    float* __restrict__ S_final, E* __restrict__ o, E* __restrict__ states,
+    float* __restrict__ chunk_states, int H, int n_pairs)
 {
     using C = RingCfg<E, DK, DV, SW>;
     using V4 = typename Vec<E>::v4;
@@ -629,7 +640,7 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_
         auto step = [&](TouchSet& tv, int it) {
             fold(tv);   // issued three chunks ago
             touch(tv, min(it + TOUCH_DIST, n - 1));
-            send_operands(it);
+            if constexpr (!C::FUSED_OUT) send_operands(it);
             if (chunk_states) send_state(it);
             bare_barrier();
         };
@@ -641,7 +652,48 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_
         fold(tv0);
         fold(tv1);
         fold(tv2);
-        if (n_pairs < 0) states[0] = from_f32<E>((float)sink);   // keeps the touches; never taken
+        if (n_pairs < 0) o[0] = from_f32<E>((float)sink);   // keeps the touches; never taken
+    } else if (wave >= NSER + 1 + C::NSTG) {
+        // ------------------------------------------------ output waves (one slice)
+        // O = QM S_c + OI for the chunk whose start state the serial waves
+        // handed over last: output wave ow takes row tiles 2 ow, 2 ow + 1 as
+        // O^T tiles (lane: row 16R + ln, columns j0 + 4g .. +3), the state
+        // slots as A operands and QM rows (ring slot) as B.
+        if constexpr (C::FUSED_OUT) {
+            const int ow = wave - (NSER + 1 + C::NSTG);
+            constexpr int RPW = C::OUT_RPW;
+            int n_all;
+            ChunkInfo first, last;   // token range of the sequence
+            chunk_of(src, c_begin, n_all, first);
+            chunk_of(src, c_begin + n - 1, n_all, last);
+            const int seq_len = CHUNK * (n - 1) + last.len;
+            bare_barrier();
+            for (int it = 0; it < n; ++it) {
+                const unsigned char* sl = slot(it);
+                const E* xs = xslot(it);   // chunk-start state it: valid until the barrier that ends chunk it + 1
+                V8 Sa[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) Sa[ks] = load_vec<V8>(xs + (ks * 64 + l) * 8);
+#pragma unroll
+                for (int rr = 0; rr < RPW; ++rr) {
+                    const int R = RPW * ow + rr;
+                    // OI[16R + ln][perm_index(j0 + 4g) ..]: half of fragment (R, j0/32)'s slots 8g .. 8g + 7
+                    const V4 oi = load_frag_half(reinterpret_cast<const E*>(sl + C::OFF_OI) + 512 * R, l, (j0 >> 4) & 1);
+                    f32x4 acc = {to_f32(oi[0]), to_f32(oi[1]), to_f32(oi[2]), to_f32(oi[3])};
+                    const E* qrow = reinterpret_cast<const E*>(sl + C::OFF_QM + (16 * R + ln) * C::RS) + 8 * g;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) acc = mma32(Sa[ks], load_vec<V8>(qrow + 32 * ks), acc);
+                    const int r = CHUNK * it + 16 * R + ln;   // token of the sequence
+                    if (r < seq_len) {
+                        V4 w;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(acc[i]);
+                        store_vec(o + ((size_t)(first.start + r) * H + h) * DV + j0 + 4 * g, w);
+                    }
+                }
+                bare_barrier();   // every LDS read above was consumed before its store
+            }
+        }
     } else {
         // ------------------------------------------------ stager waves: direct loads into the ring
         const int sw = wave - NSER - 1;
@@ -659,8 +711,16 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_
                 const int v = u - C::PM_UNITS;
                 const int row = v / (C::RW + 1), col = v % (C::RW + 1);
                 x = (int)C::RL.hc + (j0 + row) * DK * (int)sizeof(E) + (col < C::RW ? col : 0) * 16;
-            } else if (u < C::UNITS) {
+            } else if (u < C::PM_UNITS + C::HC_UNITS + C::G_UNITS) {
                 x = (int)C::RL.g + (u - C::PM_UNITS - C::HC_UNITS) * 16;
+            } else if (u < C::PM_UNITS + C::HC_UNITS + C::G_UNITS + C::QM_UNITS) {
+                const int v = u - (C::PM_UNITS + C::HC_UNITS + C::G_UNITS);
+                const int row = v / (C::RW + 1), col = v % (C::RW + 1);
+                x = (int)C::RL.qm + row * DK * (int)sizeof(E) + (col < C::RW ? col : 0) * 16;
+            } else if (u < C::UNITS) {
+                const int v = u - (C::PM_UNITS + C::HC_UNITS + C::G_UNITS + C::QM_UNITS);
+                const int R = v / C::OI_FRAG_UNITS, k = v % C::OI_FRAG_UNITS;
+                x = (int)C::RL.oi + frag_at<DV / 32>(R, j0 >> 5) * (int)sizeof(E) + 16 * k;
             } else {
                 x = (int)C::RL.g;   // past the slot's data: lands in the slot's tail padding
             }
@@ -718,7 +778,7 @@ static int device_cus() {
 
 template <typename E, int DK, int DV, int SW>
 static hipError_t launch_state_ring_t(const void* rec, ChunkSrc src, const float* S0, float* S_final,
-                                      void* states, float* chunk_states, int H, hipStream_t stream)
+                                      void* o, void* states, float* chunk_states, int H, hipStream_t stream)
 {
     using C = RingCfg<E, DK, DV, SW>;
     const int n_pairs = src.N * H;
@@ -726,8 +786,13 @@ static hipError_t launch_state_ring_t(const void* rec, ChunkSrc src, const float
     const long long blocks = (long long)groups * 8 * C::NWG;
     hipLaunchKernelGGL((prefill_state_ring_kernel<E, DK, DV, SW>), dim3((unsigned)blocks),
                        dim3(64 * C::WAVES), 0, stream, (const unsigned char*)rec, src, S0, S_final,
-                       (E*)states, chunk_states, H, n_pairs);
+                       (E*)o, (E*)states, chunk_states, H, n_pairs);
     return hipGetLastError();
+}
+
+static bool ring_is_wide(int N, int H, int dv, bool chunk_states)
+{
+    return !chunk_states && (long long)N * H * (dv / 16) > device_cus();
 }
 
 // Two value slices per workgroup once the one-slice grid has more chains
@@ -736,11 +801,16 @@ static hipError_t launch_state_ring_t(const void* rec, ChunkSrc src, const float
 // is sized for one slice).
 template <typename E, int DK, int DV>
 static hipError_t launch_state_ring(const void* rec, ChunkSrc src, const float* S0, float* S_final,
-                                    void* states, float* chunk_states, int H, hipStream_t stream)
+                                    void* o, void* states, float* chunk_states, int H, hipStream_t stream)
 {
-    const bool wide = !chunk_states && (long long)src.N * H * (DV / 16) > device_cus();
-    return wide ? launch_state_ring_t<E, DK, DV, 2>(rec, src, S0, S_final, states, chunk_states, H, stream)
-                : launch_state_ring_t<E, DK, DV, 1>(rec, src, S0, S_final, states, chunk_states, H, stream);
+    return ring_is_wide(src.N, H, DV, chunk_states != nullptr)
+               ? launch_state_ring_t<E, DK, DV, 2>(rec, src, S0, S_final, o, states, chunk_states, H, stream)
+               : launch_state_ring_t<E, DK, DV, 1>(rec, src, S0, S_final, o, states, chunk_states, H, stream);
+}
+
+bool state_pass_writes_output(bool bf16_io, int dk, int dv, int N, int H, bool chunk_states)
+{
+    return !uses_output_pass(bf16_io, dk) || !ring_is_wide(N, H, dv, chunk_states);
 }
 
 template <typename E, int DK, int DV>
@@ -762,7 +832,7 @@ hipError_t launch_prefill_state(const void* rec, ChunkSrc src, const float* S0, 
 {
 #define KDA_RING_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
-        return launch_state_ring<E, DK_, DV_>(rec, src, S0, S_final, states, chunk_states, H, stream);
+        return launch_state_ring<E, DK_, DV_>(rec, src, S0, S_final, o, states, chunk_states, H, stream);
 #define KDA_STATE_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
         return launch_state_t<E, DK_, DV_>(rec, src, S0, S_final, o, chunk_states, H, stream);
