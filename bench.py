@@ -162,10 +162,12 @@ def main():
     token_heads = T * H
     # Algorithmic bytes of each kernel: its share of the path's 1540 B per token-head
     # (the intra-chunk kernel reads q, k, v, log_alpha, beta; the sequential kernel writes
-    # the final state; the output pass writes o).  The per-chunk records one kernel hands to the other are
-    # this design's own traffic: they show up in `traffic`, not in `achieved`.
+    # the final state, and o when it forms the outputs itself; otherwise the output pass
+    # writes o).  The per-chunk records one kernel hands to the other are this design's
+    # own traffic: they show up in `traffic`, not in `achieved`.
+    fused_out = "prefill_output" not in kern_ms
     kern_bytes = {"prefill_intra": INTRA_READ * token_heads,
-                  "prefill_state": H * dk * dv * 4,          # the final state
+                  "prefill_state": H * dk * dv * 4 + (256 * token_heads if fused_out else 0),
                   "prefill_output": 256 * token_heads,       # o
                   "chunk_table": 0}
     record_bytes_per_step = int(RECORD_PER_TOKEN_HEAD * token_heads)
