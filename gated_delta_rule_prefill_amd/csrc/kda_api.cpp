@@ -26,13 +26,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Workspace layout of one prefill call: one record per (chunk, head) slot,
-// then (with the output pass) one chunk-start state per (chunk, head) slot,
 // then the chunk table.
 struct Plan {
     int64_t max_chunks = 0;
     size_t rec_bytes = 0;   // bytes of one (chunk, head) record
-    bool output_pass = false;
-    size_t off_states = 0;  // chunk-start states [max_chunks * H] (output pass only)
     size_t off_seq = 0;     // seq_chunk_start [N+1]
     size_t off_chunks = 0;  // ChunkInfo [max_chunks]
     size_t total = 0;
@@ -44,11 +41,7 @@ bool make_plan(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtyp
     const int es = dtype == KDA_DTYPE_BF16 ? 2 : 4;
     p.max_chunks = (T + kda::CHUNK - 1) / kda::CHUNK + N;
     p.rec_bytes = kda::rec_layout(es, dk, dv).bytes;
-    p.output_pass = kda::uses_output_pass(dtype == KDA_DTYPE_BF16, dk);
     size_t at = align256((size_t)p.max_chunks * (size_t)H * p.rec_bytes);
-    p.off_states = at;
-    if (p.output_pass)
-        at += align256((size_t)p.max_chunks * (size_t)H * kda::chunk_state_bytes(es, dk, dv));
     p.off_seq = at;
     at += align256(((size_t)N + 1) * 4);
     p.off_chunks = at;
@@ -59,8 +52,8 @@ bool make_plan(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtyp
 
 bool supported_dim(int32_t d) { return d == 64 || d == 128; }
 
-// Workspace of one backward call: the forward plan (chunk table, records and
-// chunk-start operand states for a recomputation), then the recomputed fp32
+// Workspace of one backward call: the forward plan (chunk table and records for
+// a recomputation), then the recomputed fp32
 // chunk states, an output scratch for the recomputation, the per-slice
 // partial gradients and the per-workgroup scratch.
 struct BwdPlan {
@@ -240,20 +233,11 @@ kda_status kda_prefill_ex(const void* q, const void* k, const void* v, const flo
                                   "intra-chunk kernel", stream);
                 timer.mark("prefill_intra");
             }
-            void* states = plan.output_pass ? (void*)(ws + plan.off_states) : nullptr;
             if (st == KDA_OK) {
                 st = check_launch(kda::launch_prefill_state(ws, src, initial_state, final_state, o,
-                                                            states, chunk_states, H, dk, dv, bf16,
-                                                            stream),
+                                                            chunk_states, H, dk, dv, bf16, stream),
                                   "state kernel", stream);
                 timer.mark("prefill_state");
-            }
-            if (st == KDA_OK && plan.output_pass && total_tokens > 0 &&
-                !kda::state_pass_writes_output(bf16, dk, dv, src.N, H, chunk_states != nullptr)) {
-                st = check_launch(kda::launch_prefill_output(ws, states, src, (int)plan.max_chunks,
-                                                             H, dk, dv, bf16, o, stream),
-                                  "output kernel", stream);
-                timer.mark("prefill_output");
             }
         }
         if (owned) {
@@ -340,15 +324,14 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const float
             // forward recomputation: records, then the chain with its chunk states
             float* own_cs = reinterpret_cast<float*>(ws + b.off_cs);
             void* o_scratch = ws + b.off_o;
-            void* states = plan.output_pass ? (void*)(ws + plan.off_states) : nullptr;
             st = check_launch(kda::launch_prefill_intra(q, k, v, log_alpha, beta, src,
                                                         (int)plan.max_chunks, H, dk, dv, bf16, 0u,
                                                         ws, stream),
                               "intra-chunk kernel", stream);
             if (st == KDA_OK)
                 st = check_launch(kda::launch_prefill_state(ws, src, initial_state, nullptr,
-                                                            o_scratch, states, own_cs, H, dk, dv,
-                                                            bf16, stream),
+                                                            o_scratch, own_cs, H, dk, dv, bf16,
+                                                            stream),
                                   "state kernel", stream);
             cs = own_cs;
         }

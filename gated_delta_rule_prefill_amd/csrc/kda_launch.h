@@ -66,31 +66,15 @@ hipError_t launch_prefill_intra(const void* q, const void* k, const void* v, con
                                 int dv, bool bf16_io, unsigned flags, void* rec,
                                 hipStream_t stream);
 
-// Sequential inter-chunk pass.  It writes o itself when
-// state_pass_writes_output(); otherwise it stores every chunk-start state into
-// `states` and leaves o to launch_prefill_output.
+// Sequential inter-chunk pass; it also forms every chunk's output O = QM S_c + OI.
 // chunk_states (or NULL): every chunk-start state in fp32, [chunk][H][dk][dv].
 hipError_t launch_prefill_state(const void* rec, ChunkSrc src, const float* S0, float* S_final,
-                                void* o, void* states, float* chunk_states, int H, int dk, int dv,
-                                bool bf16_io, hipStream_t stream);
+                                void* o, float* chunk_states, int H, int dk, int dv, bool bf16_io,
+                                hipStream_t stream);
 
 // Whether a configuration runs the LDS-ring sequential kernel (its ring fits),
-// or the fused register-staged one.
-constexpr bool uses_output_pass(bool bf16_io, int dk) { return bf16_io || dk == 64; }
-
-// Whether the sequential pass forms the outputs itself (the register-staged
-// kernel, and the ring kernel with one value slice per workgroup), so that
-// launch_prefill_output is not needed.  Depends on the current device's CU count.
-bool state_pass_writes_output(bool bf16_io, int dk, int dv, int N, int H, bool chunk_states);
-
-// Bytes of one (chunk, head) chunk-start state: dk x dv in the q/k/v dtype, laid
-// out as MFMA operand slots [dv/16 slices][dk/32 steps][64 lanes][8].
-constexpr size_t chunk_state_bytes(int es, int dk, int dv) { return (size_t)dk * dv * es; }
-
-// Parallel output pass: O = QM S_c + OI for every (chunk, head).
-hipError_t launch_prefill_output(const void* rec, const void* states, ChunkSrc src,
-                                 int max_chunks, int H, int dk, int dv, bool bf16_io, void* o,
-                                 hipStream_t stream);
+// or the register-staged one (fp32 with dk = 128).
+constexpr bool uses_ring_kernel(bool bf16_io, int dk) { return bf16_io || dk == 64; }
 
 // Recurrent tokens of a packed batch on pooled states (see kda_decode_tokens).
 hipError_t launch_recurrent(float* pool, int num_slots, const int32_t* slots, const void* q,

@@ -297,76 +297,66 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 // ---------------------------------------------------------------------------
 // LDS-ring variant, for every configuration whose ring fits in LDS.  It runs
-// only the sequential chain; the outputs come from a separate parallel pass
-// over the chunk-start states this kernel stores.
+// the sequential chain and forms every chunk's output from the chunk-start
+// state while that state is in LDS.
 //
-// One workgroup per (sequence, head, 16 SW value columns), SW DK/32 serial
-// waves, a touch wave and 1 (SW = 1) or 4 (SW = 2) stager waves (SW = 2 for
-// batches with more chains than CUs: the slices of a workgroup share the PM
-// it moves through its CU):
-//   serial waves w < SW DK/32  own rows 32w'..32w'+31 (w' = w mod DK/32) of
-//       the fp32 state tile of value slice w / (DK/32); per
+// One workgroup per (sequence, head, 16 value columns): DK/32 serial waves, a
+// touch wave, a stager wave and two output waves:
+//   serial waves w < DK/32  own rows 32w..32w+31 of the fp32 state tile; per
 //       chunk each applies S' = Diag(gamma_C) S + Hc + PM S to its rows (8
 //       MFMAs), reading the whole chunk-start state as bf16 operand slots from
 //       LDS and writing its own rows' slots for the next chunk to LDS.  A
 //       16x16 accumulator tile gives lane group g rows 4g..4g+3, so the two
 //       tiles of rows 32w.. are exactly operand step w of the next product.
 //       Their PM rows (fragment order in the record, 1 KiB per fragment) come
-//       from the ring slot when SW = 2, else straight from the record into a
-//       register ring PM_DIST - 1 chunks ahead: with one slice nothing shares
-//       them, and the LDS round trip would cost the CU twice the bytes;
-//   touch wave  copies each chunk-start state slot from LDS to the
-//       chunk-state buffer (keeping those stores off the serial waves'
-//       chain) and, for chains of TOUCH_MIN_CHUNKS or more, touches every
-//       line of chunk it + TOUCH_DIST so that the loads hit L2 (plain loads,
-//       folded into a value three chunks later);
-//   stager waves  move this slice's Hc^T rows, gamma_C (and PM, SW = 2) into
-//       a three-slot LDS ring by direct global->LDS loads
+//       straight from the record into a register ring PM_DIST - 1 chunks
+//       ahead: nothing else in the workgroup reads them, and an LDS round
+//       trip would cost the CU twice the bytes;
+//   output waves  form O = QM S_c + OI for the chunk whose start state is in
+//       LDS: row tiles 2ow, 2ow + 1 as O^T tiles, the state slots as A, QM rows
+//       (ring slot) as B, the OI fragment halves as the accumulators' start;
+//   touch wave  for chains of TOUCH_MIN_CHUNKS or more touches every line
+//       the chain will read TOUCH_DIST chunks ahead so that the loads hit L2
+//       (plain loads, folded into a value three chunks later), and with
+//       chunk_states sends the fp32 chunk-start states to memory;
+//   stager wave  moves this slice's Hc^T rows, gamma_C, QM and the slice's OI
+//       fragments into a three-slot LDS ring by direct global->LDS loads
 //       (global_load_lds_dwordx4), two chunks ahead.
 // Every wave passes one barrier per chunk.  A ring slot or state slot is
 // written only after the barrier that ends the chunk which last read it.
-template <typename E, int DK, int DV, int SW>
+template <typename E, int DK, int DV>
 struct RingCfg {
     static constexpr int ES = sizeof(E);
     static constexpr int KS = DK / 32, KT = DK / 16, NSL = DV / 16;
-    static constexpr int NWG = NSL / SW;             // workgroups per (sequence, head)
-    static constexpr int NSER = KS * SW;             // serial waves
-    // PM through the LDS ring when two slices share it; with one slice each
-    // serial wave loads its own PM rows straight into registers
-    static constexpr bool PM_IN_RING = SW == 2;
-    static constexpr int NSTG = PM_IN_RING ? 4 : 1;  // stager waves
-    // with one slice the chunks' outputs are formed here, by NOUT output waves
-    static constexpr bool FUSED_OUT = SW == 1;
-    static constexpr int NOUT = FUSED_OUT ? 2 : 0;
+    static constexpr int NSER = KS;                  // serial waves
+    static constexpr int NSTG = 1;                   // stager waves
+    static constexpr int NOUT = 2;                   // output waves
     static constexpr int WAVES = NSER + 1 + NSTG + NOUT;   // + the touch wave
     static constexpr int FRAG = 8 * ES;
-    static constexpr int XSLOT = SW * KS * 64 * FRAG;   // one chunk-start state (operand slots)
+    static constexpr int XSLOT = KS * 64 * FRAG;     // one chunk-start state (operand slots)
     static constexpr int NX = 2;                     // state slots: it (read), it + 1 (written)
     static constexpr int RW = DK * ES / 16;          // 16-byte units per PM / Hc^T row
     static constexpr int RS = (RW + 1) * 16;         // padded LDS row stride (bytes)
-    static constexpr int PM_UNITS = PM_IN_RING ? DK * DK * ES / 16 : 0;   // fragment order: copied as is
-    static constexpr int HC_UNITS = 16 * SW * (RW + 1);
+    static constexpr int HC_UNITS = 16 * (RW + 1);
     static constexpr int G_UNITS = DK / 4;
-    // with the outputs formed here: QM rows, padded like Hc^T, and this
-    // slice's OI fragments (R, j0/32), R = 0 .. CHUNK/16 - 1
-    static constexpr int QM_UNITS = FUSED_OUT ? CHUNK * (RW + 1) : 0;
+    // QM rows, padded like Hc^T, and this slice's OI fragments (R, j0/32)
+    static constexpr int QM_UNITS = CHUNK * (RW + 1);
     static constexpr int OI_FRAG_UNITS = 512 * ES / 16;
-    static constexpr int OI_UNITS = FUSED_OUT ? (CHUNK / 16) * OI_FRAG_UNITS : 0;
-    static constexpr int UNITS = PM_UNITS + HC_UNITS + G_UNITS + QM_UNITS + OI_UNITS;
+    static constexpr int OI_UNITS = (CHUNK / 16) * OI_FRAG_UNITS;
+    static constexpr int UNITS = HC_UNITS + G_UNITS + QM_UNITS + OI_UNITS;
     static constexpr int LOADS = (UNITS + 63) / 64;  // direct loads per chunk
     static constexpr int LOADS_W = (LOADS + NSTG - 1) / NSTG;   // per stager wave
     static constexpr int LOADS_LAST = LOADS - (NSTG - 1) * LOADS_W;   // the last stager's share
     static constexpr int SLOT = LOADS * 1024;
-    static constexpr int OFF_HC = PM_UNITS * 16;
+    static constexpr int OFF_HC = 0;
     static constexpr int OFF_G = OFF_HC + HC_UNITS * 16;
     static constexpr int OFF_QM = OFF_G + G_UNITS * 16;
     static constexpr int OFF_OI = OFF_QM + QM_UNITS * 16;
-    static constexpr int OUT_RPW = CHUNK / 16 / (NOUT > 0 ? NOUT : 1);   // row tiles per output wave
+    static constexpr int OUT_RPW = CHUNK / 16 / NOUT;   // row tiles per output wave
     static constexpr int NSLOT = 3;
     static constexpr int LDS_BYTES = NSLOT * SLOT + NX * XSLOT;
     static constexpr RecLayout RL = rec_layout(ES, DK, DV);
-    static constexpr int TOUCH_LINES = DK * DK * ES / 128 / NWG + 16 * SW * DK * ES / 128 + DK * 4 / 128;
-    static constexpr int CST_COLS = SW == 1 ? 16 : 1;   // fp32 state staging (chunk_states; SW = 1 only)
+    static constexpr int TOUCH_LINES = DK * DK * ES / 128 / NSL + 16 * DK * ES / 128 + DK * 4 / 128;
     static constexpr int TOUCH_PER_LANE = (TOUCH_LINES + 63) / 64;
     static_assert(2 * LOADS_W <= 60, "two chunks of one stager's direct loads must fit its counter");
     static_assert(LOADS_LAST > 0 && LOADS_LAST <= LOADS_W, "stager split");
@@ -413,40 +403,40 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <typename E, int DK, int DV, int SW>
-__global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_state_ring_kernel(
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_state_ring_kernel(
     const unsigned char* __restrict__ rec, const ChunkSrc src, const float* __restrict__ S0,
-    float* __restrict__ S_final, E* __restrict__ o, E* __restrict__ states,
-    float* __restrict__ chunk_states, int H, int n_pairs)
+    float* __restrict__ S_final, E* __restrict__ o, float* __restrict__ chunk_states, int H,
+    int n_pairs)
 {
-    using C = RingCfg<E, DK, DV, SW>;
+    using C = RingCfg<E, DK, DV>;
     using V4 = typename Vec<E>::v4;
     using V8 = typename Vec<E>::v8;
-    constexpr int KS = C::KS, NWG = C::NWG, NSER = C::NSER;
+    constexpr int KS = C::KS, NSL = C::NSL, NSER = C::NSER;
 
     __shared__ __attribute__((aligned(1024))) unsigned char ring[C::NSLOT * C::SLOT];
     __shared__ __attribute__((aligned(16))) unsigned char xfer[C::NX * C::XSLOT];
     // fp32 chunk-start states for the chunk_states output, column-major
     // [slot][16 columns][DK rows (+4 padding)]; written by the serial waves with
-    // 16-byte LDS stores, sent to memory row-major by the touch wave (SW = 1)
-    __shared__ __attribute__((aligned(16))) float cst[C::NX][C::CST_COLS][DK + 4];
+    // 16-byte LDS stores, sent to memory row-major by the touch wave
+    __shared__ __attribute__((aligned(16))) float cst[C::NX][16][DK + 4];
 
     const int b = blockIdx.x;
     const int xcd = b & 7, q8 = b >> 3;
-    const int grp = q8 / NWG, slice = q8 % NWG;   // slice: 16 SW value columns
+    const int grp = q8 / NSL, slice = q8 % NSL;   // slice: 16 value columns
     const int pair = grp * 8 + xcd;
     if (pair >= n_pairs) return;
     const int s = pair / H, h = pair % H;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, g = l >> 4, ln = l & 15;
-    const int j0 = slice * 16 * SW;
+    const int j0 = slice * 16;
     int c_begin, n;   // first chunk and chunk count of this sequence
     seq_chunks(src, s, c_begin, n);
     const size_t sbase = (size_t)pair * DK * DV;
     if (n == 0) {   // empty sequence: the final state is the initial one (or zero)
         if (S_final)
-            for (int x = tid; x < DK * 16 * SW; x += blockDim.x) {
-                const size_t at = sbase + (size_t)(x / (16 * SW)) * DV + j0 + x % (16 * SW);
+            for (int x = tid; x < DK * 16; x += blockDim.x) {
+                const size_t at = sbase + (size_t)(x >> 4) * DV + j0 + (x & 15);
                 S_final[at] = S0 ? S0[at] : 0.f;
             }
         return;   // uniform over the workgroup: no barrier is skipped by part of it
@@ -457,10 +447,8 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_
 
     if (wave < NSER) {
         // ------------------------------------------------ serial waves
-        const int w = wave % KS;        // row group: rows 32w .. 32w + 31
-        const int sub = wave / KS;      // value slice inside the workgroup
-        const int jc = j0 + 16 * sub;   // its first column
-        f32x4 S[2];   // S[h2]: lane holds S[32w + 16 h2 + 4g + i][jc + ln]
+        const int w = wave;   // row group: rows 32w .. 32w + 31
+        f32x4 S[2];   // S[h2]: lane holds S[32w + 16 h2 + 4g + i][j0 + ln]
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) S[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (S0) {
@@ -468,10 +456,10 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S[h2][i] = S0[sbase + (size_t)(32 * w + 16 * h2 + 4 * g + i) * DV + jc + ln];
+                    S[h2][i] = S0[sbase + (size_t)(32 * w + 16 * h2 + 4 * g + i) * DV + j0 + ln];
         }
-        // chunk-start state of chunk it, this wave's operand step, to LDS (the
-        // touch wave copies the slot to the chunk-state buffer)
+        // chunk-start state of chunk it, this wave's operand step, to LDS (and
+        // its fp32 rows to the staging the touch wave sends to chunk_states)
         auto put = [&](int it) {
             V8 f;
 #pragma unroll
@@ -479,20 +467,18 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_
                 f[i] = from_f32<E>(S[0][i]);
                 f[4 + i] = from_f32<E>(S[1][i]);
             }
-            store_vec(xslot(it) + ((sub * KS + w) * 64 + l) * 8, f);
-            if constexpr (SW == 1) {
-                if (chunk_states) {
+            store_vec(xslot(it) + (w * 64 + l) * 8, f);
+            if (chunk_states) {
 #pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2)
-                        *reinterpret_cast<f32x4*>(&cst[it % C::NX][ln][32 * w + 16 * h2 + 4 * g]) = S[h2];
-                }
+                for (int h2 = 0; h2 < 2; ++h2)
+                    *reinterpret_cast<f32x4*>(&cst[it % C::NX][ln][32 * w + 16 * h2 + 4 * g]) = S[h2];
             }
         };
         // PM rows 32w .. 32w + 31 of chunk c (clamped): this lane's A fragments
-        // of row tiles 2w, 2w + 1 -- from the ring slot (PM_IN_RING), else
-        // straight from the record into a register ring of PM_DIST sets
+        // of row tiles 2w, 2w + 1, straight from the record into a register
+        // ring of PM_DIST sets
         using PmSet = V8[2][KS];
-        constexpr int NSET = C::PM_IN_RING ? 1 : PM_DIST;
+        constexpr int NSET = PM_DIST;
         // fragments f0 .. f1 - 1 of a set (f: row tile 2w + (f & 1), step f >> 1)
         auto pm_load = [&](PmSet& pf, int c, int f0, int f1) {
             const E* pm = reinterpret_cast<const E*>(record(min(c, n - 1)) + C::RL.pm);
@@ -501,42 +487,32 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_
                 if (f >= f0 && f < f1) pf[f & 1][f >> 1] = load_frag(pm + frag_at<KS>(2 * w + (f & 1), f >> 1), l);
         };
         PmSet pfr[NSET];
-        if constexpr (!C::PM_IN_RING) {
 #pragma unroll
-            for (int u = 0; u < PM_DIST - 1; ++u) pm_load(pfr[u], u, 0, 2 * KS);
-        }
+        for (int u = 0; u < PM_DIST - 1; ++u) pm_load(pfr[u], u, 0, 2 * KS);
         put(0);
         lds_barrier();
-        // chunk it: the MFMAs take set pf; in the register ring, set pn (free
-        // since chunk it - 1) takes chunk it + PM_DIST - 1, its loads issued
-        // in two parts so that the CU's load path never holds a whole set of
-        // all serial waves at once: the first while the LDS operands of this
-        // chunk are in flight, the rest after the MFMAs
+        // chunk it: the MFMAs take set pf; set pn (free since chunk it - 1)
+        // takes chunk it + PM_DIST - 1, its loads issued in two parts so that
+        // the CU's load path never holds a whole set of all serial waves at
+        // once: the first while the LDS operands of this chunk are in flight,
+        // the rest after the MFMAs
         auto step = [&](PmSet& pf, PmSet& pn, int it) {
             const unsigned char* sl = slot(it);
             const E* xs = xslot(it);
             V8 Sf[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) Sf[ks] = load_vec<V8>(xs + ((sub * KS + ks) * 64 + l) * 8);
+            for (int ks = 0; ks < KS; ++ks) Sf[ks] = load_vec<V8>(xs + (ks * 64 + l) * 8);
             V4 hc[2];
             f32x4 gc[2];
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const int t = 2 * w + h2;
-                hc[h2] = load_vec<V4>(reinterpret_cast<const E*>(sl + C::OFF_HC + (16 * sub + ln) * C::RS) + perm_index(16 * t + 4 * g));
+                hc[h2] = load_vec<V4>(reinterpret_cast<const E*>(sl + C::OFF_HC + ln * C::RS) + perm_index(16 * t + 4 * g));
                 gc[h2] = load_vec<f32x4>(reinterpret_cast<const float*>(sl + C::OFF_G) + 16 * t + 4 * g);
             }
-            if constexpr (C::PM_IN_RING) {
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        pf[h2][ks] = load_frag(reinterpret_cast<const E*>(sl) + frag_at<KS>(2 * w + h2, ks), l);
-            } else {
-                __builtin_amdgcn_sched_barrier(0);   // LDS reads first, then the early loads
-                pm_load(pn, it + PM_DIST - 1, 0, PM_EARLY);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            __builtin_amdgcn_sched_barrier(0);   // LDS reads first, then the early loads
+            pm_load(pn, it + PM_DIST - 1, 0, PM_EARLY);
+            __builtin_amdgcn_sched_barrier(0);
             // S' = Diag(gamma_C) S + Hc + PM S
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
@@ -546,49 +522,44 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) S[h2] = mma32(pf[h2][ks], Sf[ks], S[h2]);
-            if constexpr (!C::PM_IN_RING) pm_load(pn, it + PM_DIST - 1, PM_EARLY, 2 * KS);
+            pm_load(pn, it + PM_DIST - 1, PM_EARLY, 2 * KS);
             if (it + 1 < n) put(it + 1);
             lds_barrier();
         };
-        if constexpr (C::PM_IN_RING) {
-            for (int it = 0; it < n; ++it) step(pfr[0], pfr[0], it);
-        } else {
-            // whole rounds of the register ring without branches (so that each
-            // step waits only for its own set), then the remaining chunks
-            int it0 = 0;
-            for (; it0 + PM_DIST <= n; it0 += PM_DIST) {
+        // whole rounds of the register ring without branches (so that each
+        // step waits only for its own set), then the remaining chunks
+        int it0 = 0;
+        for (; it0 + PM_DIST <= n; it0 += PM_DIST) {
 #pragma unroll
-                for (int u = 0; u < NSET; ++u) step(pfr[u], pfr[(u + NSET - 1) % NSET], it0 + u);
-            }
-#pragma unroll
-            for (int u = 0; u < NSET - 1; ++u)
-                if (it0 + u < n) step(pfr[u], pfr[(u + NSET - 1) % NSET], it0 + u);
+            for (int u = 0; u < NSET; ++u) step(pfr[u], pfr[(u + NSET - 1) % NSET], it0 + u);
         }
+#pragma unroll
+        for (int u = 0; u < NSET - 1; ++u)
+            if (it0 + u < n) step(pfr[u], pfr[(u + NSET - 1) % NSET], it0 + u);
         if (S_final) {
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S_final[sbase + (size_t)(32 * w + 16 * h2 + 4 * g + i) * DV + jc + ln] = S[h2][i];
+                    S_final[sbase + (size_t)(32 * w + 16 * h2 + 4 * g + i) * DV + j0 + ln] = S[h2][i];
         }
     } else if (wave == NSER) {
         // ------------------------------------------------ touch wave
         // Plain loads whose values are folded into `sink` three chunks later;
         // unconditional (clamped chunk index) so that each load writes its own
         // registers and the compiler has no reason to wait for it early.
-        // Lines touched per chunk: 1/NWG of PM (shared by the workgroups of a
-        // head), this workgroup's 16 SW rows of Hc^T, and gamma_C; QM and OI are
-        // not read here.
+        // Lines touched per chunk: 1/NSL of PM (shared by the workgroups of a
+        // head), this workgroup's 16 rows of Hc^T, and gamma_C.
         using TouchSet = uint32_t[C::TOUCH_PER_LANE];
         uint32_t toff[C::TOUCH_PER_LANE];
 #pragma unroll
         for (int k = 0; k < C::TOUCH_PER_LANE; ++k) {
             const int u = l + 64 * k;
             constexpr int PM_LINES = DK * DK * (int)sizeof(E) / 128;
-            constexpr int HC_LINES = 16 * SW * DK * (int)sizeof(E) / 128;
-            constexpr int PM_MINE = PM_LINES / NWG;
+            constexpr int HC_LINES = 16 * DK * (int)sizeof(E) / 128;
+            constexpr int PM_MINE = PM_LINES / NSL;
             size_t x;
-            if (u < PM_MINE) x = C::RL.pm + 128 * (size_t)(slice + NWG * u);
+            if (u < PM_MINE) x = C::RL.pm + 128 * (size_t)(slice + NSL * u);
             else if (u < PM_MINE + HC_LINES) x = C::RL.hc + (size_t)j0 * DK * sizeof(E) + 128 * (size_t)(u - PM_MINE);
             else x = C::RL.g + 128 * (size_t)((u - PM_MINE - HC_LINES) % (DK * 4 / 128));
             toff[k] = (uint32_t)x;
@@ -614,33 +585,19 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_
         // rewritten only after the barrier that ends chunk it) to chunk_states,
         // fp32 [chunk][H][DK][DV]: 16-byte stores of 4 columns of a row
         auto send_state = [&](int it) {
-            if constexpr (SW == 1) {
-                float* cs = chunk_states + ((size_t)(c_begin + it) * H + h) * DK * DV + j0;
+            float* cs = chunk_states + ((size_t)(c_begin + it) * H + h) * DK * DV + j0;
 #pragma unroll
-                for (int k = 0; k < DK * 4 / 64; ++k) {
-                    const int u = l + 64 * k, row = u >> 2, qd = u & 3;
-                    const f32x4 val = {cst[it % C::NX][4 * qd][row], cst[it % C::NX][4 * qd + 1][row],
-                                       cst[it % C::NX][4 * qd + 2][row], cst[it % C::NX][4 * qd + 3][row]};
-                    // streaming stores: the records this kernel still has to read stay cached
-                    __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(cs + (size_t)row * DV + 4 * qd));
-                }
+            for (int k = 0; k < DK * 4 / 64; ++k) {
+                const int u = l + 64 * k, row = u >> 2, qd = u & 3;
+                const f32x4 val = {cst[it % C::NX][4 * qd][row], cst[it % C::NX][4 * qd + 1][row],
+                                   cst[it % C::NX][4 * qd + 2][row], cst[it % C::NX][4 * qd + 3][row]};
+                // streaming stores: the records this kernel still has to read stay cached
+                __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(cs + (size_t)row * DV + 4 * qd));
             }
-        };
-        // chunk-start state `it` as operand slots (in xfer slot it since the barrier
-        // that ended chunk it - 1, rewritten only after the barrier that ends chunk
-        // it + 1) to the chunk-state buffer [chunk, head][slice][step][lane][8]:
-        // the workgroup's slices are one contiguous run of XSLOT bytes
-        auto send_operands = [&](int it) {
-            const f32x4* from = reinterpret_cast<const f32x4*>(xslot(it));
-            f32x4* to = reinterpret_cast<f32x4*>(states + ((size_t)(c_begin + it) * H + h) * DK * DV +
-                                                 (size_t)slice * SW * KS * 64 * 8);
-#pragma unroll
-            for (int k = 0; k < C::XSLOT / 16 / 64; ++k) to[l + 64 * k] = from[l + 64 * k];
         };
         auto step = [&](TouchSet& tv, int it) {
             fold(tv);   // issued three chunks ago
             touch(tv, min(it + TOUCH_DIST, n - 1));
-            if constexpr (!C::FUSED_OUT) send_operands(it);
             if (chunk_states) send_state(it);
             bare_barrier();
         };
@@ -654,12 +611,12 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_
         fold(tv2);
         if (n_pairs < 0) o[0] = from_f32<E>((float)sink);   // keeps the touches; never taken
     } else if (wave >= NSER + 1 + C::NSTG) {
-        // ------------------------------------------------ output waves (one slice)
+        // ------------------------------------------------ output waves
         // O = QM S_c + OI for the chunk whose start state the serial waves
         // handed over last: output wave ow takes row tiles 2 ow, 2 ow + 1 as
         // O^T tiles (lane: row 16R + ln, columns j0 + 4g .. +3), the state
         // slots as A operands and QM rows (ring slot) as B.
-        if constexpr (C::FUSED_OUT) {
+        {
             const int ow = wave - (NSER + 1 + C::NSTG);
             constexpr int RPW = C::OUT_RPW;
             int n_all;
@@ -705,20 +662,17 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_
         for (int k = 0; k < C::LOADS_W; ++k) {
             const int u = 64 * (i0 + k) + l;
             int x;
-            if (u < C::PM_UNITS) {
-                x = (int)C::RL.pm + 16 * u;
-            } else if (u < C::PM_UNITS + C::HC_UNITS) {
-                const int v = u - C::PM_UNITS;
-                const int row = v / (C::RW + 1), col = v % (C::RW + 1);
+            if (u < C::HC_UNITS) {
+                const int row = u / (C::RW + 1), col = u % (C::RW + 1);
                 x = (int)C::RL.hc + (j0 + row) * DK * (int)sizeof(E) + (col < C::RW ? col : 0) * 16;
-            } else if (u < C::PM_UNITS + C::HC_UNITS + C::G_UNITS) {
-                x = (int)C::RL.g + (u - C::PM_UNITS - C::HC_UNITS) * 16;
-            } else if (u < C::PM_UNITS + C::HC_UNITS + C::G_UNITS + C::QM_UNITS) {
-                const int v = u - (C::PM_UNITS + C::HC_UNITS + C::G_UNITS);
+            } else if (u < C::HC_UNITS + C::G_UNITS) {
+                x = (int)C::RL.g + (u - C::HC_UNITS) * 16;
+            } else if (u < C::HC_UNITS + C::G_UNITS + C::QM_UNITS) {
+                const int v = u - (C::HC_UNITS + C::G_UNITS);
                 const int row = v / (C::RW + 1), col = v % (C::RW + 1);
                 x = (int)C::RL.qm + row * DK * (int)sizeof(E) + (col < C::RW ? col : 0) * 16;
             } else if (u < C::UNITS) {
-                const int v = u - (C::PM_UNITS + C::HC_UNITS + C::G_UNITS + C::QM_UNITS);
+                const int v = u - (C::HC_UNITS + C::G_UNITS + C::QM_UNITS);
                 const int R = v / C::OI_FRAG_UNITS, k = v % C::OI_FRAG_UNITS;
                 x = (int)C::RL.oi + frag_at<DV / 32>(R, j0 >> 5) * (int)sizeof(E) + 16 * k;
             } else {
@@ -762,55 +716,18 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV, SW>::WAVES)) void prefill_
     }
 }
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-    static int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cache[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
-}
-
-template <typename E, int DK, int DV, int SW>
-static hipError_t launch_state_ring_t(const void* rec, ChunkSrc src, const float* S0, float* S_final,
-                                      void* o, void* states, float* chunk_states, int H, hipStream_t stream)
-{
-    using C = RingCfg<E, DK, DV, SW>;
-    const int n_pairs = src.N * H;
-    const int groups = (n_pairs + 7) / 8;
-    const long long blocks = (long long)groups * 8 * C::NWG;
-    hipLaunchKernelGGL((prefill_state_ring_kernel<E, DK, DV, SW>), dim3((unsigned)blocks),
-                       dim3(64 * C::WAVES), 0, stream, (const unsigned char*)rec, src, S0, S_final,
-                       (E*)o, (E*)states, chunk_states, H, n_pairs);
-    return hipGetLastError();
-}
-
-static bool ring_is_wide(int N, int H, int dv, bool chunk_states)
-{
-    return !chunk_states && (long long)N * H * (dv / 16) > device_cus();
-}
-
-// Two value slices per workgroup once the one-slice grid has more chains
-// than the device has CUs (each workgroup takes a CU): a CU then moves each
-// chunk's PM once for both slices.  Not with chunk_states (its fp32 staging
-// is sized for one slice).
 template <typename E, int DK, int DV>
 static hipError_t launch_state_ring(const void* rec, ChunkSrc src, const float* S0, float* S_final,
-                                    void* o, void* states, float* chunk_states, int H, hipStream_t stream)
+                                    void* o, float* chunk_states, int H, hipStream_t stream)
 {
-    return ring_is_wide(src.N, H, DV, chunk_states != nullptr)
-               ? launch_state_ring_t<E, DK, DV, 2>(rec, src, S0, S_final, o, states, chunk_states, H, stream)
-               : launch_state_ring_t<E, DK, DV, 1>(rec, src, S0, S_final, o, states, chunk_states, H, stream);
-}
-
-bool state_pass_writes_output(bool bf16_io, int dk, int dv, int N, int H, bool chunk_states)
-{
-    return !uses_output_pass(bf16_io, dk) || !ring_is_wide(N, H, dv, chunk_states);
+    using C = RingCfg<E, DK, DV>;
+    const int n_pairs = src.N * H;
+    const int groups = (n_pairs + 7) / 8;
+    const long long blocks = (long long)groups * 8 * C::NSL;
+    hipLaunchKernelGGL((prefill_state_ring_kernel<E, DK, DV>), dim3((unsigned)blocks),
+                       dim3(64 * C::WAVES), 0, stream, (const unsigned char*)rec, src, S0, S_final,
+                       (E*)o, chunk_states, H, n_pairs);
+    return hipGetLastError();
 }
 
 template <typename E, int DK, int DV>
@@ -827,16 +744,16 @@ static hipError_t launch_state_t(const void* rec, ChunkSrc src, const float* S0,
 }
 
 hipError_t launch_prefill_state(const void* rec, ChunkSrc src, const float* S0, float* S_final,
-                                void* o, void* states, float* chunk_states, int H, int dk, int dv,
-                                bool bf16_io, hipStream_t stream)
+                                void* o, float* chunk_states, int H, int dk, int dv, bool bf16_io,
+                                hipStream_t stream)
 {
 #define KDA_RING_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
-        return launch_state_ring<E, DK_, DV_>(rec, src, S0, S_final, o, states, chunk_states, H, stream);
+        return launch_state_ring<E, DK_, DV_>(rec, src, S0, S_final, o, chunk_states, H, stream);
 #define KDA_STATE_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
         return launch_state_t<E, DK_, DV_>(rec, src, S0, S_final, o, chunk_states, H, stream);
-    if (uses_output_pass(bf16_io, dk)) {
+    if (uses_ring_kernel(bf16_io, dk)) {
         if (bf16_io) {
             KDA_RING_CASE(bf16, 128, 128)
             KDA_RING_CASE(bf16, 64, 64)
