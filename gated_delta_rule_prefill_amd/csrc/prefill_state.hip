@@ -334,7 +334,8 @@ struct RingCfg {
     static constexpr int WAVES = NSER + 1 + NSTG + NOUT;   // + the touch wave
     static constexpr int FRAG = 8 * ES;
     static constexpr int XSLOT = KS * 64 * FRAG;     // one chunk-start state (operand slots)
-    static constexpr int NX = 2;                     // state slots: it (read), it + 1 (written)
+    // state slots: it (serial waves read), it + 1 (written), it - 1 (output waves)
+    static constexpr int NX = 3;
     static constexpr int RW = DK * ES / 16;          // 16-byte units per PM / Hc^T row
     static constexpr int RS = (RW + 1) * 16;         // padded LDS row stride (bytes)
     static constexpr int HC_UNITS = 16 * (RW + 1);
@@ -353,7 +354,7 @@ struct RingCfg {
     static constexpr int OFF_QM = OFF_G + G_UNITS * 16;
     static constexpr int OFF_OI = OFF_QM + QM_UNITS * 16;
     static constexpr int OUT_RPW = CHUNK / 16 / NOUT;   // row tiles per output wave
-    static constexpr int NSLOT = 3;
+    static constexpr int NSLOT = 4;                  // it - 1 (output waves), it, it + 1, it + 2
     static constexpr int LDS_BYTES = NSLOT * SLOT + NX * XSLOT;
     static constexpr RecLayout RL = rec_layout(ES, DK, DV);
     static constexpr int TOUCH_LINES = DK * DK * ES / 128 / NSL + 16 * DK * ES / 128 + DK * 4 / 128;
@@ -624,10 +625,13 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
             chunk_of(src, c_begin, n_all, first);
             chunk_of(src, c_begin + n - 1, n_all, last);
             const int seq_len = CHUNK * (n - 1) + last.len;
-            bare_barrier();
-            for (int it = 0; it < n; ++it) {
-                const unsigned char* sl = slot(it);
-                const E* xs = xslot(it);   // chunk-start state it: valid until the barrier that ends chunk it + 1
+            // chunk c's output is formed while the serial waves run chunk c + 1:
+            // its ring slot and state slot live until the barrier that ends
+            // chunk c + 1 (NSLOT = 4, NX = 3), so these waves never hold up a
+            // barrier with work of the chunk the chain is on
+            auto form = [&](int c) {
+                const unsigned char* sl = slot(c);
+                const E* xs = xslot(c);
                 V8 Sa[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) Sa[ks] = load_vec<V8>(xs + (ks * 64 + l) * 8);
@@ -640,7 +644,7 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
                     const E* qrow = reinterpret_cast<const E*>(sl + C::OFF_QM + (16 * R + ln) * C::RS) + 8 * g;
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) acc = mma32(Sa[ks], load_vec<V8>(qrow + 32 * ks), acc);
-                    const int r = CHUNK * it + 16 * R + ln;   // token of the sequence
+                    const int r = CHUNK * c + 16 * R + ln;   // token of the sequence
                     if (r < seq_len) {
                         V4 w;
 #pragma unroll
@@ -648,8 +652,13 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
                         store_vec(o + ((size_t)(first.start + r) * H + h) * DV + j0 + 4 * g, w);
                     }
                 }
+            };
+            bare_barrier();
+            for (int it = 0; it < n; ++it) {
+                if (it > 0) form(it - 1);
                 bare_barrier();   // every LDS read above was consumed before its store
             }
+            form(n - 1);   // its slots are not rewritten after the last barrier
         }
     } else {
         // ------------------------------------------------ stager waves: direct loads into the ring
