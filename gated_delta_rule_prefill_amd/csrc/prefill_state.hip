@@ -9,18 +9,18 @@
 //
 // One workgroup per (sequence, head, 16 value columns): the columns of S evolve
 // independently, so a head's state is split over DV/16 workgroups that never
-// communicate.  Roles inside the workgroup:
-//   wave 0     the serial chain: it keeps the fp32 state tile (DK x 16) in MFMA
-//              accumulator registers for the whole sequence, hands each
-//              chunk-start state to wave 1 through LDS, and applies S';
-//   wave 1     the output of the previous chunk (one chunk behind wave 0);
-//   waves 2-3  stage PM into an LDS double buffer, two chunks ahead, and
-//              touch each record a few chunks ahead so it is in L2.
-// Waves 0 and 1 load their remaining operands straight from L2 into registers
-// one chunk ahead (two register sets).  Every wave stays well under the 63
-// vector-memory operations a wave may have in flight, so the loads for the
-// next chunk never stall the current one, and one barrier per chunk orders
-// all hand-overs.
+// communicate.  Two kernels implement it:
+//   prefill_state_ring_kernel  (bf16 q/k/v, and fp32 with dk = 64): DK/32
+//       serial waves share the chain, PM streams into their registers, the
+//       other operands through an LDS ring, and two output waves form O from
+//       each chunk-start state in LDS (described above the kernel);
+//   prefill_state_kernel  (fp32 with dk = 128, whose ring does not fit in
+//       LDS): wave 0 runs the chain, wave 1 the output of the previous chunk
+//       (one chunk behind), waves 2-3 stage PM into an LDS double buffer two
+//       chunks ahead and touch each record a few chunks ahead so it is in L2;
+//       waves 0 and 1 load their remaining operands straight from L2 into
+//       registers one chunk ahead.
+// One barrier per chunk orders all hand-overs.
 //
 // Every product takes the state straight from its accumulator tiles: a 16x16
 // tile gives lane group g rows 4g..4g+3, the slot set that the perm32 column
