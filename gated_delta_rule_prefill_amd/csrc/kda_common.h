@@ -109,12 +109,22 @@ __device__ __forceinline__ f32x8 load_frag(const float* f, int l) {
 __device__ __forceinline__ void store_frag(bf16* f, int l, bf16x8 v) {
     *reinterpret_cast<bf16x8*>(f + 8 * l) = v;
 }
-// elements 4h .. 4h + 3 of lane l (h = 0, 1)
-__device__ __forceinline__ bf16x4 load_frag_half(const bf16* f, int l, int h) {
-    return *reinterpret_cast<const bf16x4*>(f + 8 * l + 4 * h);
+// Planar fragments: slots 0..3 of all 64 lanes, then slots 4..7 (256
+// elements each), for matrices whose readers take one half of each lane's
+// slots (the fp32 fragment layout above is already planar).
+__device__ __forceinline__ void store_frag_planar(bf16* f, int l, bf16x8 v) {
+    *reinterpret_cast<bf16x4*>(f + 4 * l) = bf16x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<bf16x4*>(f + 256 + 4 * l) = bf16x4{v[4], v[5], v[6], v[7]};
 }
-__device__ __forceinline__ f32x4 load_frag_half(const float* f, int l, int h) {
-    return *reinterpret_cast<const f32x4*>(f + 256 * h + 4 * l);
+__device__ __forceinline__ void store_frag_planar(float* f, int l, f32x8 v) {
+    *reinterpret_cast<f32x4*>(f + 4 * l) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(f + 256 + 4 * l) = f32x4{v[4], v[5], v[6], v[7]};
+}
+// slots 4h .. 4h + 3 of lane l from plane h of a planar fragment (h = 0, 1),
+// or from a plane stored on its own (h = 0)
+template <typename E>
+__device__ __forceinline__ typename Vec<E>::v4 load_plane(const E* f, int l, int h) {
+    return *reinterpret_cast<const typename Vec<E>::v4*>(f + 256 * h + 4 * l);
 }
 __device__ __forceinline__ void store_frag(float* f, int l, f32x8 v) {
     *reinterpret_cast<f32x4*>(f + 4 * l) = f32x4{v[0], v[1], v[2], v[3]};

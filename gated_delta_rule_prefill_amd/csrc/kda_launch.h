@@ -37,7 +37,9 @@ struct ChunkSrc {
 //   HCt  [dv][dk]   (Khat^T U)^T, columns in perm32 order
 //   QM   [64][dk]   Qg - A_qk W, columns in perm32 order (row-major: it is
 //                   written from the row mapping, where a row is contiguous)
-//   OI   64 x dv    A_qk U, columns in perm32 order, in fragment order
+//   OI   64 x dv    A_qk U, columns in perm32 order, in planar fragment order
+//                   (slots 0..3 of the 64 lanes, then 4..7: value slice 2m is
+//                   plane 0 of block m, slice 2m + 1 plane 1)
 //   gC   [dk] fp32  e^{g_C}
 struct RecLayout {
     size_t pm, hc, qm, oi, g, bytes;

@@ -665,7 +665,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 2))) void prefill_intra_
                 w[i] = from_f32<E>(acc[0][i]);
                 w[4 + i] = from_f32<E>(acc[1][i]);
             }
-            store_frag(out.OI + frag_at<DV / 32>(Rr, pr), lane, w);   // slots 8g .. 8g + 7 of block pr
+            store_frag_planar(out.OI + frag_at<DV / 32>(Rr, pr), lane, w);   // slots 8g .. 8g + 7 of block pr
         }
     }
     __syncthreads();

@@ -91,8 +91,8 @@ __device__ __forceinline__ void load_output(OutputOps<E, DK>& op, const unsigned
     for (int R = 0; R < 4; ++R) {
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) op.q[R][ks] = load_vec<V8>(QM + (16 * R + ln) * DK + 32 * ks + 8 * g);
-        // OI[16R + ln][perm_index(j0 + 4g) ..]: half of fragment (R, j0/32)'s slots 8g .. 8g + 7
-        op.oi[R] = load_frag_half(OI + frag_at<DV / 32>(R, j0 >> 5), l, (j0 >> 4) & 1);
+        // OI[16R + ln][perm_index(j0 + 4g) ..]: plane (j0/16) mod 2 of fragment (R, j0/32)
+        op.oi[R] = load_plane(OI + frag_at<DV / 32>(R, j0 >> 5), l, (j0 >> 4) & 1);
     }
     op.start = ci.start;
     op.len = ci.len;
@@ -340,10 +340,10 @@ struct RingCfg {
     static constexpr int RS = (RW + 1) * 16;         // padded LDS row stride (bytes)
     static constexpr int HC_UNITS = 16 * (RW + 1);
     static constexpr int G_UNITS = DK / 4;
-    // QM rows, padded like Hc^T, and this slice's OI fragments (R, j0/32)
+    // QM rows, padded like Hc^T, and this slice's planes of the OI fragments (R, j0/32)
     static constexpr int QM_UNITS = CHUNK * (RW + 1);
-    static constexpr int OI_FRAG_UNITS = 512 * ES / 16;
-    static constexpr int OI_UNITS = (CHUNK / 16) * OI_FRAG_UNITS;
+    static constexpr int OI_PLANE_UNITS = 256 * ES / 16;   // this slice's plane of one OI fragment
+    static constexpr int OI_UNITS = (CHUNK / 16) * OI_PLANE_UNITS;
     static constexpr int UNITS = HC_UNITS + G_UNITS + QM_UNITS + OI_UNITS;
     static constexpr int LOADS = (UNITS + 63) / 64;  // direct loads per chunk
     static constexpr int LOADS_W = (LOADS + NSTG - 1) / NSTG;   // per stager wave
@@ -638,8 +638,8 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
 #pragma unroll
                 for (int rr = 0; rr < RPW; ++rr) {
                     const int R = RPW * ow + rr;
-                    // OI[16R + ln][perm_index(j0 + 4g) ..]: half of fragment (R, j0/32)'s slots 8g .. 8g + 7
-                    const V4 oi = load_frag_half(reinterpret_cast<const E*>(sl + C::OFF_OI) + 512 * R, l, (j0 >> 4) & 1);
+                    // OI[16R + ln][perm_index(j0 + 4g) ..]: this slice's plane of fragment (R, j0/32)
+                    const V4 oi = load_plane(reinterpret_cast<const E*>(sl + C::OFF_OI) + 256 * R, l, 0);
                     f32x4 acc = {to_f32(oi[0]), to_f32(oi[1]), to_f32(oi[2]), to_f32(oi[3])};
                     const E* qrow = reinterpret_cast<const E*>(sl + C::OFF_QM + (16 * R + ln) * C::RS) + 8 * g;
 #pragma unroll
@@ -682,8 +682,8 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
                 x = (int)C::RL.qm + row * DK * (int)sizeof(E) + (col < C::RW ? col : 0) * 16;
             } else if (u < C::UNITS) {
                 const int v = u - (C::HC_UNITS + C::G_UNITS + C::QM_UNITS);
-                const int R = v / C::OI_FRAG_UNITS, k = v % C::OI_FRAG_UNITS;
-                x = (int)C::RL.oi + frag_at<DV / 32>(R, j0 >> 5) * (int)sizeof(E) + 16 * k;
+                const int R = v / C::OI_PLANE_UNITS, k = v % C::OI_PLANE_UNITS;
+                x = (int)C::RL.oi + (frag_at<DV / 32>(R, j0 >> 5) + 256 * ((j0 >> 4) & 1)) * (int)sizeof(E) + 16 * k;
             } else {
                 x = (int)C::RL.g;   // past the slot's data: lands in the slot's tail padding
             }
