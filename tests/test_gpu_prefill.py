@@ -54,8 +54,9 @@ def test_varlen_edges(dtype):
                                          ("f32", 64, 128)])
 def test_many_chains(dtype, dk, dv):
     """More (sequence, head, 16-column) chains than the GPU has CUs, so the
-    sequential kernel takes two value slices per workgroup: a packed batch of
-    40 sequences with an empty and a one-token one, nonzero initial states."""
+    sequential kernel's workgroups (one CU each) run in several rounds: a
+    packed batch of 40 sequences with an empty and a one-token one, nonzero
+    initial states."""
     g = np.random.default_rng(33)
     lens = [int(n) for n in g.integers(0, 150, 40)]
     lens[3], lens[7] = 0, 1
