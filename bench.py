@@ -162,13 +162,10 @@ def main():
     token_heads = T * H
     # Algorithmic bytes of each kernel: its share of the path's 1540 B per token-head
     # (the intra-chunk kernel reads q, k, v, log_alpha, beta; the sequential kernel writes
-    # the final state, and o when it forms the outputs itself; otherwise the output pass
-    # writes o).  The per-chunk records one kernel hands to the other are this design's
-    # own traffic: they show up in `traffic`, not in `achieved`.
-    fused_out = "prefill_output" not in kern_ms
+    # o and the final state).  The per-chunk records one kernel hands to the other are this
+    # design's own traffic: they show up in `traffic`, not in `achieved`.
     kern_bytes = {"prefill_intra": INTRA_READ * token_heads,
-                  "prefill_state": H * dk * dv * 4 + (256 * token_heads if fused_out else 0),
-                  "prefill_output": 256 * token_heads,       # o
+                  "prefill_state": H * dk * dv * 4 + 256 * token_heads,
                   "chunk_table": 0}
     record_bytes_per_step = int(RECORD_PER_TOKEN_HEAD * token_heads)
     dom = max((k for k in kern_ms if kern_bytes.get(k)), key=lambda k: kern_ms[k])
