@@ -34,7 +34,9 @@ struct ChunkSrc {
 // (the chunk's transition and read-out folded in by the intra kernel):
 //   PM   dk x dk    -Khat^T W, columns in perm32 order, stored in fragment
 //                   order (frag_at: the A operands of the state product)
-//   HCt  [dv][dk]   (Khat^T U)^T, columns in perm32 order
+//   HCt  dv x dk    (Khat^T U)^T, columns in perm32 order, in planar fragment
+//                   order: fragment (value slice j/16, block c/32); a value
+//                   slice's fragments are one contiguous run
 //   QM   [64][dk]   Qg - A_qk W, columns in perm32 order (row-major: it is
 //                   written from the row mapping, where a row is contiguous)
 //   OI   64 x dv    A_qk U, columns in perm32 order, in planar fragment order

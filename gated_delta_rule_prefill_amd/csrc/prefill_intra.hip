@@ -643,7 +643,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 2))) void prefill_intra_
                     w[i] = from_f32<E>(acc[bu][0][i]);
                     w[4 + i] = from_f32<E>(acc[bu][1][i]);
                 }
-                store_vec(out.HCt + (16 * (ct0 + bu) + ln) * DK + 32 * m + 8 * g, w);
+                store_frag_planar(out.HCt + frag_at<DK / 32>(ct0 + bu, m), lane, w);   // rows 2m, 2m + 1 as the planes
             }
         }
         // OI[r][perm(j)] for r = 16Rr + ln, j = 16ct + 4g + i

@@ -72,7 +72,7 @@ __device__ __forceinline__ void load_serial(SerialOps<E, DK>& op, const unsigned
     const float* G = reinterpret_cast<const float*>(r + C::RL.g);
 #pragma unroll
     for (int t = 0; t < C::KT; ++t) {
-        op.hc[t] = load_vec<V4>(HC + (j0 + ln) * DK + perm_index(16 * t + 4 * g));
+        op.hc[t] = load_plane(HC + frag_at<DK / 32>(j0 >> 4, t >> 1), 16 * g + ln, t & 1);   // row j0 + ln
         op.gc[t] = load_vec<f32x4>(G + 16 * t + 4 * g);
     }
 }
@@ -338,7 +338,7 @@ struct RingCfg {
     static constexpr int NX = 3;
     static constexpr int RW = DK * ES / 16;          // 16-byte units per PM / Hc^T row
     static constexpr int RS = (RW + 1) * 16;         // padded LDS row stride (bytes)
-    static constexpr int HC_UNITS = 16 * (RW + 1);
+    static constexpr int HC_UNITS = DK * ES;         // this slice's Hc^T fragments (16 rows)
     static constexpr int G_UNITS = DK / 4;
     // QM rows, padded like Hc^T, and this slice's planes of the OI fragments (R, j0/32)
     static constexpr int QM_UNITS = CHUNK * (RW + 1);
@@ -508,7 +508,7 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const int t = 2 * w + h2;
-                hc[h2] = load_vec<V4>(reinterpret_cast<const E*>(sl + C::OFF_HC + ln * C::RS) + perm_index(16 * t + 4 * g));
+                hc[h2] = load_plane(reinterpret_cast<const E*>(sl + C::OFF_HC) + 512 * w, l, h2);   // Hc^T[j0 + ln][perm_index(16t + 4g) ..]
                 gc[h2] = load_vec<f32x4>(reinterpret_cast<const float*>(sl + C::OFF_G) + 16 * t + 4 * g);
             }
             __builtin_amdgcn_sched_barrier(0);   // LDS reads first, then the early loads
@@ -672,8 +672,7 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
             const int u = 64 * (i0 + k) + l;
             int x;
             if (u < C::HC_UNITS) {
-                const int row = u / (C::RW + 1), col = u % (C::RW + 1);
-                x = (int)C::RL.hc + (j0 + row) * DK * (int)sizeof(E) + (col < C::RW ? col : 0) * 16;
+                x = (int)C::RL.hc + j0 * DK * (int)sizeof(E) + 16 * u;   // the slice's fragments
             } else if (u < C::HC_UNITS + C::G_UNITS) {
                 x = (int)C::RL.g + (u - C::HC_UNITS) * 16;
             } else if (u < C::HC_UNITS + C::G_UNITS + C::QM_UNITS) {
