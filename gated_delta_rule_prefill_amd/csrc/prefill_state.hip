@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 //       (plain loads, folded into a value three chunks later), and with
 //       chunk_states sends the fp32 chunk-start states to memory;
 //   stager wave  moves this slice's Hc^T rows, gamma_C, QM and the slice's OI
-//       fragments into a three-slot LDS ring by direct global->LDS loads
+//       fragments into a four-slot LDS ring by direct global->LDS loads
 //       (global_load_lds_dwordx4), two chunks ahead.
 // Every wave passes one barrier per chunk.  A ring slot or state slot is
 // written only after the barrier that ends the chunk which last read it.
