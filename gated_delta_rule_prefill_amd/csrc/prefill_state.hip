@@ -319,8 +319,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 //       the chain will read TOUCH_DIST chunks ahead so that the loads hit L2
 //       (plain loads, folded into a value three chunks later), and with
 //       chunk_states sends the fp32 chunk-start states to memory;
-//   stager wave  moves this slice's Hc^T rows, gamma_C, QM and the slice's OI
-//       fragments into a four-slot LDS ring by direct global->LDS loads
+//   stager wave  moves this slice's Hc^T fragments, gamma_C, QM and the
+//       slice's OI planes into a four-slot LDS ring by direct global->LDS loads
 //       (global_load_lds_dwordx4), two chunks ahead.
 // Every wave passes one barrier per chunk.  A ring slot or state slot is
 // written only after the barrier that ends the chunk which last read it.
@@ -336,11 +336,11 @@ struct RingCfg {
     static constexpr int XSLOT = KS * 64 * FRAG;     // one chunk-start state (operand slots)
     // state slots: it (serial waves read), it + 1 (written), it - 1 (output waves)
     static constexpr int NX = 3;
-    static constexpr int RW = DK * ES / 16;          // 16-byte units per PM / Hc^T row
-    static constexpr int RS = (RW + 1) * 16;         // padded LDS row stride (bytes)
+    static constexpr int RW = DK * ES / 16;          // 16-byte units per QM row
+    static constexpr int RS = (RW + 1) * 16;         // padded LDS row stride of QM (bytes)
     static constexpr int HC_UNITS = DK * ES;         // this slice's Hc^T fragments (16 rows)
     static constexpr int G_UNITS = DK / 4;
-    // QM rows, padded like Hc^T, and this slice's planes of the OI fragments (R, j0/32)
+    // QM rows (padded stride RS, against LDS bank conflicts) and this slice's planes of the OI fragments (R, j0/32)
     static constexpr int QM_UNITS = CHUNK * (RW + 1);
     static constexpr int OI_PLANE_UNITS = 256 * ES / 16;   // this slice's plane of one OI fragment
     static constexpr int OI_UNITS = (CHUNK / 16) * OI_PLANE_UNITS;
