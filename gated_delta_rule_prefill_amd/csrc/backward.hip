@@ -37,16 +37,10 @@ constexpr int BWD_PIECE = 8;   // tokens per recomputed piece
 constexpr int BWD_PIECES = CHUNK / BWD_PIECE;
 
 // Totals over the 64 lanes of 4 values per lane (a transposing butterfly:
-// the first two exchanges also halve the values), returned uniform.
+// the two permlane folds also halve the values, then a DPP row sum),
+// returned uniform.
 __device__ __forceinline__ void wave_sum4(const float (&a)[4], int lane, float (&t)[4]) {
-    const bool h5 = lane & 32, h4 = lane & 16;
-    const float b0 = (h5 ? a[2] : a[0]) + lane_xor<32>(h5 ? a[0] : a[2]);
-    const float b1 = (h5 ? a[3] : a[1]) + lane_xor<32>(h5 ? a[1] : a[3]);
-    float c = (h4 ? b1 : b0) + lane_xor<16>(h4 ? b0 : b1);
-    c += lane_xor<8>(c);
-    c += lane_xor<4>(c);
-    c += lane_xor<2>(c);
-    c += lane_xor<1>(c);
+    const float c = row16_sum(fold16(fold32(a[0], a[2]), fold32(a[1], a[3])));
     // lane 16 i now holds the total of value i
 #pragma unroll
     for (int i = 0; i < 4; ++i) t[i] = read_lane(c, 16 * i);

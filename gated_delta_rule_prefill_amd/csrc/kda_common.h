@@ -146,43 +146,91 @@ __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-
 __host__ __device__ constexpr int row_lane(int r) {
     return (((r >> 2) & 1) << 5) | (((r >> 1) & 1) << 4) | ((r & 1) << 3);
 }
+// Exchanges across lane bits 4 and 5 on the VALU (CDNA4 permlane swaps).
+// permlane32_swap(x, y) trades lanes 32-63 of x with lanes 0-31 of y, so x
+// then holds (x low, y low) and y holds (x high, y high); their sum is, in
+// the low half, x summed over lane bit 5 and, in the high half, y summed
+// over it.  permlane16_swap does the same for lane bit 4 (odd rows of x
+// with even rows of y).  The swapped halves are copied out of the result
+// vector before the bit cast: a bit cast of a vector element in place
+// compiles as element 0 here.
+__device__ __forceinline__ float fold32(float x, float y) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, y), false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float fold16(float x, float y) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, y), false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    const int v = __builtin_bit_cast(int, x);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false));
+}
 // Value of lane l ^ M: quad permutations and the row rotation by 8 through
-// DPP, xor 4 and 16 through a swizzle (within 32 lanes), 32 through a permute.
+// DPP, xor 4 through a swizzle, 16 and 32 through the permlane swaps.
 template <int M>
 __device__ __forceinline__ float lane_xor(float x) {
-    const int v = __builtin_bit_cast(int, x);
-    int r;
-    if constexpr (M == 1) r = __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);        // quad_perm 1,0,3,2
-    else if constexpr (M == 2) r = __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
-    else if constexpr (M == 8) r = __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false);  // row_ror 8
-    else if constexpr (M == 4 || M == 16) r = __builtin_amdgcn_ds_swizzle(v, 0x1F | (M << 10));
-    else r = __builtin_bit_cast(int, __shfl_xor(x, M));
-    return __builtin_bit_cast(float, r);
+    if constexpr (M == 1) return dpp<0xB1>(x);        // quad_perm 1,0,3,2
+    else if constexpr (M == 2) return dpp<0x4E>(x);   // quad_perm 2,3,0,1
+    else if constexpr (M == 8) return dpp<0x128>(x);  // row_ror 8
+    else if constexpr (M == 4)
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (4 << 10)));
+    else {
+        static_assert(M == 16 || M == 32, "lane_xor: 1, 2, 4, 8, 16 or 32");
+        const unsigned v = __builtin_bit_cast(unsigned, x);
+        const bool hi = __lane_id() & M;
+        if constexpr (M == 16) {
+            const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+            const unsigned r0 = r[0], r1 = r[1];
+            return __builtin_bit_cast(float, hi ? r0 : r1);
+        } else {
+            const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+            const unsigned r0 = r[0], r1 = r[1];
+            return __builtin_bit_cast(float, hi ? r0 : r1);
+        }
+    }
+}
+// Sum over the 8 lanes that share bits 3-5 of the lane index: the row
+// half-mirror (lane i with 7 - i) and two quad permutations, all DPP.
+__device__ __forceinline__ float group8_sum(float d) {
+    d += dpp<0x141>(d);
+    d += dpp<0x4E>(d);
+    return d + dpp<0xB1>(d);
+}
+// Sum over the 16 lanes of a row (row rotations by 8 and 4, then the quads).
+__device__ __forceinline__ float row16_sum(float d) {
+    d += dpp<0x128>(d);
+    d += dpp<0x124>(d);
+    d += dpp<0x4E>(d);
+    return d + dpp<0xB1>(d);
 }
 
 __device__ __forceinline__ float wave_sum8(const float (&a)[8], int lane) {
-    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
+    const bool h3 = lane & 8;
     float b[4], c[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = (h5 ? a[4 + j] : a[j]) + lane_xor<32>(h5 ? a[j] : a[4 + j]);
+    for (int j = 0; j < 4; ++j) b[j] = fold32(a[j], a[4 + j]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) c[j] = (h4 ? b[2 + j] : b[j]) + lane_xor<16>(h4 ? b[j] : b[2 + j]);
-    float d = (h3 ? c[1] : c[0]) + lane_xor<8>(h3 ? c[0] : c[1]);
-    d += lane_xor<4>(d);
-    d += lane_xor<2>(d);
-    d += lane_xor<1>(d);
-    return d;
+    for (int j = 0; j < 2; ++j) c[j] = fold16(b[j], b[2 + j]);
+    const float d = (h3 ? c[1] : c[0]) + lane_xor<8>(h3 ? c[0] : c[1]);
+    return group8_sum(d);
 }
 // Sums of 8 values over the lanes that share bits 0-2 of the lane index
 // (a transposing butterfly over lane bits 3-5: 7 exchanges).  Lane l gets
 // the total of a[4 b5 + 2 b4 + b3] over its 8 lanes, b_i bit i of l.
 __device__ __forceinline__ float rowgroup_sum8(const float (&a)[8], int lane) {
-    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
+    const bool h3 = lane & 8;
     float b[4], c[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = (h5 ? a[4 + j] : a[j]) + lane_xor<32>(h5 ? a[j] : a[4 + j]);
+    for (int j = 0; j < 4; ++j) b[j] = fold32(a[j], a[4 + j]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) c[j] = (h4 ? b[2 + j] : b[j]) + lane_xor<16>(h4 ? b[j] : b[2 + j]);
+    for (int j = 0; j < 2; ++j) c[j] = fold16(b[j], b[2 + j]);
     return (h3 ? c[1] : c[0]) + lane_xor<8>(h3 ? c[0] : c[1]);
 }
 
