@@ -46,8 +46,10 @@ __device__ __forceinline__ void wave_sum4(const float (&a)[4], int lane, float (
     for (int i = 0; i < 4; ++i) t[i] = read_lane(c, 16 * i);
 }
 
+// The LDS it stages holds the CU to one workgroup, one wave per SIMD: the
+// compiler may spend registers on hiding latency.
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void backward_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void backward_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const ChunkSrc src, const float* __restrict__ chunk_states, const E* __restrict__ d_o,
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(256) void backward_kernel(
 {
     constexpr int RPL = DK / 64, NSL = DV / BWD_COLS, CW = BWD_CW;
     constexpr int NV = RPL * CW;   // state values per lane
-    __shared__ float sQ[CHUNK][DK], sK[CHUNK][DK], sA[CHUNK][DK];
+    __shared__ __attribute__((aligned(16))) float sQ[CHUNK][DK], sK[CHUNK][DK], sA[CHUNK][DK];
     __shared__ __attribute__((aligned(16))) float sV[CHUNK][BWD_COLS], sDO[CHUNK][BWD_COLS];
     __shared__ float sB[CHUNK];
     __shared__ float comb[BWD_PIECE][4][3][DK];   // per-wave row sums of a piece: dq, dk, dlog_alpha
@@ -82,29 +84,49 @@ __global__ __launch_bounds__(256) void backward_kernel(
         for (int e = 0; e < CW; ++e)
             G[rr][e] = d_final ? d_final[((size_t)pair * DK + r0 + rr) * DV + j0 + e] : 0.f;
 
-    // one forward token (index i of the staged chunk) on S; y and nu (uniform) returned
-    auto fwd = [&](float (&S)[RPL][CW], int i, float (&y)[CW], float (&nu)[CW]) {
+    // A staged token's values as one lane uses them, read from LDS a token
+    // ahead of their use so that the read is off the chain's critical path
+    // (index clamped to the staged chunk).
+    struct Tok {
+        float a[RPL], k[RPL], q[RPL], v[CW], dov[CW], b;
+    };
+    auto tok = [&](int i, bool with_q) {
+        i = min(i, CHUNK - 1);
+        Tok t;
+#pragma unroll
+        for (int rr = 0; rr < RPL; ++rr) {
+            t.a[rr] = sA[i][r0 + rr];
+            t.k[rr] = sK[i][r0 + rr];
+            t.q[rr] = with_q ? sQ[i][r0 + rr] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < CW; ++e) {
+            t.v[e] = sV[i][cw0 + e];
+            t.dov[e] = with_q ? sDO[i][cw0 + e] : 0.f;
+        }
+        t.b = sB[i];
+        return t;
+    };
+    // one forward token on S; y and nu (uniform) returned
+    auto fwd = [&](float (&S)[RPL][CW], const Tok& t, float (&y)[CW], float (&nu)[CW]) {
         float pp[CW];
 #pragma unroll
         for (int e = 0; e < CW; ++e) pp[e] = 0.f;
 #pragma unroll
         for (int rr = 0; rr < RPL; ++rr) {
-            const float a = sA[i][r0 + rr], kc = sK[i][r0 + rr];
 #pragma unroll
             for (int e = 0; e < CW; ++e) {
-                S[rr][e] *= a;
-                pp[e] += kc * S[rr][e];
+                S[rr][e] *= t.a[rr];
+                pp[e] += t.k[rr] * S[rr][e];
             }
         }
         wave_sum4(pp, lane, y);
-        const float b = sB[i];
 #pragma unroll
-        for (int e = 0; e < CW; ++e) nu[e] = b * (sV[i][cw0 + e] - y[e]);
+        for (int e = 0; e < CW; ++e) nu[e] = t.b * (t.v[e] - y[e]);
 #pragma unroll
         for (int rr = 0; rr < RPL; ++rr) {
-            const float kc = sK[i][r0 + rr];
 #pragma unroll
-            for (int e = 0; e < CW; ++e) S[rr][e] += kc * nu[e];
+            for (int e = 0; e < CW; ++e) S[rr][e] += t.k[rr] * nu[e];
         }
     };
 
@@ -112,21 +134,52 @@ __global__ __launch_bounds__(256) void backward_kernel(
         const ChunkInfo ci = chunk_desc(src, c_begin + c);
         const int L = ci.len;
         // ---- stage the chunk's inputs (fp32) ----
-        __syncthreads();   // the previous chunk's staged values are no longer read
-        for (int x = tid; x < CHUNK * DK; x += 256) {
-            const int i = x / DK, r = x % DK;
-            const size_t at = ((size_t)(ci.start + min(i, L - 1)) * H + h) * DK + r;
-            sQ[i][r] = to_f32(q[at]);
-            sK[i][r] = to_f32(k[at]);
-            sA[i][r] = __expf(log_alpha[at]);
+        // Every thread issues all of its loads (4 elements each; rows past
+        // the chunk's end repeat its last token) before waiting on any, and
+        // before the barrier that frees the previous chunk's staged values.
+        {
+            using V4 = typename Vec<E>::v4;
+            constexpr int NL = CHUNK * DK / 4 / 256;   // loads per thread per array
+            static_assert(CHUNK * BWD_COLS == 4 * 256, "one load of v and dO per thread");
+            V4 lq[NL], lk[NL];
+            f32x4 la[NL];
+#pragma unroll
+            for (int m = 0; m < NL; ++m) {
+                const int x = 4 * (m * 256 + tid), i = x / DK, r = x % DK;
+                const size_t at = ((size_t)(ci.start + min(i, L - 1)) * H + h) * DK + r;
+                lq[m] = load_vec<V4>(q + at);
+                lk[m] = load_vec<V4>(k + at);
+                la[m] = *reinterpret_cast<const f32x4*>(log_alpha + at);
+            }
+            const int iv = tid / 4, jv = 4 * (tid % 4);
+            const size_t atv = ((size_t)(ci.start + min(iv, L - 1)) * H + h) * DV + slice * BWD_COLS + jv;
+            const V4 lv = load_vec<V4>(v + atv), ld = load_vec<V4>(d_o + atv);
+            const float lb = tid < CHUNK ? beta[(size_t)(ci.start + min(tid, L - 1)) * H + h] : 0.f;
+            __syncthreads();   // the previous chunk's staged values are no longer read
+#pragma unroll
+            for (int m = 0; m < NL; ++m) {
+                const int x = 4 * (m * 256 + tid), i = x / DK, r = x % DK;
+                f32x4 fq, fk, fa;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    fq[e] = to_f32(lq[m][e]);
+                    fk[e] = to_f32(lk[m][e]);
+                    fa[e] = __expf(la[m][e]);
+                }
+                *reinterpret_cast<f32x4*>(&sQ[i][r]) = fq;
+                *reinterpret_cast<f32x4*>(&sK[i][r]) = fk;
+                *reinterpret_cast<f32x4*>(&sA[i][r]) = fa;
+            }
+            f32x4 fv, fd;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                fv[e] = to_f32(lv[e]);
+                fd[e] = to_f32(ld[e]);
+            }
+            *reinterpret_cast<f32x4*>(&sV[iv][jv]) = fv;
+            *reinterpret_cast<f32x4*>(&sDO[iv][jv]) = fd;
+            if (tid < CHUNK) sB[tid] = lb;
         }
-        for (int x = tid; x < CHUNK * BWD_COLS; x += 256) {
-            const int i = x / BWD_COLS, j = x % BWD_COLS;
-            const size_t at = ((size_t)(ci.start + min(i, L - 1)) * H + h) * DV + slice * BWD_COLS + j;
-            sV[i][j] = to_f32(v[at]);
-            sDO[i][j] = to_f32(d_o[at]);
-        }
-        if (tid < CHUNK) sB[tid] = beta[(size_t)(ci.start + min(tid, L - 1)) * H + h];
         __syncthreads();
 
         // ---- first sweep: the state entering every piece, to scratch ----
@@ -138,6 +191,7 @@ __global__ __launch_bounds__(256) void backward_kernel(
             for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
                 for (int e = 0; e < CW; ++e) S[rr][e] = cs[(size_t)rr * DV + e];
+            Tok t = tok(0, false);
             for (int p = 0; p < npieces; ++p) {
 #pragma unroll
                 for (int rr = 0; rr < RPL; ++rr)
@@ -146,8 +200,10 @@ __global__ __launch_bounds__(256) void backward_kernel(
                 if (p + 1 < npieces) {   // the last piece's successors are not needed
 #pragma unroll
                     for (int i = 0; i < BWD_PIECE; ++i) {
+                        const Tok nx = tok(BWD_PIECE * p + i + 1, false);
                         float y[CW], nu[CW];
-                        fwd(S, BWD_PIECE * p + i, y, nu);
+                        fwd(S, t, y, nu);
+                        t = nx;
                     }
                 }
             }
@@ -164,34 +220,40 @@ __global__ __launch_bounds__(256) void backward_kernel(
                 for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
                     for (int e = 0; e < CW; ++e) S[rr][e] = scr[(p * NV + rr * CW + e) * 256 + tid];
+                Tok t = tok(i0, false);
 #pragma unroll
                 for (int i = 0; i < BWD_PIECE; ++i) {
                     if (i < np) {
+                        const Tok nx = tok(i0 + i + 1, false);
 #pragma unroll
                         for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
                             for (int e = 0; e < CW; ++e) Sp[i][rr][e] = S[rr][e];
-                        fwd(S, i0 + i, yP[i], nuP[i]);
+                        fwd(S, t, yP[i], nuP[i]);
+                        t = nx;
                     }
                 }
             }
+            Tok tr = tok(i0 + np - 1, true);
 #pragma unroll
             for (int i = BWD_PIECE - 1; i >= 0; --i) {
                 if (i >= np) continue;
                 const int ti = i0 + i;
-                const float b = sB[ti];
+                const Tok t = tr;
+                tr = tok(max(ti - 1, 0), true);
+                const float b = t.b;
                 float dov[CW], vr[CW];
 #pragma unroll
                 for (int e = 0; e < CW; ++e) {
-                    dov[e] = sDO[ti][cw0 + e];
-                    vr[e] = sV[ti][cw0 + e] - yP[i][e];   // v - y
+                    dov[e] = t.dov[e];
+                    vr[e] = t.v[e] - yP[i][e];   // v - y
                 }
                 float X[RPL][CW], dq[RPL], gkp[CW];
 #pragma unroll
                 for (int e = 0; e < CW; ++e) gkp[e] = 0.f;
 #pragma unroll
                 for (int rr = 0; rr < RPL; ++rr) {
-                    const float a = sA[ti][r0 + rr], kc = sK[ti][r0 + rr], qc = sQ[ti][r0 + rr];
+                    const float a = t.a[rr], kc = t.k[rr], qc = t.q[rr];
                     dq[rr] = 0.f;
 #pragma unroll
                     for (int e = 0; e < CW; ++e) {
@@ -211,7 +273,7 @@ __global__ __launch_bounds__(256) void backward_kernel(
                 }
 #pragma unroll
                 for (int rr = 0; rr < RPL; ++rr) {
-                    const float a = sA[ti][r0 + rr], kc = sK[ti][r0 + rr];
+                    const float a = t.a[rr], kc = t.k[rr];
                     float dk = 0.f, dl = 0.f;
 #pragma unroll
                     for (int e = 0; e < CW; ++e) {

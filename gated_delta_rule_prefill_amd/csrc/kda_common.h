@@ -167,10 +167,12 @@ __device__ __forceinline__ float fold16(float x, float y) {
     return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
 }
 
+// DPP move for patterns that read inside the lane's own row (rotations,
+// mirrors, quad permutations): no lane is out of bounds, so bound_ctrl is
+// free to set, which lets the compiler fold the move into the add using it.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-    const int v = __builtin_bit_cast(int, x);
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 // Value of lane l ^ M: quad permutations and the row rotation by 8 through
 // DPP, xor 4 through a swizzle, 16 and 32 through the permlane swaps.
