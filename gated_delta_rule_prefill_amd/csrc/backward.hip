@@ -133,10 +133,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int c = n - 1; c >= 0; --c) {
         const ChunkInfo ci = chunk_desc(src, c_begin + c);
         const int L = ci.len;
+        // the state entering the chunk (its columns of this lane), loaded with the inputs
+        float Sc[RPL][CW];
         // ---- stage the chunk's inputs (fp32) ----
-        // Every thread issues all of its loads (4 elements each; rows past
-        // the chunk's end repeat its last token) before waiting on any, and
-        // before the barrier that frees the previous chunk's staged values.
+        // Every thread issues all of its loads (4 elements each) before
+        // waiting on any, and before the barrier that frees the previous
+        // chunk's staged values.  Rows past the chunk's end are staged as a
+        // neutral token (alpha = 1, beta = 0, q = k = v = dO = 0), which
+        // leaves S and G unchanged, so every piece runs all of its tokens.
         {
             using V4 = typename Vec<E>::v4;
             constexpr int NL = CHUNK * DK / 4 / 256;   // loads per thread per array
@@ -155,16 +159,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const size_t atv = ((size_t)(ci.start + min(iv, L - 1)) * H + h) * DV + slice * BWD_COLS + jv;
             const V4 lv = load_vec<V4>(v + atv), ld = load_vec<V4>(d_o + atv);
             const float lb = tid < CHUNK ? beta[(size_t)(ci.start + min(tid, L - 1)) * H + h] : 0.f;
+            const float* cs = chunk_states + ((size_t)(c_begin + c) * H + h) * DK * DV + (size_t)r0 * DV + j0;
+#pragma unroll
+            for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+                for (int e = 0; e < CW; ++e) Sc[rr][e] = cs[(size_t)rr * DV + e];
             __syncthreads();   // the previous chunk's staged values are no longer read
 #pragma unroll
             for (int m = 0; m < NL; ++m) {
                 const int x = 4 * (m * 256 + tid), i = x / DK, r = x % DK;
+                const bool pad = i >= L;
                 f32x4 fq, fk, fa;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    fq[e] = to_f32(lq[m][e]);
-                    fk[e] = to_f32(lk[m][e]);
-                    fa[e] = __expf(la[m][e]);
+                    fq[e] = pad ? 0.f : to_f32(lq[m][e]);
+                    fk[e] = pad ? 0.f : to_f32(lk[m][e]);
+                    fa[e] = pad ? 1.f : __expf(la[m][e]);
                 }
                 *reinterpret_cast<f32x4*>(&sQ[i][r]) = fq;
                 *reinterpret_cast<f32x4*>(&sK[i][r]) = fk;
@@ -173,40 +183,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             f32x4 fv, fd;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                fv[e] = to_f32(lv[e]);
-                fd[e] = to_f32(ld[e]);
+                fv[e] = iv < L ? to_f32(lv[e]) : 0.f;
+                fd[e] = iv < L ? to_f32(ld[e]) : 0.f;
             }
             *reinterpret_cast<f32x4*>(&sV[iv][jv]) = fv;
             *reinterpret_cast<f32x4*>(&sDO[iv][jv]) = fd;
-            if (tid < CHUNK) sB[tid] = lb;
+            if (tid < CHUNK) sB[tid] = tid < L ? lb : 0.f;
         }
         __syncthreads();
 
         // ---- first sweep: the state entering every piece, to scratch ----
         const int npieces = (L + BWD_PIECE - 1) / BWD_PIECE;
+        // The last piece's entry state stays in registers; the others go to
+        // scratch and come back a piece ahead of their use.
+        float Sn[RPL][CW];   // the state entering the piece walked next
         {
             float S[RPL][CW];
-            const float* cs = chunk_states + ((size_t)(c_begin + c) * H + h) * DK * DV + (size_t)r0 * DV + j0;
 #pragma unroll
             for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
-                for (int e = 0; e < CW; ++e) S[rr][e] = cs[(size_t)rr * DV + e];
+                for (int e = 0; e < CW; ++e) S[rr][e] = Sc[rr][e];
             Tok t = tok(0, false);
-            for (int p = 0; p < npieces; ++p) {
+            for (int p = 0; p + 1 < npieces; ++p) {
 #pragma unroll
                 for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
                     for (int e = 0; e < CW; ++e) scr[(p * NV + rr * CW + e) * 256 + tid] = S[rr][e];
-                if (p + 1 < npieces) {   // the last piece's successors are not needed
 #pragma unroll
-                    for (int i = 0; i < BWD_PIECE; ++i) {
-                        const Tok nx = tok(BWD_PIECE * p + i + 1, false);
-                        float y[CW], nu[CW];
-                        fwd(S, t, y, nu);
-                        t = nx;
-                    }
+                for (int i = 0; i < BWD_PIECE; ++i) {
+                    const Tok nx = tok(BWD_PIECE * p + i + 1, false);
+                    float y[CW], nu[CW];
+                    fwd(S, t, y, nu);
+                    t = nx;
                 }
             }
+#pragma unroll
+            for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+                for (int e = 0; e < CW; ++e) Sn[rr][e] = S[rr][e];
         }
         // ---- pieces, last first: sweep forward keeping states, then backwards ----
         for (int p = npieces - 1; p >= 0; --p) {
@@ -216,37 +230,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             float yP[BWD_PIECE][CW], nuP[BWD_PIECE][CW];
             {
                 float S[RPL][CW];
+                const int pn = max(p - 1, 0);   // the next piece (p = 0: a load left unused)
 #pragma unroll
                 for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
-                    for (int e = 0; e < CW; ++e) S[rr][e] = scr[(p * NV + rr * CW + e) * 256 + tid];
+                    for (int e = 0; e < CW; ++e) {
+                        S[rr][e] = Sn[rr][e];
+                        Sn[rr][e] = scr[(pn * NV + rr * CW + e) * 256 + tid];
+                    }
                 Tok t = tok(i0, false);
 #pragma unroll
                 for (int i = 0; i < BWD_PIECE; ++i) {
-                    if (i < np) {
-                        const Tok nx = tok(i0 + i + 1, false);
+                    const Tok nx = tok(i0 + i + 1, false);
 #pragma unroll
-                        for (int rr = 0; rr < RPL; ++rr)
+                    for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
-                            for (int e = 0; e < CW; ++e) Sp[i][rr][e] = S[rr][e];
-                        fwd(S, t, yP[i], nuP[i]);
-                        t = nx;
-                    }
+                        for (int e = 0; e < CW; ++e) Sp[i][rr][e] = S[rr][e];
+                    fwd(S, t, yP[i], nuP[i]);
+                    t = nx;
                 }
             }
-            Tok tr = tok(i0 + np - 1, true);
+            Tok tr = tok(i0 + BWD_PIECE - 1, true);
 #pragma unroll
             for (int i = BWD_PIECE - 1; i >= 0; --i) {
-                if (i >= np) continue;
                 const int ti = i0 + i;
                 const Tok t = tr;
                 tr = tok(max(ti - 1, 0), true);
                 const float b = t.b;
-                float dov[CW], vr[CW];
+                // dq = S' dO with S' = X + k nu^T: X dO + k (nu . dO)
+                float dov[CW], vr[CW], bvr[CW], ndo = 0.f;
 #pragma unroll
                 for (int e = 0; e < CW; ++e) {
                     dov[e] = t.dov[e];
                     vr[e] = t.v[e] - yP[i][e];   // v - y
+                    bvr[e] = b * vr[e];
+                    ndo += nuP[i][e] * dov[e];
                 }
                 float X[RPL][CW], dq[RPL], gkp[CW];
 #pragma unroll
@@ -254,11 +272,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int rr = 0; rr < RPL; ++rr) {
                     const float a = t.a[rr], kc = t.k[rr], qc = t.q[rr];
-                    dq[rr] = 0.f;
+                    dq[rr] = kc * ndo;
 #pragma unroll
                     for (int e = 0; e < CW; ++e) {
                         X[rr][e] = a * Sp[i][rr][e];
-                        dq[rr] += (X[rr][e] + kc * nuP[i][e]) * dov[e];
+                        dq[rr] += X[rr][e] * dov[e];
                         G[rr][e] += qc * dov[e];
                         gkp[e] += G[rr][e] * kc;
                     }
@@ -277,7 +295,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     float dk = 0.f, dl = 0.f;
 #pragma unroll
                     for (int e = 0; e < CW; ++e) {
-                        dk += b * G[rr][e] * vr[e] + X[rr][e] * dy[e];
+                        dk += G[rr][e] * bvr[e] + X[rr][e] * dy[e];
                         G[rr][e] += kc * dy[e];
                         dl += G[rr][e] * X[rr][e];
                         G[rr][e] *= a;
@@ -287,7 +305,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     comb[i][wave][2][r0 + rr] = dl;
                 }
                 if (lane == 0) combB[i][wave] = db;
-                if (lane < CW) {
+                if (lane < CW && i < np) {
                     const size_t t = (size_t)ci.start + ti;
                     // dv = beta dnu = -dy; lane e writes column e
                     float dve = -dy[0];
