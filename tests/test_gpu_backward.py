@@ -65,6 +65,15 @@ def test_backward_matches_oracle(dtype, dk, dv):
     _check(x, d_o, d_fin, "packed")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_ragged_pieces(dtype):
+    """Chunks whose last 8-token piece is cut short after full pieces (22, 13
+    and 9 tokens): the tail of the piece past the chunk's end must leave every
+    gradient alone."""
+    x, d_o, d_fin = _case(75, [150, 77, 9], 2, 128, 128, dtype)
+    _check(x, d_o, d_fin, "ragged pieces")
+
+
 def test_backward_equal_rows_long():
     """Two equal sequences of 1,000 tokens (16 chunks each), bf16, d = 128."""
     x, d_o, d_fin = _case(72, [1000, 1000], 3, 128, 128, "bf16", packed=False)
