@@ -59,9 +59,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 {
     constexpr int RPL = DK / 64, NSL = DV / BWD_COLS, CW = BWD_CW;
     constexpr int NV = RPL * CW;   // state values per lane
-    __shared__ __attribute__((aligned(16))) float sQ[CHUNK][DK], sK[CHUNK][DK], sA[CHUNK][DK];
-    __shared__ __attribute__((aligned(16))) float sV[CHUNK][BWD_COLS], sDO[CHUNK][BWD_COLS];
-    __shared__ float sB[CHUNK];
+    // Staged token i sits in row i + 1: rows 0 and CHUNK + 1 are never
+    // written, so the look-ahead reads of tokens -1 and CHUNK (whose values
+    // go unused) need no clamping.
+    __shared__ __attribute__((aligned(16))) float sQ[CHUNK + 2][DK], sK[CHUNK + 2][DK], sA[CHUNK + 2][DK];
+    __shared__ __attribute__((aligned(16))) float sV[CHUNK + 2][BWD_COLS], sDO[CHUNK + 2][BWD_COLS];
+    __shared__ float sB[CHUNK + 2];
     __shared__ float comb[BWD_PIECE][4][3][DK];   // per-wave row sums of a piece: dq, dk, dlog_alpha
     __shared__ float combB[BWD_PIECE][4];
 
@@ -86,12 +89,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // A staged token's values as one lane uses them, read from LDS a token
     // ahead of their use so that the read is off the chain's critical path
-    // (index clamped to the staged chunk).
+    // (i from -1 to CHUNK).
     struct Tok {
         float a[RPL], k[RPL], q[RPL], v[CW], dov[CW], b;
     };
     auto tok = [&](int i, bool with_q) {
-        i = min(i, CHUNK - 1);
+        ++i;
         Tok t;
 #pragma unroll
         for (int rr = 0; rr < RPL; ++rr) {
@@ -176,9 +179,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     fk[e] = pad ? 0.f : to_f32(lk[m][e]);
                     fa[e] = pad ? 1.f : __expf(la[m][e]);
                 }
-                *reinterpret_cast<f32x4*>(&sQ[i][r]) = fq;
-                *reinterpret_cast<f32x4*>(&sK[i][r]) = fk;
-                *reinterpret_cast<f32x4*>(&sA[i][r]) = fa;
+                *reinterpret_cast<f32x4*>(&sQ[i + 1][r]) = fq;
+                *reinterpret_cast<f32x4*>(&sK[i + 1][r]) = fk;
+                *reinterpret_cast<f32x4*>(&sA[i + 1][r]) = fa;
             }
             f32x4 fv, fd;
 #pragma unroll
@@ -186,9 +189,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 fv[e] = iv < L ? to_f32(lv[e]) : 0.f;
                 fd[e] = iv < L ? to_f32(ld[e]) : 0.f;
             }
-            *reinterpret_cast<f32x4*>(&sV[iv][jv]) = fv;
-            *reinterpret_cast<f32x4*>(&sDO[iv][jv]) = fd;
-            if (tid < CHUNK) sB[tid] = tid < L ? lb : 0.f;
+            *reinterpret_cast<f32x4*>(&sV[iv + 1][jv]) = fv;
+            *reinterpret_cast<f32x4*>(&sDO[iv + 1][jv]) = fd;
+            if (tid < CHUNK) sB[tid + 1] = tid < L ? lb : 0.f;
         }
         __syncthreads();
 
@@ -251,11 +254,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 }
             }
             Tok tr = tok(i0 + BWD_PIECE - 1, true);
+            // dv rows of the piece; every lane stores its column's value
+            // (lanes 4 and up repeat lanes 0-3), so no lane mask is needed
+            E* const dvp = dv_out + ((size_t)(ci.start + i0) * H + h) * DV + j0 + (lane & (CW - 1));
 #pragma unroll
             for (int i = BWD_PIECE - 1; i >= 0; --i) {
                 const int ti = i0 + i;
                 const Tok t = tr;
-                tr = tok(max(ti - 1, 0), true);
+                tr = tok(ti - 1, true);
                 const float b = t.b;
                 // dq = S' dO with S' = X + k nu^T: X dO + k (nu . dO)
                 float dov[CW], vr[CW], bvr[CW], ndo = 0.f;
@@ -305,13 +311,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     comb[i][wave][2][r0 + rr] = dl;
                 }
                 if (lane == 0) combB[i][wave] = db;
-                if (lane < CW && i < np) {
-                    const size_t t = (size_t)ci.start + ti;
-                    // dv = beta dnu = -dy; lane e writes column e
+                if (i < np) {
+                    // dv = beta dnu = -dy
                     float dve = -dy[0];
 #pragma unroll
-                    for (int e = 1; e < CW; ++e) dve = lane == e ? -dy[e] : dve;
-                    dv_out[(t * H + h) * DV + j0 + lane] = from_f32<E>(dve);
+                    for (int e = 1; e < CW; ++e) dve = (lane & (CW - 1)) == e ? -dy[e] : dve;
+                    dvp[(size_t)i * H * DV] = from_f32<E>(dve);
                 }
             }
             __syncthreads();   // the piece's per-wave row sums are in LDS
