@@ -1,20 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of the KDA hot path on one MI355X.
 
-One JSON line on stdout:
-  value    prefill tokens/s of the single-sequence workload (B=1, T=4096, H=32,
-           dk=dv=128, bf16 q/k/v, fp32 log_alpha/beta/state), inputs resident in
-           HBM, several input sets rotated so that no step reads what the
-           previous one left in the 256 MB last-level cache;
-  roofline the dominant prefill kernel: algorithmic bytes per launch divided by
-           its average duration (HIP events the library records on its own
-           stream), against the 8 TB/s HBM peak; traffic from rocprofv3 counters
-           when the committed measurement matches the current kernel source;
-  path     the whole prefill path against its HBM roofline (1540 B per token-head);
-  decode   the batched decode workload (256 seqs x 32 heads, 128 steps) in GB/s;
-  options  the optional paths: chunk-state export, in-kernel preprocessing and
-           the pooled multi-token recurrent path;
-  cpu_baseline  the fp64 oracle on the host cores, same inputs.
+One JSON line on stdout.  The headline is the long-context prefill, the
+largest single-GPU prefill workload (B=1, T=65536, H=32, dk=dv=128, bf16
+q/k/v, fp32 log_alpha/beta/state, log_alpha = logsigmoid(N(4, 1))):
+
+  value      prefill tokens/s over exactly --steps timed steps (after --warmup
+             untimed ones), inputs resident in HBM, wall clock bracketed by
+             device synchronisation;
+  roofline   the prefill's kernels against the 8 TB/s HBM peak: algorithmic
+             bytes of one step (1540 B per token-head plus the final state)
+             over the summed average durations of the step's kernels, from HIP
+             events the library records on the stream it launches on; traffic
+             from rocprofv3 counters when the committed measurement matches the
+             current kernel sources;
+  path       the same step against its HBM roofline from the wall clock, and
+             the MFMA rate at the dense-tile flop count;
+  ceilings   measured alongside: a plain device copy (HBM) and a large bf16
+             GEMM (MFMA), each with its fraction of the datasheet peak;
+  configs    the other prefill workloads: the single 4096-token sequence
+             (rotated input sets, so no step reads what the previous one left
+             in the 256 MB last-level cache) and the packed batch of 16
+             sequences with nonzero initial states;
+  decode     the batched decode workload (256 seqs x 32 heads, 128 steps), GB/s;
+  options    chunk-state export, in-kernel preprocessing, the pooled recurrent
+             path and the backward pass, on the 4096-token workload;
+  cpu_baseline  the fp64 oracle on the host cores, on the headline's inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -36,23 +47,12 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # dense
 METRIC = "KDA prefill tokens/s (H=32,d=128) + decode state GB/s, % of roofline"
 
-# Algorithmic bytes per token-head at H=32, dk=dv=128 (bf16 q/k/v/o, fp32 log_alpha/beta).
+# Algorithmic bytes per token-head at dk=dv=128 (bf16 q/k/v/o, fp32 log_alpha/beta).
 CHUNK = 64
 PATH_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 256          # 1540: q,k,v + log_alpha + beta + o
-INTRA_READ = 3 * 256 + 512 + 4                                # 1284: q,k,v + log_alpha + beta
-
-
-def record_bytes(dk=128, dv=128, es=2):
-    """Bytes of one chunk-head record the intra-chunk kernel writes and the sequential
-    kernel reads: PM (dk x dk), Hc (dk x dv), QM (C x dk), OI (C x dv) in the I/O type,
-    the chunk decay gamma_C (dk fp32), padded to 256 B."""
-    b = (dk * dk + dk * dv + CHUNK * dk + CHUNK * dv) * es + dk * 4
-    return (b + 255) // 256 * 256
-
-
-RECORD_PER_TOKEN_HEAD = record_bytes() / CHUNK                # 1544
 DECODE_BYTES_PER_UNIT = 2 * 128 * 128 * 4 + 3 * 256 + 512 + 4 + 256   # 132,612
 FLOP_PER_TOKEN_HEAD_DENSE = 180224                             # chunkwise form, dense 64-tiles
+STATE_BYTES = 128 * 128 * 4                                    # one head's fp32 state
 CPU_MIN_SECONDS = 10.0
 
 
@@ -68,14 +68,14 @@ def kernel_source_sha(names):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str):
-    """HBM traffic of `kernel` from the committed rocprofv3 counter summary, if it
-    was measured on the current source of that kernel; else None."""
+def traffic_for(kernel: str, workload: str):
+    """HBM traffic of `kernel` on `workload` from the committed rocprofv3 counter
+    summary, if it was measured on the current source of that kernel; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(kernel)
+        rec = json.load(open(path)).get(workload, {}).get(kernel)
         if not rec or rec.get("source_sha") != kernel_source_sha(rec["sources"]):
             return None
         return rec["bytes_per_launch"]
@@ -83,17 +83,157 @@ def traffic_for(kernel: str):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class Prefill:
+    """Device buffers of one prefill workload and a step that runs it."""
+
+    def __init__(self, x, dev, sets=1):
+        import torch
+        import gated_delta_rule_prefill_amd as kdalib
+        self.x, self.kdalib = x, kdalib
+        T, H, dk, dv, N = x.T, x.H, x.dk, x.dv, x.num_seqs
+
+        def dq(a):
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        # distinct buffers with identical contents: the work stays the same while
+        # consecutive steps read different memory
+        self.sets = [dict(q=dq(x.q), k=dq(x.k), v=dq(x.v),
+                          la=torch.from_numpy(x.log_alpha).to(dev),
+                          beta=torch.from_numpy(x.beta).to(dev)) for _ in range(sets)]
+        self.s0 = None if x.initial_state is None else torch.from_numpy(x.initial_state).to(dev)
+        self.cu = None if x.cu_seqlens is None else \
+            torch.from_numpy(np.ascontiguousarray(x.cu_seqlens, dtype=np.int32)).to(dev)
+        self.out = [torch.empty((T, H, dv), dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+        self.fin = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(kdalib.workspace_bytes(T, N, H, dk, dv, True), dtype=torch.uint8,
+                              device=dev)
+        self.token_heads = T * H
+        self.path_bytes = PATH_BYTES_PER_TOKEN_HEAD * T * H + N * H * STATE_BYTES * \
+            (2 if x.initial_state is not None else 1)
+
+    def step(self, i=0, **kw):
+        s = self.sets[i % len(self.sets)]
+        self.kdalib.prefill(s["q"], s["k"], s["v"], s["la"], s["beta"], self.s0, self.cu,
+                            num_seqs=self.x.num_seqs, final_state=self.fin,
+                            out=self.out[i % len(self.sets)], workspace=self.ws, **kw)
+
+    def event_time_us(self, reps, warm=3):
+        import torch
+        for i in range(warm):
+            self.step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            self.step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def kernel_us(self, reps):
+        """Average duration of each kernel of a step (HIP events recorded by the
+        library around each kernel on its stream)."""
+        self.kdalib.set_kernel_timing(True)
+        sums = {}
+        try:
+            for i in range(reps):
+                self.step(i)
+                for name, ms in self.kdalib.prefill_kernel_times():
+                    sums[name] = sums.get(name, 0.0) + ms
+        finally:
+            self.kdalib.set_kernel_timing(False)
+        return {k: v * 1e3 / reps for k, v in sums.items()}
+
+    def summary(self, us):
+        x = self.x
+        tok_s = x.T / (us * 1e-6)
+        roof_tok_s = x.T * HBM_PEAK_GBS * 1e9 / self.path_bytes
+        return {"us_per_step": round(us, 2), "tokens_per_s": round(tok_s, 1),
+                "algorithmic_bytes_per_step": self.path_bytes,
+                "achieved_GBs": round(self.path_bytes / (us * 1e-6) / 1e9, 1),
+                "roofline_tokens_per_s": round(roof_tok_s),
+                "frac_of_roofline": round(tok_s / roof_tok_s, 4),
+                "mfma_tflops_dense_count": round(FLOP_PER_TOKEN_HEAD_DENSE * self.token_heads /
+                                                 (us * 1e-6) / 1e12, 1)}
+
+
+def ceilings(dev):
+    """Achievable rates measured in the same run: a device copy and a bf16 GEMM."""
+    import torch
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    n = 1 << 31
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    best = 1e9
+    for i in range(8):
+        e0, e1 = ev(), ev()
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            best = min(best, e0.elapsed_time(e1))
+    copy_gbs = 2 * n / (best * 1e-3) / 1e9
+    del b
+    f = a.view(torch.float32)   # in-place scale of the same 2 GiB: one read and one write
+    best = 1e9
+    for i in range(8):
+        e0, e1 = ev(), ev()
+        e0.record()
+        f.mul_(1.0)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            best = min(best, e0.elapsed_time(e1))
+    scale_gbs = 2 * n / (best * 1e-3) / 1e9
+    del a, f
+    copy_gbs = max(copy_gbs, scale_gbs)
+    m = 8192
+    x = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    y = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    best = 1e9
+    for i in range(8):
+        e0, e1 = ev(), ev()
+        e0.record()
+        torch.mm(x, y)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            best = min(best, e0.elapsed_time(e1))
+    mm_tflops = 2 * m ** 3 / (best * 1e-3) / 1e12
+    del x, y
+    return {"hbm_copy_GBs": round(copy_gbs, 1), "hbm_copy_frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "hbm_copy": "the faster of a torch copy of a 2 GiB device buffer and an in-place "
+                        "scale of one (read + write counted), best of 6 runs each",
+            "bf16_gemm_TFLOPs": round(mm_tflops, 1),
+            "bf16_gemm_frac_of_peak": round(mm_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "bf16_gemm": "torch.mm of two 8192x8192 bf16 matrices (hipBLASLt), best of 6"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--sets", type=int, default=3, help="rotated input sets (defeat the MALL)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other prefill workloads, ceilings and optional paths")
     ap.add_argument("--no-options", action="store_true",
-                    help="skip the optional paths (chunk states, preprocessing, pooled tokens)")
+                    help="skip the optional paths (chunk states, preprocessing, pooled tokens, backward)")
+    ap.add_argument("--headline", choices=["long", "single"], default="long",
+                    help="headline workload: the 65536-token sequence (default) or the 4096-token one")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -112,83 +252,37 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
-    # ---------------- prefill workload (config 2) ----------------
-    x = gen.config_prefill(2)
-    T, H, dk, dv = x.T, x.H, x.dk, x.dv
-    log(f"[bench] prefill workload: B=1 T={T} H={H} dk={dk} dv={dv} bf16, {args.sets} input sets")
-
     def dq(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    sets = []
-    for i in range(args.sets):
-        # distinct buffers with identical contents (a different permutation of heads would
-        # change the work; copies keep the work identical while defeating cache reuse)
-        sets.append(dict(q=dq(x.q), k=dq(x.k), v=dq(x.v),
-                         la=torch.from_numpy(x.log_alpha).to(dev),
-                         beta=torch.from_numpy(x.beta).to(dev)))
-    out = [torch.empty((T, H, dv), dtype=torch.bfloat16, device=dev) for _ in range(args.sets)]
-    fin = torch.empty((1, H, dk, dv), dtype=torch.float32, device=dev)
-    ws = torch.empty(kdalib.workspace_bytes(T, 1, H, dk, dv, True), dtype=torch.uint8, device=dev)
+    rec_extra = {}
+    single = None
+    if not args.no_extra or args.headline == "single":
+        log("[bench] single-sequence workload T=4096 H=32 d=128, 3 rotated input sets")
+        single = Prefill(gen.config_prefill(2), dev, sets=3)
 
-    def step(i):
-        s = sets[i % args.sets]
-        kdalib.prefill(s["q"], s["k"], s["v"], s["la"], s["beta"], None, None, num_seqs=1,
-                       final_state=fin, out=out[i % args.sets], workspace=ws)
+    if not args.no_extra:
+        rec_extra["ceilings"] = ceilings(dev)
+        log(f"[bench] ceilings: {rec_extra['ceilings']}")
+        # -- the other prefill workloads ------------------------------------
+        us = single.event_time_us(100, warm=20)
+        c2 = single.summary(us)
+        c2["workload"] = "single-sequence prefill B=1 T=4096 H=32 dk=dv=128 bf16, zero initial state"
+        c2["kernel_us"] = {k: round(v, 2) for k, v in single.kernel_us(50).items()}
+        log(f"[bench] T=4096: {us:.1f} us/step, {c2['tokens_per_s'] / 1e6:.2f} M tok/s, "
+            f"{c2['frac_of_roofline']:.3f} of roofline")
+        packed = Prefill(gen.config_prefill(3), dev)
+        us = packed.event_time_us(20)
+        c3 = packed.summary(us)
+        c3["workload"] = (f"packed varlen prefill, 16 sequences U[256,4096] (T={packed.x.T}), H=32 "
+                          f"dk=dv=128 bf16, nonzero fp32 initial states, per-sequence final states")
+        c3["kernel_us"] = {k: round(v, 2) for k, v in packed.kernel_us(10).items()}
+        log(f"[bench] packed: {us:.1f} us/step, {c3['tokens_per_s'] / 1e6:.2f} M tok/s, "
+            f"{c3['frac_of_roofline']:.3f} of roofline")
+        rec_extra["configs"] = {"single_4096": c2, "packed_16": c3}
+        del packed
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_per_step = 1e3 * dt / args.steps
-    tok_s = T / (dt / args.steps)
-    log(f"[bench] prefill: {ms_per_step * 1e3:.1f} us/step, {tok_s / 1e6:.2f} M tokens/s")
-
-    # per-kernel durations from events recorded by the library on its stream
-    kdalib.set_kernel_timing(True)
-    sums = {}
-    nrep = max(20, min(args.steps, 100))
-    for i in range(nrep):
-        step(i)
-        for name, ms in kdalib.prefill_kernel_times():
-            sums[name] = sums.get(name, 0.0) + ms
-    kdalib.set_kernel_timing(False)
-    kern_ms = {k: v / nrep for k, v in sums.items()}
-    log("[bench] kernel averages (ms): " + ", ".join(f"{k}={v * 1e3:.1f}us" for k, v in kern_ms.items()))
-    token_heads = T * H
-    # Algorithmic bytes of each kernel: its share of the path's 1540 B per token-head
-    # (the intra-chunk kernel reads q, k, v, log_alpha, beta; the sequential kernel writes
-    # o and the final state).  The per-chunk records one kernel hands to the other are this
-    # design's own traffic: they show up in `traffic`, not in `achieved`.
-    kern_bytes = {"prefill_intra": INTRA_READ * token_heads,
-                  "prefill_state": H * dk * dv * 4 + 256 * token_heads,
-                  "chunk_table": 0}
-    record_bytes_per_step = int(RECORD_PER_TOKEN_HEAD * token_heads)
-    dom = max((k for k in kern_ms if kern_bytes.get(k)), key=lambda k: kern_ms[k])
-    achieved = kern_bytes[dom] / (kern_ms[dom] * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_for(dom), "kernel": dom,
-                "algorithmic_bytes_per_launch": kern_bytes[dom],
-                "record_bytes_per_launch": record_bytes_per_step,
-                "avg_launch_us": round(kern_ms[dom] * 1e3, 2)}
-    path_bytes = PATH_BYTES_PER_TOKEN_HEAD * token_heads
-    path_roof_tok_s = HBM_PEAK_GBS * 1e9 / (PATH_BYTES_PER_TOKEN_HEAD * H)
-    path = {"bound": "hbm", "algorithmic_bytes_per_step": path_bytes,
-            "achieved_GBs": round(path_bytes / (dt / args.steps) / 1e9, 1),
-            "roofline_tokens_per_s": round(path_roof_tok_s),
-            "frac_of_roofline": round(tok_s / path_roof_tok_s, 4),
-            "mfma_tflops_dense_count": round(FLOP_PER_TOKEN_HEAD_DENSE * token_heads /
-                                             (dt / args.steps) / 1e12, 1),
-            "mfma_frac_of_bf16_peak": round(FLOP_PER_TOKEN_HEAD_DENSE * token_heads /
-                                            (dt / args.steps) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-            "kernel_us": {k: round(v * 1e3, 2) for k, v in kern_ms.items()}}
-
-    # ---------------- decode workload (config 5) ----------------
+    # ---------------- decode workload ----------------
     decode = None
     if not args.no_decode:
         c = gen.DECODE_CONFIG
@@ -216,13 +310,17 @@ def main():
                   "us_per_step": round(us, 2), "value": round(gbs, 1), "unit": "GB/s",
                   "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                   "algorithmic_bytes_per_step": DECODE_BYTES_PER_UNIT * N * Hd}
+        if "ceilings" in rec_extra:
+            decode["frac_of_copy_ceiling"] = round(gbs / rec_extra["ceilings"]["hbm_copy_GBs"], 4)
         log(f"[bench] decode: {us:.1f} us/step, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak)")
         del state
 
-    # ---------------- optional paths ----------------
+    # ---------------- optional paths (on the 4096-token workload) ----------------
     options = None
-    if not args.no_options:
+    if not args.no_options and not args.no_extra:
         options = {}
+        x = single.x
+        T, H, dk, dv = x.T, x.H, x.dk, x.dv
         ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
         def timed(fn, reps):
@@ -237,90 +335,63 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) * 1e3 / reps
 
-        reps = max(20, min(args.steps, 100))
-        base_us = timed(step, reps)
-        # chunk-state export: fp32 state entering each of the 64 chunks, per head
+        reps = 50
+        base_us = timed(single.step, reps)
         nc = kdalib.num_chunk_states(T, 1)
         cs = torch.empty((nc, H, dk, dv), dtype=torch.float32, device=dev)
-
-        def step_cs(i):
-            s = sets[i % args.sets]
-            kdalib.prefill(s["q"], s["k"], s["v"], s["la"], s["beta"], None, None, num_seqs=1,
-                           final_state=fin, out=out[i % args.sets], workspace=ws, chunk_states=cs)
-        cs_us = timed(step_cs, reps)
-        cs_bytes = nc * H * dk * dv * 4
+        cs_us = timed(lambda i: single.step(i, chunk_states=cs), reps)
         options["chunk_states"] = {
-            "workload": "the prefill workload, also writing the fp32 state entering each of "
+            "workload": "the 4096-token prefill, also writing the fp32 state entering each of "
                         "its 64 chunks", "us_per_step": round(cs_us, 2),
-            "extra_us": round(cs_us - base_us, 2), "extra_bytes": cs_bytes,
+            "extra_us": round(cs_us - base_us, 2), "extra_bytes": nc * H * dk * dv * 4,
             "tokens_per_s": round(T / (cs_us * 1e-6), 1)}
-        # in-kernel q/k normalisation and beta sigmoid on raw inputs
         r = gen.make_prefill(2, [T], H=H, dk=dk, dv=dv, dtype="bf16", raw=True)
-        raw = dict(q=dq(r.q), k=dq(r.k), v=dq(r.v), la=torch.from_numpy(r.log_alpha).to(dev),
-                   beta=torch.from_numpy(r.beta).to(dev))
-
-        def step_pre(i):
-            kdalib.prefill(raw["q"], raw["k"], raw["v"], raw["la"], raw["beta"], None, None,
-                           num_seqs=1, final_state=fin, out=out[0], workspace=ws,
-                           l2norm_qk=True, beta_sigmoid=True)
-
-        def step_plain_same_buffers(i):
-            kdalib.prefill(raw["q"], raw["k"], raw["v"], raw["la"], raw["beta"], None, None,
-                           num_seqs=1, final_state=fin, out=out[0], workspace=ws)
-        # alternating runs, best of two each: the clock drifts over a long run
+        raw = Prefill(r, dev)
         pre_runs, plain_runs = [], []
-        for _ in range(2):
-            pre_runs.append(timed(step_pre, reps))
-            plain_runs.append(timed(step_plain_same_buffers, reps))
-        pre_us, plain_us = min(pre_runs), min(plain_runs)
+        for _ in range(2):   # alternating runs, best of two each: the clock drifts
+            pre_runs.append(timed(lambda i: raw.step(i, l2norm_qk=True, beta_sigmoid=True), reps))
+            plain_runs.append(timed(raw.step, reps))
         options["preprocessing"] = {
-            "workload": "the prefill workload from raw q/k and beta logits, L2 normalisation "
+            "workload": "the 4096-token prefill from raw q/k and beta logits, L2 normalisation "
                         "and sigmoid in the kernels (one input set, cache-warm; best of two "
                         "alternating runs with and without)",
-            "us_per_step": round(pre_us, 2), "us_per_step_without": round(plain_us, 2)}
-        # pooled recurrent tokens: 256 sequences x 8 tokens (speculative verification)
-        Nr, Tr, Hr = 256, 8, H
-        rr = gen.make_prefill(9, [Tr] * Nr, H=Hr, dk=dk, dv=dv, dtype="bf16")
-        pool = torch.from_numpy(gen.decode_state(9, Nr, Hr, dk, dv)).to(dev)
+            "us_per_step": round(min(pre_runs), 2), "us_per_step_without": round(min(plain_runs), 2)}
+        del raw
+        Nr, Tr = 256, 8
+        rr = gen.make_prefill(9, [Tr] * Nr, H=H, dk=dk, dv=dv, dtype="bf16")
+        pool = torch.from_numpy(gen.decode_state(9, Nr, H, dk, dv)).to(dev)
         slots = torch.from_numpy(np.random.default_rng(9).permutation(Nr).astype(np.int32)).to(dev)
         rin = dict(q=dq(rr.q), k=dq(rr.k), v=dq(rr.v), la=torch.from_numpy(rr.log_alpha).to(dev),
                    beta=torch.from_numpy(rr.beta).to(dev))
-        o_r = torch.empty((Nr * Tr, Hr, dv), dtype=torch.bfloat16, device=dev)
-
-        def step_rec(i):
-            kdalib.decode_tokens(pool, rin["q"], rin["k"], rin["v"], rin["la"], rin["beta"],
-                                 state_indices=slots, num_seqs=Nr, out=o_r)
-        rec_us = timed(step_rec, reps)
-        rec_bytes = Nr * Hr * (2 * dk * dv * 4 + Tr * PATH_BYTES_PER_TOKEN_HEAD)
+        o_r = torch.empty((Nr * Tr, H, dv), dtype=torch.bfloat16, device=dev)
+        rec_us = timed(lambda i: kdalib.decode_tokens(pool, rin["q"], rin["k"], rin["v"], rin["la"],
+                                                      rin["beta"], state_indices=slots,
+                                                      num_seqs=Nr, out=o_r), reps)
+        rec_bytes = Nr * H * (2 * dk * dv * 4 + Tr * PATH_BYTES_PER_TOKEN_HEAD)
         rec_gbs = rec_bytes / (rec_us * 1e-6) / 1e9
         options["decode_tokens"] = {
             "workload": "pooled recurrent tokens: 256 seqs x 8 tokens, H=32, dk=dv=128, bf16, "
                         "fp32 states in permuted slots", "us_per_call": round(rec_us, 2),
             "algorithmic_bytes": rec_bytes, "achieved_GBs": round(rec_gbs, 1),
             "frac_of_hbm_peak": round(rec_gbs / HBM_PEAK_GBS, 4)}
-        # backward of the prefill workload from the exported chunk states
         g = np.random.default_rng(11)
         d_o = dq(gen.bf16_bits(g.standard_normal((T, H, dv)).astype(np.float32)))
-        s0set = sets[0]
+        s0 = single.sets[0]
         bws = torch.empty(kdalib.backward_workspace_bytes(T, 1, H, dk, dv, True), dtype=torch.uint8,
                           device=dev)
-        kdalib.prefill(s0set["q"], s0set["k"], s0set["v"], s0set["la"], s0set["beta"], None, None,
-                       num_seqs=1, final_state=fin, out=out[0], workspace=ws, chunk_states=cs)
-
-        def step_bwd(i):
-            kdalib.backward(s0set["q"], s0set["k"], s0set["v"], s0set["la"], s0set["beta"], d_o,
-                            chunk_states=cs, need_initial_state_grad=False, workspace=bws)
-        bwd_us = timed(step_bwd, max(3, reps // 10))
-        bwd_bytes = (PATH_BYTES_PER_TOKEN_HEAD + 768 + 512 + 4) * token_heads
+        single.step(0, chunk_states=cs)
+        bwd_us = timed(lambda i: kdalib.backward(s0["q"], s0["k"], s0["v"], s0["la"], s0["beta"],
+                                                 d_o, chunk_states=cs,
+                                                 need_initial_state_grad=False, workspace=bws), 5)
+        bwd_bytes = (PATH_BYTES_PER_TOKEN_HEAD + 768 + 512 + 4) * T * H
         options["backward"] = {
-            "workload": "gradients of the prefill workload (T=4096, H=32, d=128, bf16) from its "
+            "workload": "gradients of the 4096-token prefill (H=32, d=128, bf16) from its "
                         "exported chunk states", "us_per_call": round(bwd_us, 1),
-            "tokens_per_s": round(T / (bwd_us * 1e-6), 1),
-            "algorithmic_bytes": bwd_bytes,
+            "tokens_per_s": round(T / (bwd_us * 1e-6), 1), "algorithmic_bytes": bwd_bytes,
             "achieved_GBs": round(bwd_bytes / (bwd_us * 1e-6) / 1e9, 1)}
-        log(f"[bench] options: chunk states {cs_us:.1f} us (+{cs_us - base_us:.1f}), "
-            f"preprocessing {pre_us:.1f} us (plain {plain_us:.1f}), "
-            f"decode_tokens 256x8 {rec_us:.1f} us = {rec_gbs:.0f} GB/s, backward {bwd_us:.0f} us")
+        log(f"[bench] options: chunk states +{cs_us - base_us:.1f} us, preprocessing "
+            f"{min(pre_runs):.1f} us (plain {min(plain_runs):.1f}), decode_tokens {rec_us:.1f} us "
+            f"= {rec_gbs:.0f} GB/s, backward {bwd_us:.0f} us")
         del pool, cs, bws
 
     if args.copy_calib:
@@ -330,36 +401,81 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log("[bench] ran 3 plain copies of 1 GiB (counter calibration)")
+        del a, b
 
-    # ---------------- CPU baseline: the oracle on the same inputs ----------------
+    # ---------------- headline: the long-context prefill ----------------
+    if args.headline == "long":
+        log("[bench] headline workload: B=1 T=65536 H=32 d=128 bf16 (generating inputs)")
+        head = Prefill(gen.config_prefill(4), dev)
+        workload = ("long-context KDA prefill B=1 T=65536 H=32 dk=dv=128, bf16 q/k/v, fp32 "
+                    "log_alpha (logsigmoid(N(4,1)))/beta/state, chunk 64, zero initial state")
+        wl_key = "long_65536"
+    else:
+        head = single
+        workload = ("single-sequence KDA prefill B=1 T=4096 H=32 dk=dv=128, bf16 q/k/v, fp32 "
+                    "log_alpha/beta/state, chunk 64, zero initial state")
+        wl_key = "single_4096"
+    T, H = head.x.T, head.x.H
+    for i in range(args.warmup):
+        head.step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        head.step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = 1e3 * dt / args.steps
+    tok_s = T / (dt / args.steps)
+    log(f"[bench] headline: {ms_per_step * 1e3:.1f} us/step, {tok_s / 1e6:.2f} M tokens/s "
+        f"({args.steps} timed steps after {args.warmup} warm-up steps)")
+    kern = head.kernel_us(max(5, min(args.steps, 20)))
+    log("[bench] kernel averages: " + ", ".join(f"{k}={v:.1f}us" for k, v in kern.items()))
+    kern_total = sum(kern.values())
+    achieved = head.path_bytes / (kern_total * 1e-6) / 1e9
+    traffic = [traffic_for(k, wl_key) for k in kern if k != "chunk_table"]
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if any(t is None for t in traffic) else int(sum(traffic)),
+                "kernel": "+".join(k for k in kern),
+                "algorithmic_bytes_per_launch": head.path_bytes,
+                "avg_launch_us": round(kern_total, 2),
+                "kernels_us": {k: round(v, 2) for k, v in kern.items()},
+                "note": "the prefill's kernels together, one launch of each per step; "
+                        "algorithmic bytes = 1540 per token-head plus the final state"}
+    if "ceilings" in rec_extra:
+        roofline["frac_of_copy_ceiling"] = round(achieved / rec_extra["ceilings"]["hbm_copy_GBs"], 4)
+    path = head.summary(dt / args.steps * 1e6)
+    path["mfma_frac_of_bf16_peak"] = round(path["mfma_tflops_dense_count"] / BF16_MFMA_PEAK_TFLOPS, 4)
+
+    # ---------------- CPU baseline: the oracle on the headline's inputs ----------------
     cpu = None
     if not args.no_cpu:
         import oracle
+        x = head.x
         threads = oracle.default_threads()
-        used = min(oracle.max_threads(threads), H)
+        used = min(oracle.max_threads(threads), H * x.num_seqs)
         reps, ct = 0, 0.0
         while ct < CPU_MIN_SECONDS and reps < 200:
-            t0 = time.perf_counter()
-            oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, None, None, num_seqs=1,
-                           nthreads=threads)
-            ct += time.perf_counter() - t0
+            t1 = time.perf_counter()
+            oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.initial_state, x.cu_seqlens,
+                           num_seqs=x.num_seqs, nthreads=threads)
+            ct += time.perf_counter() - t1
             reps += 1
         cpu = {"value": round(reps * T / ct, 1), "unit": "tokens/s", "cores": used,
-               "kind": "oracle",
-               "sample": f"the single-sequence workload (T={T}, H={H}, dk=dv=128) in fp64, "
-                         f"run {reps} times back to back: {ct:.1f} s wall on {used} threads"}
+               "kind": "oracle", "cpu_model": cpu_model(),
+               "host_threads_available": len(os.sched_getaffinity(0)),
+               "sample": f"the headline workload itself (T={T}, H={H}, dk=dv=128), fp64 token "
+                         f"loop, run {reps} times back to back: {ct:.1f} s wall on {used} threads"}
         log(f"[bench] oracle: {reps} runs in {ct:.1f} s, {reps * T / ct:.0f} tokens/s "
-            f"on {used} threads")
+            f"on {used} threads ({cpu['cpu_model']})")
 
     rec = {"metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic",
-           "config": {"workload": "single-sequence KDA prefill B=1 T=4096 H=32 dk=dv=128, "
-                                  "bf16 q/k/v, fp32 log_alpha/beta/state, chunk 64",
-                      "global_batch": 1, "seq_len": T, "heads": H, "head_dim": dk,
-                      "parallelism": "single GPU"},
-           "roofline": roofline, "path": path, "decode": decode, "options": options,
+           "config": {"workload": workload, "global_batch": head.x.num_seqs, "seq_len": T,
+                      "heads": H, "head_dim": 128, "parallelism": "single GPU"},
+           "roofline": roofline, "path": path, **rec_extra, "decode": decode, "options": options,
            "cpu_baseline": cpu}
     print(json.dumps(rec), flush=True)
 

@@ -5,11 +5,12 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
-#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/kda.h"
 #include "kda_launch.h"
+#include "kda_internal.h"
 
 
 namespace {
@@ -88,38 +89,38 @@ unsigned pre_flags(uint32_t flags) {
 }
 
 // -- optional kernel timing ---------------------------------------------------
+// Per calling thread, like the error text: each thread that enables timing
+// gets its own events (created on first use, kept until the process ends),
+// and kda_prefill_kernel_times() reports the last call timed on that thread.
 constexpr int kMaxTimed = 8;
-std::mutex g_timing_mu;
-bool g_timing = false;
-hipEvent_t g_ev[kMaxTimed + 1] = {};
-const char* g_names[kMaxTimed] = {};
-int g_n_timed = -1;
+struct TimingState {
+    bool on = false;
+    hipEvent_t ev[kMaxTimed + 1] = {};
+    const char* names[kMaxTimed] = {};
+    int n_timed = -1;
+};
+thread_local TimingState t_timing;
 
 struct Timer {
     bool on;
     int n = 0;
     hipStream_t stream;
-    explicit Timer(hipStream_t s) : on(false), stream(s) {
-        std::lock_guard<std::mutex> lk(g_timing_mu);
-        on = g_timing;
+    explicit Timer(hipStream_t s) : on(t_timing.on), stream(s) {
         if (on) {
             for (int i = 0; i <= kMaxTimed; ++i)
-                if (!g_ev[i] && hipEventCreate(&g_ev[i]) != hipSuccess) on = false;
-            g_n_timed = -1;
+                if (!t_timing.ev[i] && hipEventCreate(&t_timing.ev[i]) != hipSuccess) on = false;
+            t_timing.n_timed = -1;
         }
-        if (on) hipEventRecord(g_ev[0], stream);
+        if (on) hipEventRecord(t_timing.ev[0], stream);
     }
     void mark(const char* name) {
         if (!on || n >= kMaxTimed) return;
-        g_names[n] = name;
-        hipEventRecord(g_ev[n + 1], stream);
+        t_timing.names[n] = name;
+        hipEventRecord(t_timing.ev[n + 1], stream);
         ++n;
     }
     ~Timer() {
-        if (on) {
-            std::lock_guard<std::mutex> lk(g_timing_mu);
-            g_n_timed = n;
-        }
+        if (on) t_timing.n_timed = n;
     }
 };
 
@@ -129,6 +130,26 @@ bool debug_sync() {
         return e && e[0] && e[0] != '0';
     }();
     return on;
+}
+
+// KDA_DEBUG_SYNC: copy the device offsets to the host and check what the
+// kernels take as a precondition (0 = c_0 <= c_1 <= ... <= c_N = T).
+kda_status debug_check_cu_seqlens(const int32_t* cu, int32_t N, int64_t T, hipStream_t stream) {
+    if (!cu || !debug_sync()) return KDA_OK;
+    std::vector<int32_t> h((size_t)N + 1);
+    hipError_t e = hipMemcpyAsync(h.data(), cu, ((size_t)N + 1) * sizeof(int32_t),
+                                  hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+        return fail(KDA_ERR_HIP, std::string("KDA_DEBUG_SYNC copy of cu_seqlens: ") + hipGetErrorString(e));
+    if (h[0] != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[0] must be 0");
+    for (int32_t i = 0; i < N; ++i)
+        if (h[i + 1] < h[i])
+            return fail(KDA_ERR_INVALID_ARGUMENT,
+                        "cu_seqlens must be non-decreasing (entry " + std::to_string(i + 1) + ")");
+    if ((int64_t)h[N] != T)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[N] must equal total_tokens");
+    return KDA_OK;
 }
 
 kda_status check_launch(hipError_t e, const char* what, hipStream_t stream) {
@@ -166,6 +187,23 @@ kda_status kda_prefill_ex(const void* q, const void* k, const void* v, const flo
                           int32_t H, int32_t dk, int32_t dv, kda_dtype dtype, uint32_t flags,
                           void* o, float* final_state, float* chunk_states, void* workspace,
                           size_t workspace_bytes, void* stream_ptr) {
+    return kda::prefill_impl(q, k, v, log_alpha, beta, initial_state, cu_seqlens, total_tokens,
+                             num_seqs, H, dk, dv, dtype, flags, o, final_state, chunk_states,
+                             workspace, workspace_bytes, true, stream_ptr);
+}
+
+}  // extern "C"
+
+namespace kda {
+
+void set_last_error(const std::string& msg) { g_last_error = msg; }
+
+kda_status prefill_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                        int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk, int32_t dv,
+                        kda_dtype dtype, uint32_t flags, void* o, float* final_state,
+                        float* chunk_states, void* workspace, size_t workspace_bytes,
+                        bool may_allocate, void* stream_ptr) {
     try {
         if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
             return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_DTYPE_F32 or KDA_DTYPE_BF16");
@@ -188,6 +226,8 @@ kda_status kda_prefill_ex(const void* q, const void* k, const void* v, const flo
                 return fail(KDA_ERR_INVALID_ARGUMENT, "every pointer must be 16-byte aligned");
         if (!workspace && workspace_bytes != 0)
             return fail(KDA_ERR_INVALID_ARGUMENT, "workspace_bytes given without a workspace");
+        if (!workspace && !may_allocate)
+            return fail(KDA_ERR_WORKSPACE, "no workspace and no allocation allowed");
         Plan plan;
         if (!make_plan(total_tokens, num_seqs, H, dk, dv, dtype, plan))
             return fail(KDA_ERR_INVALID_ARGUMENT, "invalid sizes");
@@ -201,6 +241,8 @@ kda_status kda_prefill_ex(const void* q, const void* k, const void* v, const flo
             return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs * H too large");
 
         hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+        if (kda_status dc = debug_check_cu_seqlens(cu_seqlens, num_seqs, total_tokens, stream))
+            return dc;
         const bool bf16 = dtype == KDA_DTYPE_BF16;
         unsigned char* ws = static_cast<unsigned char*>(workspace);
         bool owned = false;
@@ -250,6 +292,10 @@ kda_status kda_prefill_ex(const void* q, const void* k, const void* v, const flo
         return fail(KDA_ERR_HIP, "unexpected C++ exception inside kda_prefill");
     }
 }
+
+}  // namespace kda
+
+extern "C" {
 
 size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H,
                                     int32_t dk, int32_t dv, kda_dtype dtype) {
@@ -301,6 +347,8 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const float
                                                " bytes");
 
         hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+        if (kda_status dc = debug_check_cu_seqlens(cu_seqlens, num_seqs, total_tokens, stream))
+            return dc;
         const bool bf16 = dtype == KDA_DTYPE_BF16;
         unsigned char* ws = static_cast<unsigned char*>(workspace);
         bool owned = false;
@@ -386,6 +434,8 @@ kda_status kda_decode_tokens(float* state_pool, int32_t num_slots, const int32_t
             if (p && !aligned16(p))
                 return fail(KDA_ERR_INVALID_ARGUMENT, "every pointer must be 16-byte aligned");
         hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+        if (kda_status dc = debug_check_cu_seqlens(cu_seqlens, num_seqs, total_tokens, stream))
+            return dc;
         const int rows = cu_seqlens ? -1 : (int)(total_tokens / num_seqs);
         return check_launch(kda::launch_recurrent(state_pool, num_slots, state_indices, q, k, v,
                                                   log_alpha, beta, cu_seqlens, rows, num_seqs, H,
@@ -441,22 +491,21 @@ const char* kda_last_error_message(void) { return g_last_error.c_str(); }
 int32_t kda_version(void) { return 100; }
 
 kda_status kda_set_kernel_timing(int32_t enabled) {
-    std::lock_guard<std::mutex> lk(g_timing_mu);
-    g_timing = enabled != 0;
+    t_timing.on = enabled != 0;
     return KDA_OK;
 }
 
 int32_t kda_prefill_kernel_times(float* ms, const char** names, int32_t max_kernels) {
-    std::lock_guard<std::mutex> lk(g_timing_mu);
-    if (g_n_timed < 0) return -1;
-    if (hipEventSynchronize(g_ev[g_n_timed]) != hipSuccess) return -1;
-    for (int i = 0; i < g_n_timed && i < max_kernels; ++i) {
+    const TimingState& ts = t_timing;
+    if (ts.n_timed < 0) return -1;
+    if (hipEventSynchronize(ts.ev[ts.n_timed]) != hipSuccess) return -1;
+    for (int i = 0; i < ts.n_timed && i < max_kernels; ++i) {
         float t = 0.f;
-        if (hipEventElapsedTime(&t, g_ev[i], g_ev[i + 1]) != hipSuccess) return -1;
+        if (hipEventElapsedTime(&t, ts.ev[i], ts.ev[i + 1]) != hipSuccess) return -1;
         if (ms) ms[i] = t;
-        if (names) names[i] = g_names[i];
+        if (names) names[i] = ts.names[i];
     }
-    return g_n_timed;
+    return ts.n_timed;
 }
 
 }  // extern "C"

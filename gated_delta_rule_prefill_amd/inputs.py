@@ -146,8 +146,12 @@ def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def make_prefill(seed: int, lengths: Sequence[int], H: int, dk: int, dv: int,
                  dtype: str = "bf16", mu: float = 3.0, state_std: float = 0.0,
-                 packed: Optional[bool] = None, raw: bool = False) -> KDAInputs:
+                 packed: Optional[bool] = None, raw: bool = False,
+                 fixed_even_log_alpha: Optional[float] = None) -> KDAInputs:
     """Inputs for one prefill call over sequences of the given lengths.
+
+    ``fixed_even_log_alpha`` sets log_alpha of every even key channel to that
+    value (strong, mixed per-channel decay next to the drawn odd channels).
 
     ``packed`` (default: more than one distinct length) selects cu_seqlens;
     otherwise the batch is N equal rows and cu_seqlens is None.  ``raw`` draws
@@ -172,6 +176,8 @@ def make_prefill(seed: int, lengths: Sequence[int], H: int, dk: int, dv: int,
         beta = _sigmoid(_normal(rng(seed, BETA), (T, H)))
     v = _normal(rng(seed, V), (T, H, dv))
     la = _log_sigmoid(_normal(rng(seed, LOG_ALPHA), (T, H, dk), loc=mu))
+    if fixed_even_log_alpha is not None:
+        la[:, :, 0::2] = np.float32(fixed_even_log_alpha)
     s0 = None
     if state_std:
         s0 = (np.float32(state_std) * _normal(rng(seed, STATE), (N, H, dk, dv))).astype(np.float32)

@@ -33,7 +33,16 @@
  *   Errors     a call returns a status and never aborts, prints or throws.
  *              Host-checkable argument errors are reported before any HIP
  *              call is made; kda_last_error_message() gives detail (per
- *              thread).
+ *              thread).  The contents of device-resident cu_seqlens are a
+ *              precondition and are not read on the host, except with the
+ *              environment variable KDA_DEBUG_SYNC=1: then every call copies
+ *              them, returns KDA_ERR_INVALID_ARGUMENT unless
+ *              0 = c_0 <= c_1 <= ... <= c_N = T, and synchronises the stream
+ *              after each kernel so that execution faults surface as
+ *              KDA_ERR_HIP from the call that caused them.
+ *   Threads    calls are reentrant and may come from several threads.  The
+ *              library keeps no mutable state shared between threads: the
+ *              error text and the optional kernel timing are per thread.
  *   Values     log_alpha must be finite and <= 0 (alpha in (0, 1]).  Within
  *              every aligned 16-token block of a 64-token chunk the summed
  *              log_alpha of one channel must stay above -80; inside that range
@@ -230,13 +239,15 @@ const char *kda_last_error_message(void);
 int32_t kda_version(void);
 
 /*
- * Kernel timing for measurement (not needed for normal use).  While enabled,
- * kda_prefill records a HIP event before and after each of its kernels on its
- * stream.  kda_prefill_kernel_times() waits for the last recorded call's
- * events and writes, for up to max_kernels kernels in launch order, the
- * elapsed milliseconds (ms) and a static kernel name (names, may be NULL).
- * It returns the number of kernels of that call, or -1 when nothing was
- * recorded or a HIP call failed.
+ * Kernel timing for measurement (not needed for normal use), per calling
+ * thread.  While enabled on a thread, kda_prefill called from that thread
+ * records a HIP event before and after each of its kernels on its stream
+ * (the events are created on first use and kept until the process ends).
+ * kda_prefill_kernel_times() waits for the events of the last call timed on
+ * the calling thread and writes, for up to max_kernels kernels in launch
+ * order, the elapsed milliseconds (ms) and a static kernel name (names, may
+ * be NULL).  It returns the number of kernels of that call, or -1 when
+ * nothing was recorded on this thread or a HIP call failed.
  */
 kda_status kda_set_kernel_timing(int32_t enabled);
 int32_t kda_prefill_kernel_times(float *ms, const char **names, int32_t max_kernels);
