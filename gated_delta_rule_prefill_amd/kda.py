@@ -28,6 +28,8 @@ SIGNATURES = {
     "kda_prefill_ex": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
                                       _i32, _i32, ctypes.c_int, ctypes.c_uint32, _vp, _vp, _vp,
                                       _vp, _sz, _vp]),
+    "kda_prefill_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
+                                           _i32, _i32, ctypes.c_int, _vp, _vp, _vp]),
     "kda_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                        ctypes.c_int, _vp, _vp]),
     "kda_decode_tokens": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,

@@ -121,6 +121,33 @@ kda_status kda_prefill(const void *q, const void *k, const void *v,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_prefill without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  The call allocates nothing (no hipMalloc,
+ * no stream-ordered allocation, no allocating library routine).  Its
+ * workspace is a fixed array of KDA_NOALLOC_SCRATCH_BYTES in the library's
+ * device code: every GPU the library is loaded on holds one copy of it from
+ * module load until the process ends.
+ *   Limit    sizes for which kda_prefill_workspace_bytes() exceeds
+ *            KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_WORKSPACE before any
+ *            HIP call (at H = 32, dk = dv = 128, bf16 that is beyond 1,280
+ *            tokens of one sequence; smaller H or head sizes allow more).
+ *   Sharing  every call on one GPU uses that GPU's one array and leaves its
+ *            contents behind; nothing in it needs to start at zero.  Calls
+ *            that overlap on one GPU (concurrent streams, or threads without
+ *            an order between them) race on the array: the caller must order
+ *            them, e.g. by issuing them on one stream.
+ * Arguments, results and errors otherwise as for kda_prefill.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_prefill_noalloc(const void *q, const void *k, const void *v,
+                               const float *log_alpha, const float *beta,
+                               const float *initial_state, const int32_t *cu_seqlens,
+                               int64_t total_tokens, int32_t num_seqs, int32_t H,
+                               int32_t dk, int32_t dv, kda_dtype dtype,
+                               void *o, float *final_state, void *stream);
+
+/*
  * kda_prefill with options.  The extra arguments:
  *   flags         KDA_FLAG_* bits (0 = kda_prefill)
  *   chunk_states  fp32 [NC,H,dk,dv] (device, written), or NULL: the state

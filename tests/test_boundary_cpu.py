@@ -199,3 +199,16 @@ def test_backward_workspace_bytes():
     w = kda.backward_workspace_bytes(4096, 1, 32, 128, 128, True)
     assert w >= kda.workspace_bytes(4096, 1, 32, 128, 128, True) and w % 256 == 0
     assert kda.backward_workspace_bytes(10, 0, 1, 64, 64, False) == 0
+
+
+def test_noalloc_rejects_sizes_beyond_its_array_before_any_hip_call():
+    lib = kda.lib()
+    scratch = 64 << 20
+    assert lib.kda_prefill_workspace_bytes(1280, 1, 32, 128, 128, kda.KDA_DTYPE_BF16) <= scratch
+    assert lib.kda_prefill_workspace_bytes(1344, 1, 32, 128, 128, kda.KDA_DTYPE_BF16) > scratch
+    st = lib.kda_prefill_noalloc(A, A, A, A, A, None, None, 1344, 1, 32, 128, 128,
+                                 kda.KDA_DTYPE_BF16, A, None, None)
+    assert st == kda.KDA_ERR_WORKSPACE and "fixed scratch" in kda.last_error()
+    st = lib.kda_prefill_noalloc(A, A, A, A, A, None, None, 128, 0, 2, 64, 64,
+                                 kda.KDA_DTYPE_BF16, A, None, None)
+    assert st == kda.KDA_ERR_INVALID_ARGUMENT
