@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const size_t atv = ((size_t)(ci.start + min(iv, L - 1)) * H + h) * DV + slice * BWD_COLS + jv;
             const V4 lv = load_vec<V4>(v + atv), ld = load_vec<V4>(d_o + atv);
             const float lb = tid < CHUNK ? beta[(size_t)(ci.start + min(tid, L - 1)) * H + h] : 0.f;
-            const float* cs = chunk_states + ((size_t)(c_begin + c) * H + h) * DK * DV + (size_t)r0 * DV + j0;
+            const float* cs = chunk_states + (chunk_state_row(src, s, c_begin, c) * H + h) * DK * DV + (size_t)r0 * DV + j0;
 #pragma unroll
             for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll

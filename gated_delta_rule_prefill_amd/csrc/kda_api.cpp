@@ -4,6 +4,7 @@
 
 #include <cstdint>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -28,25 +29,61 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Workspace layout of one prefill call: one record per (chunk, head) slot,
 // then the chunk table.
+//
+// Long batches of equal rows run in segments: token ranges of every sequence
+// whose records together stay near the size of the 256 MB last-level cache,
+// so that the sequential pass reads records the intra pass has just written
+// instead of fetching them from HBM.  Only one segment's records exist at a
+// time; the fp32 state passes from segment to segment through final_state
+// (or, without it, a carry area at the end of the workspace).
+// The record budget of one segment: 208 MiB, or KDA_SEGMENT_RECORD_BYTES from
+// the environment (read once; for tests and tuning).
+size_t segment_record_bytes() {
+    static const size_t v = [] {
+        const char* e = std::getenv("KDA_SEGMENT_RECORD_BYTES");
+        const long long x = e ? std::atoll(e) : 0;
+        return x > 0 ? (size_t)x : (size_t)208 << 20;
+    }();
+    return v;
+}
+
 struct Plan {
-    int64_t max_chunks = 0;
-    size_t rec_bytes = 0;   // bytes of one (chunk, head) record
-    size_t off_seq = 0;     // seq_chunk_start [N+1]
-    size_t off_chunks = 0;  // ChunkInfo [max_chunks]
+    int64_t max_chunks = 0;  // record slots per head (one segment's chunks)
+    size_t rec_bytes = 0;    // bytes of one (chunk, head) record
+    int seg_tokens = 0;      // equal rows: tokens per segment (== rows: one segment)
+    size_t off_seq = 0;      // seq_chunk_start [N+1]
+    size_t off_chunks = 0;   // ChunkInfo [max_chunks]
+    size_t off_carry = 0;    // fp32 [N,H,dk,dv] state between segments (segmented only)
     size_t total = 0;
 };
 
+// segment: plan equal-row batches in segments (prefill); false keeps every
+// chunk's record (the backward's recomputation reads them all at once).
 bool make_plan(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype,
-               Plan& p) {
+               Plan& p, bool segment = false, bool equal_rows = false) {
     if (T < 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return false;
     const int es = dtype == KDA_DTYPE_BF16 ? 2 : 4;
-    p.max_chunks = (T + kda::CHUNK - 1) / kda::CHUNK + N;
     p.rec_bytes = kda::rec_layout(es, dk, dv).bytes;
+    p.max_chunks = (T + kda::CHUNK - 1) / kda::CHUNK + N;
+    p.seg_tokens = 0;
+    bool carry = false;
+    if (segment && equal_rows && T % N == 0 && T / N > 0) {
+        const int64_t rows = T / N, cps = (rows + kda::CHUNK - 1) / kda::CHUNK;
+        const int64_t per_chunk = (int64_t)N * H * (int64_t)p.rec_bytes;
+        const int64_t max_seg = std::max<int64_t>(1, (int64_t)segment_record_bytes() / per_chunk);
+        const int64_t nseg = (cps + max_seg - 1) / max_seg;
+        const int64_t seg_chunks = (cps + nseg - 1) / nseg;
+        p.seg_tokens = (int)std::min<int64_t>(rows, seg_chunks * kda::CHUNK);
+        p.max_chunks = (int64_t)N * seg_chunks;
+        carry = nseg > 1;
+    }
     size_t at = align256((size_t)p.max_chunks * (size_t)H * p.rec_bytes);
     p.off_seq = at;
     at += align256(((size_t)N + 1) * 4);
     p.off_chunks = at;
     at += align256((size_t)p.max_chunks * sizeof(kda::ChunkInfo));
+    p.off_carry = at;
+    if (carry) at += align256((size_t)N * H * dk * dv * 4);
     p.total = at;
     return true;
 }
@@ -92,7 +129,7 @@ unsigned pre_flags(uint32_t flags) {
 // Per calling thread, like the error text: each thread that enables timing
 // gets its own events (created on first use, kept until the process ends),
 // and kda_prefill_kernel_times() reports the last call timed on that thread.
-constexpr int kMaxTimed = 8;
+constexpr int kMaxTimed = 256;
 struct TimingState {
     bool on = false;
     hipEvent_t ev[kMaxTimed + 1] = {};
@@ -165,10 +202,12 @@ extern "C" {
 
 size_t kda_prefill_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H,
                                    int32_t dk, int32_t dv, kda_dtype dtype) {
-    Plan p;
+    // the larger of the two layouts, so one size serves packed and equal-row calls
+    Plan a, b;
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return 0;
-    if (!make_plan(total_tokens, num_seqs, H, dk, dv, dtype, p)) return 0;
-    return p.total;
+    if (!make_plan(total_tokens, num_seqs, H, dk, dv, dtype, a)) return 0;
+    if (!make_plan(total_tokens, num_seqs, H, dk, dv, dtype, b, true, true)) return 0;
+    return std::max(a.total, b.total);
 }
 
 kda_status kda_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -229,7 +268,7 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
         if (!workspace && !may_allocate)
             return fail(KDA_ERR_WORKSPACE, "no workspace and no allocation allowed");
         Plan plan;
-        if (!make_plan(total_tokens, num_seqs, H, dk, dv, dtype, plan))
+        if (!make_plan(total_tokens, num_seqs, H, dk, dv, dtype, plan, true, !cu_seqlens))
             return fail(KDA_ERR_INVALID_ARGUMENT, "invalid sizes");
         if (plan.max_chunks > 0x7fffffffLL / 2 || plan.max_chunks * H > 0x7fffffffLL)
             return fail(KDA_ERR_INVALID_ARGUMENT, "too many chunks (chunks * H must be < 2^31)");
@@ -258,28 +297,58 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
         kda_status st = KDA_OK;
         {
             Timer timer(stream);
-            // N equal rows need no chunk table: the kernels derive their chunks
-            kda::ChunkSrc src{chunks, seq_start, cu_seqlens ? -1 : (int)(total_tokens / num_seqs),
-                              num_seqs};
             if (cu_seqlens) {
+                kda::ChunkSrc src{chunks, seq_start, -1, num_seqs, 0, 0};
                 st = check_launch(kda::launch_chunk_table(cu_seqlens, total_tokens, num_seqs,
                                                           seq_start, chunks, (int)plan.max_chunks,
                                                           stream),
                                   "chunk table kernel", stream);
                 timer.mark("chunk_table");
-            }
-            if (st == KDA_OK && total_tokens > 0) {
-                st = check_launch(kda::launch_prefill_intra(q, k, v, log_alpha, beta, src,
-                                                            (int)plan.max_chunks, H, dk, dv, bf16,
-                                                            pre_flags(flags), ws, stream),
-                                  "intra-chunk kernel", stream);
-                timer.mark("prefill_intra");
-            }
-            if (st == KDA_OK) {
-                st = check_launch(kda::launch_prefill_state(ws, src, initial_state, final_state, o,
-                                                            chunk_states, H, dk, dv, bf16, stream),
-                                  "state kernel", stream);
-                timer.mark("prefill_state");
+                if (st == KDA_OK && total_tokens > 0) {
+                    st = check_launch(kda::launch_prefill_intra(q, k, v, log_alpha, beta, src,
+                                                                (int)plan.max_chunks, H, dk, dv,
+                                                                bf16, pre_flags(flags), ws, stream),
+                                      "intra-chunk kernel", stream);
+                    timer.mark("prefill_intra");
+                }
+                if (st == KDA_OK) {
+                    st = check_launch(kda::launch_prefill_state(ws, src, initial_state, final_state,
+                                                                o, chunk_states, H, dk, dv, bf16,
+                                                                stream),
+                                      "state kernel", stream);
+                    timer.mark("prefill_state");
+                }
+            } else {
+                // N equal rows need no chunk table: the kernels derive their chunks.
+                // Segments of seg_tokens rows of every sequence, in order; the
+                // state leaving one segment enters the next in fp32.
+                const int rows = (int)(total_tokens / num_seqs);
+                const int seg = plan.seg_tokens > 0 ? plan.seg_tokens : rows;
+                float* carry = final_state ? final_state
+                                           : reinterpret_cast<float*>(ws + plan.off_carry);
+                int off = 0;
+                do {
+                    const int len = std::min(seg, rows - off);
+                    const bool first = off == 0, last = off + len >= rows;
+                    kda::ChunkSrc src{chunks, seq_start, len, num_seqs, rows, off};
+                    if (len > 0) {
+                        st = check_launch(kda::launch_prefill_intra(q, k, v, log_alpha, beta, src,
+                                                                    (int)plan.max_chunks, H, dk,
+                                                                    dv, bf16, pre_flags(flags), ws,
+                                                                    stream),
+                                          "intra-chunk kernel", stream);
+                        timer.mark("prefill_intra");
+                    }
+                    if (st == KDA_OK) {
+                        st = check_launch(
+                            kda::launch_prefill_state(ws, src, first ? initial_state : carry,
+                                                      last ? final_state : carry, o, chunk_states,
+                                                      H, dk, dv, bf16, stream),
+                            "state kernel", stream);
+                        timer.mark("prefill_state");
+                    }
+                    off += len;
+                } while (st == KDA_OK && off < rows);
             }
         }
         if (owned) {
@@ -360,8 +429,8 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const float
         }
         int32_t* seq_start = reinterpret_cast<int32_t*>(ws + plan.off_seq);
         kda::ChunkInfo* chunks = reinterpret_cast<kda::ChunkInfo*>(ws + plan.off_chunks);
-        kda::ChunkSrc src{chunks, seq_start, cu_seqlens ? -1 : (int)(total_tokens / num_seqs),
-                          num_seqs};
+        const int rows = cu_seqlens ? -1 : (int)(total_tokens / num_seqs);
+        kda::ChunkSrc src{chunks, seq_start, rows, num_seqs, rows, 0};
         kda_status st = KDA_OK;
         if (cu_seqlens)
             st = check_launch(kda::launch_chunk_table(cu_seqlens, total_tokens, num_seqs, seq_start,

@@ -274,7 +274,7 @@ __device__ __forceinline__ void chunk_of(const ChunkSrc& src, int cid, int& n_ch
         n_chunks = src.N * cps;
         const int sq = cps > 0 ? cid / cps : 0, k = cps > 0 ? cid - sq * cps : 0;
         ci.seq = sq;
-        ci.start = sq * src.rows + CHUNK * k;
+        ci.start = sq * src.stride + src.offset + CHUNK * k;
         ci.len = min(CHUNK, src.rows - CHUNK * k);
         ci.pad = 0;
     } else {
@@ -290,7 +290,7 @@ __device__ __forceinline__ ChunkInfo chunk_desc(const ChunkSrc& src, int cid) {
     const int sq = cid / cps, k = cid - sq * cps;
     ChunkInfo ci;
     ci.seq = sq;
-    ci.start = sq * src.rows + CHUNK * k;
+    ci.start = sq * src.stride + src.offset + CHUNK * k;
     ci.len = min(CHUNK, src.rows - CHUNK * k);
     ci.pad = 0;
     return ci;
@@ -315,6 +315,13 @@ __device__ __forceinline__ void chunk_head_of_block(int H, bool descending, int&
         h = L % H;
     }
     cid = descending ? n - 1 - q : q;
+}
+
+// Row of a chunk-state output for chunk `it` of sequence s in this launch
+// (c_begin from seq_chunks): rows count the chunks of whole sequences.
+__device__ __forceinline__ size_t chunk_state_row(const ChunkSrc& src, int s, int c_begin, int it) {
+    if (src.rows < 0) return (size_t)c_begin + it;
+    return (size_t)s * chunks_per_row(src.stride) + src.offset / CHUNK + it;
 }
 
 // First chunk and chunk count of sequence s.

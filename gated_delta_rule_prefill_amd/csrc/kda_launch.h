@@ -20,11 +20,18 @@ struct ChunkInfo {
 // Where the kernels find the chunks of a batch: the chunk table (packed
 // batches, rows < 0), or N equal sequences of `rows` tokens each, whose chunks
 // follow arithmetically (no table, no extra kernel).
+//
+// In rows mode a launch may cover one token range [offset, offset + rows) of
+// every sequence (the prefill processes long equal-row batches in such
+// segments): sequence s's rows start at s * stride, and its chunk c in the
+// launch is its chunk offset / CHUNK + c overall.
 struct ChunkSrc {
     const ChunkInfo* chunks;          // [max_chunks], table mode
     const int32_t* seq_chunk_start;   // [N + 1], table mode
-    int rows;                         // >= 0: tokens per sequence; < 0: table mode
+    int rows;                         // >= 0: tokens per sequence in this launch; < 0: table mode
     int N;
+    int stride;                       // rows mode: tokens from one sequence to the next
+    int offset;                       // rows mode: first token of the launch in each sequence
 };
 
 // Per-(chunk, head) record of the chunk intermediates in the workspace

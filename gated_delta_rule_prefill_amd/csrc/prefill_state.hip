@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             // the next chunk's loads are unconditional (the last chunk reloads itself)
             load_serial<E, DK, DV>(nxt, record(min(it + 1, n - 1)), g, ln, j0);
             if (chunk_states) {   // the chunk-start state, fp32 [chunk][H][DK][DV]
-                float* cs = chunk_states + ((size_t)(c_begin + it) * H + h) * DK * DV + j0 + ln;
+                float* cs = chunk_states + (chunk_state_row(src, s, c_begin, it) * H + h) * DK * DV + j0 + ln;
 #pragma unroll
                 for (int t = 0; t < KT; ++t)
 #pragma unroll
@@ -586,7 +586,7 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
         // rewritten only after the barrier that ends chunk it) to chunk_states,
         // fp32 [chunk][H][DK][DV]: 16-byte stores of 4 columns of a row
         auto send_state = [&](int it) {
-            float* cs = chunk_states + ((size_t)(c_begin + it) * H + h) * DK * DV + j0;
+            float* cs = chunk_states + (chunk_state_row(src, s, c_begin, it) * H + h) * DK * DV + j0;
 #pragma unroll
             for (int k = 0; k < DK * 4 / 64; ++k) {
                 const int u = l + 64 * k, row = u >> 2, qd = u & 3;

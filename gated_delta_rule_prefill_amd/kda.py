@@ -324,10 +324,11 @@ def set_kernel_timing(enabled: bool) -> None:
 
 
 def prefill_kernel_times():
-    """[(kernel name, ms)] of the last prefill recorded with timing enabled."""
-    ms = (ctypes.c_float * 8)()
-    names = (ctypes.c_char_p * 8)()
-    n = lib().kda_prefill_kernel_times(ms, names, 8)
+    """[(kernel name, ms)] of the last prefill recorded with timing enabled on
+    this thread, in launch order (a long batch runs its kernels once per segment)."""
+    ms = (ctypes.c_float * 256)()
+    names = (ctypes.c_char_p * 256)()
+    n = min(lib().kda_prefill_kernel_times(ms, names, 256), 256)
     if n < 0:
         raise RuntimeError("no timed prefill recorded")
     return [(names[i].decode(), float(ms[i])) for i in range(n)]
