@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libkda.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 ARCH = "gfx950"
-KERNEL_SOURCES = ["chunk_table.hip", "prefill_intra.hip", "prefill_state.hip",
+KERNEL_SOURCES = ["chunk_table.hip", "prefill_intra.hip", "prefill_state.hip", "prefill_chain.hip",
                   "decode.hip", "recurrent.hip", "backward.hip", "kda_noalloc.hip"]
 HOST_SOURCES = ["kda_api.cpp"]
 

@@ -83,6 +83,12 @@ hipError_t launch_prefill_state(const void* rec, ChunkSrc src, const float* S0, 
                                 void* o, float* chunk_states, int H, int dk, int dv, bool bf16_io,
                                 hipStream_t stream);
 
+// The same pass over two value slices per workgroup (bf16, dk = 128,
+// dv = 64 or 128; see prefill_chain.hip).
+hipError_t launch_prefill_chain2(const void* rec, ChunkSrc src, const float* S0, float* S_final,
+                                 void* o, float* chunk_states, int H, int dk, int dv,
+                                 hipStream_t stream);
+
 // Whether a configuration runs the LDS-ring sequential kernel (its ring fits),
 // or the register-staged one (fp32 with dk = 128).
 constexpr bool uses_ring_kernel(bool bf16_io, int dk) { return bf16_io || dk == 64; }

@@ -751,6 +751,21 @@ static hipError_t launch_state_t(const void* rec, ChunkSrc src, const float* S0,
     return hipGetLastError();
 }
 
+// Compute units of the current device (queried once per device).
+static int device_cu_count()
+{
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
+    }
+    return v;
+}
+
 hipError_t launch_prefill_state(const void* rec, ChunkSrc src, const float* S0, float* S_final,
                                 void* o, float* chunk_states, int H, int dk, int dv, bool bf16_io,
                                 hipStream_t stream)
@@ -761,6 +776,10 @@ hipError_t launch_prefill_state(const void* rec, ChunkSrc src, const float* S0, 
 #define KDA_STATE_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)     \
         return launch_state_t<E, DK_, DV_>(rec, src, S0, S_final, o, chunk_states, H, stream);
+    // More one-slice chains than CUs (they hold a CU each): two slices per
+    // workgroup halve the rounds.
+    if (bf16_io && dk == 128 && (long long)src.N * H * (dv / 16) > device_cu_count())
+        return launch_prefill_chain2(rec, src, S0, S_final, o, chunk_states, H, dk, dv, stream);
     if (uses_ring_kernel(bf16_io, dk)) {
         if (bf16_io) {
             KDA_RING_CASE(bf16, 128, 128)
