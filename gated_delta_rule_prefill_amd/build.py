@@ -18,7 +18,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 ARCH = "gfx950"
 KERNEL_SOURCES = ["chunk_table.hip", "prefill_intra.hip", "prefill_state.hip", "prefill_chain.hip",
-                  "decode.hip", "recurrent.hip", "backward.hip", "kda_noalloc.hip"]
+                  "decode.hip", "recurrent.hip", "backward.hip", "backward_chunk.hip",
+                  "kda_noalloc.hip"]
 HOST_SOURCES = ["kda_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", CSRC, "-I", INCLUDE]

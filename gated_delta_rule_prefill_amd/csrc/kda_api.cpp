@@ -91,13 +91,26 @@ bool make_plan(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtyp
 bool supported_dim(int32_t d) { return d == 64 || d == 128; }
 
 // Workspace of one backward call: the forward plan (chunk table and records for
-// a recomputation), then the recomputed fp32
-// chunk states, an output scratch for the recomputation, the per-slice
-// partial gradients and the per-workgroup scratch.
+// a recomputation, reused for the reverse-chain records), then the recomputed
+// fp32 chunk states, an output scratch for the recomputation, and one area
+// that holds either the token-serial path's per-slice partial gradients and
+// per-workgroup scratch or the chunkwise path's gradients leaving every chunk.
 struct BwdPlan {
     Plan fwd;
-    size_t off_cs = 0, off_o = 0, off_part = 0, off_scratch = 0, total = 0;
+    size_t off_cs = 0, off_o = 0, off_part = 0, off_scratch = 0, off_dsc = 0, total = 0;
 };
+
+// The chunkwise backward (reverse chain over per-chunk records, then one
+// gradient workgroup per chunk) covers bf16 with dk = dv = 128; the other
+// configurations walk the tokens.  KDA_BACKWARD_SERIAL=1 in the environment
+// forces the token walk (read once; for tests and measurement).
+bool chunkwise_backward(kda_dtype dtype, int32_t dk, int32_t dv) {
+    static const bool serial = [] {
+        const char* e = std::getenv("KDA_BACKWARD_SERIAL");
+        return e && e[0] == '1';
+    }();
+    return !serial && dtype == KDA_DTYPE_BF16 && dk == 128 && dv == 128;
+}
 
 bool make_bwd_plan(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype,
                    BwdPlan& b) {
@@ -111,9 +124,12 @@ bool make_bwd_plan(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_
     b.off_o = at;
     at += align256((size_t)T * H * dv * es);
     b.off_part = at;
-    at += align256(kda::backward_partial_bytes(T, H, dk, dv));
-    b.off_scratch = at;
-    at += align256(kda::backward_scratch_bytes(N, H, dk, dv));
+    b.off_dsc = at;
+    const size_t serial = align256(kda::backward_partial_bytes(T, H, dk, dv)) +
+                          align256(kda::backward_scratch_bytes(N, H, dk, dv));
+    const size_t dsc = align256((size_t)b.fwd.max_chunks * H * dk * dv * 4);
+    b.off_scratch = at + align256(kda::backward_partial_bytes(T, H, dk, dv));
+    at += std::max(serial, dsc);
     b.total = at;
     return true;
 }
@@ -452,7 +468,25 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const float
                                   "state kernel", stream);
             cs = own_cs;
         }
-        if (st == KDA_OK)
+        if (st == KDA_OK && chunkwise_backward(dtype, dk, dv)) {
+            // reverse-chain records over the forward's, the chain (gradient
+            // leaving every chunk, and entering each sequence), then the
+            // per-chunk gradients
+            float* dsc = reinterpret_cast<float*>(ws + b.off_dsc);
+            const int mc = (int)plan.max_chunks;
+            st = check_launch(kda::launch_reverse_records(q, k, v, log_alpha, beta, d_o, src, mc, H,
+                                                          dk, dv, ws, stream),
+                              "reverse-record kernel", stream);
+            if (st == KDA_OK)
+                st = check_launch(kda::launch_reverse_chain(ws, src, d_final_state, d_initial_state,
+                                                            dsc, H, dk, dv, stream),
+                                  "reverse chain kernel", stream);
+            if (st == KDA_OK)
+                st = check_launch(kda::launch_chunk_grad(q, k, v, log_alpha, beta, d_o, src, mc, H,
+                                                         dk, dv, ws, cs, dsc, dq, dk_out, dv_out,
+                                                         dlog_alpha, dbeta, stream),
+                                  "chunk gradient kernel", stream);
+        } else if (st == KDA_OK)
             st = check_launch(kda::launch_backward(q, k, v, log_alpha, beta, src, cs, d_o,
                                                    d_final_state, H, total_tokens, dk, dv, bf16, dq,
                                                    dk_out, dv_out, dlog_alpha, dbeta,

@@ -89,6 +89,32 @@ hipError_t launch_prefill_chain2(const void* rec, ChunkSrc src, const float* S0,
                                  void* o, float* chunk_states, int H, int dk, int dv,
                                  hipStream_t stream);
 
+// The backward pass's reverse chain (bf16, dk = dv = 128).  Records: for each
+// (chunk, head) PM^T in PM's place, E = QM^T dO in Hc's place, gamma_C (intra
+// kernel in its reverse-record mode, d_o the output gradient).  The chain
+// then runs dS_in = Diag(gamma_C) dS + PM^T dS + E from the last chunk of
+// each sequence to the first, starting from dS_last (the final-state
+// gradient, NULL = 0); dS_chunks receives the gradient leaving every chunk
+// ([chunk][H][dk][dv] fp32, chunk-state rows) and dS_first (or NULL) the
+// gradient entering each sequence's first chunk.
+hipError_t launch_reverse_records(const void* q, const void* k, const void* v, const float* la,
+                                  const float* beta, const void* d_o, ChunkSrc src, int max_chunks,
+                                  int H, int dk, int dv, void* rec, hipStream_t stream);
+hipError_t launch_reverse_chain(const void* rec, ChunkSrc src, const float* dS_last,
+                                float* dS_first, float* dS_chunks, int H, int dk, int dv,
+                                hipStream_t stream);
+
+// Per-chunk gradients of the chunkwise backward (bf16, dk = dv = 128): rec
+// holds the reverse-chain records (for X, X^T and A_qk^T), chunk_states the
+// state entering every chunk and dS_chunks the gradient leaving it (both
+// [chunk][H][dk][dv] fp32, rows = table chunks).  Writes dq, dk, dv, dlog_alpha
+// and dbeta of every token.
+hipError_t launch_chunk_grad(const void* q, const void* k, const void* v, const float* la,
+                             const float* beta, const void* d_o, ChunkSrc src, int max_chunks,
+                             int H, int dk, int dv, const void* rec, const float* chunk_states,
+                             const float* dS_chunks, void* dq, void* dk_out, void* dv_out,
+                             float* dla, float* dbeta, hipStream_t stream);
+
 // Whether a configuration runs the LDS-ring sequential kernel (its ring fits),
 // or the register-staged one (fp32 with dk = 128).
 constexpr bool uses_ring_kernel(bool bf16_io, int dk) { return bf16_io || dk == 64; }

@@ -254,13 +254,17 @@ __device__ __forceinline__ void diag_inverse(const f32x4& am, float* sX, int g, 
 // NORM: L2-normalise q and k rows first; beta_logit: beta arrives as a logit.
 // bf16 operands fit 128 registers per lane (four waves per SIMD: two
 // workgroups per CU, bounded by LDS); fp32 operands take up to 256.
-template <typename E, int DK, int DV, bool NORM>
+// BWD: the record of the reverse chain of the backward pass instead (see the
+// launcher): PM^T in PM's place, E = QM^T dO (dO: the output gradient) in
+// Hc's place, gamma_C as before; QM's area takes X and X^T (64 x 64 each,
+// row-major) and OI's area A_qk^T, which the gradient kernel reads.
+template <typename E, int DK, int DV, bool NORM, bool BWD = false>
 __global__ __launch_bounds__(64 * INTRA_WAVES)
 __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 2))) void prefill_intra_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const ChunkSrc src, int H, int beta_logit,
-    unsigned char* __restrict__ rec)
+    unsigned char* __restrict__ rec, const E* __restrict__ d_o = nullptr)
 {
     using L = IntraLayout<E, DK, DV>;
     using V4 = typename Vec<E>::v4;
@@ -532,6 +536,22 @@ __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 2))) void prefill_intra_
             w[m] = from_f32<E>(x * (m < 4 ? b0[m] : b1[m - 4]));
         }
         store_vec(sTL + r * L::LT + cg, w);
+        if constexpr (BWD) {
+            // X row-major (zeros above the unit diagonal) and X^T for the
+            // gradient kernel, in the record's QM area: X[r][cg..cg+7] from
+            // the values above, X^T[lane][8w..8w+7] = X[8w+m][lane] from row
+            // `lane` of sAL
+            V8 xr, xt;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int c = cg + m;
+                xr[m] = from_f32<E>(r > c ? xv[m] : (r == c ? 1.f : 0.f));
+                const float a = sAL[r * L::LA + c];   // X[c][r] for c > r
+                xt[m] = from_f32<E>(c > r ? a : (c == r ? 1.f : 0.f));
+            }
+            store_vec(out.QM + r * CHUNK + cg, xr);
+            store_vec(out.QM + CHUNK * CHUNK + r * CHUNK + cg, xt);
+        }
     }
     __syncthreads();   // X dead: its bytes become Khat^T
 
@@ -581,10 +601,42 @@ __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 2))) void prefill_intra_
     // In perm32 order the columns 4g..4g+3 and 16+4g..16+4g+3 of a tile pair
     // are the 8 consecutive slots 8g..8g+7 of its 32-column block, so each
     // lane writes 16 contiguous bytes.
+    if (wside && BWD) {
+        // PM^T as A operands of the reverse chain: fragment (t, ks) holds, for
+        // PM^T row 16t + ln (a PM column), PM rows 32ks + 4g + i and
+        // 32ks + 16 + 4g + i -- two stacked accumulator tiles of K^T W with
+        // K^T rows as the A operand and the W column tile t as the B operand
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks) {
+            f32x4 acc[2][2];   // [column tile bw][row tile 2ks + h2]
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                V8 kf[2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) kf[s] = frag8<E>(sKHT + (16 * (2 * ks + h2) + ln) * L::LT + 32 * s + 8 * g);
+#pragma unroll
+                for (int bw = 0; bw < 2; ++bw) {
+                    acc[bw][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) acc[bw][h2] = mma32(kf[s], opf[bw][s], acc[bw][h2]);
+                }
+            }
+#pragma unroll
+            for (int bw = 0; bw < 2; ++bw) {
+                V8 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    w[i] = from_f32<E>(-acc[bw][0][i]);
+                    w[4 + i] = from_f32<E>(-acc[bw][1][i]);
+                }
+                store_frag(out.PM + frag_at<DK / 32>(ct0 + bw, ks), lane, w);
+            }
+        }
+    }
     if (wside) {
         // PM rows c = 16a + ln; columns 16 ct0 + 4g + i and 16 (ct0 + 1) + 4g + i
 #pragma unroll
-        for (int a = 0; a < DK / 16; ++a) {
+        for (int a = 0; a < DK / 16 && !BWD; ++a) {
             V8 kf[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) kf[s] = frag8<E>(sKHT + (16 * a + ln) * L::LT + 32 * s + 8 * g);
@@ -617,7 +669,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 2))) void prefill_intra_
                 *reinterpret_cast<f32x4*>(sQA + (16 * Rr + ln) * L::LQA + 16 * (ct0 + bw) + 4 * g) = acc;
             }
         }
-    } else if (uside) {
+    } else if (uside && !BWD) {
         // Hc rows c = 16a + 4g + i, column j = 16ct + ln  ->  Hc^T[j][perm(c)]:
         // row tiles a = 2m and 2m + 1 fill slots 32m + 8g .. +7
 #pragma unroll
@@ -671,17 +723,78 @@ __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 2))) void prefill_intra_
     __syncthreads();
 
     // ---- phase 6: QM = Qg - A_qk W in the row mapping ------------------------
+    if constexpr (!BWD) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const int row = rb + r;
-        typename Vec<E>::v2 w2;
+        for (int r = 0; r < NR; ++r) {
+            const int row = rb + r;
+            typename Vec<E>::v2 w2;
 #pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-            const E val = from_f32<E>(to_f32(raw_get<CPT>(qg[r], e)) - sQA[row * L::LQA + c0 + e]);
-            if constexpr (CPT == 2) w2[e] = val;
-            else out.QM[row * DK + perm_index(c0 + e)] = val;
+            for (int e = 0; e < CPT; ++e) {
+                const E val = from_f32<E>(to_f32(raw_get<CPT>(qg[r], e)) - sQA[row * L::LQA + c0 + e]);
+                if constexpr (CPT == 2) w2[e] = val;
+                else out.QM[row * DK + perm_index(c0 + e)] = val;
+            }
+            if constexpr (CPT == 2) store_vec(out.QM + row * DK + perm_index(c0), w2);
         }
-        if constexpr (CPT == 2) store_vec(out.QM + row * DK + perm_index(c0), w2);
+    } else {
+        // ---- phases 6-7 of the reverse-chain record: E = QM^T dO ----------------
+        // QM^T and dO^T go to LDS with the tokens contiguous (the rows of the
+        // wave in order), over the area A_qk W occupied; rows past the end of the
+        // sequence get dO = 0 so that they add nothing to E.
+        V8 qmt[CPT], dot[CPTV];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int row = rb + r;
+#pragma unroll
+            for (int e = 0; e < CPT; ++e)
+                qmt[e][r] = from_f32<E>(to_f32(raw_get<CPT>(qg[r], e)) - sQA[row * L::LQA + c0 + e]);
+            const RV dr = load_raw<CPTV>(d_o + rowoff[r] * DV + cv0);
+#pragma unroll
+            for (int e = 0; e < CPTV; ++e) dot[e][r] = row < ci.len ? raw_get<CPTV>(dr, e) : from_f32<E>(0.f);
+        }
+        __syncthreads();   // A_qk W dead: its area holds QM^T and dO^T
+        E* sQMT = sKGT;    // [DK][LT], tokens in order
+        E* sDOT = sVT;     // [DV][LT]
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) store_vec(sQMT + (c0 + e) * L::LT + rb, qmt[e]);
+#pragma unroll
+        for (int e = 0; e < CPTV; ++e) store_vec(sDOT + (cv0 + e) * L::LT + rb, dot[e]);
+        __syncthreads();
+        // A_qk^T[i][r] (row-major, zero for r < i) for the gradient kernel, in
+        // the record's OI area: thread (i, 8 tokens)
+        {
+            const int i = t >> 3, r0 = 8 * (t & 7);
+            V8 w;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) w[m] = sAQ[(r0 + m) * L::LT + perm_index(i)];
+            store_vec(out.OI + i * CHUNK + r0, w);
+        }
+        // E tiles (row tile a = 2m + h2: key channels, column tile u: value
+        // channels); wave w takes the tile pairs p = w, w + 8, ... of the
+        // DK/32 x DV/16 pairs (m, u), each stored as one planar fragment of
+        // E^T like Hc^T
+        constexpr int PAIRS = (DK / 32) * (DV / 16);
+        for (int p = wave; p < PAIRS; p += INTRA_WAVES) {
+            const int m = p / (DV / 16), u = p % (DV / 16);
+            V8 bf[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) bf[s] = frag8<E>(sDOT + (16 * u + ln) * L::LT + 32 * s + 8 * g);
+            f32x4 acc[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                acc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    acc[h2] = mma32(frag8<E>(sQMT + (16 * (2 * m + h2) + ln) * L::LT + 32 * s + 8 * g), bf[s], acc[h2]);
+            }
+            V8 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w[i] = from_f32<E>(acc[0][i]);
+                w[4 + i] = from_f32<E>(acc[1][i]);
+            }
+            store_frag_planar(out.HCt + frag_at<DK / 32>(u, m), lane, w);
+        }
     }
 }
 
@@ -699,6 +812,18 @@ static hipError_t launch_intra_t(const void* q, const void* k, const void* v, co
         hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, false>), dim3(max_chunks * H), dim3(64 * INTRA_WAVES), 0,
                            stream, (const E*)q, (const E*)k, (const E*)v, la, beta, src, H,
                            beta_logit, (unsigned char*)rec);
+    return hipGetLastError();
+}
+
+hipError_t launch_reverse_records(const void* q, const void* k, const void* v, const float* la,
+                                  const float* beta, const void* d_o, ChunkSrc src, int max_chunks,
+                                  int H, int dk, int dv, void* rec, hipStream_t stream)
+{
+    if (dk != 128 || dv != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_intra_kernel<bf16, 128, 128, false, true>), dim3(max_chunks * H),
+                       dim3(64 * INTRA_WAVES), 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, la, beta, src, H, 0, (unsigned char*)rec,
+                       (const bf16*)d_o);
     return hipGetLastError();
 }
 

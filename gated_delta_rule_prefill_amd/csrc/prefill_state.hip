@@ -404,11 +404,15 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// reverse: walk each sequence's chunks from the last to the first (the
+// backward pass's chain over reverse-chain records; o is then NULL and no
+// output is formed, and chunk_states receives the state entering each step,
+// i.e. the gradient leaving each chunk, at that chunk's row).
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_state_ring_kernel(
     const unsigned char* __restrict__ rec, const ChunkSrc src, const float* __restrict__ S0,
     float* __restrict__ S_final, E* __restrict__ o, float* __restrict__ chunk_states, int H,
-    int n_pairs)
+    int n_pairs, int reverse)
 {
     using C = RingCfg<E, DK, DV>;
     using V4 = typename Vec<E>::v4;
@@ -442,7 +446,8 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
             }
         return;   // uniform over the workgroup: no barrier is skipped by part of it
     }
-    auto record = [&](int it) { return rec + ((size_t)(c_begin + it) * H + h) * C::RL.bytes; };
+    auto chunk_at = [&](int it) { return reverse ? n - 1 - it : it; };   // chunk of step it
+    auto record = [&](int it) { return rec + ((size_t)(c_begin + chunk_at(it)) * H + h) * C::RL.bytes; };
     auto slot = [&](int it) { return ring + (it % C::NSLOT) * C::SLOT; };
     auto xslot = [&](int it) { return reinterpret_cast<E*>(xfer + (it % C::NX) * C::XSLOT); };
 
@@ -586,7 +591,7 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
         // rewritten only after the barrier that ends chunk it) to chunk_states,
         // fp32 [chunk][H][DK][DV]: 16-byte stores of 4 columns of a row
         auto send_state = [&](int it) {
-            float* cs = chunk_states + (chunk_state_row(src, s, c_begin, it) * H + h) * DK * DV + j0;
+            float* cs = chunk_states + (chunk_state_row(src, s, c_begin, chunk_at(it)) * H + h) * DK * DV + j0;
 #pragma unroll
             for (int k = 0; k < DK * 4 / 64; ++k) {
                 const int u = l + 64 * k, row = u >> 2, qd = u & 3;
@@ -630,6 +635,7 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
             // chunk c + 1 (NSLOT = 4, NX = 3), so these waves never hold up a
             // barrier with work of the chunk the chain is on
             auto form = [&](int c) {
+                if (o == nullptr) return;   // the reverse chain forms no output
                 const unsigned char* sl = slot(c);
                 const E* xs = xslot(c);
                 V8 Sa[KS];
@@ -734,7 +740,21 @@ static hipError_t launch_state_ring(const void* rec, ChunkSrc src, const float* 
     const long long blocks = (long long)groups * 8 * C::NSL;
     hipLaunchKernelGGL((prefill_state_ring_kernel<E, DK, DV>), dim3((unsigned)blocks),
                        dim3(64 * C::WAVES), 0, stream, (const unsigned char*)rec, src, S0, S_final,
-                       (E*)o, chunk_states, H, n_pairs);
+                       (E*)o, chunk_states, H, n_pairs, 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_reverse_chain(const void* rec, ChunkSrc src, const float* dS_last,
+                                float* dS_first, float* dS_chunks, int H, int dk, int dv,
+                                hipStream_t stream)
+{
+    if (dk != 128 || dv != 128) return hipErrorInvalidValue;
+    using C = RingCfg<bf16, 128, 128>;
+    const int n_pairs = src.N * H;
+    const long long blocks = (long long)((n_pairs + 7) / 8) * 8 * C::NSL;
+    hipLaunchKernelGGL((prefill_state_ring_kernel<bf16, 128, 128>), dim3((unsigned)blocks),
+                       dim3(64 * C::WAVES), 0, stream, (const unsigned char*)rec, src, dS_last,
+                       dS_first, (bf16*)nullptr, dS_chunks, H, n_pairs, 1);
     return hipGetLastError();
 }
 
