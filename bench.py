@@ -172,6 +172,37 @@ class Prefill:
                                                  (us * 1e-6) / 1e12, 1)}
 
 
+def backward_option(single, cs, reps, timed):
+    """kda_backward on the 4096-token workload (H=32, d=128, bf16) from its
+    exported chunk states cs: the chunkwise path (reverse-chain records, the
+    reverse chain, the per-chunk gradient kernel)."""
+    import torch
+    import gated_delta_rule_prefill_amd as kdalib
+    x = single.x
+    T, H, dk, dv = x.T, x.H, x.dk, x.dv
+    dev = cs.device
+    g = np.random.default_rng(11)
+    d_o = torch.from_numpy(gen_bf16(g.standard_normal((T, H, dv)).astype(np.float32))).view(
+        torch.bfloat16).to(dev)
+    s0 = single.sets[0]
+    bws = torch.empty(kdalib.backward_workspace_bytes(T, 1, H, dk, dv, True), dtype=torch.uint8,
+                      device=dev)
+    single.step(0, chunk_states=cs)
+    us = timed(lambda i: kdalib.backward(s0["q"], s0["k"], s0["v"], s0["la"], s0["beta"], d_o,
+                                         chunk_states=cs, need_initial_state_grad=False,
+                                         workspace=bws), reps)
+    nbytes = (PATH_BYTES_PER_TOKEN_HEAD + 768 + 512 + 4) * T * H
+    return {"workload": "gradients of the 4096-token prefill (H=32, d=128, bf16) from its "
+                        "exported chunk states", "path": "chunkwise", "us_per_call": round(us, 1),
+            "tokens_per_s": round(T / (us * 1e-6), 1), "algorithmic_bytes": nbytes,
+            "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def gen_bf16(a):
+    from gated_delta_rule_prefill_amd import inputs as gen
+    return gen.bf16_bits(a).view(np.int16)
+
+
 def ceilings(dev):
     """Achievable rates measured in the same run: a device copy and a bf16 GEMM."""
     import torch
@@ -241,6 +272,9 @@ def main():
                     help="headline workload: the 65536-token sequence (default) or the 4096-token one")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward option (--steps calls after --warmup; for "
+                         "profiling) and print its JSON")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -259,6 +293,26 @@ def main():
 
     def dq(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.backward_only:
+        single = Prefill(gen.config_prefill(2), dev)
+        cs = torch.empty((kdalib.num_chunk_states(single.x.T, 1), single.x.H, single.x.dk,
+                          single.x.dv), dtype=torch.float32, device=dev)
+
+        def timed(fn, reps):
+            for i in range(args.warmup):
+                fn(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / reps
+
+        print(json.dumps(backward_option(single, cs, args.steps, timed)), flush=True)
+        return
 
     rec_extra = {}
     single = None
@@ -379,25 +433,12 @@ def main():
                         "fp32 states in permuted slots", "us_per_call": round(rec_us, 2),
             "algorithmic_bytes": rec_bytes, "achieved_GBs": round(rec_gbs, 1),
             "frac_of_hbm_peak": round(rec_gbs / HBM_PEAK_GBS, 4)}
-        g = np.random.default_rng(11)
-        d_o = dq(gen.bf16_bits(g.standard_normal((T, H, dv)).astype(np.float32)))
-        s0 = single.sets[0]
-        bws = torch.empty(kdalib.backward_workspace_bytes(T, 1, H, dk, dv, True), dtype=torch.uint8,
-                          device=dev)
-        single.step(0, chunk_states=cs)
-        bwd_us = timed(lambda i: kdalib.backward(s0["q"], s0["k"], s0["v"], s0["la"], s0["beta"],
-                                                 d_o, chunk_states=cs,
-                                                 need_initial_state_grad=False, workspace=bws), 5)
-        bwd_bytes = (PATH_BYTES_PER_TOKEN_HEAD + 768 + 512 + 4) * T * H
-        options["backward"] = {
-            "workload": "gradients of the 4096-token prefill (H=32, d=128, bf16) from its "
-                        "exported chunk states", "us_per_call": round(bwd_us, 1),
-            "tokens_per_s": round(T / (bwd_us * 1e-6), 1), "algorithmic_bytes": bwd_bytes,
-            "achieved_GBs": round(bwd_bytes / (bwd_us * 1e-6) / 1e9, 1)}
+        options["backward"] = backward_option(single, cs, 20, timed)
+        bwd_us = options["backward"]["us_per_call"]
         log(f"[bench] options: chunk states +{cs_us - base_us:.1f} us, preprocessing "
             f"{min(pre_runs):.1f} us (plain {min(plain_runs):.1f}), decode_tokens {rec_us:.1f} us "
             f"= {rec_gbs:.0f} GB/s, backward {bwd_us:.0f} us")
-        del pool, cs, bws
+        del pool, cs
 
     if args.copy_calib:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -557,9 +557,16 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
 
     // ---------------- phase 6: the decayed products' gradients ------------------------
     // A operands over key tokens i = 32s + 8g + m for the lane's channel cl,
-    // with the block reference of the lane's 16-token block (2s + g/2)
+    // with the block reference of the lane's 16-token block (2s + g/2), kept
+    // in fp32 and fed to the MFMA as a bf16 pair (high part, then the rounding
+    // remainder).  The g-gradient of each decayed product enters dg twice
+    // with opposite signs (at the row token and at the key token), and the
+    // reverse cumulative sum keeps their difference only if both sides carry
+    // the same values: one bf16 rounding of these operands leaves a residue of
+    // the size of the pair terms, which under strong decay are large against
+    // dlog_alpha itself.
     {
-        bf16x8 kb[2], qb[2], kr[2];
+        float kb[2][8], qb[2][8], kr[2][8];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const float B = sBref[(2 * s + (g >> 1)) * D + cl];
@@ -568,32 +575,53 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
                 const int i = 32 * s + 8 * g + m;
                 const float gi = sG[i * LG + cl];
                 const float kv = (float)sK[i * LR + cl];
-                kb[s][m] = (bf16)(kv * cexp(B - gi));
+                kb[s][m] = kv * cexp(B - gi);
                 const float p = fast_exp(gi - B);
-                kr[s][m] = (bf16)(kv * p);
-                qb[s][m] = (bf16)((float)sQ[i * LR + cl] * p);
+                kr[s][m] = kv * p;
+                qb[s][m] = (float)sQ[i * LR + cl] * p;
             }
         }
+        // f x (8 values) as the bf16 pair hi + lo
+        auto split = [](const float (&x)[8], float f, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float y = x[m] * f;
+                hi[m] = (bf16)y;
+                lo[m] = (bf16)(y - (float)hi[m]);
+            }
+        };
         // the lane's key-token blocks (2s + g/2) as seen by its A-operand channel
         const float Bk0 = sBref[(g >> 1) * D + cl], Bk1 = sBref[(2 + (g >> 1)) * D + cl];
         // XQ, XL (row block R; key blocks I <= R) and Y (key block I; rows R >= I)
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
             f32x4 xq = zero4(), xl = zero4(), y = zero4();
+            const float BR = sBref[R * D + cl];
 #pragma unroll
             for (int s = 0; s <= R / 2; ++s) {
                 const int I = 2 * s + (g >> 1);
-                const float BR = sBref[R * D + cl];
-                const bf16x8 kf = scale8(kb[s], I <= R ? fast_exp(BR - (s ? Bk1 : Bk0)) : 0.f);
-                xq = mma32(kf, lds8(sDAq + (16 * R + ln) * LT + 32 * s + 8 * g), xq);
-                xl = mma32(kf, lds8(sDA + (16 * R + ln) * LT + 32 * s + 8 * g), xl);
+                bf16x8 hi, lo;
+                split(kb[s], I <= R ? fast_exp(BR - (s ? Bk1 : Bk0)) : 0.f, hi, lo);
+                const bf16x8 aq = lds8(sDAq + (16 * R + ln) * LT + 32 * s + 8 * g);
+                const bf16x8 al = lds8(sDA + (16 * R + ln) * LT + 32 * s + 8 * g);
+                xq = mma32(hi, aq, xq);
+                xq = mma32(lo, aq, xq);
+                xl = mma32(hi, al, xl);
+                xl = mma32(lo, al, xl);
             }
 #pragma unroll
             for (int s = R / 2; s < 2; ++s) {
                 const int Rk = 2 * s + (g >> 1);
-                const float f = Rk >= R ? fast_exp((s ? Bk1 : Bk0) - sBref[R * D + cl]) : 0.f;
-                y = mma32(scale8(qb[s], f), lds8(sDAqT + (16 * R + ln) * LT + 32 * s + 8 * g), y);
-                y = mma32(scale8(kr[s], f), lds8(sDLT + (16 * R + ln) * LT + 32 * s + 8 * g), y);
+                const float f = Rk >= R ? fast_exp((s ? Bk1 : Bk0) - BR) : 0.f;
+                const bf16x8 at = lds8(sDAqT + (16 * R + ln) * LT + 32 * s + 8 * g);
+                const bf16x8 lt = lds8(sDLT + (16 * R + ln) * LT + 32 * s + 8 * g);
+                bf16x8 hi, lo;
+                split(qb[s], f, hi, lo);
+                y = mma32(hi, at, y);
+                y = mma32(lo, at, y);
+                split(kr[s], f, hi, lo);
+                y = mma32(hi, lt, y);
+                y = mma32(lo, lt, y);
             }
             // lane: token r = 16R + ln, channels co .. co + 3
             const int r = 16 * R + ln;

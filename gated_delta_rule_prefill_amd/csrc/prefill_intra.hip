@@ -294,8 +294,11 @@ __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 2))) void prefill_intra_
     float* sEtab = reinterpret_cast<float*>(smem + L::OFF_ETAB);
     float* sBeta = reinterpret_cast<float*>(smem + L::OFF_BETA);
 
+    // chunks in descending order, so the sequential kernel (first chunk first)
+    // finds the most recently written records first; the reverse chain starts
+    // from the last chunk, so its records go in ascending order
     int cid, h;
-    chunk_head_of_block(H, true, cid, h);
+    chunk_head_of_block(H, !BWD, cid, h);
     int n_chunks;
     ChunkInfo ci;
     chunk_of(src, cid, n_chunks, ci);

@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from gated_delta_rule_prefill_amd import inputs as gen
-from gpu_util import TOL, dev_f32, dev_qkv, device_inputs, host, rel_l2
+from gpu_util import MIN_UNIT_ROWS, TOL, dev_f32, dev_qkv, device_inputs, host, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -21,9 +21,9 @@ def _gpu():
     k.lib()
 
 
-def _case(seed, lens, H, dk, dv, dtype, packed=True):
+def _case(seed, lens, H, dk, dv, dtype, packed=True, mu=3.0, fixed=None):
     x = gen.make_prefill(seed, lens, H=H, dk=dk, dv=dv, dtype=dtype, state_std=0.02,
-                         packed=packed)
+                         packed=packed, mu=mu, fixed_even_log_alpha=fixed)
     g = np.random.default_rng(seed)
     d_o = g.standard_normal((x.T, H, dv)).astype(np.float32)
     if dtype == "bf16":
@@ -53,6 +53,16 @@ def _check(x, d_o, d_fin, label):
           " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
     for n, e in errs.items():
         assert e <= TOL[x.dtype], (label, n, e)
+    # per sequence as well (sequences of at least MIN_UNIT_ROWS tokens: on
+    # shorter ones the bf16 rounding of a few products is the whole signal)
+    lens = np.diff(x.cu_seqlens) if x.cu_seqlens is not None else [x.T // x.num_seqs] * x.num_seqs
+    at = 0
+    for s, n_tok in enumerate(lens):
+        if n_tok >= MIN_UNIT_ROWS:
+            for n in GRADS[:5]:
+                e = rel_l2(host(g[n])[at:at + n_tok], ref[n][at:at + n_tok])
+                assert e <= TOL[x.dtype], (label, "sequence", s, n, e)
+        at += n_tok
     return g
 
 
@@ -110,3 +120,24 @@ def test_backward_without_final_gradient_fp32():
     ref = oracle.backward(x.q, x.k, x.v, x.log_alpha, x.beta, None, None, d_o.astype(np.float64))
     for n in GRADS:
         assert rel_l2(host(gr[n]), ref[n]) <= TOL["f32"], n
+
+
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 128), ("bf16", 64)])
+@pytest.mark.parametrize("mu,fixed", [(0.0, None), (-1.0, None), (3.0, -3.0)],
+                         ids=["mu0", "mu-1", "fixed-3"])
+def test_backward_strong_decay(dtype, dk, mu, fixed):
+    """Strong per-channel decay (paper notes section 2: every key channel has its
+    own forgetting rate): log_alpha = logsigmoid(N(mu, 1)) with mu = 0 or -1
+    (16-token block sums near -13 and -22), or the even channels fixed at -3
+    (block sums of -48); the chunkwise gradients' block-referenced decay
+    factors run near their range.  Packed with empty, one-token and cut chunks."""
+    x, d_o, d_fin = _case(81, [200, 1, 64, 0, 131, 77], 2, dk, dk, dtype, mu=mu, fixed=fixed)
+    _check(x, d_o, d_fin, f"strong decay mu={mu} fixed={fixed}")
+
+
+def test_backward_long_packed():
+    """About 4,000 tokens in four sequences (one a single chunk), H = 4, bf16,
+    d = 128: the reverse chain over up to 32 chunks and the gradient kernel on
+    every chunk."""
+    x, d_o, d_fin = _case(82, [1500, 64, 2000, 531], 4, 128, 128, "bf16")
+    _check(x, d_o, d_fin, "long packed")
