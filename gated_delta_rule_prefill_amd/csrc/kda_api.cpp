@@ -543,7 +543,7 @@ kda_status kda_decode_tokens(float* state_pool, int32_t num_slots, const int32_t
         return check_launch(kda::launch_recurrent(state_pool, num_slots, state_indices, q, k, v,
                                                   log_alpha, beta, cu_seqlens, rows, num_seqs, H,
                                                   dk, dv, dtype == KDA_DTYPE_BF16,
-                                                  pre_flags(flags), o, stream),
+                                                  pre_flags(flags), o, stream, total_tokens),
                             "recurrent kernel", stream);
     } catch (...) {
         return fail(KDA_ERR_HIP, "unexpected C++ exception inside kda_decode_tokens");

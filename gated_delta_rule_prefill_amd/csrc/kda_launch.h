@@ -123,7 +123,7 @@ constexpr bool uses_ring_kernel(bool bf16_io, int dk) { return bf16_io || dk == 
 hipError_t launch_recurrent(float* pool, int num_slots, const int32_t* slots, const void* q,
                             const void* k, const void* v, const float* la, const float* beta,
                             const int32_t* cu, int rows, int N, int H, int dk, int dv,
-                            bool bf16_io, unsigned flags, void* o, hipStream_t stream);
+                            bool bf16_io, unsigned flags, void* o, hipStream_t stream, int64_t T);
 
 // Gradients of the recurrence (see backward.hip).  chunk_states: the fp32
 // state entering every chunk, as kda_prefill_ex exports them.  part: the

@@ -348,6 +348,9 @@ struct RingCfg {
     static constexpr int LOADS = (UNITS + 63) / 64;  // direct loads per chunk
     static constexpr int LOADS_W = (LOADS + NSTG - 1) / NSTG;   // per stager wave
     static constexpr int LOADS_LAST = LOADS - (NSTG - 1) * LOADS_W;   // the last stager's share
+    // the reverse chain forms no output: its stager moves only the E^T
+    // fragments (in Hc^T's place) and gamma_C, the first units of the list
+    static constexpr int LOADS_REV = (HC_UNITS + G_UNITS + 63) / 64;
     static constexpr int SLOT = LOADS * 1024;
     static constexpr int OFF_HC = 0;
     static constexpr int OFF_G = OFF_HC + HC_UNITS * 16;
@@ -361,6 +364,7 @@ struct RingCfg {
     static constexpr int TOUCH_PER_LANE = (TOUCH_LINES + 63) / 64;
     static_assert(2 * LOADS_W <= 60, "two chunks of one stager's direct loads must fit its counter");
     static_assert(LOADS_LAST > 0 && LOADS_LAST <= LOADS_W, "stager split");
+    static_assert(NSTG == 1 && LOADS_REV <= LOADS_W, "the reverse chain's loads are the first stager's first ones");
 };
 
 constexpr int TOUCH_DIST = 6;   // chunks between the L2 touch and the first direct load
@@ -670,7 +674,7 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
         // ------------------------------------------------ stager waves: direct loads into the ring
         const int sw = wave - NSER - 1;
         const int i0 = sw * C::LOADS_W;
-        const int cnt = min(C::LOADS_W, C::LOADS - i0);
+        const int cnt = reverse ? C::LOADS_REV : min(C::LOADS_W, C::LOADS - i0);
         // This lane's byte offset inside a record, per load.
         uint32_t off[C::LOADS_W];
 #pragma unroll
@@ -711,7 +715,8 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
         };
         // wait until only the chunk issued last is in flight (cnt loads)
         auto wait_one_in_flight = [&]() {
-            if (cnt == C::LOADS_W) __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS_W));
+            if (reverse) __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS_REV));
+            else if (cnt == C::LOADS_W) __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS_W));
             else __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS_LAST));
         };
         issue(0);

@@ -170,6 +170,257 @@ __global__ __launch_bounds__(64 * (DV / 32)) void recurrent_kernel(
     for (int m = 0; m < RPL; ++m) *reinterpret_cast<f32x4*>(S + (size_t)(r0 + m) * DV + c0) = s[m];
 }
 
+// ---------------------------------------------------------------------------
+// The chunkwise form of the same path (bf16, dk = dv = 128).  The paper notes
+// (section 3) fold a run of tokens into dense products; here the run is at
+// most RC = 16 tokens of one sequence.  For such a chunk with cumulative
+// log-decay g (restarting at the chunk) and entering state S:
+//
+//   A_kk[t][t'] = beta_t sum_c k_tc k_t'c e^{g_tc - g_t'c}  (t' < t)
+//   A_qk[t][t'] =        sum_c q_tc k_t'c e^{g_tc - g_t'c}  (t' <= t)
+//   T = (I + A_kk)^{-1} Diag(beta),  W = T (e^g k),  U = T v
+//   N = U - W S,  o = (e^g q) S + A_qk N,  S' = Diag(e^{g_C}) S + (e^{g_C - g} k)^T N
+//
+// (exact algebra of the recurrence, as in the chunkwise prefill; the decay
+// factors e^{-g} span at most 16 tokens).  The fp32 state stays in MFMA
+// accumulators: wave w of 8 owns value columns 16w .. 16w + 15, tile cb
+// holding S[16cb + 4g + i][16w + (l & 15)].  The state is then touched
+// once per chunk by VALU (the Diag(e^{g_C}) scaling and its bf16 operand
+// copy) instead of four times per token, and the path is bound by the state's
+// read and write.  Products over the chunk's tokens use the 16x16x32 MFMA
+// with the upper 16 contraction slots zero.
+constexpr int RC = 16;   // tokens per chunk
+
+template <bool NORM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void recurrent_mfma_kernel(
+    float* __restrict__ pool, int num_slots, const int32_t* __restrict__ slots,
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    const int32_t* __restrict__ cu, int rows, int H, int beta_logit, bf16* __restrict__ o)
+{
+    constexpr int D = 128;
+    constexpr int LK = D + 8;    // row stride of [RC][D] bf16 arrays (channels in perm32 order)
+    constexpr int LT = RC + 8;   // row stride of [D][RC] and [RC][RC] bf16 arrays
+    constexpr int LG = D + 4;    // row stride of the fp32 g array
+    // g (fp32) until the operands are formed, then -W
+    __shared__ __attribute__((aligned(16))) float sG[RC * LG];
+    __shared__ __attribute__((aligned(16))) bf16 sKg[RC * LK], sKi[RC * LK], sQg[RC * LK];
+    __shared__ __attribute__((aligned(16))) bf16 sKgT[D * LT], sKhT[D * LT], sVT[D * LT];
+    __shared__ __attribute__((aligned(16))) bf16 sT[RC * LT], sAq[RC * LT];
+    __shared__ __attribute__((aligned(16))) float sBeta[RC], sGam[D];
+    bf16* sW = reinterpret_cast<bf16*>(sG);
+    static_assert(RC * LK * 2 <= RC * LG * 4, "-W fits over g");
+
+    const int u = blockIdx.x;   // sequence * H + head
+    const int seq = u / H, h = u % H;
+    const int t = threadIdx.x;
+    const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int g = lane >> 4, ln = lane & 15;
+    int t0, t1;
+    if (cu) {
+        t0 = cu[seq];
+        t1 = cu[seq + 1];
+    } else {
+        t0 = seq * rows;
+        t1 = t0 + rows;
+    }
+    const int slot = slots ? slots[seq] : seq;
+    if (slot < 0 || slot >= num_slots) {   // padding sequence (uniform over the workgroup)
+        for (int x = t; x < (t1 - t0) * D; x += 512)
+            o[((size_t)(t0 + x / D) * H + h) * D + x % D] = (bf16)0.f;
+        return;
+    }
+    if (t1 <= t0) return;
+    float* S = pool + ((size_t)slot * H + h) * D * D;
+    const int j = 16 * w + ln;   // the lane's value column in the state tiles
+
+    // The state through a buffer resource: the lane's part of each address in
+    // one register, the element's constant part as the scalar offset.
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(S, (short)0, D * D * 4, 0x00020000);
+    const int voff = (4 * g * D + j) * 4;
+    f32x4 st[8];   // st[cb]: lane holds S[16cb + 4g + i][j]
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            st[cb][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, voff, (16 * cb + i) * D * 4, 0));
+
+    // operand of 4 consecutive tokens (slots 0..3) with the upper slots zero
+    auto half8 = [](const bf16* p) {
+        const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+        return bf16x8{a[0], a[1], a[2], a[3], (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    };
+    // staging (waves 0-3): token row tr, channels c8 .. c8 + 7
+    const int tr = (t >> 4) & (RC - 1), c8 = 8 * (t & 15);
+
+    for (int tb = t0; tb < t1; tb += RC) {
+        const int nt = min(RC, t1 - tb);
+        __syncthreads();   // the previous chunk's operands are consumed
+        // ---- stage: q, k, v rows (waves 0-3), g (waves 4-5), beta (wave 6) --------
+        bf16x8 qv = {}, kv = {}, vv = {};
+        if (w < 4) {
+            if (tr < nt) {
+                const size_t row = ((size_t)(tb + tr) * H + h) * D + c8;
+                qv = *reinterpret_cast<const bf16x8*>(q + row);
+                kv = *reinterpret_cast<const bf16x8*>(k + row);
+                vv = *reinterpret_cast<const bf16x8*>(v + row);
+            }
+        } else if (w < 6) {
+            // rows past the chunk's end re-read its last row (added as 0)
+            const int c = t - 256;
+            const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(log_alpha) + ((size_t)tb * H + h) * D, (short)0, 0x7fffffff, 0x00020000);
+            float lv[RC];
+#pragma unroll
+            for (int r = 0; r < RC; ++r)
+                lv[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                      lrs, c * 4, min(r, nt - 1) * H * D * 4, 0));
+            float run = 0.f;
+#pragma unroll
+            for (int r = 0; r < RC; ++r) {
+                run += r < nt ? lv[r] : 0.f;
+                sG[r * LG + c] = run;
+            }
+            sGam[c] = fast_exp(run);
+        } else if (w == 6 && lane < RC) {
+            const float b = beta[(size_t)(tb + min(lane, nt - 1)) * H + h];
+            sBeta[lane] = lane < nt ? (beta_logit ? sigmoid(b) : b) : 0.f;
+        }
+        __syncthreads();
+        // ---- decayed operands (waves 0-3) -------------------------------------------
+        if (w < 4) {
+            float qf[8], kf[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                qf[m] = (float)qv[m];
+                kf[m] = (float)kv[m];
+            }
+            if constexpr (NORM) {
+                float sq = 0.f, sk = 0.f;
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    sq += qf[m] * qf[m];
+                    sk += kf[m] * kf[m];
+                }
+                const float iq = rsqrtf(row16_sum(sq) + L2NORM_EPS), ik = rsqrtf(row16_sum(sk) + L2NORM_EPS);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    qf[m] *= iq;
+                    kf[m] *= ik;
+                }
+            }
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(sG + tr * LG + c8);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(sG + tr * LG + c8 + 4);
+            const f32x4 e0 = *reinterpret_cast<const f32x4*>(sG + (RC - 1) * LG + c8);
+            const f32x4 e1 = *reinterpret_cast<const f32x4*>(sG + (RC - 1) * LG + c8 + 4);
+            bf16x8 kg, ki, qg;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float gm = m < 4 ? g0[m] : g1[m - 4], gc = m < 4 ? e0[m] : e1[m - 4];
+                const float eg = fast_exp(gm);
+                kg[m] = (bf16)(kf[m] * eg);
+                ki[m] = (bf16)(kf[m] * fast_exp(fminf(-gm, 80.f)));
+                qg[m] = (bf16)(qf[m] * eg);
+                const int c = c8 + m;
+                sKgT[c * LT + tr] = kg[m];
+                sKhT[c * LT + tr] = (bf16)(kf[m] * fast_exp(gc - gm));
+                sVT[c * LT + tr] = vv[m];
+            }
+            // channels c8 .. c8 + 7 sit at perm_index(c8) and perm_index(c8 + 4)
+            const int p0 = tr * LK + perm_index(c8), p1 = tr * LK + perm_index(c8 + 4);
+            *reinterpret_cast<bf16x4*>(sKg + p0) = bf16x4{kg[0], kg[1], kg[2], kg[3]};
+            *reinterpret_cast<bf16x4*>(sKg + p1) = bf16x4{kg[4], kg[5], kg[6], kg[7]};
+            *reinterpret_cast<bf16x4*>(sKi + p0) = bf16x4{ki[0], ki[1], ki[2], ki[3]};
+            *reinterpret_cast<bf16x4*>(sKi + p1) = bf16x4{ki[4], ki[5], ki[6], ki[7]};
+            *reinterpret_cast<bf16x4*>(sQg + p0) = bf16x4{qg[0], qg[1], qg[2], qg[3]};
+            *reinterpret_cast<bf16x4*>(sQg + p1) = bf16x4{qg[4], qg[5], qg[6], qg[7]};
+        }
+        __syncthreads();
+        // ---- A_kk and T (wave 0), A_qk (wave 1) ------------------------------------
+        if (w < 2) {
+            const bf16* A = w == 0 ? sKg : sQg;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};   // lane: [4g + i][ln]
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s)
+                acc = mma32(*reinterpret_cast<const bf16x8*>(A + ln * LK + 32 * s + 8 * g),
+                            *reinterpret_cast<const bf16x8*>(sKi + ln * LK + 32 * s + 8 * g), acc);
+            if (w == 0) {
+                f32x4 am;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) am[i] = 4 * g + i > ln ? sBeta[4 * g + i] * acc[i] : 0.f;
+                // (I + A_kk) x = e_l by forward substitution, lane l = column l
+                float x[RC];
+#pragma unroll
+                for (int r = 0; r < RC; ++r) {
+                    float a = r == ln ? 1.f : 0.f;
+#pragma unroll
+                    for (int i = 0; i < r; ++i) a -= read_lane(am[r & 3], 16 * (r >> 2) + i) * x[i];
+                    x[r] = a;
+                }
+                if (g == 0) {
+                    const float bl = sBeta[ln];
+#pragma unroll
+                    for (int r = 0; r < RC; ++r) sT[r * LT + ln] = (bf16)(x[r] * bl);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sAq[(4 * g + i) * LT + ln] = (bf16)(ln <= 4 * g + i ? acc[i] : 0.f);
+            }
+        }
+        __syncthreads();
+        // ---- W (negated, over g; wave w: key block w) and U (this wave's columns) ---------
+        {
+            const f32x4 a = mma32(half8(sKgT + (16 * w + ln) * LT + 4 * g), half8(sT + ln * LT + 4 * g),
+                                  f32x4{0.f, 0.f, 0.f, 0.f});
+            // lane: W[ln][16w + 4g + i]
+            *reinterpret_cast<bf16x4*>(sW + ln * LK + perm_index(16 * w + 4 * g)) =
+                bf16x4{(bf16)-a[0], (bf16)-a[1], (bf16)-a[2], (bf16)-a[3]};
+        }
+        // lane: [token 4g + i][j]
+        f32x4 nacc = mma32(half8(sT + ln * LT + 4 * g), half8(sVT + j * LT + 4 * g), f32x4{0.f, 0.f, 0.f, 0.f});
+        __syncthreads();
+        // ---- N = U - W S, o = Qg S + A_qk N, S' = Diag(gamma) S + Khat^T N ---------------
+        {
+            f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                bf16x8 sf;   // perm32 slots of key rows 32s .. 32s + 31
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sf[i] = (bf16)st[2 * s][i];
+                    sf[4 + i] = (bf16)st[2 * s + 1][i];
+                }
+                nacc = mma32(*reinterpret_cast<const bf16x8*>(sW + ln * LK + 32 * s + 8 * g), sf, nacc);
+                pacc = mma32(*reinterpret_cast<const bf16x8*>(sQg + ln * LK + 32 * s + 8 * g), sf, pacc);
+            }
+            const bf16x8 nb = {(bf16)nacc[0], (bf16)nacc[1], (bf16)nacc[2], (bf16)nacc[3],
+                               (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+            pacc = mma32(half8(sAq + ln * LT + 4 * g), nb, pacc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * g + i < nt) o[((size_t)(tb + 4 * g + i) * H + h) * D + j] = (bf16)pacc[i];
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) {
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(sGam + 16 * cb + 4 * g);
+                f32x4 a = st[cb];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] *= gm[i];
+                st[cb] = mma32(half8(sKhT + (16 * cb + ln) * LT + 4 * g), nb, a);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x = st[cb][i];   // a bit cast of a vector element in place reads element 0
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), srs, voff,
+                                                  (16 * cb + i) * D * 4, 0);
+        }
+}
+
 template <typename E, int DK, int DV>
 static hipError_t launch_rec_t(float* pool, int num_slots, const int32_t* slots, const void* q,
                                const void* k, const void* v, const float* la, const float* beta,
@@ -192,8 +443,24 @@ static hipError_t launch_rec_t(float* pool, int num_slots, const int32_t* slots,
 hipError_t launch_recurrent(float* pool, int num_slots, const int32_t* slots, const void* q,
                             const void* k, const void* v, const float* la, const float* beta,
                             const int32_t* cu, int rows, int N, int H, int dk, int dv,
-                            bool bf16_io, unsigned flags, void* o, hipStream_t stream)
+                            bool bf16_io, unsigned flags, void* o, hipStream_t stream, int64_t T)
 {
+    // Chunkwise MFMA form for bf16 at d = 128 when some sequence has several
+    // tokens; one token per sequence keeps the exact token step (it equals
+    // the decode step).
+    if (bf16_io && dk == 128 && dv == 128 && T > N) {
+        const dim3 grid((unsigned)((long long)N * H));
+        const int beta_logit = (flags & PRE_BETA_LOGIT) ? 1 : 0;
+        if (flags & PRE_L2NORM_QK)
+            hipLaunchKernelGGL(recurrent_mfma_kernel<true>, grid, dim3(512), 0, stream, pool, num_slots,
+                               slots, (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, cu, rows,
+                               H, beta_logit, (bf16*)o);
+        else
+            hipLaunchKernelGGL(recurrent_mfma_kernel<false>, grid, dim3(512), 0, stream, pool, num_slots,
+                               slots, (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, cu, rows,
+                               H, beta_logit, (bf16*)o);
+        return hipGetLastError();
+    }
 #define KDA_REC_CASE(E, DK_, DV_) \
     if (dk == DK_ && dv == DV_)   \
         return launch_rec_t<E, DK_, DV_>(pool, num_slots, slots, q, k, v, la, beta, cu, rows, N, H, flags, o, stream);
