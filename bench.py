@@ -198,6 +198,34 @@ def backward_option(single, cs, reps, timed):
             "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
+def decode_tokens_option(dev, reps, timed):
+    """kda_decode_tokens on 256 sequences of 8 tokens (H=32, d=128, bf16), fp32
+    states in a permuted order of pool slots."""
+    import torch
+    import gated_delta_rule_prefill_amd as kdalib
+    from gated_delta_rule_prefill_amd import inputs as gen
+    H, dk, dv, Nr, Tr = 32, 128, 128, 256, 8
+
+    def dq(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    rr = gen.make_prefill(9, [Tr] * Nr, H=H, dk=dk, dv=dv, dtype="bf16")
+    pool = torch.from_numpy(gen.decode_state(9, Nr, H, dk, dv)).to(dev)
+    slots = torch.from_numpy(np.random.default_rng(9).permutation(Nr).astype(np.int32)).to(dev)
+    rin = dict(q=dq(rr.q), k=dq(rr.k), v=dq(rr.v), la=torch.from_numpy(rr.log_alpha).to(dev),
+               beta=torch.from_numpy(rr.beta).to(dev))
+    o_r = torch.empty((Nr * Tr, H, dv), dtype=torch.bfloat16, device=dev)
+    us = timed(lambda i: kdalib.decode_tokens(pool, rin["q"], rin["k"], rin["v"], rin["la"],
+                                              rin["beta"], state_indices=slots, num_seqs=Nr,
+                                              out=o_r), reps)
+    nbytes = Nr * H * (2 * dk * dv * 4 + Tr * PATH_BYTES_PER_TOKEN_HEAD)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "pooled recurrent tokens: 256 seqs x 8 tokens, H=32, dk=dv=128, bf16, "
+                        "fp32 states in permuted slots", "us_per_call": round(us, 2),
+            "algorithmic_bytes": nbytes, "achieved_GBs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def gen_bf16(a):
     from gated_delta_rule_prefill_amd import inputs as gen
     return gen.bf16_bits(a).view(np.int16)
@@ -272,6 +300,9 @@ def main():
                     help="headline workload: the 65536-token sequence (default) or the 4096-token one")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--decode-tokens-only", action="store_true",
+                    help="time only the pooled-recurrent option (--steps calls after --warmup; "
+                         "for profiling) and print its JSON")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward option (--steps calls after --warmup; for "
                          "profiling) and print its JSON")
@@ -294,11 +325,7 @@ def main():
     def dq(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    if args.backward_only:
-        single = Prefill(gen.config_prefill(2), dev)
-        cs = torch.empty((kdalib.num_chunk_states(single.x.T, 1), single.x.H, single.x.dk,
-                          single.x.dv), dtype=torch.float32, device=dev)
-
+    if args.backward_only or args.decode_tokens_only:
         def timed(fn, reps):
             for i in range(args.warmup):
                 fn(i)
@@ -311,6 +338,12 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) * 1e3 / reps
 
+        if args.decode_tokens_only:
+            print(json.dumps(decode_tokens_option(dev, args.steps, timed)), flush=True)
+            return
+        single = Prefill(gen.config_prefill(2), dev)
+        cs = torch.empty((kdalib.num_chunk_states(single.x.T, 1), single.x.H, single.x.dk,
+                          single.x.dv), dtype=torch.float32, device=dev)
         print(json.dumps(backward_option(single, cs, args.steps, timed)), flush=True)
         return
 
@@ -416,29 +449,14 @@ def main():
                         "alternating runs with and without)",
             "us_per_step": round(min(pre_runs), 2), "us_per_step_without": round(min(plain_runs), 2)}
         del raw
-        Nr, Tr = 256, 8
-        rr = gen.make_prefill(9, [Tr] * Nr, H=H, dk=dk, dv=dv, dtype="bf16")
-        pool = torch.from_numpy(gen.decode_state(9, Nr, H, dk, dv)).to(dev)
-        slots = torch.from_numpy(np.random.default_rng(9).permutation(Nr).astype(np.int32)).to(dev)
-        rin = dict(q=dq(rr.q), k=dq(rr.k), v=dq(rr.v), la=torch.from_numpy(rr.log_alpha).to(dev),
-                   beta=torch.from_numpy(rr.beta).to(dev))
-        o_r = torch.empty((Nr * Tr, H, dv), dtype=torch.bfloat16, device=dev)
-        rec_us = timed(lambda i: kdalib.decode_tokens(pool, rin["q"], rin["k"], rin["v"], rin["la"],
-                                                      rin["beta"], state_indices=slots,
-                                                      num_seqs=Nr, out=o_r), reps)
-        rec_bytes = Nr * H * (2 * dk * dv * 4 + Tr * PATH_BYTES_PER_TOKEN_HEAD)
-        rec_gbs = rec_bytes / (rec_us * 1e-6) / 1e9
-        options["decode_tokens"] = {
-            "workload": "pooled recurrent tokens: 256 seqs x 8 tokens, H=32, dk=dv=128, bf16, "
-                        "fp32 states in permuted slots", "us_per_call": round(rec_us, 2),
-            "algorithmic_bytes": rec_bytes, "achieved_GBs": round(rec_gbs, 1),
-            "frac_of_hbm_peak": round(rec_gbs / HBM_PEAK_GBS, 4)}
+        options["decode_tokens"] = decode_tokens_option(dev, reps, timed)
+        rec_us, rec_gbs = options["decode_tokens"]["us_per_call"], options["decode_tokens"]["achieved_GBs"]
         options["backward"] = backward_option(single, cs, 20, timed)
         bwd_us = options["backward"]["us_per_call"]
         log(f"[bench] options: chunk states +{cs_us - base_us:.1f} us, preprocessing "
             f"{min(pre_runs):.1f} us (plain {min(plain_runs):.1f}), decode_tokens {rec_us:.1f} us "
             f"= {rec_gbs:.0f} GB/s, backward {bwd_us:.0f} us")
-        del pool, cs
+        del cs
 
     if args.copy_calib:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
