@@ -201,9 +201,12 @@ kda_status kda_decode_step(float *state, const void *q, const void *k, const voi
  *                  as for kda_prefill_ex (tokens packed, cu_seqlens NULL = N
  *                  equal rows)
  *   o              [T,H,dv] dtype (device, written)
- * Meant for short runs (speculative verification, chunked decoding): the
- * tokens of one sequence are processed serially.  kda_decode_step is the
- * one-token, identity-slot case without options.
+ * Meant for short runs (speculative verification, chunked decoding).  For
+ * bf16 with dk = dv = 128 and more tokens than sequences the tokens of a
+ * sequence are taken 16 at a time in the chunkwise form (section 3; bf16
+ * products, fp32 state, the precision of kda_prefill); otherwise they are
+ * processed one by one, and one token per sequence with identity slots and
+ * no options equals kda_decode_step.
  */
 kda_status kda_decode_tokens(float *state_pool, int32_t num_slots, const int32_t *state_indices,
                              const void *q, const void *k, const void *v,
@@ -215,8 +218,9 @@ kda_status kda_decode_tokens(float *state_pool, int32_t num_slots, const int32_t
 /*
  * Device workspace kda_backward needs for these sizes (bytes, 256-aligned;
  * 0 for invalid sizes).  It covers a forward recomputation of the chunk
- * states (used when the caller passes none), per-slice partial gradients and
- * per-workgroup scratch.
+ * states (used when the caller passes none) and either the per-chunk records
+ * and fp32 gradients leaving every chunk of the chunkwise path or the
+ * per-slice partial gradients and per-workgroup scratch of the token walk.
  */
 size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H,
                                     int32_t dk, int32_t dv, kda_dtype dtype);
@@ -241,10 +245,14 @@ size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int3
  *   d_initial_state [N,H,dk,dv] fp32 (device, written), or NULL
  *   workspace     at least kda_backward_workspace_bytes(), or NULL with 0
  *                 (then allocated stream-ordered on `stream`)
- * Outputs must not alias inputs.  The result is deterministic.  The state is
- * walked token by token backwards (recomputed forward from the chunk states,
- * 8 tokens at a time): sequences are processed in parallel, their tokens in
- * order.
+ * Outputs must not alias inputs.  The result is deterministic.  bf16 with
+ * dk = dv = 128 runs the chunkwise backward: a reverse pass over the chunks
+ * (the transpose of each chunk's transition, from the last chunk to the
+ * first) gives the gradient leaving every chunk, then every chunk's input
+ * gradients are formed in parallel from its entry state and that gradient.
+ * Other configurations walk the tokens backwards (recomputed forward from the
+ * chunk states, 8 tokens at a time).  KDA_BACKWARD_SERIAL=1 in the
+ * environment selects the token walk for bf16 too.
  */
 kda_status kda_backward(const void *q, const void *k, const void *v,
                         const float *log_alpha, const float *beta,
