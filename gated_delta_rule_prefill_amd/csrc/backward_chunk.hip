@@ -35,9 +35,10 @@
 // channels (gathered from LDS or read from memory), the B operand a token
 // row read with one 16-byte LDS load, and each lane ends up with 4
 // consecutive channels of one token.  The 64 x 64 products (dA_qk, dT, X^T dX,
-// dA) split their 16 x 16 tiles over the waves.  S and dS are read straight
-// from memory into operand registers (fp32 -> bf16) in the two orientations
-// the products need.
+// dA) split their 16 x 16 tiles over the waves.  S and dS are read once each
+// with coalesced 16-byte loads and reach the MFMAs through a bf16 copy in LDS,
+// from which every wave gathers them in the two orientations the products
+// need.
 #include "kda_common.h"
 
 namespace kda {
@@ -211,17 +212,18 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
         *reinterpret_cast<bf16x8*>(sXT + r * LT + c8) = *reinterpret_cast<const bf16x8*>(rXT + r * CHUNK + c8);
         *reinterpret_cast<bf16x8*>(sAqT + r * LT + c8) = *reinterpret_cast<const bf16x8*>(rAqT + r * CHUNK + c8);
     }
-    // S and dS as A operands over the key channels c (for N and dN): lane row
-    // = value channel j = cl, slots c = 32s + 8g + m
-    bf16x8 sN_op[4], dsN_op[4];
+    // S and dS once each, coalesced: thread t takes rows (t >> 5) + 16e, columns
+    // 4(t & 31) .. +3 (e = 0..7).  They reach the MFMAs through a bf16 copy in
+    // LDS (S3 + S4, free until phase 1 writes -W), from which each wave
+    // gathers both operand orientations; the per-row sums of S * dS (gamma_C's
+    // dependence on g_C) come from the fp32 values.
+    f32x4 sv[8], dsv[8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int c = 32 * s + 8 * g + m;
-            sN_op[s][m] = (bf16)Sg[c * D + cl];
-            dsN_op[s][m] = (bf16)dSg[c * D + cl];
-        }
+    for (int e = 0; e < 8; ++e) {
+        const int at = ((t >> 5) + 16 * e) * D + 4 * (t & 31);
+        sv[e] = *reinterpret_cast<const f32x4*>(Sg + at);
+        dsv[e] = *reinterpret_cast<const f32x4*>(dSg + at);
+    }
     // v as A operands over the tokens (for U): lane row j = cl, slots i = 32s + 8g + m
     bf16x8 vop[2];
 #pragma unroll
@@ -231,7 +233,29 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
             const int i = 32 * s + 8 * g + m;
             vop[s][m] = i < len ? v[row_at(i) * D + cl] : (bf16)0.f;
         }
+    bf16* sSt = reinterpret_cast<bf16*>(smem + CG_OFF_S3);   // [128][LR] staging of S, then dS
+    static_assert(D * CG_LR * 2 <= 2 * CG_SLOT, "S staging spans S3 and S4");
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int c = (t >> 5) + 16 * e;
+        *reinterpret_cast<bf16x4*>(sSt + c * LR + 4 * (t & 31)) = to_bf16x4(sv[e]);
+        float sd = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sd += sv[e][i] * dsv[e][i];
+        sd = row16_sum(sd);
+        sd += lane_xor<16>(sd);   // the 32 lanes of the row
+        if ((t & 31) == 0) sExt[c] = sd;
+    }
     __syncthreads();
+    // S as A operands over the key channels c (for N; lane row = value channel
+    // j = cl, slots c = 32s + 8g + m) and over the value channels j (for dQg,
+    // dW; lane row = key channel c = cl, slots j = 32s + 8g + m)
+    bf16x8 sN_op[4], sQ_op[4], dsN_op[4], dsQ_op[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        sN_op[s] = gather8(sSt + (32 * s + 8 * g) * LR + cl, LR);
+        sQ_op[s] = lds8(sSt + cl * LR + 32 * s + 8 * g);
+    }
     {
         float B = 0.f;
         for (int qd = 0; qd < sq; ++qd) B += sTot[qd * D + sc];
@@ -241,6 +265,16 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
         if (sq == 3) sBref[4 * D + sc] = B + sTot[3 * D + sc];
     }
     __syncthreads();
+    // dS in S's place, its operands like S's (dKhat = N dS^T, dN = dS^T Khat^T)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<bf16x4*>(sSt + ((t >> 5) + 16 * e) * LR + 4 * (t & 31)) = to_bf16x4(dsv[e]);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        dsN_op[s] = gather8(sSt + (32 * s + 8 * g) * LR + cl, LR);
+        dsQ_op[s] = lds8(sSt + cl * LR + 32 * s + 8 * g);
+    }
 
     // T = X Diag(beta) as the B operand of token block R, step s: lane column
     // r = 16R + ln, slots i = 32s + 8g + m
@@ -263,6 +297,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
     // ---------------- phase 1: W^T = (e^g K)^T T^T and U^T = V^T T^T -------------
     f32x4 accU[4];
     {
+        f32x4 aws[4];
         bf16x8 kg[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -281,9 +316,12 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
                 au = mma32(vop[s], tb, au);
             }
             accU[R] = au;
-            // lane: W[16R + ln][co + i]; stored negated for N = U - W S
-            *reinterpret_cast<bf16x4*>(sW + (16 * R + ln) * LR + co) = to_bf16x4(aw, -1.f);
+            aws[R] = aw;
         }
+        __syncthreads();   // every wave has its dS operands: -W may overwrite the staging
+#pragma unroll
+        for (int R = 0; R < 4; ++R)   // lane: W[16R + ln][co + i]; stored negated for N = U - W S
+            *reinterpret_cast<bf16x4*>(sW + (16 * R + ln) * LR + co) = to_bf16x4(aws[R], -1.f);
     }
     __syncthreads();
 
@@ -294,30 +332,6 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
 #pragma unroll
         for (int s = 0; s < 4; ++s) a = mma32(sN_op[s], lds8(sW + (16 * R + ln) * LR + 32 * s + 8 * g), a);
         *reinterpret_cast<bf16x4*>(sN + (16 * R + ln) * LR + co) = to_bf16x4(a);
-    }
-    // S and dS as A operands over the value channels j (for dQg, dW, dKhat):
-    // lane row = key channel c = cl, slots j = 32s + 8g + m; and the
-    // per-channel sum of S * dS for gamma_C's dependence on g_C
-    bf16x8 sQ_op[4], dsQ_op[4];
-    {
-        float sd = 0.f;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const float* ps = Sg + (size_t)cl * D + 32 * s + 8 * g;
-            const float* pd = dSg + (size_t)cl * D + 32 * s + 8 * g;
-            const f32x4 s0 = *reinterpret_cast<const f32x4*>(ps), s1 = *reinterpret_cast<const f32x4*>(ps + 4);
-            const f32x4 d0 = *reinterpret_cast<const f32x4*>(pd), d1 = *reinterpret_cast<const f32x4*>(pd + 4);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                sQ_op[s][m] = (bf16)s0[m];
-                sQ_op[s][4 + m] = (bf16)s1[m];
-                dsQ_op[s][m] = (bf16)d0[m];
-                dsQ_op[s][4 + m] = (bf16)d1[m];
-                sd += s0[m] * d0[m] + s1[m] * d1[m];
-            }
-        }
-        sd = group4_sum(sd);
-        if (g == 0) sExt[cl] = sd;
     }
     __syncthreads();
 

@@ -141,3 +141,46 @@ def test_backward_long_packed():
     every chunk."""
     x, d_o, d_fin = _case(82, [1500, 64, 2000, 531], 4, 128, 128, "bf16")
     _check(x, d_o, d_fin, "long packed")
+
+
+_SERIAL_CHILD = r"""
+import sys, numpy as np, torch
+root = sys.argv[1]
+sys.path.insert(0, root); sys.path.insert(0, root + '/tests')
+import oracle
+import gated_delta_rule_prefill_amd as kda
+from gated_delta_rule_prefill_amd import inputs as gen
+from gpu_util import TOL, dev_f32, dev_qkv, device_inputs, host, rel_l2
+x = gen.make_prefill(83, [150, 1, 77], H=2, dk=128, dv=128, dtype="bf16", state_std=0.02)
+g = np.random.default_rng(83)
+d_o = gen.bf16_bits(g.standard_normal((x.T, 2, 128)).astype(np.float32))
+d_fin = g.standard_normal((x.num_seqs, 2, 128, 128)).astype(np.float32)
+d = device_inputs(x)
+gr = kda.backward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], dev_qkv(d_o),
+                  d["initial_state"], d["cu_seqlens"], num_seqs=x.num_seqs,
+                  d_final_state=dev_f32(d_fin))
+torch.cuda.synchronize()
+ref = oracle.backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.initial_state, x.cu_seqlens,
+                      gen.as_f32(d_o).astype(np.float64), d_fin.astype(np.float64),
+                      num_seqs=x.num_seqs)
+for n in ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dinitial_state"):
+    e = rel_l2(host(gr[n]), ref[n])
+    print(f"[backward serial] {n}={e:.2e}", flush=True)
+    assert e <= TOL["bf16"], (n, e)
+print("RESULT|ok", flush=True)
+"""
+
+
+def test_backward_token_walk_selected_by_environment():
+    """KDA_BACKWARD_SERIAL=1 (read once per process) sends bf16 at d = 128
+    through the token-serial kernels; a child process checks them against the
+    oracle on a packed batch with a one-token sequence."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, KDA_BACKWARD_SERIAL="1")
+    r = subprocess.run([sys.executable, "-u", "-c", _SERIAL_CHILD, root], env=env,
+                       capture_output=True, text=True, timeout=600)
+    print(r.stdout[-2000:], r.stderr[-2000:])
+    assert r.returncode == 0 and "RESULT|ok" in r.stdout
