@@ -5,7 +5,8 @@
 // W = T (e^g K) and U = T V with T = (I + A_kk)^{-1} Diag(beta); the chunk
 // reads the entering state S through O = Qg S + A_qk N, N = U - W S, and
 // leaves S' = Diag(gamma_C) S + Khat^T N).  With S (the forward's chunk
-// state) and dS (the gradient leaving the chunk, from the reverse chain) every
+// state) and dS (the gradient leaving the chunk, from the reverse chain, in
+// bf16) every
 // input gradient of the chunk is local to it:
 //
 //   dN  = A_qk^T dO + Khat dS             dQg = dO S^T      dKhat = N dS^T
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const bf16* __restrict__ d_o, const ChunkSrc src, int H,
     const unsigned char* __restrict__ rec, const float* __restrict__ chunk_states,
-    const float* __restrict__ dS_chunks, bf16* __restrict__ dq, bf16* __restrict__ dk,
+    const bf16* __restrict__ dS_chunks, bf16* __restrict__ dq, bf16* __restrict__ dk,
     bf16* __restrict__ dv, float* __restrict__ dla, float* __restrict__ dbeta)
 {
     constexpr int D = 128;
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
     const bf16* rXT = rX + CHUNK * CHUNK;
     const bf16* rAqT = reinterpret_cast<const bf16*>(rec + chh * RL.bytes + RL.oi);
     const float* Sg = chunk_states + chh * D * D;
-    const float* dSg = dS_chunks + chh * D * D;
+    const bf16* dSg = dS_chunks + chh * D * D;   // bf16, as the reverse chain writes it
     auto row_at = [&](int r) { return ((size_t)ci.start + r) * H + h; };   // token row r of the chunk
 
     const int t = threadIdx.x;
@@ -217,12 +218,13 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
     // LDS (S3 + S4, free until phase 1 writes -W), from which each wave
     // gathers both operand orientations; the per-row sums of S * dS (gamma_C's
     // dependence on g_C) come from the fp32 values.
-    f32x4 sv[8], dsv[8];
+    f32x4 sv[8];
+    bf16x4 dsv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int at = ((t >> 5) + 16 * e) * D + 4 * (t & 31);
         sv[e] = *reinterpret_cast<const f32x4*>(Sg + at);
-        dsv[e] = *reinterpret_cast<const f32x4*>(dSg + at);
+        dsv[e] = *reinterpret_cast<const bf16x4*>(dSg + at);
     }
     // v as A operands over the tokens (for U): lane row j = cl, slots i = 32s + 8g + m
     bf16x8 vop[2];
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
         *reinterpret_cast<bf16x4*>(sSt + c * LR + 4 * (t & 31)) = to_bf16x4(sv[e]);
         float sd = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sd += sv[e][i] * dsv[e][i];
+        for (int i = 0; i < 4; ++i) sd += sv[e][i] * (float)dsv[e][i];
         sd = row16_sum(sd);
         sd += lane_xor<16>(sd);   // the 32 lanes of the row
         if ((t & 31) == 0) sExt[c] = sd;
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
     // dS in S's place, its operands like S's (dKhat = N dS^T, dN = dS^T Khat^T)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<bf16x4*>(sSt + ((t >> 5) + 16 * e) * LR + 4 * (t & 31)) = to_bf16x4(dsv[e]);
+        *reinterpret_cast<bf16x4*>(sSt + ((t >> 5) + 16 * e) * LR + 4 * (t & 31)) = dsv[e];
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -711,7 +713,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
 hipError_t launch_chunk_grad(const void* q, const void* k, const void* v, const float* la,
                              const float* beta, const void* d_o, ChunkSrc src, int max_chunks,
                              int H, int dk, int dv, const void* rec, const float* chunk_states,
-                             const float* dS_chunks, void* dq, void* dk_out, void* dv_out,
+                             const void* dS_chunks, void* dq, void* dk_out, void* dv_out,
                              float* dla, float* dbeta, hipStream_t stream)
 {
     if (dk != 128 || dv != 128) return hipErrorInvalidValue;
@@ -719,7 +721,7 @@ hipError_t launch_chunk_grad(const void* q, const void* k, const void* v, const 
     hipLaunchKernelGGL(chunk_grad_kernel, dim3((unsigned)max_chunks * H), dim3(64 * CG_WAVES), 0,
                        stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta,
                        (const bf16*)d_o, src, H, (const unsigned char*)rec, chunk_states,
-                       dS_chunks, (bf16*)dq, (bf16*)dk_out, (bf16*)dv_out, dla, dbeta);
+                       (const bf16*)dS_chunks, (bf16*)dq, (bf16*)dk_out, (bf16*)dv_out, dla, dbeta);
     return hipGetLastError();
 }
 

@@ -127,7 +127,7 @@ bool make_bwd_plan(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_
     b.off_dsc = at;
     const size_t serial = align256(kda::backward_partial_bytes(T, H, dk, dv)) +
                           align256(kda::backward_scratch_bytes(N, H, dk, dv));
-    const size_t dsc = align256((size_t)b.fwd.max_chunks * H * dk * dv * 4);
+    const size_t dsc = align256((size_t)b.fwd.max_chunks * H * dk * dv * 2);   // bf16
     b.off_scratch = at + align256(kda::backward_partial_bytes(T, H, dk, dv));
     at += std::max(serial, dsc);
     b.total = at;
@@ -472,7 +472,7 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const float
             // reverse-chain records over the forward's, the chain (gradient
             // leaving every chunk, and entering each sequence), then the
             // per-chunk gradients
-            float* dsc = reinterpret_cast<float*>(ws + b.off_dsc);
+            void* dsc = ws + b.off_dsc;
             const int mc = (int)plan.max_chunks;
             st = check_launch(kda::launch_reverse_records(q, k, v, log_alpha, beta, d_o, src, mc, H,
                                                           dk, dv, ws, stream),

@@ -95,24 +95,24 @@ hipError_t launch_prefill_chain2(const void* rec, ChunkSrc src, const float* S0,
 // then runs dS_in = Diag(gamma_C) dS + PM^T dS + E from the last chunk of
 // each sequence to the first, starting from dS_last (the final-state
 // gradient, NULL = 0); dS_chunks receives the gradient leaving every chunk
-// ([chunk][H][dk][dv] fp32, chunk-state rows) and dS_first (or NULL) the
-// gradient entering each sequence's first chunk.
+// ([chunk][H][dk][dv] bf16, chunk-state rows) and dS_first (or NULL, fp32)
+// the gradient entering each sequence's first chunk.
 hipError_t launch_reverse_records(const void* q, const void* k, const void* v, const float* la,
                                   const float* beta, const void* d_o, ChunkSrc src, int max_chunks,
                                   int H, int dk, int dv, void* rec, hipStream_t stream);
 hipError_t launch_reverse_chain(const void* rec, ChunkSrc src, const float* dS_last,
-                                float* dS_first, float* dS_chunks, int H, int dk, int dv,
+                                float* dS_first, void* dS_chunks, int H, int dk, int dv,
                                 hipStream_t stream);
 
 // Per-chunk gradients of the chunkwise backward (bf16, dk = dv = 128): rec
 // holds the reverse-chain records (for X, X^T and A_qk^T), chunk_states the
-// state entering every chunk and dS_chunks the gradient leaving it (both
-// [chunk][H][dk][dv] fp32, rows = table chunks).  Writes dq, dk, dv, dlog_alpha
-// and dbeta of every token.
+// state entering every chunk ([chunk][H][dk][dv] fp32) and dS_chunks the
+// gradient leaving it ([chunk][H][dk][dv] bf16; rows = table chunks).  Writes
+// dq, dk, dv, dlog_alpha and dbeta of every token.
 hipError_t launch_chunk_grad(const void* q, const void* k, const void* v, const float* la,
                              const float* beta, const void* d_o, ChunkSrc src, int max_chunks,
                              int H, int dk, int dv, const void* rec, const float* chunk_states,
-                             const float* dS_chunks, void* dq, void* dk_out, void* dv_out,
+                             const void* dS_chunks, void* dq, void* dk_out, void* dv_out,
                              float* dla, float* dbeta, hipStream_t stream);
 
 // Whether a configuration runs the LDS-ring sequential kernel (its ring fits),

@@ -594,15 +594,23 @@ __global__ __launch_bounds__((64 * RingCfg<E, DK, DV>::WAVES)) void prefill_stat
         // chunk-start state `it` (in cst since the barrier that ended chunk it - 1;
         // rewritten only after the barrier that ends chunk it) to chunk_states,
         // fp32 [chunk][H][DK][DV]: 16-byte stores of 4 columns of a row
+        // (the reverse chain's are gradients for the gradient kernel, which takes
+        // them as bf16 MFMA operands: they go out in bf16)
         auto send_state = [&](int it) {
-            float* cs = chunk_states + (chunk_state_row(src, s, c_begin, chunk_at(it)) * H + h) * DK * DV + j0;
+            const size_t at = (chunk_state_row(src, s, c_begin, chunk_at(it)) * H + h) * DK * DV + j0;
 #pragma unroll
             for (int k = 0; k < DK * 4 / 64; ++k) {
                 const int u = l + 64 * k, row = u >> 2, qd = u & 3;
                 const f32x4 val = {cst[it % C::NX][4 * qd][row], cst[it % C::NX][4 * qd + 1][row],
                                    cst[it % C::NX][4 * qd + 2][row], cst[it % C::NX][4 * qd + 3][row]};
                 // streaming stores: the records this kernel still has to read stay cached
-                __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(cs + (size_t)row * DV + 4 * qd));
+                if (reverse) {
+                    const bf16x4 b = {(bf16)val[0], (bf16)val[1], (bf16)val[2], (bf16)val[3]};
+                    __builtin_nontemporal_store(b, reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(chunk_states) + at +
+                                                                             (size_t)row * DV + 4 * qd));
+                } else {
+                    __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(chunk_states + at + (size_t)row * DV + 4 * qd));
+                }
             }
         };
         auto step = [&](TouchSet& tv, int it) {
@@ -750,7 +758,7 @@ static hipError_t launch_state_ring(const void* rec, ChunkSrc src, const float* 
 }
 
 hipError_t launch_reverse_chain(const void* rec, ChunkSrc src, const float* dS_last,
-                                float* dS_first, float* dS_chunks, int H, int dk, int dv,
+                                float* dS_first, void* dS_chunks, int H, int dk, int dv,
                                 hipStream_t stream)
 {
     if (dk != 128 || dv != 128) return hipErrorInvalidValue;
@@ -759,7 +767,7 @@ hipError_t launch_reverse_chain(const void* rec, ChunkSrc src, const float* dS_l
     const long long blocks = (long long)((n_pairs + 7) / 8) * 8 * C::NSL;
     hipLaunchKernelGGL((prefill_state_ring_kernel<bf16, 128, 128>), dim3((unsigned)blocks),
                        dim3(64 * C::WAVES), 0, stream, (const unsigned char*)rec, src, dS_last,
-                       dS_first, (bf16*)nullptr, dS_chunks, H, n_pairs, 1);
+                       dS_first, (bf16*)nullptr, (float*)dS_chunks, H, n_pairs, 1);
     return hipGetLastError();
 }
 

@@ -219,7 +219,7 @@ kda_status kda_decode_tokens(float *state_pool, int32_t num_slots, const int32_t
  * Device workspace kda_backward needs for these sizes (bytes, 256-aligned;
  * 0 for invalid sizes).  It covers a forward recomputation of the chunk
  * states (used when the caller passes none) and either the per-chunk records
- * and fp32 gradients leaving every chunk of the chunkwise path or the
+ * and bf16 gradients leaving every chunk of the chunkwise path or the
  * per-slice partial gradients and per-workgroup scratch of the token walk.
  */
 size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H,

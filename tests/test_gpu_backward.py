@@ -184,3 +184,30 @@ def test_backward_token_walk_selected_by_environment():
                        capture_output=True, text=True, timeout=600)
     print(r.stdout[-2000:], r.stderr[-2000:])
     assert r.returncode == 0 and "RESULT|ok" in r.stdout
+
+
+def test_backward_long_context_sampled_heads():
+    """The headline length: one 65,536-token sequence, H = 32, bf16, d = 128
+    (1,024 chunks: the reverse chain over the whole sequence).  Two heads,
+    the first and the last, are compared with the oracle over every token,
+    together with their initial-state gradients."""
+    T, H = 65536, 32
+    x = gen.make_prefill(84, [T], H=H, dk=128, dv=128, dtype="bf16", mu=4.0, state_std=0.02)
+    g = np.random.default_rng(84)
+    d_o = gen.bf16_bits(g.standard_normal((T, H, 128)).astype(np.float32))
+    d_fin = g.standard_normal((1, H, 128, 128)).astype(np.float32)
+    gr = _gpu_backward(x, d_o, d_fin)
+    heads = [0, H - 1]
+
+    def sub(a):
+        return np.ascontiguousarray(a[:, heads])
+
+    ref = oracle.backward(sub(x.q), sub(x.k), sub(x.v), sub(x.log_alpha), sub(x.beta),
+                          sub(x.initial_state), None, gen.as_f32(sub(d_o)).astype(np.float64),
+                          sub(d_fin).astype(np.float64), num_seqs=1)
+    for n in GRADS:
+        got = host(gr[n][:, heads])
+        for j, hd in enumerate(heads):
+            e = rel_l2(got[:, j], ref[n][:, j])
+            print(f"[backward long] head {hd} {n}={e:.2e}", flush=True)
+            assert e <= TOL["bf16"], (hd, n, e)
