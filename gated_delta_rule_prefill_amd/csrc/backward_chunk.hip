@@ -170,7 +170,10 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
     const bf16* rAqT = reinterpret_cast<const bf16*>(rec + chh * RL.bytes + RL.oi);
     const float* Sg = chunk_states + chh * D * D;
     const bf16* dSg = dS_chunks + chh * D * D;   // bf16, as the reverse chain writes it
-    auto row_at = [&](int r) { return ((size_t)ci.start + r) * H + h; };   // token row r of the chunk
+    const size_t r0 = (size_t)ci.start * H + h;
+    const int HD = H * D;
+    const bf16 *qB = q + r0 * D, *kB = k + r0 * D, *vB = v + r0 * D, *oB = d_o + r0 * D;
+    const float* laB = log_alpha + r0 * D;
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
     const int co = cw + 4 * g;      // the lane's 4 output channels
 
     // ---------------- phase 0: loads ------------------------------------------
-    if (t < CHUNK) sBeta[t] = t < len ? beta[row_at(t)] : 0.f;
+    if (t < CHUNK) sBeta[t] = t < len ? beta[r0 + (size_t)t * H] : 0.f;
     // log_alpha: thread (column c, 16-row block qd), cumulative sum inside the block
     const int sc = t & (D - 1), sq = t >> 7;
     float gl[16];
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int r = 16 * sq + u;
-            run += r < len ? log_alpha[row_at(r) * D + sc] : 0.f;
+            run += r < len ? laB[r * HD + sc] : 0.f;
             gl[u] = run;
         }
         sTot[sq * D + sc] = run;
@@ -201,8 +204,8 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
         const int u = t + 512 * e, r = u >> 4, c8 = 8 * (u & 15);
         bf16x8 kv = {}, dv8 = {};
         if (r < len) {
-            kv = *reinterpret_cast<const bf16x8*>(k + row_at(r) * D + c8);
-            dv8 = *reinterpret_cast<const bf16x8*>(d_o + row_at(r) * D + c8);
+            kv = *reinterpret_cast<const bf16x8*>(kB + r * HD + c8);
+            dv8 = *reinterpret_cast<const bf16x8*>(oB + r * HD + c8);
         }
         *reinterpret_cast<bf16x8*>(sK + r * LR + c8) = kv;
         *reinterpret_cast<bf16x8*>(sDO + r * LR + c8) = dv8;
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const int i = 32 * s + 8 * g + m;
-            vop[s][m] = i < len ? v[row_at(i) * D + cl] : (bf16)0.f;
+            vop[s][m] = i < len ? vB[i * HD + cl] : (bf16)0.f;
         }
     bf16* sSt = reinterpret_cast<bf16*>(smem + CG_OFF_S3);   // [128][LR] staging of S, then dS
     static_assert(D * CG_LR * 2 <= 2 * CG_SLOT, "S staging spans S3 and S4");
@@ -374,7 +377,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
     for (int e = 0; e < 2; ++e) {
         const int u = t + 512 * e, r = u >> 4, c8 = 8 * (u & 15);
         vrow[e] = bf16x8{};
-        if (r < len) vrow[e] = *reinterpret_cast<const bf16x8*>(v + row_at(r) * D + c8);
+        if (r < len) vrow[e] = *reinterpret_cast<const bf16x8*>(vB + r * HD + c8);
     }
     __syncthreads();
 #pragma unroll
@@ -479,7 +482,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
                 ag = mma32(dwop[s], tb, ag);
             }
             const int r = 16 * R + ln;
-            if (r < len) *reinterpret_cast<bf16x4*>(dv + row_at(r) * D + co) = to_bf16x4(av);
+            if (r < len) *reinterpret_cast<bf16x4*>(dv + r0 * D + r * HD + co) = to_bf16x4(av);
             const f32x4 B4 = lds4f(sBref + R * D + co);
 #pragma unroll
             for (int i = 0; i < 4; ++i) a2[R][i] = fast_exp(B4[i]) * ag[i];
@@ -503,7 +506,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
     for (int e = 0; e < 2; ++e) {
         const int u = t + 512 * e, r = u >> 4, c8 = 8 * (u & 15);
         qrow[e] = bf16x8{};
-        if (r < len) qrow[e] = *reinterpret_cast<const bf16x8*>(q + row_at(r) * D + c8);
+        if (r < len) qrow[e] = *reinterpret_cast<const bf16x8*>(qB + r * HD + c8);
     }
     __syncthreads();
     // lane: dT[16Rr + 4g + i][16Ri + ln]; then dbeta's column term and dX^T
@@ -677,8 +680,8 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
             dg4[i] = r < len ? (float)q4[i] * dq4[i] + (float)k4[i] * (kP - kI) : 0.f;
         }
         if (r < len) {
-            *reinterpret_cast<bf16x4*>(dq + row_at(r) * D + co) = to_bf16x4(dq4);
-            *reinterpret_cast<bf16x4*>(dk + row_at(r) * D + co) = to_bf16x4(dk4);
+            *reinterpret_cast<bf16x4*>(dq + r0 * D + r * HD + co) = to_bf16x4(dq4);
+            *reinterpret_cast<bf16x4*>(dk + r0 * D + r * HD + co) = to_bf16x4(dk4);
         }
         *reinterpret_cast<f32x4*>(sScan + r * LG + co) = dg4;
     }
@@ -698,7 +701,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int r = 16 * sq + u;
-            if (r < len) dla[row_at(r) * D + sc] = suf[u] + later;
+            if (r < len) dla[r0 * D + r * HD + sc] = suf[u] + later;
         }
     }
     if (t < len) {
@@ -706,7 +709,7 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
         for (int R = t >> 4; R < 4; ++R) b += sDBC[R * CHUNK + t];
 #pragma unroll
         for (int x = 0; x < CG_WAVES; ++x) b += sDBR[x * CHUNK + t];
-        dbeta[row_at(t)] = b;
+        dbeta[r0 + (size_t)t * H] = b;
     }
 }
 
