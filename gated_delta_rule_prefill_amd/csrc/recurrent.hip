@@ -188,11 +188,27 @@ __global__ __launch_bounds__(64 * (DV / 32)) void recurrent_kernel(
 // once per chunk by VALU (the Diag(e^{g_C}) scaling and its bf16 operand
 // copy) instead of four times per token, and the path is bound by the state's
 // read and write.  Products over the chunk's tokens use the 16x16x32 MFMA
-// with the upper 16 contraction slots zero.
+// with the upper 16 contraction slots zero.  The token data are staged by
+// every thread alike (one token row, four channels), the cumulative decay
+// summed across the lanes of a row; at under 80 registers per lane three
+// workgroups share a CU.
 constexpr int RC = 16;   // tokens per chunk
 
+// Inclusive prefix sum over the 16 lanes of a row, in lane order (row shifts
+// by 1, 2, 4 and 8; lanes before the row's start read 0).
+template <int SH>
+__device__ __forceinline__ float row_shr_or_0(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + SH, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_scan(float x) {
+    x += row_shr_or_0<1>(x);
+    x += row_shr_or_0<2>(x);
+    x += row_shr_or_0<4>(x);
+    return x + row_shr_or_0<8>(x);
+}
+
 template <bool NORM>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void recurrent_mfma_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NORM ? 4 : 6, NORM ? 4 : 6))) void recurrent_mfma_kernel(
     float* __restrict__ pool, int num_slots, const int32_t* __restrict__ slots,
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
@@ -208,14 +224,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     __shared__ __attribute__((aligned(16))) bf16 sKgT[D * LT], sKhT[D * LT], sVT[D * LT];
     __shared__ __attribute__((aligned(16))) bf16 sT[RC * LT], sAq[RC * LT];
     __shared__ __attribute__((aligned(16))) float sBeta[RC], sGam[D];
+    __shared__ float sNrm[2][8][RC];   // per-wave partial squared norms of the q and k rows
     bf16* sW = reinterpret_cast<bf16*>(sG);
-    static_assert(RC * LK * 2 <= RC * LG * 4, "-W fits over g");
+    static_assert(RC * LK * 2 <= RC * LG * 4, "-W fits over sG");
+
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    // Lane indices.  refresh() derives them anew from an opaque copy of the
+    // thread index at the start of every chunk, so that the compiler does not
+    // hoist the many values derived from them out of the chunk loop (held
+    // across it, they would not fit the registers).
+    int t, lane, g, ln, j, c4;
+    auto refresh = [&]() {
+        t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        lane = t & 63;
+        g = lane >> 4;
+        ln = lane & 15;
+        j = 16 * w + ln;    // the lane's value column in the state tiles
+        c4 = 4 * (t >> 4);  // staging: token row ln, channels c4 .. c4 + 3
+    };
+    refresh();
 
     const int u = blockIdx.x;   // sequence * H + head
     const int seq = u / H, h = u % H;
-    const int t = threadIdx.x;
-    const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int g = lane >> 4, ln = lane & 15;
     int t0, t1;
     if (cu) {
         t0 = cu[seq];
@@ -231,109 +262,123 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         return;
     }
     if (t1 <= t0) return;
-    float* S = pool + ((size_t)slot * H + h) * D * D;
-    const int j = 16 * w + ln;   // the lane's value column in the state tiles
+
+    // A chunk's token data, loaded into registers ahead of the chunk: thread
+    // (token row ln, channels c4 .. c4 + 3) holds its q, k, v and log_alpha
+    // and the row's beta.  Rows past the chunk's end re-read its last row (and
+    // count as zero).  Every thread loads the same kinds, so the wait for them
+    // is exact on every path.
+    bf16x4 qv, kv, vv;
+    f32x4 lv;
+    float bv;
+    auto load_tokens = [&](int tb, int nt) {
+        const size_t row = (size_t)(tb + min(ln, nt - 1)) * H + h;
+        qv = *reinterpret_cast<const bf16x4*>(q + row * D + c4);
+        kv = *reinterpret_cast<const bf16x4*>(k + row * D + c4);
+        vv = *reinterpret_cast<const bf16x4*>(v + row * D + c4);
+        lv = *reinterpret_cast<const f32x4*>(log_alpha + row * D + c4);
+        bv = beta[row];
+    };
 
     // The state through a buffer resource: the lane's part of each address in
-    // one register, the element's constant part as the scalar offset.
-    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(S, (short)0, D * D * 4, 0x00020000);
-    const int voff = (4 * g * D + j) * 4;
+    // one register, the row within a 16-row block as the immediate offset and
+    // the block as the scalar offset.
     f32x4 st[8];   // st[cb]: lane holds S[16cb + 4g + i][j]
+    const __amdgpu_buffer_rsrc_t srs =
+        __builtin_amdgcn_make_buffer_rsrc(pool + ((size_t)slot * H + h) * D * D, (short)0, D * D * 4, 0x00020000);
+    auto load_state = [&]() {
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
+        for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            st[cb][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, voff, (16 * cb + i) * D * 4, 0));
+            for (int i = 0; i < 4; ++i)
+                st[cb][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                          srs, (4 * g * D + j + i * D) * 4, cb * 16 * D * 4, 0));
+    };
+    auto store_state = [&]() {
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = st[cb][i];   // a bit cast of a vector element in place reads element 0
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), srs,
+                                                      (4 * g * D + j + i * D) * 4, cb * 16 * D * 4, 0);
+            }
+    };
 
     // operand of 4 consecutive tokens (slots 0..3) with the upper slots zero
     auto half8 = [](const bf16* p) {
         const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
         return bf16x8{a[0], a[1], a[2], a[3], (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
     };
-    // staging (waves 0-3): token row tr, channels c8 .. c8 + 7
-    const int tr = (t >> 4) & (RC - 1), c8 = 8 * (t & 15);
 
-    for (int tb = t0; tb < t1; tb += RC) {
-        const int nt = min(RC, t1 - tb);
+    // One chunk [tb, tb + nt), its token data in the registers.
+    auto chunk = [&](int tb, int nt) {
         __syncthreads();   // the previous chunk's operands are consumed
-        // ---- stage: q, k, v rows (waves 0-3), g (waves 4-5), beta (wave 6) --------
-        bf16x8 qv = {}, kv = {}, vv = {};
-        if (w < 4) {
-            if (tr < nt) {
-                const size_t row = ((size_t)(tb + tr) * H + h) * D + c8;
-                qv = *reinterpret_cast<const bf16x8*>(q + row);
-                kv = *reinterpret_cast<const bf16x8*>(k + row);
-                vv = *reinterpret_cast<const bf16x8*>(v + row);
-            }
-        } else if (w < 6) {
-            // rows past the chunk's end re-read its last row (added as 0)
-            const int c = t - 256;
-            const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<float*>(log_alpha) + ((size_t)tb * H + h) * D, (short)0, 0x7fffffff, 0x00020000);
-            float lv[RC];
+        // ---- decayed operands: thread (token row ln, channels c4 .. c4 + 3) ---------
+        {
+            const bool live = ln < nt;
+            float qf[4], kf[4], gl[4], gc[4];
 #pragma unroll
-            for (int r = 0; r < RC; ++r)
-                lv[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                      lrs, c * 4, min(r, nt - 1) * H * D * 4, 0));
-            float run = 0.f;
-#pragma unroll
-            for (int r = 0; r < RC; ++r) {
-                run += r < nt ? lv[r] : 0.f;
-                sG[r * LG + c] = run;
-            }
-            sGam[c] = fast_exp(run);
-        } else if (w == 6 && lane < RC) {
-            const float b = beta[(size_t)(tb + min(lane, nt - 1)) * H + h];
-            sBeta[lane] = lane < nt ? (beta_logit ? sigmoid(b) : b) : 0.f;
-        }
-        __syncthreads();
-        // ---- decayed operands (waves 0-3) -------------------------------------------
-        if (w < 4) {
-            float qf[8], kf[8];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                qf[m] = (float)qv[m];
-                kf[m] = (float)kv[m];
+            for (int m = 0; m < 4; ++m) {
+                qf[m] = live ? (float)qv[m] : 0.f;
+                kf[m] = live ? (float)kv[m] : 0.f;
+                // cumulative log-decay over the chunk: the row's lanes hold tokens 0 .. 15
+                gl[m] = row16_scan(live ? lv[m] : 0.f);
+                gc[m] = __shfl(gl[m], (lane & 48) | 15);   // the chunk's total
             }
             if constexpr (NORM) {
+                // squared norms over the row's 32 channel quads: lanes xor 16 and
+                // 32 of the wave, then the 8 waves
                 float sq = 0.f, sk = 0.f;
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
+                for (int m = 0; m < 4; ++m) {
                     sq += qf[m] * qf[m];
                     sk += kf[m] * kf[m];
                 }
-                const float iq = rsqrtf(row16_sum(sq) + L2NORM_EPS), ik = rsqrtf(row16_sum(sk) + L2NORM_EPS);
+                sq += lane_xor<16>(sq);
+                sk += lane_xor<16>(sk);
+                sq += lane_xor<32>(sq);
+                sk += lane_xor<32>(sk);
+                if (lane < RC) {
+                    sNrm[0][w][lane] = sq;
+                    sNrm[1][w][lane] = sk;
+                }
+                __syncthreads();
+                float tq = 0.f, tk = 0.f;
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
+                for (int x = 0; x < 8; ++x) {
+                    tq += sNrm[0][x][ln];
+                    tk += sNrm[1][x][ln];
+                }
+                const float iq = rsqrtf(tq + L2NORM_EPS), ik = rsqrtf(tk + L2NORM_EPS);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
                     qf[m] *= iq;
                     kf[m] *= ik;
                 }
             }
-            const f32x4 g0 = *reinterpret_cast<const f32x4*>(sG + tr * LG + c8);
-            const f32x4 g1 = *reinterpret_cast<const f32x4*>(sG + tr * LG + c8 + 4);
-            const f32x4 e0 = *reinterpret_cast<const f32x4*>(sG + (RC - 1) * LG + c8);
-            const f32x4 e1 = *reinterpret_cast<const f32x4*>(sG + (RC - 1) * LG + c8 + 4);
-            bf16x8 kg, ki, qg;
+            bf16x4 kg, ki, qg;
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const float gm = m < 4 ? g0[m] : g1[m - 4], gc = m < 4 ? e0[m] : e1[m - 4];
-                const float eg = fast_exp(gm);
+            for (int m = 0; m < 4; ++m) {
+                const float eg = fast_exp(gl[m]);
                 kg[m] = (bf16)(kf[m] * eg);
-                ki[m] = (bf16)(kf[m] * fast_exp(fminf(-gm, 80.f)));
+                ki[m] = (bf16)(kf[m] * fast_exp(fminf(-gl[m], 80.f)));
                 qg[m] = (bf16)(qf[m] * eg);
-                const int c = c8 + m;
-                sKgT[c * LT + tr] = kg[m];
-                sKhT[c * LT + tr] = (bf16)(kf[m] * fast_exp(gc - gm));
-                sVT[c * LT + tr] = vv[m];
+                const int c = c4 + m;
+                sKgT[c * LT + ln] = kg[m];
+                sKhT[c * LT + ln] = (bf16)(kf[m] * fast_exp(gc[m] - gl[m]));
+                sVT[c * LT + ln] = live ? vv[m] : (bf16)0.f;
             }
-            // channels c8 .. c8 + 7 sit at perm_index(c8) and perm_index(c8 + 4)
-            const int p0 = tr * LK + perm_index(c8), p1 = tr * LK + perm_index(c8 + 4);
-            *reinterpret_cast<bf16x4*>(sKg + p0) = bf16x4{kg[0], kg[1], kg[2], kg[3]};
-            *reinterpret_cast<bf16x4*>(sKg + p1) = bf16x4{kg[4], kg[5], kg[6], kg[7]};
-            *reinterpret_cast<bf16x4*>(sKi + p0) = bf16x4{ki[0], ki[1], ki[2], ki[3]};
-            *reinterpret_cast<bf16x4*>(sKi + p1) = bf16x4{ki[4], ki[5], ki[6], ki[7]};
-            *reinterpret_cast<bf16x4*>(sQg + p0) = bf16x4{qg[0], qg[1], qg[2], qg[3]};
-            *reinterpret_cast<bf16x4*>(sQg + p1) = bf16x4{qg[4], qg[5], qg[6], qg[7]};
+            // channels c4 .. c4 + 3 sit together at perm_index(c4)
+            const int p = ln * LK + perm_index(c4);
+            *reinterpret_cast<bf16x4*>(sKg + p) = kg;
+            *reinterpret_cast<bf16x4*>(sKi + p) = ki;
+            *reinterpret_cast<bf16x4*>(sQg + p) = qg;
+            if (ln == 0)
+                *reinterpret_cast<f32x4*>(sGam + c4) =
+                    f32x4{fast_exp(gc[0]), fast_exp(gc[1]), fast_exp(gc[2]), fast_exp(gc[3])};
+            const float b = live ? (beta_logit ? sigmoid(bv) : bv) : 0.f;
+            if (t < RC) sBeta[t] = b;
         }
         __syncthreads();
         // ---- A_kk and T (wave 0), A_qk (wave 1) ------------------------------------
@@ -409,16 +454,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 st[cb] = mma32(half8(sKhT + (16 * cb + ln) * LT + 4 * g), nb, a);
             }
         }
-    }
+    };
 
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float x = st[cb][i];   // a bit cast of a vector element in place reads element 0
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), srs, voff,
-                                                  (16 * cb + i) * D * 4, 0);
-        }
+    // The first chunk's token data, then the state: a wave's loads complete in
+    // order, so the chunk's operand work waits for its token data only, and
+    // the state, first needed by the products, streams in behind it.
+    load_tokens(t0, min(RC, t1 - t0));
+    load_state();
+    chunk(t0, min(RC, t1 - t0));
+    for (int tb = t0 + RC; tb < t1; tb += RC) {
+        refresh();
+        load_tokens(tb, min(RC, t1 - tb));
+        chunk(tb, min(RC, t1 - tb));
+    }
+    store_state();
 }
 
 template <typename E, int DK, int DV>
