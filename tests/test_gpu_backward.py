@@ -92,7 +92,9 @@ def test_backward_equal_rows_long():
 
 def test_backward_given_chunk_states_is_the_same():
     """Chunk states exported by the forward give bit-for-bit the gradients the
-    call computes when it recomputes them; and two runs are identical."""
+    call computes when it recomputes them; two runs are identical, and so is a
+    run in a caller workspace whose bytes start as garbage (nothing is read
+    before it is written)."""
     import torch
     import gated_delta_rule_prefill_amd as kda
     x, d_o, d_fin = _case(73, [150, 77], 2, 128, 128, "bf16")
@@ -102,9 +104,13 @@ def test_backward_given_chunk_states_is_the_same():
     g1 = _gpu_backward(x, d_o, d_fin, chunk_states=cs)
     g2 = _gpu_backward(x, d_o, d_fin)
     g3 = _gpu_backward(x, d_o, d_fin)
+    need = kda.backward_workspace_bytes(x.T, x.num_seqs, x.H, x.dk, x.dv, True)
+    ws = torch.full((need,), 0xA7, dtype=torch.uint8, device="cuda")
+    g4 = _gpu_backward(x, d_o, d_fin, workspace=ws)
     for n in GRADS:
         assert torch.equal(g1[n].cpu(), g2[n].cpu()), n
         assert torch.equal(g2[n].cpu(), g3[n].cpu()), n
+        assert torch.equal(g2[n].cpu(), g4[n].cpu()), n
 
 
 def test_backward_without_final_gradient_fp32():
