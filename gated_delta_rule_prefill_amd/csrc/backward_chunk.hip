@@ -184,43 +184,31 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
     const int co = cw + 4 * g;      // the lane's 4 output channels
 
     // ---------------- phase 0: loads ------------------------------------------
-    if (t < CHUNK) sBeta[t] = t < len ? beta[r0 + (size_t)t * H] : 0.f;
-    // log_alpha: thread (column c, 16-row block qd), cumulative sum inside the block
-    const int sc = t & (D - 1), sq = t >> 7;
-    float gl[16];
-    {
-        float run = 0.f;
+    // Every global load of the phase goes out before the first wait (a wave's
+    // loads complete in order, so each use below waits only for its own data
+    // and those issued before it).  Token rows past the chunk's end re-read its
+    // last row; their values are replaced by zeros where they are used.
+    const int sc = t & (D - 1), sq = t >> 7;   // log_alpha: column sc, 16-row block sq
+    const int last = len - 1;
+    float lav[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int r = 16 * sq + u;
-            run += r < len ? laB[r * HD + sc] : 0.f;
-            gl[u] = run;
-        }
-        sTot[sq * D + sc] = run;
-    }
-    // k and dO rows (zero past the end); X, X^T, A_qk^T from the record
+    for (int u = 0; u < 16; ++u) lav[u] = laB[min(16 * sq + u, last) * HD + sc];
+    const float bet = beta[r0 + (size_t)min(t & (CHUNK - 1), last) * H];
+    bf16x8 kv[2], dov[2];   // k and dO rows (t + 512e) >> 4, channels 8((t + 512e) & 15) ..
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        const int u = t + 512 * e, r = u >> 4, c8 = 8 * (u & 15);
-        bf16x8 kv = {}, dv8 = {};
-        if (r < len) {
-            kv = *reinterpret_cast<const bf16x8*>(kB + r * HD + c8);
-            dv8 = *reinterpret_cast<const bf16x8*>(oB + r * HD + c8);
-        }
-        *reinterpret_cast<bf16x8*>(sK + r * LR + c8) = kv;
-        *reinterpret_cast<bf16x8*>(sDO + r * LR + c8) = dv8;
+        const int u = t + 512 * e, r = min(u >> 4, last), c8 = 8 * (u & 15);
+        kv[e] = *reinterpret_cast<const bf16x8*>(kB + r * HD + c8);
+        dov[e] = *reinterpret_cast<const bf16x8*>(oB + r * HD + c8);
     }
-    {
-        const int r = t >> 3, c8 = 8 * (t & 7);
-        *reinterpret_cast<bf16x8*>(sX + r * LT + c8) = *reinterpret_cast<const bf16x8*>(rX + r * CHUNK + c8);
-        *reinterpret_cast<bf16x8*>(sXT + r * LT + c8) = *reinterpret_cast<const bf16x8*>(rXT + r * CHUNK + c8);
-        *reinterpret_cast<bf16x8*>(sAqT + r * LT + c8) = *reinterpret_cast<const bf16x8*>(rAqT + r * CHUNK + c8);
-    }
+    const int xr = t >> 3, x8 = 8 * (t & 7);   // X, X^T, A_qk^T from the record: row xr, columns x8 ..
+    const bf16x8 xv = *reinterpret_cast<const bf16x8*>(rX + xr * CHUNK + x8);
+    const bf16x8 xtv = *reinterpret_cast<const bf16x8*>(rXT + xr * CHUNK + x8);
+    const bf16x8 aqv = *reinterpret_cast<const bf16x8*>(rAqT + xr * CHUNK + x8);
     // S and dS once each, coalesced: thread t takes rows (t >> 5) + 16e, columns
     // 4(t & 31) .. +3 (e = 0..7).  They reach the MFMAs through a bf16 copy in
     // LDS (S3 + S4, free until phase 1 writes -W), from which each wave
-    // gathers both operand orientations; the per-row sums of S * dS (gamma_C's
-    // dependence on g_C) come from the fp32 values.
+    // gathers its operands in both orientations.
     f32x4 sv[8];
     bf16x4 dsv[8];
 #pragma unroll
@@ -229,15 +217,37 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
         sv[e] = *reinterpret_cast<const f32x4*>(Sg + at);
         dsv[e] = *reinterpret_cast<const bf16x4*>(dSg + at);
     }
-    // v as A operands over the tokens (for U): lane row j = cl, slots i = 32s + 8g + m
-    bf16x8 vop[2];
+    // v for the A operands over the tokens (for U): lane row j = cl, token
+    // 32s + 8g + m; packed into operands after the S staging, so that its
+    // waits come last
+    bf16 vr[2][8];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int i = 32 * s + 8 * g + m;
-            vop[s][m] = i < len ? vB[i * HD + cl] : (bf16)0.f;
+        for (int m = 0; m < 8; ++m) vr[s][m] = vB[min(32 * s + 8 * g + m, last) * HD + cl];
+
+    // log_alpha: cumulative sum inside the thread's 16-row block
+    float gl[16];
+    {
+        float run = 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            // masked by a product, so that every load's value is used (a select
+            // lets the compiler move the load under the condition)
+            run = fmaf(lav[u], 16 * sq + u < len ? 1.f : 0.f, run);
+            gl[u] = run;
         }
+        sTot[sq * D + sc] = run;
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int u = t + 512 * e, r = u >> 4, c8 = 8 * (u & 15);
+        *reinterpret_cast<bf16x8*>(sK + r * LR + c8) = r < len ? kv[e] : bf16x8{};
+        *reinterpret_cast<bf16x8*>(sDO + r * LR + c8) = r < len ? dov[e] : bf16x8{};
+    }
+    *reinterpret_cast<bf16x8*>(sX + xr * LT + x8) = xv;
+    *reinterpret_cast<bf16x8*>(sXT + xr * LT + x8) = xtv;
+    *reinterpret_cast<bf16x8*>(sAqT + xr * LT + x8) = aqv;
     bf16* sSt = reinterpret_cast<bf16*>(smem + CG_OFF_S3);   // [128][LR] staging of S, then dS
     static_assert(D * CG_LR * 2 <= 2 * CG_SLOT, "S staging spans S3 and S4");
 #pragma unroll
@@ -251,6 +261,12 @@ __global__ __launch_bounds__(64 * CG_WAVES) void chunk_grad_kernel(
         sd += lane_xor<16>(sd);   // the 32 lanes of the row
         if ((t & 31) == 0) sExt[c] = sd;
     }
+    if (t < CHUNK) sBeta[t] = t < len ? bet : 0.f;   // used from phase 1 on
+    bf16x8 vop[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) vop[s][m] = 32 * s + 8 * g + m < len ? vr[s][m] : (bf16)0.f;
     __syncthreads();
     // S as A operands over the key channels c (for N; lane row = value channel
     // j = cl, slots c = 32s + 8g + m) and over the value channels j (for dQg,
