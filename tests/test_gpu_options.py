@@ -159,6 +159,35 @@ def test_decode_tokens_match_oracle(dtype, dk, dv, flags):
         assert np.array_equal(host(p)[untouched], pool[untouched].astype(np.float64))
 
 
+def test_decode_tokens_benchmark_shape():
+    """The benchmark's pooled workload in its launch configuration: 256
+    sequences of 8 tokens as equal rows (no cu_seqlens), H = 32, d = 128, bf16,
+    fp32 states in a permuted order of the pool's slots.  Gated per sequence
+    (its 8 output rows over all heads) and per (slot, head) state, besides the
+    whole tensors."""
+    import torch
+    import gated_delta_rule_prefill_amd as kda
+    H, D, N, R = 32, 128, 256, 8
+    x = gen.make_prefill(9, [R] * N, H=H, dk=D, dv=D, dtype="bf16")
+    pool = gen.decode_state(9, N, H, D, D)
+    slots = np.random.default_rng(9).permutation(N).astype(np.int32)
+    d = device_inputs(x)
+    p = dev_f32(pool)
+    o = kda.decode_tokens(p, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                          state_indices=torch.from_numpy(slots).cuda(), num_seqs=N)
+    torch.cuda.synchronize()
+    ref_pool = pool.astype(np.float64)
+    ro = oracle.decode_tokens(ref_pool, slots, x.q, x.k, x.v, x.log_alpha, x.beta, num_seqs=N)
+    go, gp = host(o), host(p)
+    eo, ep = rel_l2(go, ro), rel_l2(gp, ref_pool)
+    worst_o = max(rel_l2(go[R * s:R * s + R], ro[R * s:R * s + R]) for s in range(N))
+    worst_p = max(rel_l2(gp[sl, h], ref_pool[sl, h]) for sl in range(N) for h in range(H))
+    print(f"[decode tokens] benchmark shape: o={eo:.3e} (worst sequence {worst_o:.3e}) "
+          f"pool={ep:.3e} (worst state {worst_p:.3e})", flush=True)
+    assert eo <= TOL["bf16"] and ep <= TOL["bf16"]
+    assert worst_o <= TOL["bf16"] and worst_p <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_tokens_equal_prefill(dtype):
     """The recurrent path and the chunkwise prefill compute the same function
