@@ -191,11 +191,16 @@ def backward_option(single, cs, reps, timed):
     us = timed(lambda i: kdalib.backward(s0["q"], s0["k"], s0["v"], s0["la"], s0["beta"], d_o,
                                          chunk_states=cs, need_initial_state_grad=False,
                                          workspace=bws), reps)
+    # the same gradients when the caller kept no chunk states: the call
+    # recomputes them with the forward kernels first
+    us_rc = timed(lambda i: kdalib.backward(s0["q"], s0["k"], s0["v"], s0["la"], s0["beta"], d_o,
+                                            need_initial_state_grad=False, workspace=bws), reps)
     nbytes = (PATH_BYTES_PER_TOKEN_HEAD + 768 + 512 + 4) * T * H
     return {"workload": "gradients of the 4096-token prefill (H=32, d=128, bf16) from its "
                         "exported chunk states", "path": "chunkwise", "us_per_call": round(us, 1),
             "tokens_per_s": round(T / (us * 1e-6), 1), "algorithmic_bytes": nbytes,
-            "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+            "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "us_per_call_recomputing_chunk_states": round(us_rc, 1)}
 
 
 def decode_tokens_option(dev, reps, timed):
