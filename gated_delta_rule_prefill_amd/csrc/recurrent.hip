@@ -207,6 +207,8 @@ __device__ __forceinline__ float row16_scan(float x) {
     return x + row_shr_or_0<8>(x);
 }
 
+// Register budget: 80 per lane (six waves per SIMD, three workgroups per CU);
+// the L2-normalising instance needs a few more and keeps the 128 of four.
 template <bool NORM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NORM ? 4 : 6, NORM ? 4 : 6))) void recurrent_mfma_kernel(
     float* __restrict__ pool, int num_slots, const int32_t* __restrict__ slots,
@@ -217,16 +219,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NORM ? 4 : 
     constexpr int D = 128;
     constexpr int LK = D + 8;    // row stride of [RC][D] bf16 arrays (channels in perm32 order)
     constexpr int LT = RC + 8;   // row stride of [D][RC] and [RC][RC] bf16 arrays
-    constexpr int LG = D + 4;    // row stride of the fp32 g array
-    // g (fp32) until the operands are formed, then -W
-    __shared__ __attribute__((aligned(16))) float sG[RC * LG];
+    __shared__ __attribute__((aligned(16))) bf16 sW[RC * LK];   // -W
     __shared__ __attribute__((aligned(16))) bf16 sKg[RC * LK], sKi[RC * LK], sQg[RC * LK];
     __shared__ __attribute__((aligned(16))) bf16 sKgT[D * LT], sKhT[D * LT], sVT[D * LT];
     __shared__ __attribute__((aligned(16))) bf16 sT[RC * LT], sAq[RC * LT];
     __shared__ __attribute__((aligned(16))) float sBeta[RC], sGam[D];
     __shared__ float sNrm[2][8][RC];   // per-wave partial squared norms of the q and k rows
-    bf16* sW = reinterpret_cast<bf16*>(sG);
-    static_assert(RC * LK * 2 <= RC * LG * 4, "-W fits over sG");
 
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     // Lane indices.  refresh() derives them anew from an opaque copy of the
