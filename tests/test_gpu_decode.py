@@ -168,3 +168,31 @@ def test_decode_tokens_without_write_only_decay():
     print(f"[closed form] pooled tokens, beta = 0: worst state {unit.max():.2e}, o {eo:.2e}", flush=True)
     assert unit.max() <= 1e-5
     assert eo <= TOL["bf16"]
+
+
+def test_decode_paths_are_deterministic():
+    """Two runs of the decode step and of the pooled path on the same inputs
+    and states give the same bits (no atomics, no order-dependent sums)."""
+    import torch
+    import gated_delta_rule_prefill_amd as kda
+    x, S0 = _batch(54, "bf16")
+    outs = []
+    for _ in range(2):
+        state = dev_f32(S0)
+        o = kda.decode_step(state, dev_qkv(x.q), dev_qkv(x.k), dev_qkv(x.v), dev_f32(x.log_alpha),
+                            dev_f32(x.beta))
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), state.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    N, H, D, R = 64, 32, 128, 8
+    y = gen.make_prefill(55, [R] * N, H=H, dk=D, dv=D, dtype="bf16")
+    pool = gen.decode_state(55, N, H, D, D)
+    slots = torch.from_numpy(np.random.default_rng(55).permutation(N).astype(np.int32)).cuda()
+    outs = []
+    for _ in range(2):
+        p = dev_f32(pool)
+        o = kda.decode_tokens(p, dev_qkv(y.q), dev_qkv(y.k), dev_qkv(y.v), dev_f32(y.log_alpha),
+                              dev_f32(y.beta), state_indices=slots, num_seqs=N)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), p.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
