@@ -203,6 +203,44 @@ def backward_option(single, cs, reps, timed):
             "us_per_call_recomputing_chunk_states": round(us_rc, 1)}
 
 
+def decode_option(dev, steps):
+    """The batched decode workload: 256 sequences x 32 heads, dk = dv = 128, fp32
+    states (512 MiB) updated in place by `steps` consecutive kda_decode_step calls
+    (bf16 q/k/v, 16 token sets in rotation)."""
+    import torch
+    import gated_delta_rule_prefill_amd as kdalib
+    from gated_delta_rule_prefill_amd import inputs as gen
+
+    def dq(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    c = gen.DECODE_CONFIG
+    N, Hd = c["N"], c["H"]
+    state = torch.from_numpy(gen.decode_state(c["seed"], N, Hd, c["dk"], c["dv"])).to(dev)
+    toks = []
+    for s_ in range(min(steps, 16)):
+        y = gen.decode_token(c["seed"], s_, N, Hd, c["dk"], c["dv"])
+        toks.append((dq(y.q), dq(y.k), dq(y.v), torch.from_numpy(y.log_alpha).to(dev),
+                     torch.from_numpy(y.beta).to(dev)))
+    o_dec = torch.empty((N, Hd, c["dv"]), dtype=torch.bfloat16, device=dev)
+    for s_ in range(4):
+        kdalib.decode_step(state, *toks[s_ % len(toks)], out=o_dec)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s_ in range(steps):
+        kdalib.decode_step(state, *toks[s_ % len(toks)], out=o_dec)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    gbs = DECODE_BYTES_PER_UNIT * N * Hd / (us * 1e-6) / 1e9
+    return {"workload": "batched decode: 256 seqs x 32 heads, dk=dv=128, fp32 state "
+                        "(512 MiB), bf16 q/k/v", "steps": steps,
+            "us_per_step": round(us, 2), "value": round(gbs, 1), "unit": "GB/s",
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_step": DECODE_BYTES_PER_UNIT * N * Hd}
+
+
 def decode_tokens_option(dev, reps, timed):
     """kda_decode_tokens on 256 sequences of 8 tokens (H=32, d=128, bf16), fp32
     states in a permuted order of pool slots."""
@@ -305,6 +343,8 @@ def main():
                     help="headline workload: the 65536-token sequence (default) or the 4096-token one")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the batched decode workload and print its JSON object")
     ap.add_argument("--decode-tokens-only", action="store_true",
                     help="time only the pooled-recurrent option (--steps calls after --warmup; "
                          "for profiling) and print its JSON")
@@ -330,6 +370,9 @@ def main():
     def dq(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
+    if args.decode_only:
+        print(json.dumps(decode_option(dev, args.decode_steps)), flush=True)
+        return
     if args.backward_only or args.decode_tokens_only:
         def timed(fn, reps):
             for i in range(args.warmup):
@@ -382,35 +425,11 @@ def main():
     # ---------------- decode workload ----------------
     decode = None
     if not args.no_decode:
-        c = gen.DECODE_CONFIG
-        N, Hd = c["N"], c["H"]
-        state = torch.from_numpy(gen.decode_state(c["seed"], N, Hd, c["dk"], c["dv"])).to(dev)
-        toks = []
-        for s_ in range(min(args.decode_steps, 16)):
-            y = gen.decode_token(c["seed"], s_, N, Hd, c["dk"], c["dv"])
-            toks.append((dq(y.q), dq(y.k), dq(y.v), torch.from_numpy(y.log_alpha).to(dev),
-                         torch.from_numpy(y.beta).to(dev)))
-        o_dec = torch.empty((N, Hd, c["dv"]), dtype=torch.bfloat16, device=dev)
-        for s_ in range(4):
-            kdalib.decode_step(state, *toks[s_ % len(toks)], out=o_dec)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for s_ in range(args.decode_steps):
-            kdalib.decode_step(state, *toks[s_ % len(toks)], out=o_dec)
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
-        gbs = DECODE_BYTES_PER_UNIT * N * Hd / (us * 1e-6) / 1e9
-        decode = {"workload": "batched decode: 256 seqs x 32 heads, dk=dv=128, fp32 state "
-                              "(512 MiB), bf16 q/k/v", "steps": args.decode_steps,
-                  "us_per_step": round(us, 2), "value": round(gbs, 1), "unit": "GB/s",
-                  "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                  "algorithmic_bytes_per_step": DECODE_BYTES_PER_UNIT * N * Hd}
+        decode = decode_option(dev, args.decode_steps)
         if "ceilings" in rec_extra:
-            decode["frac_of_copy_ceiling"] = round(gbs / rec_extra["ceilings"]["hbm_copy_GBs"], 4)
-        log(f"[bench] decode: {us:.1f} us/step, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak)")
-        del state
+            decode["frac_of_copy_ceiling"] = round(decode["value"] / rec_extra["ceilings"]["hbm_copy_GBs"], 4)
+        log(f"[bench] decode: {decode['us_per_step']:.1f} us/step, {decode['value']:.0f} GB/s "
+            f"({100 * decode['frac_of_hbm_peak']:.1f}% of peak)")
 
     # ---------------- optional paths (on the 4096-token workload) ----------------
     options = None
