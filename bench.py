@@ -234,11 +234,27 @@ def decode_option(dev, steps):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
     gbs = DECODE_BYTES_PER_UNIT * N * Hd / (us * 1e-6) / 1e9
+    # the same step as kda_decode_tokens on the states as a pool in permuted slot order
+    slots = torch.from_numpy(np.random.default_rng(c["seed"]).permutation(N).astype(np.int32)).to(dev)
+
+    def pooled(t):
+        q_, k_, v_, la_, b_ = t
+        kdalib.decode_tokens(state, q_, k_, v_, la_, b_, state_indices=slots, num_seqs=N, out=o_dec)
+    for s_ in range(4):
+        pooled(toks[s_ % len(toks)])
+    torch.cuda.synchronize()
+    e0.record()
+    for s_ in range(steps):
+        pooled(toks[s_ % len(toks)])
+    e1.record()
+    torch.cuda.synchronize()
+    us_pool = e0.elapsed_time(e1) * 1e3 / steps
     return {"workload": "batched decode: 256 seqs x 32 heads, dk=dv=128, fp32 state "
                         "(512 MiB), bf16 q/k/v", "steps": steps,
             "us_per_step": round(us, 2), "value": round(gbs, 1), "unit": "GB/s",
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes_per_step": DECODE_BYTES_PER_UNIT * N * Hd}
+            "algorithmic_bytes_per_step": DECODE_BYTES_PER_UNIT * N * Hd,
+            "us_per_step_decode_tokens_permuted_slots": round(us_pool, 2)}
 
 
 def decode_tokens_option(dev, reps, timed):

@@ -26,11 +26,16 @@ namespace kda {
 // streaming stores for the state (measured fastest; an earlier layout with
 // one workgroup per 64 columns and partial sums over four waves reached
 // 5.8 TB/s on the 512 MiB state, this one 6.2).
+//
+// slots (or NULL): the states are a pool and sequence s's state of head h is
+// pool slot slots[s] (H heads per slot); a slot outside [0, num_slots) marks
+// a padding sequence, whose output is zeroed and whose state is not touched.
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(64 * (DV / 32)) void decode_step_kernel(
     float* __restrict__ state, const E* __restrict__ q, const E* __restrict__ k,
     const E* __restrict__ v, const float* __restrict__ log_alpha,
-    const float* __restrict__ beta, E* __restrict__ o)
+    const float* __restrict__ beta, E* __restrict__ o,
+    const int32_t* __restrict__ slots, int num_slots, int H)
 {
     constexpr int RPL = DK / 8;   // key rows per lane
     const int u = blockIdx.x;     // sequence * H + head
@@ -40,6 +45,14 @@ __global__ __launch_bounds__(64 * (DV / 32)) void decode_step_kernel(
     // value index of this lane after the row-group sums: 0..3 -> p, 4..7 -> r
     const int vi = 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
     float* S = state + (size_t)u * DK * DV;
+    if (slots) {
+        const int seq = u / H, slot = slots[seq];
+        if (slot < 0 || slot >= num_slots) {   // padding sequence (uniform over the workgroup)
+            for (int x = threadIdx.x; x < DV; x += blockDim.x) o[(size_t)u * DV + x] = from_f32<E>(0.f);
+            return;
+        }
+        S = state + ((size_t)slot * H + (u - seq * H)) * DK * DV;
+    }
 
     // the state loads first: they dominate and depend on nothing else
     f32x4 s[RPL];
@@ -92,19 +105,21 @@ __global__ __launch_bounds__(64 * (DV / 32)) void decode_step_kernel(
 template <typename E, int DK, int DV>
 static hipError_t launch_decode(float* state, const void* q, const void* k, const void* v,
                                 const float* la, const float* beta, void* o, int units,
-                                hipStream_t stream)
+                                const int32_t* slots, int num_slots, int H, hipStream_t stream)
 {
     hipLaunchKernelGGL((decode_step_kernel<E, DK, DV>), dim3(units), dim3(64 * (DV / 32)), 0, stream,
-                       state, (const E*)q, (const E*)k, (const E*)v, la, beta, (E*)o);
+                       state, (const E*)q, (const E*)k, (const E*)v, la, beta, (E*)o, slots, num_slots, H);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_step(float* state, const void* q, const void* k, const void* v,
-                              const float* la, const float* beta, void* o, int units, int dk,
-                              int dv, bool bf16_io, hipStream_t stream)
+static hipError_t launch_decode_any(float* state, const void* q, const void* k, const void* v,
+                                    const float* la, const float* beta, void* o, int units,
+                                    const int32_t* slots, int num_slots, int H, int dk, int dv,
+                                    bool bf16_io, hipStream_t stream)
 {
 #define KDA_DECODE_CASE(E, DK_, DV_) \
-    if (dk == DK_ && dv == DV_) return launch_decode<E, DK_, DV_>(state, q, k, v, la, beta, o, units, stream);
+    if (dk == DK_ && dv == DV_)      \
+        return launch_decode<E, DK_, DV_>(state, q, k, v, la, beta, o, units, slots, num_slots, H, stream);
     if (bf16_io) {
         KDA_DECODE_CASE(bf16, 128, 128)
         KDA_DECODE_CASE(bf16, 64, 64)
@@ -118,6 +133,23 @@ hipError_t launch_decode_step(float* state, const void* q, const void* k, const 
     }
 #undef KDA_DECODE_CASE
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_step(float* state, const void* q, const void* k, const void* v,
+                              const float* la, const float* beta, void* o, int units, int dk,
+                              int dv, bool bf16_io, hipStream_t stream)
+{
+    return launch_decode_any(state, q, k, v, la, beta, o, units, nullptr, 0, 1, dk, dv, bf16_io, stream);
+}
+
+// One token for each of N sequences on pooled states (see kda_decode_tokens):
+// the decode step with slot indirection.
+hipError_t launch_decode_slots(float* pool, int num_slots, const int32_t* slots, const void* q,
+                               const void* k, const void* v, const float* la, const float* beta,
+                               void* o, int N, int H, int dk, int dv, bool bf16_io, hipStream_t stream)
+{
+    if (!slots) return launch_decode_any(pool, q, k, v, la, beta, o, N * H, nullptr, 0, 1, dk, dv, bf16_io, stream);
+    return launch_decode_any(pool, q, k, v, la, beta, o, N * H, slots, num_slots, H, dk, dv, bf16_io, stream);
 }
 
 }  // namespace kda

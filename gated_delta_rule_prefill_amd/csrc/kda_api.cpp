@@ -540,6 +540,14 @@ kda_status kda_decode_tokens(float* state_pool, int32_t num_slots, const int32_t
         if (kda_status dc = debug_check_cu_seqlens(cu_seqlens, num_seqs, total_tokens, stream))
             return dc;
         const int rows = cu_seqlens ? -1 : (int)(total_tokens / num_seqs);
+        // Exactly one token per sequence (equal rows of one, no options): the
+        // decode step's kernel, which streams the state without the token
+        // loop's staging.
+        if (!cu_seqlens && rows == 1 && flags == 0)
+            return check_launch(kda::launch_decode_slots(state_pool, num_slots, state_indices, q, k,
+                                                         v, log_alpha, beta, o, num_seqs, H, dk, dv,
+                                                         dtype == KDA_DTYPE_BF16, stream),
+                                "decode kernel", stream);
         return check_launch(kda::launch_recurrent(state_pool, num_slots, state_indices, q, k, v,
                                                   log_alpha, beta, cu_seqlens, rows, num_seqs, H,
                                                   dk, dv, dtype == KDA_DTYPE_BF16,

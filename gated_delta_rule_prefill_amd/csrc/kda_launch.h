@@ -141,4 +141,12 @@ hipError_t launch_decode_step(float* state, const void* q, const void* k, const 
                               const float* la, const float* beta, void* o, int units, int dk,
                               int dv, bool bf16_io, hipStream_t stream);
 
+// One token for each of N sequences on pooled states through slot indices
+// (NULL = slot s for sequence s; a slot outside [0, num_slots) pads): the
+// decode step's kernel with slot indirection.
+hipError_t launch_decode_slots(float* pool, int num_slots, const int32_t* slots, const void* q,
+                               const void* k, const void* v, const float* la, const float* beta,
+                               void* o, int N, int H, int dk, int dv, bool bf16_io,
+                               hipStream_t stream);
+
 }  // namespace kda

@@ -205,8 +205,10 @@ kda_status kda_decode_step(float *state, const void *q, const void *k, const voi
  * bf16 with dk = dv = 128 and more tokens than sequences the tokens of a
  * sequence are taken 16 at a time in the chunkwise form (section 3; bf16
  * products, fp32 state, the precision of kda_prefill); otherwise they are
- * processed one by one, and one token per sequence with identity slots and
- * no options equals kda_decode_step.
+ * processed one by one.  One token per sequence given as equal rows
+ * (cu_seqlens NULL, total_tokens = num_seqs) with no flags runs
+ * kda_decode_step's kernel through the slots: with identity slots its
+ * results are kda_decode_step's, bit for bit.
  */
 kda_status kda_decode_tokens(float *state_pool, int32_t num_slots, const int32_t *state_indices,
                              const void *q, const void *k, const void *v,

@@ -117,8 +117,8 @@ def test_prefill_normalisation_is_scale_invariant():
 
 
 # -- pooled multi-token recurrent path -------------------------------------------
-def _pool_case(seed, lens, dtype, dk=128, dv=128, H=4, P=7, raw=False):
-    x = gen.make_prefill(seed, lens, H=H, dk=dk, dv=dv, dtype=dtype, packed=True, raw=raw)
+def _pool_case(seed, lens, dtype, dk=128, dv=128, H=4, P=7, raw=False, packed=True):
+    x = gen.make_prefill(seed, lens, H=H, dk=dk, dv=dv, dtype=dtype, packed=packed, raw=raw)
     g = np.random.default_rng(seed)
     pool = (0.02 * g.standard_normal((P, H, dk, dv))).astype(np.float32)
     return x, pool
@@ -199,8 +199,37 @@ def test_decode_tokens_equal_prefill(dtype):
     assert rel_l2(host(pool), host(f_p)) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("f32", 128, 128), ("f32", 64, 64),
+                                         ("bf16", 128, 64), ("bf16", 64, 128)])
+@pytest.mark.parametrize("flags", [False, True])
+def test_decode_tokens_one_token_per_sequence(dtype, dk, dv, flags):
+    """One token per sequence as equal rows (the serving step on a pool):
+    permuted slots, a slot of -1 and one past the pool pad; without options
+    this takes the decode step's kernel with slot indirection, with them the
+    token loop."""
+    N, P, H = 9, 12, 3
+    slots = [7, 0, -1, 11, 3, 12, 5, 1, 9]
+    x, pool = _pool_case(71, [1] * N, dtype, dk, dv, H=H, P=P, raw=flags, packed=False)
+    assert x.cu_seqlens is None
+    kw = dict(l2norm_qk=flags, beta_sigmoid=flags)
+    o, p = _decode_tokens(x, pool, slots, **kw)
+    ref_pool = pool.astype(np.float64)
+    ro = oracle.decode_tokens(ref_pool, np.asarray(slots, np.int32), x.q, x.k, x.v, x.log_alpha,
+                              x.beta, num_seqs=N, l2norm_qk=flags, beta_logit=flags)
+    go, gp = host(o), host(p)
+    eo, ep = rel_l2(go, ro), rel_l2(gp, ref_pool)
+    worst_o = max(rel_l2(go[s], ro[s]) for s in range(N) if 0 <= slots[s] < P)
+    print(f"[decode tokens] one token {dtype} {dk}x{dv} flags={flags}: o={eo:.3e} "
+          f"(worst sequence {worst_o:.3e}) pool={ep:.3e}", flush=True)
+    assert eo <= TOL[dtype] and ep <= TOL[dtype] and worst_o <= TOL[dtype]
+    assert not np.any(go[2]) and not np.any(go[5])
+    for untouched in (2, 4, 6, 8, 10):   # slots no sequence names
+        assert np.array_equal(gp[untouched], pool[untouched].astype(np.float64))
+
+
 def test_decode_tokens_one_token_equals_decode_step():
-    """One token per sequence with identity slots is kda_decode_step."""
+    """One token per sequence with identity slots and no options is
+    kda_decode_step, bit for bit (the same kernel)."""
     import torch
     import gated_delta_rule_prefill_amd as kda
     t = gen.decode_token(68, 0, 16, 4, 128, 128, dtype="bf16")
@@ -210,4 +239,4 @@ def test_decode_tokens_one_token_equals_decode_step():
     o1 = kda.decode_step(s1, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"])
     o2 = kda.decode_tokens(s2, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], num_seqs=16)
     torch.cuda.synchronize()
-    assert rel_l2(host(o2), host(o1)) <= 1e-5 and rel_l2(host(s2), host(s1)) <= 1e-6
+    assert np.array_equal(host(o2), host(o1)) and np.array_equal(host(s2), host(s1))
