@@ -422,6 +422,11 @@ __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 2))) void prefill_intra_
         store_row<CPT>(sKD + row * L::LK + c0, kd);
         store_row<CPT>(sQP + row * L::LK + c0, qp);
     }
+    // Qg stays packed from here to the QM phase: left free, the compiler
+    // forms it there from the fp32 q rows and decays, which keeps twice the
+    // registers alive across every phase and spills.
+#pragma unroll
+    for (int r = 0; r < NR; ++r) asm volatile("" : "+v"(qg[r]));
     V8 vt[CPTV];       // v, the wave's rows of value channel cv0 + e
 #pragma unroll
     for (int e = 0; e < CPTV; ++e)
