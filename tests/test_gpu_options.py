@@ -159,15 +159,17 @@ def test_decode_tokens_match_oracle(dtype, dk, dv, flags):
         assert np.array_equal(host(p)[untouched], pool[untouched].astype(np.float64))
 
 
-def test_decode_tokens_benchmark_shape():
-    """The benchmark's pooled workload in its launch configuration: 256
-    sequences of 8 tokens as equal rows (no cu_seqlens), H = 32, d = 128, bf16,
-    fp32 states in a permuted order of the pool's slots.  Gated per sequence
-    (its 8 output rows over all heads) and per (slot, head) state, besides the
-    whole tensors."""
+@pytest.mark.parametrize("R", [8, 1])
+def test_decode_tokens_benchmark_shape(R):
+    """The benchmark's pooled workloads in their launch configurations: 256
+    sequences of 8 tokens (the chunkwise form) or of one token (the decode
+    step through the slots) as equal rows, H = 32, d = 128, bf16, fp32 states
+    in a permuted order of the pool's slots.  Gated per sequence (its output
+    rows over all heads) and per (slot, head) state, besides the whole
+    tensors."""
     import torch
     import gated_delta_rule_prefill_amd as kda
-    H, D, N, R = 32, 128, 256, 8
+    H, D, N = 32, 128, 256
     x = gen.make_prefill(9, [R] * N, H=H, dk=D, dv=D, dtype="bf16")
     pool = gen.decode_state(9, N, H, D, D)
     slots = np.random.default_rng(9).permutation(N).astype(np.int32)
@@ -182,7 +184,7 @@ def test_decode_tokens_benchmark_shape():
     eo, ep = rel_l2(go, ro), rel_l2(gp, ref_pool)
     worst_o = max(rel_l2(go[R * s:R * s + R], ro[R * s:R * s + R]) for s in range(N))
     worst_p = max(rel_l2(gp[sl, h], ref_pool[sl, h]) for sl in range(N) for h in range(H))
-    print(f"[decode tokens] benchmark shape: o={eo:.3e} (worst sequence {worst_o:.3e}) "
+    print(f"[decode tokens] benchmark shape, {R} token(s): o={eo:.3e} (worst sequence {worst_o:.3e}) "
           f"pool={ep:.3e} (worst state {worst_p:.3e})", flush=True)
     assert eo <= TOL["bf16"] and ep <= TOL["bf16"]
     assert worst_o <= TOL["bf16"] and worst_p <= TOL["bf16"]
