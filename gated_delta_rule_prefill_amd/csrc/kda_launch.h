@@ -119,6 +119,11 @@ hipError_t launch_chunk_grad(const void* q, const void* k, const void* v, const 
 // or the register-staged one (fp32 with dk = 128).
 constexpr bool uses_ring_kernel(bool bf16_io, int dk) { return bf16_io || dk == 64; }
 
+// Pooled paths walk the pool's slots in order (states streamed in address
+// order) when the batch has at most this many sequences and the pool at most
+// twice as many slots; otherwise they walk the sequences.
+constexpr int SLOT_ORDER_MAX_SEQS = 4096;
+
 // Recurrent tokens of a packed batch on pooled states (see kda_decode_tokens).
 hipError_t launch_recurrent(float* pool, int num_slots, const int32_t* slots, const void* q,
                             const void* k, const void* v, const float* la, const float* beta,

@@ -209,12 +209,18 @@ __device__ __forceinline__ float row16_scan(float x) {
 
 // Register budget: 80 per lane (six waves per SIMD, three workgroups per CU);
 // the L2-normalising instance needs a few more and keeps the 128 of four.
+// n_seqs > 0 (slot order): the grid walks the pool's slots, workgroup b taking
+// slot b / H and head b % H, so that the states stream in address order
+// whatever order the slots are given in; the workgroup finds the sequence
+// holding its slot by one pass over the slot array (a slot no sequence holds
+// is skipped), and the o rows of padding sequence s are zeroed by the
+// workgroups of slot s mod num_slots.
 template <bool NORM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NORM ? 4 : 6, NORM ? 4 : 6))) void recurrent_mfma_kernel(
     float* __restrict__ pool, int num_slots, const int32_t* __restrict__ slots,
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    const int32_t* __restrict__ cu, int rows, int H, int beta_logit, bf16* __restrict__ o)
+    const int32_t* __restrict__ cu, int rows, int H, int beta_logit, bf16* __restrict__ o, int n_seqs)
 {
     constexpr int D = 128;
     constexpr int LK = D + 8;    // row stride of [RC][D] bf16 arrays (channels in perm32 order)
@@ -243,21 +249,49 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NORM ? 4 : 
     };
     refresh();
 
-    const int u = blockIdx.x;   // sequence * H + head
-    const int seq = u / H, h = u % H;
-    int t0, t1;
-    if (cu) {
-        t0 = cu[seq];
-        t1 = cu[seq + 1];
+    // token range of sequence s
+    auto range_of = [&](int s_, int& a, int& b) {
+        if (cu) {
+            a = cu[s_];
+            b = cu[s_ + 1];
+        } else {
+            a = s_ * rows;
+            b = a + rows;
+        }
+    };
+    int seq, h, slot, t0, t1;
+    if (n_seqs > 0) {   // slot order (uniform over the launch)
+        __shared__ int sSeq;
+        slot = blockIdx.x / H;
+        h = blockIdx.x - slot * H;
+        if (t == 0) sSeq = -1;
+        __syncthreads();
+        for (int i = t; i < n_seqs; i += 512) {
+            const int si = slots[i];
+            if (si == slot) {
+                sSeq = i;
+            } else if ((si < 0 || si >= num_slots) && i % num_slots == slot) {
+                int a, b;   // padding sequence i: zero its o rows of head h
+                range_of(i, a, b);
+                for (int r = a; r < b; ++r)
+                    for (int x = 0; x < D; x += 4)
+                        *reinterpret_cast<bf16x4*>(o + ((size_t)r * H + h) * D + x) = bf16x4{};
+            }
+        }
+        __syncthreads();
+        seq = sSeq;
+        if (seq < 0) return;   // no sequence holds this slot (uniform over the workgroup)
+        range_of(seq, t0, t1);
     } else {
-        t0 = seq * rows;
-        t1 = t0 + rows;
-    }
-    const int slot = slots ? slots[seq] : seq;
-    if (slot < 0 || slot >= num_slots) {   // padding sequence (uniform over the workgroup)
-        for (int x = t; x < (t1 - t0) * D; x += 512)
-            o[((size_t)(t0 + x / D) * H + h) * D + x % D] = (bf16)0.f;
-        return;
+        seq = blockIdx.x / H;
+        h = blockIdx.x % H;
+        range_of(seq, t0, t1);
+        slot = slots ? slots[seq] : seq;
+        if (slot < 0 || slot >= num_slots) {   // padding sequence (uniform over the workgroup)
+            for (int x = t; x < (t1 - t0) * D; x += 512)
+                o[((size_t)(t0 + x / D) * H + h) * D + x % D] = (bf16)0.f;
+            return;
+        }
     }
     if (t1 <= t0) return;
 
@@ -496,16 +530,20 @@ hipError_t launch_recurrent(float* pool, int num_slots, const int32_t* slots, co
     // tokens; one token per sequence keeps the exact token step (it equals
     // the decode step).
     if (bf16_io && dk == 128 && dv == 128 && T > N) {
-        const dim3 grid((unsigned)((long long)N * H));
+        // slot order where the pool is not much larger than the batch (the
+        // grid walks every slot) and one pass over the slot array stays short
+        const bool by_slot = slots && N <= SLOT_ORDER_MAX_SEQS && (long long)num_slots <= 2LL * N;
+        const dim3 grid((unsigned)((long long)(by_slot ? num_slots : N) * H));
+        const int n_seqs = by_slot ? N : 0;
         const int beta_logit = (flags & PRE_BETA_LOGIT) ? 1 : 0;
         if (flags & PRE_L2NORM_QK)
             hipLaunchKernelGGL(recurrent_mfma_kernel<true>, grid, dim3(512), 0, stream, pool, num_slots,
                                slots, (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, cu, rows,
-                               H, beta_logit, (bf16*)o);
+                               H, beta_logit, (bf16*)o, n_seqs);
         else
             hipLaunchKernelGGL(recurrent_mfma_kernel<false>, grid, dim3(512), 0, stream, pool, num_slots,
                                slots, (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, cu, rows,
-                               H, beta_logit, (bf16*)o);
+                               H, beta_logit, (bf16*)o, n_seqs);
         return hipGetLastError();
     }
 #define KDA_REC_CASE(E, DK_, DV_) \

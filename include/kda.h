@@ -196,7 +196,8 @@ kda_status kda_decode_step(float *state, const void *q, const void *k, const voi
  *                  sequence s (then num_slots >= N).  A slot outside
  *                  [0, num_slots) marks a padding sequence: its o rows are
  *                  zeroed and no state is read or written.  Sequences must
- *                  name distinct slots (overlapping ones race).
+ *                  name distinct slots (with a repeated slot the results
+ *                  are undefined).
  *   q, k, v, log_alpha, beta, cu_seqlens, total_tokens, num_seqs, flags:
  *                  as for kda_prefill_ex (tokens packed, cu_seqlens NULL = N
  *                  equal rows)

@@ -159,6 +159,30 @@ def test_decode_tokens_match_oracle(dtype, dk, dv, flags):
         assert np.array_equal(host(p)[untouched], pool[untouched].astype(np.float64))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("lens", [[5, 1, 0, 16, 17, 70, 3], [1] * 7])
+def test_decode_tokens_sparse_pool(dtype, lens):
+    """A pool of 40 slots for 7 sequences: the kernels walk the sequences (the
+    slot-order walk is for pools at most twice the batch), with permuted and
+    padding slots, several tokens per sequence and one."""
+    slots = [31, -1, 0, 12, 39, 7, 40]
+    x, pool = _pool_case(72, lens, dtype, P=40, packed=len(set(lens)) > 1)
+    o, p = _decode_tokens(x, pool, slots)
+    ref_pool = pool.astype(np.float64)
+    ro = oracle.decode_tokens(ref_pool, np.asarray(slots, np.int32), x.q, x.k, x.v, x.log_alpha,
+                              x.beta, x.cu_seqlens, num_seqs=len(lens))
+    go, gp = host(o), host(p)
+    eo, ep = rel_l2(go, ro), rel_l2(gp, ref_pool)
+    print(f"[decode tokens] sparse pool {dtype} lens={lens}: o={eo:.3e} pool={ep:.3e}", flush=True)
+    assert eo <= TOL[dtype] and ep <= TOL[dtype]
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    for pad in (1, 6):
+        assert not np.any(go[starts[pad]:starts[pad + 1]])
+    used = {sl for sl in slots if 0 <= sl < 40}
+    for untouched in set(range(40)) - used:
+        assert np.array_equal(gp[untouched], pool[untouched].astype(np.float64))
+
+
 @pytest.mark.parametrize("R", [8, 1])
 def test_decode_tokens_benchmark_shape(R):
     """The benchmark's pooled workloads in their launch configurations: 256
