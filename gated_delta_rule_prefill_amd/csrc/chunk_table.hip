@@ -5,6 +5,9 @@
 // last chunk of a sequence may be partial.  Outputs
 //   seq_chunk_start[N+1]  exclusive prefix of chunks per sequence
 //   chunks[]              (sequence, first token, length) per chunk, in order
+//   seq_order[N]          the sequences longest first (a chain kernel that runs
+//                         the sequences in rounds starts the long ones first,
+//                         so that the short ones fill in behind them)
 // Reading cu_seqlens on the device avoids a host synchronisation.
 #include "kda_common.h"
 
@@ -27,7 +30,7 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int64_t T, int N, 
 
 __global__ __launch_bounds__(TABLE_THREADS) void chunk_table_kernel(
     const int32_t* __restrict__ cu, int64_t T, int N, int32_t* __restrict__ seq_chunk_start,
-    ChunkInfo* __restrict__ chunks, int max_chunks)
+    ChunkInfo* __restrict__ chunks, int max_chunks, int32_t* __restrict__ seq_order)
 {
     __shared__ int32_t s_scan[TABLE_THREADS];
     __shared__ int32_t s_base;
@@ -61,6 +64,22 @@ __global__ __launch_bounds__(TABLE_THREADS) void chunk_table_kernel(
     __threadfence_block();
     __syncthreads();
 
+    if (seq_order) {
+        if (N <= SEQ_ORDER_MAX_N) {
+            // rank of every sequence by (chunk count descending, index)
+            for (int s = tid; s < N; s += TABLE_THREADS) s_scan[s] = seq_chunk_start[s + 1] - seq_chunk_start[s];
+            __syncthreads();
+            for (int s = tid; s < N; s += TABLE_THREADS) {
+                const int n = s_scan[s];
+                int rank = 0;
+                for (int j = 0; j < N; ++j) rank += (s_scan[j] > n || (s_scan[j] == n && j < s)) ? 1 : 0;
+                seq_order[rank] = s;
+            }
+        } else {
+            for (int s = tid; s < N; s += TABLE_THREADS) seq_order[s] = s;
+        }
+    }
+
     const int total = s_base < max_chunks ? s_base : max_chunks;
     for (int c = tid; c < total; c += TABLE_THREADS) {
         // last sequence whose first chunk is <= c (skips empty sequences)
@@ -83,10 +102,11 @@ __global__ __launch_bounds__(TABLE_THREADS) void chunk_table_kernel(
 }
 
 hipError_t launch_chunk_table(const int32_t* cu, int64_t T, int N, int32_t* seq_chunk_start,
-                              ChunkInfo* chunks, int max_chunks, hipStream_t stream)
+                              ChunkInfo* chunks, int max_chunks, int32_t* seq_order,
+                              hipStream_t stream)
 {
     hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(TABLE_THREADS), 0, stream, cu, T, N,
-                       seq_chunk_start, chunks, max_chunks);
+                       seq_chunk_start, chunks, max_chunks, seq_order);
     return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@ struct Plan {
     int64_t max_chunks = 0;  // record slots per head (one segment's chunks)
     size_t rec_bytes = 0;    // bytes of one (chunk, head) record
     int seg_tokens = 0;      // equal rows: tokens per segment (== rows: one segment)
-    size_t off_seq = 0;      // seq_chunk_start [N+1]
+    size_t off_seq = 0;      // seq_chunk_start [N+1], then seq_order [N]
     size_t off_chunks = 0;   // ChunkInfo [max_chunks]
     size_t off_carry = 0;    // fp32 [N,H,dk,dv] state between segments (segmented only)
     size_t total = 0;
@@ -79,7 +79,7 @@ bool make_plan(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtyp
     }
     size_t at = align256((size_t)p.max_chunks * (size_t)H * p.rec_bytes);
     p.off_seq = at;
-    at += align256(((size_t)N + 1) * 4);
+    at += align256(((size_t)2 * N + 1) * 4);   // seq_chunk_start [N+1], then seq_order [N]
     p.off_chunks = at;
     at += align256((size_t)p.max_chunks * sizeof(kda::ChunkInfo));
     p.off_carry = at;
@@ -314,10 +314,10 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
         {
             Timer timer(stream);
             if (cu_seqlens) {
-                kda::ChunkSrc src{chunks, seq_start, -1, num_seqs, 0, 0};
+                kda::ChunkSrc src{chunks, seq_start, -1, num_seqs, 0, 0, seq_start + num_seqs + 1};
                 st = check_launch(kda::launch_chunk_table(cu_seqlens, total_tokens, num_seqs,
                                                           seq_start, chunks, (int)plan.max_chunks,
-                                                          stream),
+                                                          seq_start + num_seqs + 1, stream),
                                   "chunk table kernel", stream);
                 timer.mark("chunk_table");
                 if (st == KDA_OK && total_tokens > 0) {
@@ -446,11 +446,13 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const float
         int32_t* seq_start = reinterpret_cast<int32_t*>(ws + plan.off_seq);
         kda::ChunkInfo* chunks = reinterpret_cast<kda::ChunkInfo*>(ws + plan.off_chunks);
         const int rows = cu_seqlens ? -1 : (int)(total_tokens / num_seqs);
-        kda::ChunkSrc src{chunks, seq_start, rows, num_seqs, rows, 0};
+        kda::ChunkSrc src{chunks, seq_start, rows, num_seqs, rows, 0,
+                          cu_seqlens ? seq_start + num_seqs + 1 : nullptr};
         kda_status st = KDA_OK;
         if (cu_seqlens)
             st = check_launch(kda::launch_chunk_table(cu_seqlens, total_tokens, num_seqs, seq_start,
-                                                      chunks, (int)plan.max_chunks, stream),
+                                                      chunks, (int)plan.max_chunks,
+                                                      seq_start + num_seqs + 1, stream),
                               "chunk table kernel", stream);
         const float* cs = chunk_states;
         if (st == KDA_OK && !cs && total_tokens > 0) {

@@ -32,6 +32,7 @@ struct ChunkSrc {
     int N;
     int stride;                       // rows mode: tokens from one sequence to the next
     int offset;                       // rows mode: first token of the launch in each sequence
+    const int32_t* seq_order = nullptr;   // table mode: the sequences longest first, or NULL
 };
 
 // Per-(chunk, head) record of the chunk intermediates in the workspace
@@ -68,8 +69,12 @@ constexpr RecLayout rec_layout(int es, int dk, int dv) {
 // beta arrives as a logit and goes through a sigmoid.
 constexpr unsigned PRE_L2NORM_QK = 1u, PRE_BETA_LOGIT = 2u;
 
+// seq_order (or NULL): [N] the sequences by descending chunk count (ties by
+// index) for N <= SEQ_ORDER_MAX_N, else in index order.
+constexpr int SEQ_ORDER_MAX_N = 1024;
 hipError_t launch_chunk_table(const int32_t* cu, int64_t T, int N, int32_t* seq_chunk_start,
-                              ChunkInfo* chunks, int max_chunks, hipStream_t stream);
+                              ChunkInfo* chunks, int max_chunks, int32_t* seq_order,
+                              hipStream_t stream);
 
 // rec: [max_chunks * H] records of rec_layout() bytes
 hipError_t launch_prefill_intra(const void* q, const void* k, const void* v, const float* la,

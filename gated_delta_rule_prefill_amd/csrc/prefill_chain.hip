@@ -114,13 +114,15 @@ __global__ __launch_bounds__(64 * Chain2Cfg<DV>::WAVES) void prefill_chain2_kern
     const int grp = q8 / NPAIR, ps = q8 % NPAIR;   // ps: which 32 value columns
     const int pair = grp * 8 + xcd;
     if (pair >= n_pairs) return;
-    const int s = pair / H, h = pair % H;
+    // the sequences longest first where the table gives their order: this
+    // kernel runs the chains in rounds, and short ones then fill in behind
+    const int s = src.seq_order ? src.seq_order[pair / H] : pair / H, h = pair % H;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, g = l >> 4, ln = l & 15;
     const int j0 = 32 * ps;
     int c_begin, n;
     seq_chunks(src, s, c_begin, n);
-    const size_t sbase = (size_t)pair * DK * DV;
+    const size_t sbase = ((size_t)s * H + h) * DK * DV;
     if (n == 0) {   // empty sequence: the final state is the initial one (or zero)
         if (S_final)
             for (int x = tid; x < DK * 32; x += blockDim.x) {
