@@ -65,3 +65,62 @@ def test_two_slice_kernel_odd_head_count():
     x = gen.make_prefill(421, lens, H=3, dk=128, dv=128, dtype="bf16", state_std=0.02,
                          packed=True)
     check_prefill(x, label="two-slice kernel, H = 3")
+
+
+def draw_pool_case(seed: int):
+    g = np.random.default_rng([21, seed])
+    dtype = ["f32", "bf16"][int(g.integers(2))]
+    dk, dv = [(64, 64), (128, 128), (64, 128), (128, 64)][int(g.integers(4))]
+    H = int(g.choice([1, 2, 3, 8]))
+    N = int(g.integers(1, 20))
+    one_token = bool(g.integers(2))
+    lens = [1] * N if one_token else [int(x) for x in g.integers(0, 41, N)]
+    P = int(g.integers(N, 3 * N + 2))   # dense enough for the slot walk, or not
+    slots = [int(x) for x in g.permutation(P)[:N]]
+    for _ in range(int(g.integers(0, 3))):   # padding: -1 or past the pool
+        slots[int(g.integers(N))] = int(g.choice([-1, P, P + 5]))
+    flags = bool(g.integers(2))
+    return dict(dtype=dtype, dk=dk, dv=dv, H=H, lens=lens, P=P, slots=slots, flags=flags,
+                one_token=one_token)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_pooled_tokens(seed):
+    """kda_decode_tokens on seeded random pools against the oracle: the pool
+    after the call (slots no sequence names unchanged, bit for bit) and every
+    output row (padding sequences' rows zero)."""
+    import torch
+    import oracle
+    import gated_delta_rule_prefill_amd as kda
+    from gpu_util import TOL, dev_f32, device_inputs, host, rel_l2
+    c = draw_pool_case(seed)
+    N = len(c["lens"])
+    x = gen.make_prefill(500 + seed, c["lens"], H=c["H"], dk=c["dk"], dv=c["dv"], dtype=c["dtype"],
+                         raw=c["flags"], packed=not c["one_token"] and len(set(c["lens"])) > 1)
+    pool = (0.02 * np.random.default_rng([22, seed]).standard_normal(
+        (c["P"], c["H"], c["dk"], c["dv"]))).astype(np.float32)
+    d = device_inputs(x)
+    p = dev_f32(pool)
+    sl = torch.tensor(c["slots"], dtype=torch.int32, device="cuda")
+    o = kda.decode_tokens(p, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], state_indices=sl,
+                          cu_seqlens=d["cu_seqlens"], num_seqs=N, l2norm_qk=c["flags"],
+                          beta_sigmoid=c["flags"])
+    torch.cuda.synchronize()
+    ref_pool = pool.astype(np.float64)
+    ro = oracle.decode_tokens(ref_pool, np.asarray(c["slots"], np.int32), x.q, x.k, x.v,
+                              x.log_alpha, x.beta, x.cu_seqlens, num_seqs=N,
+                              l2norm_qk=c["flags"], beta_logit=c["flags"])
+    go, gp = host(o), host(p)
+    eo = rel_l2(go, ro) if ro.size else 0.0
+    ep = rel_l2(gp, ref_pool)
+    print(f"[pooled] random case {seed}: {c['dtype']} {c['dk']}x{c['dv']} H={c['H']} N={N} "
+          f"P={c['P']} one_token={c['one_token']} flags={c['flags']}: o={eo:.3e} pool={ep:.3e}",
+          flush=True)
+    assert eo <= TOL[c["dtype"]] and ep <= TOL[c["dtype"]]
+    starts = np.concatenate([[0], np.cumsum(c["lens"])])
+    for s, sl_ in enumerate(c["slots"]):
+        if not 0 <= sl_ < c["P"]:
+            assert not np.any(go[starts[s]:starts[s + 1]]), (seed, s)
+    used = {sl_ for sl_ in c["slots"] if 0 <= sl_ < c["P"]}
+    for untouched in set(range(c["P"])) - used:
+        assert np.array_equal(gp[untouched], pool[untouched].astype(np.float64)), (seed, untouched)
