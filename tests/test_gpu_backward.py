@@ -217,3 +217,28 @@ def test_backward_long_context_sampled_heads():
             e = rel_l2(got[:, j], ref[n][:, j])
             print(f"[backward long] head {hd} {n}={e:.2e}", flush=True)
             assert e <= TOL["bf16"], (hd, n, e)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_backward_random_configuration(seed):
+    """Seeded random batches across the axes the backward branches on: the
+    chunkwise path (bf16, d = 128) or the token walk, head counts that are
+    not a multiple of 8, packed or equal rows with empty, one-token and
+    partial-chunk sequences, and the decay strength."""
+    g = np.random.default_rng([23, seed])
+    if seed < 4:   # the chunkwise path
+        dtype, dk, dv = "bf16", 128, 128
+    else:
+        dtype = ["f32", "bf16"][int(g.integers(2))]
+        dk, dv = [(64, 64), (128, 64), (64, 128), (128, 128)][int(g.integers(4))]
+    H = int(g.choice([1, 2, 3, 5, 8]))
+    packed = seed % 2 == 1
+    N = int(g.integers(2 if packed else 1, 9))
+    if packed:
+        lens = [int(x) for x in g.integers(0, 300, N)]
+        lens[int(g.integers(N))] = int(g.choice([0, 1, 63, 65]))
+    else:
+        lens = [int(g.choice([64, 97, 200]))] * N
+    mu = float(g.choice([0.0, 3.0, 4.0]))
+    x, d_o, d_fin = _case(600 + seed, lens, H, dk, dv, dtype, packed=packed, mu=mu)
+    _check(x, d_o, d_fin, f"random case {seed} (H={H}, N={N}, {'packed' if packed else 'equal rows'}, mu={mu})")
