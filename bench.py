@@ -214,7 +214,7 @@ def decode_option(dev, steps):
     def dq(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    c = gen.DECODE_CONFIG
+    c = gen.DECODE_WORKLOAD
     N, Hd = c["N"], c["H"]
     state = torch.from_numpy(gen.decode_state(c["seed"], N, Hd, c["dk"], c["dv"])).to(dev)
     toks = []
@@ -405,7 +405,7 @@ def main():
         if args.decode_tokens_only:
             print(json.dumps(decode_tokens_option(dev, args.steps, timed)), flush=True)
             return
-        single = Prefill(gen.config_prefill(2), dev)
+        single = Prefill(gen.workload_prefill("single_T4096"), dev)
         cs = torch.empty((kdalib.num_chunk_states(single.x.T, 1), single.x.H, single.x.dk,
                           single.x.dv), dtype=torch.float32, device=dev)
         print(json.dumps(backward_option(single, cs, args.steps, timed)), flush=True)
@@ -415,7 +415,7 @@ def main():
     single = None
     if not args.no_extra or args.headline == "single":
         log("[bench] single-sequence workload T=4096 H=32 d=128, 3 rotated input sets")
-        single = Prefill(gen.config_prefill(2), dev, sets=3)
+        single = Prefill(gen.workload_prefill("single_T4096"), dev, sets=3)
 
     if not args.no_extra:
         rec_extra["ceilings"] = ceilings(dev)
@@ -427,7 +427,7 @@ def main():
         c2["kernel_us"] = {k: round(v, 2) for k, v in single.kernel_us(50).items()}
         log(f"[bench] T=4096: {us:.1f} us/step, {c2['tokens_per_s'] / 1e6:.2f} M tok/s, "
             f"{c2['frac_of_roofline']:.3f} of roofline")
-        packed = Prefill(gen.config_prefill(3), dev)
+        packed = Prefill(gen.workload_prefill("packed_16"), dev)
         us = packed.event_time_us(20)
         c3 = packed.summary(us)
         c3["workload"] = (f"packed varlen prefill, 16 sequences U[256,4096] (T={packed.x.T}), H=32 "
@@ -510,7 +510,7 @@ def main():
     # ---------------- headline: the long-context prefill ----------------
     if args.headline == "long":
         log("[bench] headline workload: B=1 T=65536 H=32 d=128 bf16 (generating inputs)")
-        head = Prefill(gen.config_prefill(4), dev)
+        head = Prefill(gen.workload_prefill("long_T65536"), dev)
         workload = ("long-context KDA prefill B=1 T=65536 H=32 dk=dv=128, bf16 q/k/v, fp32 "
                     "log_alpha (logsigmoid(N(4,1)))/beta/state, chunk 64, zero initial state")
         wl_key = "long_65536"

@@ -186,40 +186,33 @@ def make_prefill(seed: int, lengths: Sequence[int], H: int, dk: int, dv: int,
                      beta=beta, initial_state=s0, cu_seqlens=cu, num_seqs=N, dtype=dtype)
 
 
-# The five named workloads.
-CONFIG_NAMES = {
-    1: "tiny fp32 prefill B=1 T=256 H=2 d=64",
-    2: "single-sequence prefill B=1 T=4096 H=32 d=128 bf16",
-    3: "packed varlen prefill 16 seqs U[256,4096] H=32 d=128 bf16, nonzero states",
-    4: "long-context prefill B=1 T=65536 H=32 d=128 bf16",
-    5: "batched decode 256 seqs H=32 d=128, 128 steps",
+# The named workloads (each with its own fixed seed).
+WORKLOADS = {
+    "tiny_T256": "tiny fp32 prefill B=1 T=256 H=2 d=64",
+    "single_T4096": "single-sequence prefill B=1 T=4096 H=32 d=128 bf16",
+    "packed_16": "packed varlen prefill 16 seqs U[256,4096] H=32 d=128 bf16, nonzero states",
+    "long_T65536": "long-context prefill B=1 T=65536 H=32 d=128 bf16",
+    "decode_256x32": "batched decode 256 seqs H=32 d=128, 128 steps",
 }
 
 
-def config_lengths(i: int) -> List[int]:
-    if i == 1:
-        return [256]
-    if i == 2:
-        return [4096]
-    if i == 3:
-        return [int(x) for x in rng(3, LENGTHS).integers(256, 4096, size=16, endpoint=True)]
-    if i == 4:
-        return [65536]
-    raise ValueError(i)
+def packed_16_lengths() -> List[int]:
+    """The 16 sequence lengths of the packed workload, uniform in [256, 4096]."""
+    return [int(x) for x in rng(3, LENGTHS).integers(256, 4096, size=16, endpoint=True)]
 
 
-def config_prefill(i: int) -> KDAInputs:
-    """Inputs of prefill workload i (1..4), seed = i."""
-    if i == 1:
+def workload_prefill(name: str) -> KDAInputs:
+    """Inputs of a named prefill workload (see WORKLOADS)."""
+    if name == "tiny_T256":
         return make_prefill(1, [256], H=2, dk=64, dv=64, dtype="f32", mu=3.0)
-    if i == 2:
+    if name == "single_T4096":
         return make_prefill(2, [4096], H=32, dk=128, dv=128, dtype="bf16", mu=3.0)
-    if i == 3:
-        return make_prefill(3, config_lengths(3), H=32, dk=128, dv=128, dtype="bf16", mu=3.0,
+    if name == "packed_16":
+        return make_prefill(3, packed_16_lengths(), H=32, dk=128, dv=128, dtype="bf16", mu=3.0,
                             state_std=0.02, packed=True)
-    if i == 4:
+    if name == "long_T65536":
         return make_prefill(4, [65536], H=32, dk=128, dv=128, dtype="bf16", mu=4.0)
-    raise ValueError(i)
+    raise ValueError(name)
 
 
 def decode_state(seed: int, N: int, H: int, dk: int, dv: int, std: float = 0.02) -> np.ndarray:
@@ -238,7 +231,8 @@ def decode_token(seed: int, step: int, N: int, H: int, dk: int, dv: int,
                      beta=beta, initial_state=None, cu_seqlens=None, num_seqs=N, dtype=dtype)
 
 
-DECODE_CONFIG = dict(seed=5, N=256, H=32, dk=128, dv=128, steps=128, dtype="bf16", mu=3.0)
+# the batched decode workload
+DECODE_WORKLOAD = dict(seed=5, N=256, H=32, dk=128, dv=128, steps=128, dtype="bf16", mu=3.0)
 
 
 def as_f32(x: np.ndarray) -> np.ndarray:

@@ -63,12 +63,12 @@ def test_decode_small(dtype, dk, dv):
     _gate(run_decode(41, N=3, H=2, dk=dk, dv=dv, steps=8, dtype=dtype), dtype, f"{dk}x{dv}")
 
 
-def test_decode_config5_full():
+def test_decode_256x32_full():
     """256 sequences x 32 heads, 128 steps; the oracle follows every one of the
     8,192 (sequence, head) states through all 128 steps."""
-    c = gen.DECODE_CONFIG
+    c = gen.DECODE_WORKLOAD
     _gate(run_decode(c["seed"], c["N"], c["H"], c["dk"], c["dv"], c["steps"], c["dtype"]),
-          c["dtype"], "config 5 (all 8192 units, 128 steps)")
+          c["dtype"], "256 x 32 decode (all 8192 units, 128 steps)")
 
 
 def test_hand_worked_example():

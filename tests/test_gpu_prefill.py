@@ -36,9 +36,9 @@ def test_hand_worked_example(d):
     assert np.abs(host(fin) - fin_ref).max() < 1e-5
 
 
-def test_config1_tiny_fp32():
-    x = gen.config_prefill(1)
-    check_prefill(x, label="config 1")
+def test_tiny_T256_fp32():
+    x = gen.workload_prefill("tiny_T256")
+    check_prefill(x, label="tiny T=256")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -65,29 +65,29 @@ def test_many_chains(dtype, dk, dv):
     check_prefill(x, label=f"many chains {dk}x{dv}")
 
 
-def test_config2_single_sequence():
-    x = gen.config_prefill(2)
-    check_prefill(x, label="config 2")
+def test_single_sequence_T4096():
+    x = gen.workload_prefill("single_T4096")
+    check_prefill(x, label="single sequence T=4096")
 
 
-def test_config3_packed_varlen_full():
+def test_packed_16_sequences_full():
     """The packed 16-sequence batch with nonzero initial states: every
     sequence and head against the oracle, gated per (sequence, head), per
     64-token chunk and per row."""
     import torch
-    x = gen.config_prefill(3)
+    x = gen.workload_prefill("packed_16")
     o, fin = gpu_prefill(x)
     torch.cuda.synchronize()
     ro, rf = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.initial_state, x.cu_seqlens)
     errs = unit_errors(host(o), ro, host(fin), rf, x.lengths())
-    assert_units(errs, "bf16", f"config 3, 16 sequences, T={x.T}")
+    assert_units(errs, "bf16", f"packed 16 sequences, T={x.T}")
 
 
-def test_config4_long_all_heads():
+def test_long_T65536_all_heads():
     """T = 65536 on the GPU in one call; the oracle checks all 32 heads over the
     whole sequence, eight heads at a time (keeps its fp64 output near 0.5 GB)."""
     import torch
-    x = gen.config_prefill(4)
+    x = gen.workload_prefill("long_T65536")
     o, fin = gpu_prefill(x)
     torch.cuda.synchronize()
     worst = None
@@ -97,10 +97,10 @@ def test_config4_long_all_heads():
         ro, rf = oracle.prefill(y.q, y.k, y.v, y.log_alpha, y.beta, y.initial_state, None,
                                 num_seqs=1)
         errs = unit_errors(host(o[:, h0:h0 + 8]), ro, host(fin[:, h0:h0 + 8]), rf, x.lengths())
-        assert_units(errs, "bf16", f"config 4 heads {h0}..{h0 + 7}")
+        assert_units(errs, "bf16", f"T=65536 heads {h0}..{h0 + 7}")
         worst = errs if worst is None else {k: max(worst[k], errs[k]) if k != "worst_row" else
                                             worst[k] for k in errs}
-    print(f"[parity] config 4 all heads: worst o={worst['o']:.3e} state={worst['state']:.3e} "
+    print(f"[parity] T=65536 all heads: worst o={worst['o']:.3e} state={worst['state']:.3e} "
           f"chunk={worst['chunk_o']:.3e} row={worst['row_o']:.3e}", flush=True)
 
 
