@@ -28,6 +28,8 @@ q/k/v, fp32 log_alpha/beta/state, log_alpha = logsigmoid(N(4, 1))):
   cpu_baseline  the fp64 oracle on the host cores, on the headline's inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Single workloads for profiling (one JSON object each): --decode-only,
+--decode-tokens-only, --backward-only, --packed-only.
 """
 from __future__ import annotations
 
@@ -364,6 +366,9 @@ def main():
     ap.add_argument("--decode-tokens-only", action="store_true",
                     help="time only the pooled-recurrent option (--steps calls after --warmup; "
                          "for profiling) and print its JSON")
+    ap.add_argument("--packed-only", action="store_true",
+                    help="time only the packed 16-sequence prefill (--steps steps after --warmup; "
+                         "for profiling) and print its JSON")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward option (--steps calls after --warmup; for "
                          "profiling) and print its JSON")
@@ -388,6 +393,14 @@ def main():
 
     if args.decode_only:
         print(json.dumps(decode_option(dev, args.decode_steps)), flush=True)
+        return
+    if args.packed_only:
+        packed = Prefill(gen.workload_prefill("packed_16"), dev)
+        us = packed.event_time_us(args.steps, warm=args.warmup)
+        c3 = packed.summary(us)
+        c3["workload"] = (f"packed varlen prefill, 16 sequences U[256,4096] (T={packed.x.T}), H=32 "
+                          f"dk=dv=128 bf16, nonzero fp32 initial states, per-sequence final states")
+        print(json.dumps(c3), flush=True)
         return
     if args.backward_only or args.decode_tokens_only:
         def timed(fn, reps):
