@@ -7,7 +7,9 @@ seeds at random and check the same independent facts on each draw:
   * the chunkwise form (tests/chunkwise_mirror.py, written from the chunk
     algebra, not from the oracle) reproduces it for a random chunk size;
   * a packed batch equals separate calls per sequence, bit for bit;
-  * token-by-token decode steps reproduce the prefill.
+  * token-by-token decode steps reproduce the prefill;
+  * pooled tokens are decode steps on each sequence's slot (padding and
+    unnamed slots untouched).
 """
 import numpy as np
 from hypothesis import HealthCheck, given, settings
@@ -79,3 +81,39 @@ def test_decode_steps_reproduce_prefill(seed, T, H, dk, dv, dtype):
                                 x.log_alpha[t][None], x.beta[t][None])
         assert rel_err(ot[0], o[t]) < 1e-12
     assert rel_err(S, fin) < 1e-12
+
+
+@settings(**SETTINGS)
+@given(seed=seeds, lengths=st.lists(st.integers(0, 8), min_size=1, max_size=6), dk=dims, dv=dims,
+       extra_slots=st.integers(0, 6), n_pad=st.integers(0, 2))
+def test_pooled_tokens_are_decode_steps_on_the_slots(seed, lengths, dk, dv, extra_slots, n_pad):
+    """Each sequence starts from its slot's state and leaves its final state
+    there; padding sequences (a slot outside the pool) give zero output and
+    touch nothing; slots no sequence names are unchanged."""
+    x = _case(seed, 0, 2, dk, dv, lengths=lengths)
+    N = x.num_seqs
+    g = np.random.default_rng(seed)
+    P = N + extra_slots
+    slots = g.permutation(P)[:N].astype(np.int32)
+    for i in g.choice(N, size=min(n_pad, N), replace=False):
+        slots[i] = g.choice([-1, P, P + 3])
+    pool = 0.3 * g.standard_normal((P, x.H, dk, dv))
+    got = pool.copy()
+    o = oracle.decode_tokens(got, slots, x.q, x.k, x.v, x.log_alpha, x.beta, x.cu_seqlens,
+                             num_seqs=N)
+    ref = pool.copy()
+    cu = x.cu_seqlens if x.cu_seqlens is not None else np.arange(N + 1) * (x.T // N)
+    for s in range(N):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if not 0 <= slots[s] < P:
+            assert not np.any(o[a:b])
+            continue
+        S = ref[slots[s]][None].copy()
+        for t in range(a, b):
+            ot = oracle.decode_step(S, x.q[t][None], x.k[t][None], x.v[t][None],
+                                    x.log_alpha[t][None], x.beta[t][None])
+            assert rel_err(ot[0], o[t]) < 1e-12
+        ref[slots[s]] = S[0]
+    assert rel_err(got, ref) < 1e-12
+    unused = sorted(set(range(P)) - {int(v) for v in slots if 0 <= v < P})
+    assert np.array_equal(got[unused], pool[unused])
