@@ -212,3 +212,50 @@ def test_noalloc_rejects_sizes_beyond_its_array_before_any_hip_call():
     st = lib.kda_prefill_noalloc(A, A, A, A, A, None, None, 128, 0, 2, 64, 64,
                                  kda.KDA_DTYPE_BF16, A, None, None)
     assert st == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "kda.h"
+
+int main(void) {
+    if (kda_version() <= 0) return 1;
+    if (strcmp(kda_status_string(KDA_ERR_WORKSPACE), "KDA_ERR_WORKSPACE") != 0) return 2;
+    size_t ws = kda_prefill_workspace_bytes(4096, 1, 32, 128, 128, KDA_DTYPE_BF16);
+    if (ws == 0 || ws % 256 != 0) return 3;
+    /* an unsupported head size is rejected before any HIP call */
+    kda_status st = kda_prefill(NULL, NULL, NULL, NULL, NULL, NULL, NULL, 64, 1, 1, 96, 128,
+                                KDA_DTYPE_BF16, NULL, NULL, NULL, 0, NULL);
+    if (st != KDA_ERR_UNSUPPORTED) return 4;
+    if (strlen(kda_last_error_message()) == 0) return 5;
+    printf("ok %zu\n", ws);
+    return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/kda.h compiles as C11 and a C program links against libkda.so
+    and calls its host-side entry points (no GPU needed)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    lib_dir = os.path.dirname(kda.LIB_PATH)
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    src = tmp_path / "use_kda.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "use_kda"
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    cmd = [gcc, "-std=c11", "-Wall", "-Werror", "-I", os.path.join(root, "include"), str(src),
+           "-o", str(exe), kda.LIB_PATH, f"-Wl,-rpath,{lib_dir}",
+           "-Wl,-rpath,/opt/rocm/lib"]
+    # under the host sanitizer run the library is instrumented: link its runtime too
+    cmd += [p for p in os.environ.get("LD_PRELOAD", "").split(":") if "asan" in p]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0 and run.stdout.startswith("ok"), (run.returncode, run.stdout, run.stderr)
