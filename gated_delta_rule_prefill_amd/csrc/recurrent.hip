@@ -425,13 +425,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NORM ? 4 : 
                 f32x4 am;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) am[i] = 4 * g + i > ln ? sBeta[4 * g + i] * acc[i] : 0.f;
-                // (I + A_kk) x = e_l by forward substitution, lane l = column l
+                // (I + A_kk) x = e_l by forward substitution, lane l = column l.
+                // Rows from the chunk's end on hold no A_kk entries, so their
+                // solution is e_l itself: the substitution stops at nt rows.
+                const int nr = __builtin_amdgcn_readfirstlane(nt);
                 float x[RC];
 #pragma unroll
                 for (int r = 0; r < RC; ++r) {
                     float a = r == ln ? 1.f : 0.f;
+                    if (r < nr) {
 #pragma unroll
-                    for (int i = 0; i < r; ++i) a -= read_lane(am[r & 3], 16 * (r >> 2) + i) * x[i];
+                        for (int i = 0; i < r; ++i) a -= read_lane(am[r & 3], 16 * (r >> 2) + i) * x[i];
+                    }
                     x[r] = a;
                 }
                 if (g == 0) {
