@@ -570,6 +570,20 @@ def main():
                         "hands to the other are in traffic, not in achieved"}
     if "ceilings" in rec_extra:
         roofline["frac_of_copy_ceiling"] = round(achieved / rec_extra["ceilings"]["hbm_copy_GBs"], 4)
+    # The rate at which each kernel moves the bytes it really moves (the counted
+    # traffic per launch over the launch time): set beside the copy ceiling, it
+    # shows how much of a kernel's time its own traffic accounts for.
+    rates = {}
+    for k, v in kern.items():
+        tb = traffic_for(k, wl_key)
+        if tb is not None and v[0] > 0:
+            rates[k] = {"traffic_bytes_per_launch": tb,
+                        "traffic_GBs": round(tb / (v[0] * 1e-6) / 1e9, 1)}
+            if "ceilings" in rec_extra:
+                rates[k]["frac_of_copy_ceiling"] = round(
+                    rates[k]["traffic_GBs"] / rec_extra["ceilings"]["hbm_copy_GBs"], 4)
+    if rates:
+        roofline["traffic_rate"] = rates
     path = head.summary(dt / args.steps * 1e6)
     path["mfma_frac_of_bf16_peak"] = round(path["mfma_tflops_dense_count"] / BF16_MFMA_PEAK_TFLOPS, 4)
     if "ceilings" in rec_extra:
