@@ -25,7 +25,11 @@ q/k/v, fp32 log_alpha/beta/state, log_alpha = logsigmoid(N(4, 1))):
   decode     the batched decode workload (256 seqs x 32 heads, 128 steps), GB/s;
   options    chunk-state export, in-kernel preprocessing, the pooled recurrent
              path and the backward pass, on the 4096-token workload;
-  cpu_baseline  the fp64 oracle on the host cores, on the headline's inputs.
+  cpu_baseline  the fp64 oracle on the host cores, on the headline's inputs;
+  parity     the headline's output and final state against that oracle run
+             (relative L2 of the whole tensors, every head and every 64-token
+             chunk); the run exits with status 1 after its line if any is
+             outside the tolerance.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Single workloads for profiling (one JSON object each): --decode-only,
@@ -84,6 +88,36 @@ def traffic_for(kernel: str, workload: str):
         return rec["bytes_per_launch"]
     except Exception:
         return None
+
+
+PARITY_TOL = 2e-2   # relative L2 for bf16 q/k/v: whole tensors, every head, every chunk
+
+
+def headline_parity(head, ref):
+    """The headline's output and final state (from its last timed step) against
+    the oracle's, on the same inputs: relative L2 of the whole tensors, of every
+    head, and of every (64-token chunk, head)."""
+    o_ref, s_ref = ref[0], ref[1]
+    o = head.out[0].float().cpu().numpy().astype(np.float64)
+    fin = head.fin.cpu().numpy().astype(np.float64)
+    e2 = ((o - o_ref) ** 2).sum(axis=2)          # [T, H]
+    r2 = (o_ref ** 2).sum(axis=2)
+    del o
+    T, H = e2.shape
+    nc = -(-T // CHUNK)
+    pad = nc * CHUNK - T
+    ce = np.pad(e2, ((0, pad), (0, 0))).reshape(nc, CHUNK, H).sum(1)
+    cr = np.pad(r2, ((0, pad), (0, 0))).reshape(nc, CHUNK, H).sum(1)
+    rel = lambda e, r: np.sqrt(e / np.maximum(r, 1e-300))  # noqa: E731
+    res = {"o": float(rel(e2.sum(), r2.sum())),
+           "final_state": float(rel(((fin - s_ref) ** 2).sum(), (s_ref ** 2).sum())),
+           "worst_head_o": float(rel(e2.sum(0), r2.sum(0)).max()),
+           "worst_chunk_o": float(rel(ce, cr).max())}
+    ok = all(v <= PARITY_TOL for v in res.values())
+    out = {k: float(f"{v:.3e}") for k, v in res.items()}
+    out.update({"tol": PARITY_TOL, "ok": bool(ok),
+                "against": "the fp64 oracle's output on the same inputs (the CPU leg's run)"})
+    return out
 
 
 def cpu_model() -> str:
@@ -536,11 +570,17 @@ def main():
     for i in range(args.warmup):
         head.step(i)
     torch.cuda.synchronize()
+    # events between the steps (on the stream the library launches on) give the
+    # spread of single steps; the wall clock over all of them gives `value`
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
+    marks[0].record()
     for i in range(args.steps):
         head.step(i)
+        marks[i + 1].record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    step_us = sorted(1e3 * marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     ms_per_step = 1e3 * dt / args.steps
     tok_s = T / (dt / args.steps)
     log(f"[bench] headline: {ms_per_step * 1e3:.1f} us/step, {tok_s / 1e6:.2f} M tokens/s "
@@ -585,12 +625,16 @@ def main():
     if rates:
         roofline["traffic_rate"] = rates
     path = head.summary(dt / args.steps * 1e6)
+    if step_us:
+        path["step_us_events"] = {"min": round(step_us[0], 1),
+                                  "median": round(step_us[len(step_us) // 2], 1),
+                                  "max": round(step_us[-1], 1)}
     path["mfma_frac_of_bf16_peak"] = round(path["mfma_tflops_dense_count"] / BF16_MFMA_PEAK_TFLOPS, 4)
     if "ceilings" in rec_extra:
         path["frac_of_copy_ceiling"] = round(path["achieved_GBs"] / rec_extra["ceilings"]["hbm_copy_GBs"], 4)
 
     # ---------------- CPU baseline: the oracle on the headline's inputs ----------------
-    cpu = None
+    cpu, parity = None, None
     if not args.no_cpu:
         import oracle
         x = head.x
@@ -599,10 +643,13 @@ def main():
         reps, ct = 0, 0.0
         while ct < CPU_MIN_SECONDS and reps < 200:
             t1 = time.perf_counter()
-            oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.initial_state, x.cu_seqlens,
-                           num_seqs=x.num_seqs, nthreads=threads)
+            ref = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.initial_state,
+                                 x.cu_seqlens, num_seqs=x.num_seqs, nthreads=threads)
             ct += time.perf_counter() - t1
             reps += 1
+        parity = headline_parity(head, ref)
+        del ref
+        log(f"[bench] parity of the headline against the oracle: {parity}")
         cpu = {"value": round(reps * T / ct, 1), "unit": "tokens/s", "cores": used,
                "kind": "oracle", "cpu_model": cpu_model(),
                "host_threads_available": len(os.sched_getaffinity(0)),
@@ -618,8 +665,13 @@ def main():
            "config": {"workload": workload, "global_batch": head.x.num_seqs, "seq_len": T,
                       "heads": H, "head_dim": 128, "parallelism": "single GPU"},
            "roofline": roofline, "path": path, **rec_extra, "decode": decode, "options": options,
-           "cpu_baseline": cpu}
+           "cpu_baseline": cpu, "parity": parity}
+    if cpu:
+        cpu["gpu_over_oracle"] = round(tok_s / cpu["value"], 1)
     print(json.dumps(rec), flush=True)
+    if parity is not None and not parity["ok"]:
+        log("[bench] the headline's output is outside the parity tolerance")
+        sys.exit(1)
 
 
 if __name__ == "__main__":
