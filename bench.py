@@ -475,6 +475,9 @@ def main():
         c3 = packed.summary(us)
         c3["workload"] = (f"packed varlen prefill, 16 sequences U[256,4096] (T={packed.x.T}), H=32 "
                           f"dk=dv=128 bf16, nonzero fp32 initial states, per-sequence final states")
+        c3["kernel_us"] = {k: round(v, 2) for k, v in packed.kernel_us(10).items()}
+        c3["kernel_us_per_launch"] = {k: [round(v[0], 2), v[1]] for k, v in
+                                      packed.kernel_us(10, per_launch=True).items()}
         print(json.dumps(c3), flush=True)
         return
     if args.backward_only or args.decode_tokens_only:
