@@ -9,6 +9,8 @@
 //                         the sequences in rounds starts the long ones first,
 //                         so that the short ones fill in behind them)
 // Reading cu_seqlens on the device avoids a host synchronisation.
+#include <hip/hip_ext.h>
+
 #include "kda_common.h"
 
 namespace kda {
@@ -105,7 +107,7 @@ hipError_t launch_chunk_table(const int32_t* cu, int64_t T, int N, int32_t* seq_
                               ChunkInfo* chunks, int max_chunks, int32_t* seq_order,
                               hipStream_t stream)
 {
-    hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(TABLE_THREADS), 0, stream, cu, T, N,
+    hipExtLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(TABLE_THREADS), 0, stream, launch_events().start, launch_events().stop, 0, cu, T, N,
                        seq_chunk_start, chunks, max_chunks, seq_order);
     return hipGetLastError();
 }

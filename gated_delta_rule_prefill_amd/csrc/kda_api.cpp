@@ -148,31 +148,42 @@ unsigned pre_flags(uint32_t flags) {
 constexpr int kMaxTimed = 256;
 struct TimingState {
     bool on = false;
-    hipEvent_t ev[kMaxTimed + 1] = {};
+    hipEvent_t ev[2 * kMaxTimed] = {};   // start and stop of each timed kernel
     const char* names[kMaxTimed] = {};
     int n_timed = -1;
 };
 thread_local TimingState t_timing;
+thread_local kda::LaunchEvents t_launch;
 
+// Each timed kernel gets its own pair of events, which the launcher hands to
+// hipExtLaunchKernelGGL: they take the kernel's own start and end, so a
+// kernel's time excludes the gap to the work before it.  The events are
+// timing-only (no system-scope fence when one is recorded).
 struct Timer {
     bool on;
     int n = 0;
-    hipStream_t stream;
-    explicit Timer(hipStream_t s) : on(t_timing.on), stream(s) {
+    explicit Timer(hipStream_t) : on(t_timing.on) {
         if (on) {
-            for (int i = 0; i <= kMaxTimed; ++i)
-                if (!t_timing.ev[i] && hipEventCreate(&t_timing.ev[i]) != hipSuccess) on = false;
+            for (int i = 0; i < 2 * kMaxTimed; ++i)
+                if (!t_timing.ev[i] && hipEventCreateWithFlags(&t_timing.ev[i],
+                                                               hipEventDisableSystemFence) != hipSuccess)
+                    on = false;
             t_timing.n_timed = -1;
         }
-        if (on) hipEventRecord(t_timing.ev[0], stream);
     }
+    // before a kernel launch: the launch takes this kernel's events
+    void arm() {
+        if (on && n < kMaxTimed) t_launch = kda::LaunchEvents{t_timing.ev[2 * n], t_timing.ev[2 * n + 1]};
+    }
+    // after it: the kernel's name; the next launch is untimed until armed
     void mark(const char* name) {
+        t_launch = kda::LaunchEvents{};
         if (!on || n >= kMaxTimed) return;
         t_timing.names[n] = name;
-        hipEventRecord(t_timing.ev[n + 1], stream);
         ++n;
     }
     ~Timer() {
+        t_launch = kda::LaunchEvents{};
         if (on) t_timing.n_timed = n;
     }
 };
@@ -315,12 +326,14 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
             Timer timer(stream);
             if (cu_seqlens) {
                 kda::ChunkSrc src{chunks, seq_start, -1, num_seqs, 0, 0, seq_start + num_seqs + 1};
+                timer.arm();
                 st = check_launch(kda::launch_chunk_table(cu_seqlens, total_tokens, num_seqs,
                                                           seq_start, chunks, (int)plan.max_chunks,
                                                           seq_start + num_seqs + 1, stream),
                                   "chunk table kernel", stream);
                 timer.mark("chunk_table");
                 if (st == KDA_OK && total_tokens > 0) {
+                    timer.arm();
                     st = check_launch(kda::launch_prefill_intra(q, k, v, log_alpha, beta, src,
                                                                 (int)plan.max_chunks, H, dk, dv,
                                                                 bf16, pre_flags(flags), ws, stream),
@@ -328,6 +341,7 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
                     timer.mark("prefill_intra");
                 }
                 if (st == KDA_OK) {
+                    timer.arm();
                     st = check_launch(kda::launch_prefill_state(ws, src, initial_state, final_state,
                                                                 o, chunk_states, H, dk, dv, bf16,
                                                                 stream),
@@ -348,7 +362,8 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
                     const bool first = off == 0, last = off + len >= rows;
                     kda::ChunkSrc src{chunks, seq_start, len, num_seqs, rows, off};
                     if (len > 0) {
-                        st = check_launch(kda::launch_prefill_intra(q, k, v, log_alpha, beta, src,
+                        timer.arm();
+                    st = check_launch(kda::launch_prefill_intra(q, k, v, log_alpha, beta, src,
                                                                     (int)plan.max_chunks, H, dk,
                                                                     dv, bf16, pre_flags(flags), ws,
                                                                     stream),
@@ -356,6 +371,7 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
                         timer.mark("prefill_intra");
                     }
                     if (st == KDA_OK) {
+                        timer.arm();
                         st = check_launch(
                             kda::launch_prefill_state(ws, src, first ? initial_state : carry,
                                                       last ? final_state : carry, o, chunk_states,
@@ -611,10 +627,10 @@ kda_status kda_set_kernel_timing(int32_t enabled) {
 int32_t kda_prefill_kernel_times(float* ms, const char** names, int32_t max_kernels) {
     const TimingState& ts = t_timing;
     if (ts.n_timed < 0) return -1;
-    if (hipEventSynchronize(ts.ev[ts.n_timed]) != hipSuccess) return -1;
     for (int i = 0; i < ts.n_timed && i < max_kernels; ++i) {
         float t = 0.f;
-        if (hipEventElapsedTime(&t, ts.ev[i], ts.ev[i + 1]) != hipSuccess) return -1;
+        if (hipEventSynchronize(ts.ev[2 * i + 1]) != hipSuccess) return -1;
+        if (hipEventElapsedTime(&t, ts.ev[2 * i], ts.ev[2 * i + 1]) != hipSuccess) return -1;
         if (ms) ms[i] = t;
         if (names) names[i] = ts.names[i];
     }
@@ -622,3 +638,7 @@ int32_t kda_prefill_kernel_times(float* ms, const char** names, int32_t max_kern
 }
 
 }  // extern "C"
+
+namespace kda {
+LaunchEvents& launch_events() { return t_launch; }
+}  // namespace kda

@@ -7,6 +7,14 @@
 
 namespace kda {
 
+// Events that time the calling thread's next prefill kernel (set by the C ABI
+// while kernel timing is on, both NULL otherwise): the launchers hand them to
+// hipExtLaunchKernelGGL, which records the kernel's own start and end in them.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+
 constexpr int CHUNK = 64;  // tokens per chunk of the chunkwise prefill
 
 // Chunk descriptor produced by the chunk-table kernel.

@@ -26,6 +26,8 @@
 // halves the workgroups (and the CU time) of a chain while each CU moves
 // about 62 KiB per chunk, and it needs 67 KiB of LDS and one wave per SIMD,
 // so an intra-chunk workgroup fits beside it on the same CU.
+#include <hip/hip_ext.h>
+
 #include "kda_common.h"
 
 namespace kda {
@@ -313,8 +315,8 @@ static hipError_t launch_chain2_t(const void* rec, ChunkSrc src, const float* S0
     using C = Chain2Cfg<DV>;
     const int n_pairs = src.N * H;
     const long long blocks = (long long)((n_pairs + 7) / 8) * 8 * C::NPAIR;
-    hipLaunchKernelGGL((prefill_chain2_kernel<DV>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
-                       stream, (const unsigned char*)rec, src, S0, S_final, (bf16*)o, chunk_states,
+    hipExtLaunchKernelGGL((prefill_chain2_kernel<DV>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
+                       stream, launch_events().start, launch_events().stop, 0, (const unsigned char*)rec, src, S0, S_final, (bf16*)o, chunk_states,
                        H, n_pairs);
     return hipGetLastError();
 }

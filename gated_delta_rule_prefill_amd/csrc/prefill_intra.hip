@@ -42,6 +42,8 @@
 // Row factors e^{g_r - B_R} and cross-block factors e^{B_R - B_I} are <= 1;
 // only the within-block factor e^{B_I - g_i} exceeds 1, bounded by the decay
 // of at most 16 tokens.
+#include <hip/hip_ext.h>
+
 #include "kda_common.h"
 
 namespace kda {
@@ -813,13 +815,13 @@ static hipError_t launch_intra_t(const void* q, const void* k, const void* v, co
 {
     const int beta_logit = (flags & PRE_BETA_LOGIT) ? 1 : 0;
     if (flags & PRE_L2NORM_QK)
-        hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, true>), dim3(max_chunks * H), dim3(64 * INTRA_WAVES), 0,
-                           stream, (const E*)q, (const E*)k, (const E*)v, la, beta, src, H,
-                           beta_logit, (unsigned char*)rec);
+        hipExtLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, true>), dim3(max_chunks * H), dim3(64 * INTRA_WAVES), 0,
+                           stream, launch_events().start, launch_events().stop, 0, (const E*)q, (const E*)k, (const E*)v, la, beta, src, H,
+                           beta_logit, (unsigned char*)rec, (const E*)nullptr);
     else
-        hipLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, false>), dim3(max_chunks * H), dim3(64 * INTRA_WAVES), 0,
-                           stream, (const E*)q, (const E*)k, (const E*)v, la, beta, src, H,
-                           beta_logit, (unsigned char*)rec);
+        hipExtLaunchKernelGGL((prefill_intra_kernel<E, DK, DV, false>), dim3(max_chunks * H), dim3(64 * INTRA_WAVES), 0,
+                           stream, launch_events().start, launch_events().stop, 0, (const E*)q, (const E*)k, (const E*)v, la, beta, src, H,
+                           beta_logit, (unsigned char*)rec, (const E*)nullptr);
     return hipGetLastError();
 }
 
@@ -828,8 +830,8 @@ hipError_t launch_reverse_records(const void* q, const void* k, const void* v, c
                                   int H, int dk, int dv, void* rec, hipStream_t stream)
 {
     if (dk != 128 || dv != 128) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_intra_kernel<bf16, 128, 128, false, true>), dim3(max_chunks * H),
-                       dim3(64 * INTRA_WAVES), 0, stream, (const bf16*)q, (const bf16*)k,
+    hipExtLaunchKernelGGL((prefill_intra_kernel<bf16, 128, 128, false, true>), dim3(max_chunks * H),
+                       dim3(64 * INTRA_WAVES), 0, stream, launch_events().start, launch_events().stop, 0, (const bf16*)q, (const bf16*)k,
                        (const bf16*)v, la, beta, src, H, 0, (unsigned char*)rec,
                        (const bf16*)d_o);
     return hipGetLastError();

@@ -25,6 +25,8 @@
 // Every product takes the state straight from its accumulator tiles: a 16x16
 // tile gives lane group g rows 4g..4g+3, the slot set that the perm32 column
 // order of PM and QM matches.
+#include <hip/hip_ext.h>
+
 #include "kda_common.h"
 
 namespace kda {
@@ -751,8 +753,8 @@ static hipError_t launch_state_ring(const void* rec, ChunkSrc src, const float* 
     const int n_pairs = src.N * H;
     const int groups = (n_pairs + 7) / 8;
     const long long blocks = (long long)groups * 8 * C::NSL;
-    hipLaunchKernelGGL((prefill_state_ring_kernel<E, DK, DV>), dim3((unsigned)blocks),
-                       dim3(64 * C::WAVES), 0, stream, (const unsigned char*)rec, src, S0, S_final,
+    hipExtLaunchKernelGGL((prefill_state_ring_kernel<E, DK, DV>), dim3((unsigned)blocks),
+                       dim3(64 * C::WAVES), 0, stream, launch_events().start, launch_events().stop, 0, (const unsigned char*)rec, src, S0, S_final,
                        (E*)o, chunk_states, H, n_pairs, 0);
     return hipGetLastError();
 }
@@ -765,8 +767,8 @@ hipError_t launch_reverse_chain(const void* rec, ChunkSrc src, const float* dS_l
     using C = RingCfg<bf16, 128, 128>;
     const int n_pairs = src.N * H;
     const long long blocks = (long long)((n_pairs + 7) / 8) * 8 * C::NSL;
-    hipLaunchKernelGGL((prefill_state_ring_kernel<bf16, 128, 128>), dim3((unsigned)blocks),
-                       dim3(64 * C::WAVES), 0, stream, (const unsigned char*)rec, src, dS_last,
+    hipExtLaunchKernelGGL((prefill_state_ring_kernel<bf16, 128, 128>), dim3((unsigned)blocks),
+                       dim3(64 * C::WAVES), 0, stream, launch_events().start, launch_events().stop, 0, (const unsigned char*)rec, src, dS_last,
                        dS_first, (bf16*)nullptr, (float*)dS_chunks, H, n_pairs, 1);
     return hipGetLastError();
 }
@@ -778,8 +780,8 @@ static hipError_t launch_state_t(const void* rec, ChunkSrc src, const float* S0,
     const int n_pairs = src.N * H;
     const int groups = (n_pairs + 7) / 8;
     const long long blocks = (long long)groups * 8 * (DV / 16);
-    hipLaunchKernelGGL((prefill_state_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(256), 0,
-                       stream, (const unsigned char*)rec, src, S0, S_final, (E*)o, chunk_states, H,
+    hipExtLaunchKernelGGL((prefill_state_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, launch_events().start, launch_events().stop, 0, (const unsigned char*)rec, src, S0, S_final, (E*)o, chunk_states, H,
                        n_pairs);
     return hipGetLastError();
 }

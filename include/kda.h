@@ -279,8 +279,10 @@ int32_t kda_version(void);
 /*
  * Kernel timing for measurement (not needed for normal use), per calling
  * thread.  While enabled on a thread, kda_prefill called from that thread
- * records a HIP event before and after each of its kernels on its stream
- * (the events are created on first use and kept until the process ends).
+ * has each of its kernels record its own start and end in a pair of HIP
+ * events (hipExtLaunchKernelGGL; timing-only events without a system-scope
+ * fence, created on first use and kept until the process ends), so a
+ * kernel's time excludes the gap to the work queued before it.
  * kda_prefill_kernel_times() waits for the events of the last call timed on
  * the calling thread and writes, for up to max_kernels kernels in launch
  * order, the elapsed milliseconds (ms) and a static kernel name (names, may
