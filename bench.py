@@ -10,9 +10,11 @@ q/k/v, fp32 log_alpha/beta/state, log_alpha = logsigmoid(N(4, 1))):
              device synchronisation;
   roofline   the dominant prefill kernel (most time per step) against the
              8 TB/s HBM peak: its algorithmic bytes per launch over its average
-             launch duration, from HIP events the library records on the
-             stream it launches on; traffic from rocprofv3 counters when the
-             committed measurement matches the current kernel sources;
+             launch duration, from HIP events each kernel records at its own
+             start and end (the library's kernel timing); traffic from
+             rocprofv3 counters when the committed measurement matches the
+             current kernel sources, and the rate of that traffic against the
+             copy ceilings;
   path       the whole step against its HBM roofline (1540 B per token-head
              plus the final state) from the wall clock, and the MFMA rate at
              the dense-tile flop count;
@@ -181,8 +183,8 @@ class Prefill:
         return e0.elapsed_time(e1) * 1e3 / reps
 
     def kernel_us(self, reps, per_launch=False):
-        """Time of each kernel per step (HIP events recorded by the library around
-        each kernel on its stream); with per_launch, (average us per launch,
+        """Time of each kernel per step (HIP events each kernel records at its own
+        start and end); with per_launch, (average us per launch,
         launches per step) instead: a long batch runs its kernels per segment."""
         self.kdalib.set_kernel_timing(True)
         sums, counts = {}, {}
